@@ -1,0 +1,27 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built libdsa.so")
+    config.addinivalue_line("markers", "slow: long-running (large workload) test")
+
+
+def pytest_collection_modifyitems(config, items):
+    # GPU tests at the end, large ones last, so a quick failure shows first.
+    def key(item):
+        return (1 if item.get_closest_marker("gpu") else 0,
+                1 if item.get_closest_marker("slow") else 0)
+    items.sort(key=key)
+
+
+@pytest.fixture(scope="session")
+def gpu_available():
+    import torch
+    return torch.cuda.is_available()

@@ -1,0 +1,383 @@
+"""Pins of the CPU oracle against things other than itself (no GPU).
+
+Method source: SkyRL blog "Scaling Training to 1M Token Context on
+GLM-5.3-Flash" -- section "DeepSeek Sparse Attention (DSA) Optimizations"
+(score every earlier pool of 4 tokens, attend only to the selected tokens),
+"Making Sparse Attention Actually Sparse" (2,051 keys), "Over Time: Chunking"
+(fp32 scores) and "Across GPUs: Sharding" (int32 pool ids).  The page prints
+no worked example, so the pins are: hand-derived closed forms on tiny inputs,
+published number-format definitions (bfloat16, OCP E4M3) checked against
+torch's own casts, brute force by a different route (tests/brute.py), the
+special case that reduces to dense masked attention (torch SDPA), and
+invariants.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from long_context_sparse_dsa_amd import inputs
+import brute
+
+
+def bf(x):
+    return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- formats
+
+def test_bf16_decode_known_patterns():
+    assert oracle.bf16_value(0x3F80) == 1.0
+    assert oracle.bf16_value(0xC000) == -2.0
+    assert oracle.bf16_value(0x3E00) == 0.125
+    assert oracle.bf16_value(0x0001) == 2.0 ** -133          # smallest subnormal
+    assert oracle.bf16_value(0x7F7F) == (2 - 2 ** -7) * 2.0 ** 127
+    assert oracle.bf16_value(0x8000) == 0.0 and math.copysign(1, oracle.bf16_value(0x8000)) < 0
+
+
+def test_bf16_decode_matches_torch_on_all_finite_patterns():
+    bits = np.arange(0, 1 << 16, 97, dtype=np.uint16)
+    t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    for b, ref in zip(bits, t):
+        v = oracle.bf16_value(int(b))
+        if np.isnan(ref):
+            assert np.isnan(v)
+        else:
+            assert v == ref
+
+
+def test_e4m3_table_values_from_the_ocp_definition():
+    assert oracle.e4m3_value(0x38) == 1.0             # exponent 7 = bias
+    assert oracle.e4m3_value(0x7E) == 448.0           # largest finite
+    assert oracle.e4m3_value(0xFE) == -448.0
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6       # smallest normal
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9       # smallest subnormal
+    assert oracle.e4m3_value(0x07) == 7 * 2.0 ** -9
+    assert math.isnan(oracle.e4m3_value(0x7F))
+    assert math.isnan(oracle.e4m3_value(0xFF))
+
+
+def test_e4m3_decode_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c, r in zip(codes, ref):
+        v = oracle.e4m3_value(int(c))
+        assert (np.isnan(v) and np.isnan(r)) or v == r
+
+
+def test_e4m3_encode_ties_and_saturation():
+    assert oracle.e4m3_encode(1.0) == 0x38
+    assert oracle.e4m3_encode(1.0625) == 0x38          # tie between 1.0 and 1.125 -> even
+    assert oracle.e4m3_encode(1.1875) == 0x3A          # tie between 1.125 and 1.25 -> even
+    assert oracle.e4m3_encode(2.0 ** -10) == 0x00      # tie between 0 and 2^-9 -> 0
+    assert oracle.e4m3_encode(3 * 2.0 ** -10) == 0x02  # tie between 2^-9 and 2^-8 -> even
+    assert oracle.e4m3_encode(460.0) == 0x7E           # saturates
+    assert oracle.e4m3_encode(-1e6) == 0xFE
+    assert oracle.e4m3_encode(-1.0) == 0xB8
+
+
+def test_e4m3_encode_matches_torch_cast_in_range():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(4000) * s for s in (1e-3, 0.05, 1.0, 30.0, 150.0)])
+    x = x[np.abs(x) <= 448.0]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(float(v)) for v in x], dtype=np.uint8)
+    # torch may keep the sign of an underflow to zero; compare values
+    gv = np.array([oracle.e4m3_value(int(c)) for c in got])
+    rv = torch.from_numpy(ref).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(gv, rv)
+
+
+# ---------------------------------------------------------------- hand example
+
+# Three pools of 4 tokens, D_I = 2, H_I = 2.
+#   pool 0 rows [1,0],[2,0],[3,0],[2,4]    -> kbar0 = [2, 1]
+#   pool 1 rows [0,1],[0,1],[-4,1],[0,1]   -> kbar1 = [-1, 1]
+#   pool 2 rows [1,-2] x 4                 -> kbar2 = [1, -2]
+# Query heads h0 = [1, 1], h1 = [0.5, -1].
+#   dots h0: [3, 0, -1]; h1: [0, -1.5, 2.5]
+# w = [1, 2]:  s = [1*3 + 2*0, 0 + 0, 0 + 2*2.5] = [3, 0, 5]
+# w = [1, -1]: s = [3, 0, -2.5]
+HAND_K = [[1, 0], [2, 0], [3, 0], [2, 4],
+          [0, 1], [0, 1], [-4, 1], [0, 1],
+          [1, -2], [1, -2], [1, -2], [1, -2]]
+HAND_Q = [[1, 1], [0.5, -1]]
+
+
+def _hand(q_pos_list, w):
+    k = bf(HAND_K)
+    q = bf([HAND_Q] * len(q_pos_list))
+    return q, k, torch.tensor(w, dtype=torch.float32)
+
+
+def test_hand_pooled_keys():
+    kbar = oracle.pool_keys(bf(HAND_K))
+    assert np.array_equal(kbar, [[2, 1], [-1, 1], [1, -2]])
+
+
+def test_hand_scores_and_causality():
+    # one query per position; rows map to positions q_pos0 + row
+    q, k, w = _hand(range(13), [1.0, 2.0])
+    s = oracle.index_scores(q, k, w, q_pos0=0)
+    inf = -np.inf
+    expect = {0: [inf, inf, inf], 3: [inf, inf, inf],      # no complete pool before t
+              4: [3, inf, inf], 7: [3, inf, inf],          # pool 1 holds token 7 itself
+              8: [3, 0, inf], 11: [3, 0, inf],
+              12: [3, 0, 5]}
+    for t, e in expect.items():
+        assert np.array_equal(s[t], np.array(e, dtype=np.float32)), (t, s[t])
+
+
+def test_hand_scores_negative_weight_applies_after_relu():
+    q, k, w = _hand([12], [1.0, -1.0])
+    s = oracle.index_scores(q, k, w, q_pos0=12)
+    assert np.array_equal(s[0], np.array([3, 0, -2.5], dtype=np.float32))
+
+
+def test_hand_topk():
+    q, k, w = _hand(range(13), [1.0, 2.0])
+    idx, sc = oracle.index_topk(q, k, w, k_pools=2, q_pos0=0)
+    assert idx[12].tolist() == [0, 2] and sc[12].tolist() == [3.0, 5.0]
+    assert idx[8].tolist() == [0, 1]             # n(t) <= k: every eligible pool
+    assert idx[5].tolist() == [0, -1]
+    assert idx[2].tolist() == [-1, -1] and np.all(np.isneginf(sc[2]))
+    idx1, _ = oracle.index_topk(q, k, w, k_pools=1, q_pos0=0)
+    assert idx1[12].tolist() == [2] and idx1[9].tolist() == [0]
+
+
+def test_hand_q_pos0_offsets_positions():
+    q, k, w = _hand([12], [1.0, 2.0])
+    s = oracle.index_scores(q, k, w, q_pos0=12)
+    assert np.array_equal(s[0], np.array([3, 0, 5], dtype=np.float32))
+    s = oracle.index_scores(q, k, w, q_pos0=9)
+    assert np.array_equal(s[0], np.array([3, 0, -np.inf], dtype=np.float32))
+
+
+# ---------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("s,h_idx,d_idx,k_pools,w_per_query,q_pos0", [
+    (8, 4, 64, 1, False, 0), (13, 4, 64, 2, False, 0), (64, 8, 32, 4, True, 0),
+    (256, 32, 128, 16, False, 0), (301, 4, 96, 8, True, 40),
+])
+def test_scores_and_selection_match_brute_force(s, h_idx, d_idx, k_pools, w_per_query, q_pos0):
+    wl = inputs.custom(s_q=s - q_pos0 if q_pos0 else s, s_k=s, q_pos0=q_pos0, h_idx=h_idx,
+                       d_idx=d_idx, k_pools=k_pools, idx_std=0.125)
+    x = inputs.make_inputs(wl, seed=11 + s, attention=False, w_per_query=w_per_query)
+    got = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=q_pos0)
+    ref = brute.raw_token_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=q_pos0)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(got))
+    # the two fp64 roads differ only by summation order: at most 1 fp32 ulp
+    assert np.all(np.abs(got[fin] - ref[fin]) <= np.spacing(np.abs(ref[fin])) + 1e-30)
+    idx, sc = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], k_pools, q_pos0=q_pos0)
+    for r in range(wl.s_q):
+        n = min((q_pos0 + r) // 4, wl.n_pools)
+        expect = brute.rank_select(got[r], n, k_pools)
+        assert np.array_equal(idx[r], expect), r
+        sel = idx[r][idx[r] >= 0]
+        assert np.array_equal(sc[r][: len(sel)], got[r][sel])
+
+
+def test_all_zero_weights_select_lowest_ids():
+    wl = inputs.custom(s_q=64, s_k=64, h_idx=4, d_idx=64, k_pools=3)
+    x = inputs.make_inputs(wl, seed=3, attention=False)
+    w = torch.zeros(4)
+    idx, sc = oracle.index_topk(x["q_idx"], x["k_idx"], w, 3)
+    assert idx[63].tolist() == [0, 1, 2] and np.all(sc[63] == 0)
+    assert np.all(np.signbit(sc[63]) == False)  # +0, never -0
+
+
+def test_duplicate_pools_tie_to_lower_index():
+    wl = inputs.custom(s_q=40, s_k=40, h_idx=4, d_idx=64, k_pools=2)
+    x = inputs.make_inputs(wl, seed=5, attention=False)
+    s = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], rows=[39])[0]
+    best = int(np.argmax(s))
+    k = x["k_idx"].clone()
+    k[8:12] = x["k_idx"][4 * best: 4 * best + 4]    # pools 2 and 7 copy the best pool
+    k[28:32] = x["k_idx"][4 * best: 4 * best + 4]
+    s = oracle.index_scores(x["q_idx"], k, x["w"], rows=[39])[0]
+    assert s[2] == s[7] == s.max()
+    ties = [p for p in range(9) if s[p] == s.max()]
+    idx, _ = oracle.index_topk(x["q_idx"], k, x["w"], 1, rows=[39])
+    assert idx[0].tolist() == [ties[0]] and ties[0] <= 2
+    idx, _ = oracle.index_topk(x["q_idx"], k, x["w"], len(ties), rows=[39])
+    assert idx[0].tolist() == ties
+
+
+def test_metamorphic_scaling_and_head_permutation():
+    wl = inputs.custom(s_q=200, s_k=200, h_idx=8, d_idx=64, k_pools=8)
+    x = inputs.make_inputs(wl, seed=9, attention=False)
+    rows = [50, 123, 199]
+    s0 = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], rows=rows)
+    s2 = oracle.index_scores(x["q_idx"], x["k_idx"], 2 * x["w"], rows=rows)
+    assert np.array_equal(np.where(np.isfinite(s0), 2 * s0, s0), s2)
+    q2 = (x["q_idx"].float() * 2).to(torch.bfloat16)
+    s2q = oracle.index_scores(q2, x["k_idx"], x["w"], rows=rows)
+    assert np.array_equal(s2q, s2)
+    perm = torch.randperm(8, generator=torch.Generator().manual_seed(1))
+    sp = oracle.index_scores(x["q_idx"][:, perm], x["k_idx"], x["w"][perm], rows=rows)
+    fin = np.isfinite(s0)
+    assert np.all(np.abs(sp[fin] - s0[fin]) <= np.spacing(np.abs(s0[fin])))
+    i0, _ = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], 8, rows=rows)
+    i2, _ = oracle.index_topk(x["q_idx"], x["k_idx"], 2 * x["w"], 8, rows=rows)
+    assert np.array_equal(i0, i2)
+
+
+def test_selection_is_strictly_causal_and_ascending():
+    wl = inputs.custom(s_q=500, s_k=500, h_idx=4, d_idx=64, k_pools=16)
+    x = inputs.make_inputs(wl, seed=21, attention=False)
+    idx, _ = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], 16)
+    for t in range(500):
+        row = idx[t]
+        v = row[row >= 0]
+        assert np.all(4 * v + 3 < t)
+        assert np.all(np.diff(v) > 0)
+        assert np.all(row[len(v):] == -1)
+        assert len(v) == min(t // 4, 16)
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn_case(s, h=4, d=32, dv=None, q_pos0=0, seed=0):
+    wl = inputs.custom(s_q=s - q_pos0, s_k=s, q_pos0=q_pos0, h=h, d=d, dv=dv, h_idx=4, d_idx=32,
+                       k_pools=4)
+    return wl, inputs.make_inputs(wl, seed=seed, indexer=False)
+
+
+@pytest.mark.parametrize("n_tail", [0, 3])
+def test_attention_with_every_pool_equals_dense_masked_attention(n_tail):
+    wl, x = _attn_case(67, h=4, d=32, dv=48, seed=1)
+    P = wl.n_pools
+    rows = np.arange(wl.s_q)
+    idx = np.full((len(rows), P), -1, dtype=np.int32)
+    for r in rows:
+        n = min(r // 4, P)
+        idx[r, :n] = np.arange(n)
+    scale = float(np.float32(1 / math.sqrt(32)))
+    o, lse = oracle.sparse_attn(x["q"], x["k"], x["v"], idx, P, rows=rows, n_tail=n_tail,
+                                scale=scale)
+    ro, rlse = brute.dense_attention(x["q"], x["k"], x["v"], 0, rows, n_tail == 3, scale)
+    for r in rows:
+        visible = r if n_tail == 3 else 4 * (r // 4)
+        if visible == 0:
+            assert np.all(o[r] == 0) and np.all(np.isneginf(lse[r]))
+        else:
+            np.testing.assert_allclose(o[r], ro[r], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[r], rlse[r], rtol=0, atol=1e-12)
+
+
+def test_attention_partial_tail_lengths():
+    wl, x = _attn_case(40, seed=2)
+    rows = [37, 38, 39]                   # t mod 4 = 1, 2, 3
+    idx = np.array([[0, 3, -1, -1]] * 3, dtype=np.int32)
+    for n_tail, expect in [(1, [9, 9, 9]), (2, [9, 10, 10]), (3, [9, 10, 11])]:
+        counts = [oracle.token_count(idx[i:i + 1], 0, 40, 4, [r], n_tail) for i, r in enumerate(rows)]
+        assert counts == expect
+    # the tail tokens are the ones right before t: compare with an explicit set
+    o, _ = oracle.sparse_attn(x["q"], x["k"], x["v"], idx, 4, rows=rows, n_tail=2, scale=0.25)
+    q = x["q"].double(); k = x["k"].double(); v = x["v"].double()
+    for i, r in enumerate(rows):
+        toks = [0, 1, 2, 3, 12, 13, 14, 15] + list(range(max(36, r - 2), r))
+        lg = (q[r] @ k[toks].T) * 0.25
+        ref = torch.softmax(lg, dim=-1) @ v[toks]
+        np.testing.assert_allclose(o[i], ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    wl, x = _attn_case(64, h=2, d=32, seed=3)
+    rows = [40, 63]
+    idx = np.array([[1, 4, 6, -1], [0, 2, 9, 14]], dtype=np.int32)
+    # all value rows equal c  ->  o = c
+    v = torch.full_like(x["v"], 0.375)
+    o, _ = oracle.sparse_attn(x["q"], x["k"], v, idx, 4, rows=rows)
+    np.testing.assert_allclose(o, 0.375, rtol=1e-14, atol=0)
+    # all key rows equal  ->  uniform weights, o = mean of v over T(t)
+    k = x["k"][:1].expand_as(x["k"]).contiguous()
+    o, lse = oracle.sparse_attn(x["q"], k, x["v"], idx, 4, rows=rows)
+    vd = x["v"].double().numpy()
+    for i, row in enumerate(idx):
+        toks = [4 * p + u for p in row if p >= 0 for u in range(4)]
+        np.testing.assert_allclose(o[i], np.broadcast_to(vd[toks].mean(0), o[i].shape),
+                                   rtol=0, atol=1e-13)
+        # o lies inside the per-column range of v over T(t)
+    o, _ = oracle.sparse_attn(x["q"], x["k"], x["v"], idx, 4, rows=rows)
+    for i, row in enumerate(idx):
+        toks = [4 * p + u for p in row if p >= 0 for u in range(4)]
+        assert np.all(o[i] >= vd[toks].min(0) - 1e-12) and np.all(o[i] <= vd[toks].max(0) + 1e-12)
+
+
+def test_attention_rejects_malformed_index_rows():
+    wl, x = _attn_case(64, seed=4)
+    for bad in ([3, 1, -1, -1],       # not ascending
+                [0, 0, -1, -1],       # duplicate
+                [0, -1, 2, -1],       # id after padding
+                [0, 15, -1, -1],      # pool 15 holds tokens 60..63 >= t
+                [-2, -1, -1, -1]):
+        with pytest.raises(RuntimeError):
+            oracle.sparse_attn(x["q"], x["k"], x["v"], np.array([bad], dtype=np.int32), 4,
+                               rows=[60])
+
+
+# ---------------------------------------------------------------- fp8 indexer
+
+def _fp8(vals):
+    return torch.tensor(vals, dtype=torch.float32).to(torch.float8_e4m3fn)
+
+
+def test_fp8_pool_requantisation_hand_example():
+    # pool rows [1, 2], [1, 2], [1, 2], [1, 2.5]: mean [1, 2.125]; amax 2.125
+    # smallest e with 2.125 <= 448 * 2^e is e = -7; scaled mean [128, 272];
+    # 272 lies halfway between 256 and 288 -> ties to even -> 256.
+    k8 = _fp8([[1, 2], [1, 2], [1, 2], [1, 2.5]])
+    codes, exps = oracle.pool_keys_fp8(k8)
+    assert exps.tolist() == [-7]
+    assert [oracle.e4m3_value(int(c)) for c in codes[0]] == [128.0, 256.0]
+
+
+@pytest.mark.parametrize("amax,e", [(448.0, 0), (224.0, -1), (240.0, 0), (0.5, -9), (0.0, 0)])
+def test_fp8_pool_exponent_rule(amax, e):
+    row = [amax, -amax / 2]
+    k8 = _fp8([row] * 4)
+    assert oracle.e4m3_value(int(k8.view(torch.uint8)[0, 0])) == amax   # exact in E4M3
+    _, exps = oracle.pool_keys_fp8(k8)
+    assert exps.tolist() == [e]
+
+
+def test_fp8_scores_hand_example():
+    # pool 0 = HAND pool with E4M3-exact values; q heads in E4M3 too
+    k8 = _fp8(HAND_K)
+    q8 = _fp8([HAND_Q])
+    w = torch.tensor([1.0, 2.0])
+    codes, exps = oracle.pool_keys_fp8(k8)
+    kb = np.array([[oracle.e4m3_value(int(c)) for c in row] for row in codes]) * \
+        np.exp2(exps.astype(np.float64))[:, None]
+    assert np.array_equal(kb, [[2, 1], [-1, 1], [1, -2]])     # these means are E4M3-exact
+    s = oracle.index_scores_fp8(q8, k8, w, q_scale=0.5, k_scale=4.0, q_pos0=12)
+    assert np.array_equal(s[0], np.array([6, 0, 10], dtype=np.float32))   # 2x the bf16 case
+
+
+def test_fp8_scores_close_to_exact_scores():
+    wl = inputs.custom(s_q=300, s_k=300, h_idx=8, d_idx=96, k_pools=8, fp8=True)
+    x = inputs.make_inputs(wl, seed=17, attention=False)
+    rows = [150, 299]
+    s8 = oracle.index_scores_fp8(x["q_idx8"], x["k_idx8"], x["w"], rows=rows)
+    qd = x["q_idx8"].float().to(torch.bfloat16)   # E4M3 values are bf16-exact
+    kd = x["k_idx8"].float().to(torch.bfloat16)
+    s = oracle.index_scores(qd, kd, x["w"], rows=rows)
+    fin = np.isfinite(s)
+    # re-quantising the pooled key costs ~ 2^-4 relative per element
+    err = np.abs(s8[fin] - s[fin]) / (np.abs(s[fin]).max())
+    assert err.max() < 0.06
+
+
+# ---------------------------------------------------------------- memory model
+
+def test_unchunked_indexer_memory_matches_the_page():
+    # section "Over Time: Chunking": 64 GiB at 32k, about 1 TiB at 128k for the
+    # unchunked score buffer.  Both equal 2 copies x 4 B x S x S/4 x 32 heads.
+    def unchunked(s):
+        return 2 * 4 * s * (s // 4) * 32
+    assert unchunked(32768) == 64 * 2 ** 30
+    assert unchunked(131072) == 2 ** 40
