@@ -1,0 +1,192 @@
+"""Throughput of the DSA forward path on one MI355X.
+
+A step is one pass of the whole path over one sequence's queries: pool the
+indexer keys, score every query against every earlier pool in query chunks,
+keep the top-k pools per query (int32 ids), and run sparse attention over
+the kept tokens.  Inputs are seeded synthetic tensors resident in HBM before
+the timed region (the page's own throughput runs used random tokens and
+random-initialised weights).
+
+Prints one JSON line: queries/s for the whole path, TFLOP/s of the
+algorithmic work, the roofline of the dominant kernel (from HIP events around
+every launch inside the timed region), and the CPU oracle timed on a bounded
+sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "DSA fwd queries/sec at S=128k (indexer+topk+attn); TFLOP/s vs MFMA peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def work_counts(wl):
+    """Algorithmic work of one step (closed forms over the query positions)."""
+    t = wl.q_pos0 + np.arange(wl.s_q, dtype=np.int64)
+    n = np.minimum(t // 4, wl.n_pools)
+    pairs = int(n.sum())
+    kept = np.minimum(n, wl.k_pools)
+    tail = np.minimum(wl.n_tail, t % 4) if wl.n_tail else np.zeros_like(t)
+    if wl.n_tail:
+        tail = np.where(t - 1 < wl.s_k, tail, 0)
+    tokens = int((4 * kept + tail).sum())
+    f_score = 2.0 * wl.h_idx * wl.d_idx * pairs
+    f_attn = 2.0 * wl.h * (wl.d + wl.dv) * tokens
+    b_attn = (tokens * (wl.d + wl.dv) * 2 + wl.s_q * wl.h * (wl.d + wl.dv) * 2
+              + wl.s_q * wl.k_pools * 4)
+    b_select = pairs * 4 + wl.s_q * wl.k_pools * 4
+    b_pool = wl.n_pools * 4 * wl.d_idx * 2 + wl.n_pools * 4 * wl.d_idx * 2
+    return dict(pairs=pairs, tokens=tokens, f_score=f_score, f_attn=f_attn, b_attn=b_attn,
+                b_select=b_select, b_pool=b_pool)
+
+
+def cpu_baseline(wl, x, target_s: float):
+    """The oracle as it stands, on a strided sample of query rows."""
+    from oracle import oracle
+    threads = os.cpu_count() or 1
+
+    def run(rows):
+        t0 = time.perf_counter()
+        idx, _ = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], wl.k_pools, q_pos0=wl.q_pos0,
+                                   rows=rows)
+        oracle.sparse_attn(x["q"], x["k"], x["v"], idx, wl.k_pools, q_pos0=wl.q_pos0, rows=rows,
+                           n_tail=wl.n_tail, scale=float(np.float32(1 / math.sqrt(wl.d))))
+        return time.perf_counter() - t0
+
+    def strided(r):
+        return np.linspace(0, wl.s_q - 1, r).round().astype(np.int64)
+
+    probe = max(threads, 8)
+    t_probe = run(strided(probe))
+    r = int(max(probe, min(wl.s_q, probe * target_s / max(t_probe, 1e-3))))
+    rows = strided(r)
+    t = run(rows)
+    return {"value": r / t, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{r} query rows evenly spaced over the {wl.s_q} queries of {wl.name} "
+                      f"(pooling of all keys included), {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="s128k")
+    ap.add_argument("--chunk-q", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_sparse_dsa_amd import dsa, inputs
+
+    wl = inputs.WORKLOADS[args.workload]
+    dsa.load_library()
+    dev = torch.device("cuda")
+    log(f"workload {wl}")
+    t0 = time.time()
+    x = inputs.make_inputs(wl)
+    log(f"inputs generated in {time.time() - t0:.1f} s")
+    g = {k: v.to(dev) for k, v in x.items() if not k.endswith("8")}
+    ws_bytes, chunk_q = dsa.dsa_index_workspace_size(wl.s_q, wl.s_k, wl.h_idx, wl.d_idx,
+                                                     wl.k_pools, 4, args.chunk_q)
+    ws = dsa.new_workspace(ws_bytes, dev)
+    idx = torch.empty((wl.s_q, wl.k_pools), dtype=torch.int32, device=dev)
+    out = torch.empty((wl.s_q, wl.h, wl.dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dsa.dsa_index_score_topk(g["q_idx"], g["k_idx"], g["w"], wl.k_pools, q_pos0=wl.q_pos0,
+                                 chunk_q=chunk_q, idx_out=idx, workspace=ws, stream=stream)
+        dsa.dsa_sparse_attn_fwd(g["q"], g["k"], g["v"], idx, q_pos0=wl.q_pos0,
+                                n_tail=wl.n_tail, out=out, stream=stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    dsa.dsa_profile_read()
+    dsa.dsa_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dsa.dsa_profile_enable(False)
+    stats = dsa.dsa_profile_read()
+    ms = (t1 - t0) * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step; kernels {stats}")
+
+    w = work_counts(wl)
+    qps = wl.s_q / (ms / 1e3)
+    tflops = (w["f_score"] + w["f_attn"]) / (ms / 1e3) / 1e12
+    stages = {}
+    for name, (launches, total) in stats.items():
+        stages[name] = {"ms_per_step": total / args.steps, "launches_per_step": launches / args.steps}
+    rl = {}
+    for name, (launches, total) in stats.items():
+        t_s = total / 1e3
+        if name == "index_score":
+            a = w["f_score"] * args.steps / t_s / 1e12
+            rl[name] = {"bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS, "traffic": None}
+        elif name == "sparse_attn":
+            a = w["b_attn"] * args.steps / t_s / 1e9
+            rl[name] = {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": a / PEAK_HBM_GBS, "traffic": None}
+        elif name == "topk_select":
+            a = w["b_select"] * args.steps / t_s / 1e9
+            rl[name] = {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": a / PEAK_HBM_GBS, "traffic": None}
+        elif name == "pool_keys":
+            a = w["b_pool"] * args.steps / t_s / 1e9
+            rl[name] = {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": a / PEAK_HBM_GBS, "traffic": None}
+        stages[name].update(rl.get(name, {}))
+    dominant = max(stats, key=lambda k: stats[k][1]) if stats else None
+
+    result = {
+        "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "s_q": wl.s_q, "s_k": wl.s_k, "q_pos0": wl.q_pos0,
+                   "indexer": f"{wl.h_idx}x{wl.d_idx}", "pool": 4, "k_pools": wl.k_pools,
+                   "attention": f"{wl.h}x{wl.d}", "kv_heads": 1, "n_tail": wl.n_tail,
+                   "chunk_q": chunk_q},
+        "tflops": tflops, "tflops_frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "roofline": dict(rl[dominant], kernel=dominant) if dominant in rl else None,
+        "stages": stages,
+        "work": {"pairs": w["pairs"], "tokens": w["tokens"], "f_score": w["f_score"],
+                 "f_attn": w["f_attn"], "b_attn": w["b_attn"], "b_select": w["b_select"]},
+        "peak_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

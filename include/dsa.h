@@ -1,0 +1,171 @@
+/*
+ * dsa.h -- C ABI of libdsa, the MI355X (gfx950) DeepSeek Sparse Attention
+ * (DSA) forward path.
+ *
+ * The method (SkyRL blog, "Scaling Training to 1M Token Context on
+ * GLM-5.3-Flash"):
+ *   section "DeepSeek Sparse Attention (DSA) Optimizations" -- a lightweight
+ *     indexer scores every query against every earlier pool of 4 tokens and
+ *     keeps the best pools, so that attention reads only 2048 tokens
+ *     (512 pools x 4);
+ *   section "Making Sparse Attention Actually Sparse" -- NoPE heads are
+ *     narrower than the rotary shapes and the pooled selection can return
+ *     2,051 keys; unsupported shapes must not silently fall back to dense;
+ *   section "Splitting the DSA Indexer / Over Time: Chunking" -- score and
+ *     select a few hundred queries at a time so indexer memory is constant;
+ *   section "Across GPUs: Sharding" -- the selected pool ids are small and
+ *     are handed on as int32.
+ * The page prints no score formula; the library computes the standard
+ * lightning-indexer form
+ *     s(t,p) = sum_h w[t,h] * max(0, q_idx[t,h,:] . kbar_p),
+ *     kbar_p = mean of key rows 4p .. 4p+3,
+ * for every pool p with 4p+3 < t (strictly earlier), keeps the k_pools best
+ * (ties to the lower pool id) and attends, with softmax, to the 4 tokens of
+ * each kept pool (plus up to n_tail tokens of t's own unfinished pool that
+ * precede t).
+ *
+ * Conventions for every call:
+ *   - Device pointers are device memory on the current HIP device, 16-byte
+ *     aligned, row-major and contiguous in the shapes given.  The caller owns
+ *     all memory; the library allocates none and keeps no state beyond
+ *     cached device properties, optional profiling events and a per-thread
+ *     error message.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously; DSA_OK means the launches were enqueued.
+ *   - On any error, nothing is launched, outputs are left untouched, and
+ *     dsa_last_error() describes the failure.  No call ever falls back to a
+ *     different algorithm: shapes outside the supported set return
+ *     DSA_ERR_UNSUPPORTED.
+ *   - Results are deterministic: identical inputs give identical outputs,
+ *     bit for bit (no floating-point atomics).
+ *   - Positions: query row i (0 <= i < s_q) sits at sequence position
+ *     t = q_pos0 + i; key row j is position j; P = floor(s_k / 4) pools;
+ *     query t sees n(t) = min(floor(t/4), P) pools.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = 1, /* null pointer, misalignment, negative size, ... */
+    DSA_ERR_UNSUPPORTED = 2, /* a shape outside the supported set */
+    DSA_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+    DSA_ERR_HIP = 4          /* a HIP runtime call failed */
+} dsa_status;
+
+typedef enum {
+    DSA_BF16 = 0,    /* indexer q/k in bfloat16 */
+    DSA_FP8_E4M3 = 1 /* indexer q/k as OCP FP8 E4M3 codes with fp32 scales */
+} dsa_dtype;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int dsa_version(void);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char *dsa_last_error(void);
+
+/*
+ * Bytes of device workspace dsa_index_score_topk / dsa_index_scores need.
+ * Holds the pooled key table (bf16: P x 2*d_idx bf16 as a two-term split;
+ * fp8: P x d_idx codes + P exponents) and the per-chunk fp32 score buffer
+ * of chunk_q x P entries ("Over Time: Chunking": the buffer is constant in
+ * s_q).  chunk_q = 0 picks the library's default for these shapes (the
+ * value is returned through *chunk_q_used when that pointer is non-NULL).
+ * Pure host computation; valid without a GPU.
+ */
+dsa_status dsa_index_workspace_size(int64_t s_q, int64_t s_k, int h_idx, int d_idx,
+                                    int k_pools, int pool_size, int64_t chunk_q, int dtype,
+                                    size_t *bytes, int64_t *chunk_q_used);
+
+/*
+ * Pooling, chunked indexer scoring and top-k selection (sections "DeepSeek
+ * Sparse Attention (DSA) Optimizations", "Over Time: Chunking", "Across
+ * GPUs: Sharding").
+ *   q_idx    [s_q, h_idx, d_idx]   bf16, or E4M3 codes when dtype = DSA_FP8_E4M3
+ *   k_idx    [s_k, d_idx]          bf16, or E4M3 codes
+ *   q_scale, k_scale               fp8 only: device pointers to one fp32 scale
+ *                                  each (NULL = 1.0); must be NULL for bf16
+ *   w        [s_q, h_idx] fp32 with row stride w_stride_q elements
+ *                                  (w_stride_q = 0: one [h_idx] row for all queries)
+ *   pool_size                      must be 4
+ *   k_pools                        pools kept per query, 1 .. 2048
+ *   chunk_q                        queries per chunk (0 = default; a multiple of 64)
+ *   idx_out  [s_q, k_pools] int32  kept pool ids, ascending, padded with -1
+ *                                  when n(t) < k_pools
+ *   score_out [s_q, k_pools] fp32  optional (NULL): the kept pools' scores,
+ *                                  -inf for padding
+ *   workspace                      >= dsa_index_workspace_size(...) bytes
+ * Supported: h_idx in {4, 8, 16, 32}; d_idx in {64, 96, 128}; s_k < 2^31.
+ * The fp32 score of a pool is a +0.0 when zero (never -0.0).
+ */
+dsa_status dsa_index_score_topk(const void *q_idx, const void *k_idx, const float *q_scale,
+                                const float *k_scale, const float *w, int64_t w_stride_q,
+                                int64_t s_q, int64_t s_k, int64_t q_pos0, int h_idx, int d_idx,
+                                int pool_size, int k_pools, int64_t chunk_q, int dtype,
+                                int32_t *idx_out, float *score_out, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
+ * Dense fp32 indexer scores of query rows [row0, row0 + n_rows) against
+ * every pool (testing and inspection): scores_out [n_rows, P], -inf where a
+ * pool is not eligible.  Same arguments and support as dsa_index_score_topk;
+ * the workspace only needs to hold the pooled key table.
+ */
+dsa_status dsa_index_scores(const void *q_idx, const void *k_idx, const float *q_scale,
+                            const float *k_scale, const float *w, int64_t w_stride_q,
+                            int64_t s_q, int64_t s_k, int64_t q_pos0, int h_idx, int d_idx,
+                            int pool_size, int dtype, int64_t row0, int64_t n_rows,
+                            float *scores_out, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
+ * Sparse attention forward over the kept pools (sections "DeepSeek Sparse
+ * Attention (DSA) Optimizations" and "Making Sparse Attention Actually
+ * Sparse"), with an online softmax.
+ *   q    [s_q, h, d]   bf16; h query heads share one key/value head
+ *   k    [s_k, d]      bf16
+ *   v    [s_k, dv]     bf16 (k == v is allowed)
+ *   idx  [s_q, k_pools] int32 pool ids as produced by dsa_index_score_topk;
+ *                      entries < 0 or >= P are skipped
+ *   n_tail             0 .. pool_size-1: also attend to the last
+ *                      min(n_tail, t mod 4) tokens before t (t's own
+ *                      unfinished pool); 3 gives the 2,051-key case
+ *   softmax_scale      logit scale; <= 0 selects 1/sqrt(d)
+ *   out  [s_q, h, dv]  bf16
+ *   lse  [s_q, h]      fp32 natural-log sum-exp of the scaled logits, or NULL
+ * A query with no token gets out = 0 and lse = -inf.
+ * Supported: h in 1 .. 16; d, dv in {64, 96, 128}; pool_size = 4.
+ */
+dsa_status dsa_sparse_attn_fwd(const void *q, const void *k, const void *v, const int32_t *idx,
+                               int64_t s_q, int64_t s_k, int64_t q_pos0, int h, int d, int dv,
+                               int k_pools, int pool_size, int n_tail, float softmax_scale,
+                               void *out, float *lse, void *stream);
+
+/*
+ * Per-kernel GPU timing.  While enabled, every kernel launch is bracketed
+ * by HIP events on its own stream; dsa_profile_read synchronises on those
+ * events and reports, per kernel kind, the number of launches and the summed
+ * duration in milliseconds, then clears the record.  Kinds: "pool_keys",
+ * "index_score", "topk_select", "sparse_attn".
+ */
+typedef struct {
+    char name[32];
+    int64_t launches;
+    double total_ms;
+} dsa_kernel_stat;
+
+dsa_status dsa_profile_enable(int on);
+dsa_status dsa_profile_read(dsa_kernel_stat *stats, int max_stats, int *n_stats);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

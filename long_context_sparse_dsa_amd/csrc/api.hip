@@ -1,0 +1,436 @@
+// C ABI of libdsa: argument checks, workspace layout, the query-chunk loop
+// and per-kernel timing.  Every entry point validates all arguments before
+// enqueuing anything; on failure nothing is launched and dsa_last_error()
+// holds the reason.  There is no fallback path: unsupported shapes are
+// rejected (SkyRL blog "Scaling Training to 1M Token Context on
+// GLM-5.3-Flash", section "Making Sparse Attention Actually Sparse", on how
+// a silent dense fallback looked like a memory problem rather than a bug).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "dsa.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+constexpr int64_t kMaxKPools = 2048;
+constexpr int64_t kDefaultChunk = 256;
+constexpr int64_t kMaxChunk = 1 << 16;
+constexpr int64_t kScoreBufferCap = int64_t(2) << 30;  // per chunk, as the page keeps it
+
+// ------------------------------------------------------------ profiling
+
+enum Kind { K_POOL = 0, K_SCORE, K_SELECT, K_ATTN, K_COUNT };
+const char* kKindName[K_COUNT] = {"pool_keys", "index_score", "topk_select", "sparse_attn"};
+
+struct Rec {
+    int kind;
+    hipEvent_t a, b;
+};
+
+struct Prof {
+    std::mutex mu;
+    bool on = false;
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> pool;
+} g_prof;
+
+hipEvent_t take_event() {
+    if (!g_prof.pool.empty()) {
+        hipEvent_t e = g_prof.pool.back();
+        g_prof.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Brackets one launch with events when profiling is on.
+struct Timed {
+    int kind;
+    hipStream_t s;
+    hipEvent_t a = nullptr, b = nullptr;
+    Timed(int k, hipStream_t st) : kind(k), s(st) {
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        if (!g_prof.on) return;
+        a = take_event();
+        b = take_event();
+        if (a && b) (void)hipEventRecord(a, s);
+    }
+    ~Timed() {
+        if (!a || !b) return;
+        (void)hipEventRecord(b, s);
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        g_prof.recs.push_back(Rec{kind, a, b});
+    }
+};
+
+dsa_status hip_fail(hipError_t e, const char* what) {
+    return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ------------------------------------------------------------ indexer checks
+
+struct IndexShape {
+    int64_t s_q, s_k, q_pos0;
+    int h_idx, d_idx, pool_size, k_pools, dtype;
+    int64_t n_pools;
+};
+
+dsa_status check_index_shape(const IndexShape& sh, bool need_k) {
+    if (sh.s_q < 0 || sh.s_k < 0 || sh.q_pos0 < 0)
+        return fail(DSA_ERR_INVALID_ARG, "negative size or position (s_q=%lld s_k=%lld q_pos0=%lld)",
+                    (long long)sh.s_q, (long long)sh.s_k, (long long)sh.q_pos0);
+    if (sh.s_k >= (int64_t(1) << 31) || sh.s_q >= (int64_t(1) << 31) ||
+        sh.q_pos0 >= (int64_t(1) << 40))
+        return fail(DSA_ERR_UNSUPPORTED, "s_q and s_k must be below 2^31");
+    if (sh.pool_size != 4)
+        return fail(DSA_ERR_UNSUPPORTED, "pool_size %d: only pools of 4 tokens are supported",
+                    sh.pool_size);
+    if (sh.h_idx != 4 && sh.h_idx != 8 && sh.h_idx != 16 && sh.h_idx != 32)
+        return fail(DSA_ERR_UNSUPPORTED, "h_idx %d: supported indexer heads are 4, 8, 16, 32",
+                    sh.h_idx);
+    if (sh.d_idx != 64 && sh.d_idx != 96 && sh.d_idx != 128)
+        return fail(DSA_ERR_UNSUPPORTED, "d_idx %d: supported indexer dims are 64, 96, 128",
+                    sh.d_idx);
+    if (sh.dtype != DSA_BF16 && sh.dtype != DSA_FP8_E4M3)
+        return fail(DSA_ERR_INVALID_ARG, "unknown dtype %d", sh.dtype);
+    if (sh.dtype == DSA_FP8_E4M3)
+        return fail(DSA_ERR_UNSUPPORTED, "the fp8 E4M3 indexer is not built in this version");
+    if (need_k && (sh.k_pools < 1 || sh.k_pools > kMaxKPools))
+        return fail(DSA_ERR_UNSUPPORTED, "k_pools %d: supported range is 1..%lld", sh.k_pools,
+                    (long long)kMaxKPools);
+    return DSA_OK;
+}
+
+int64_t kbar_bytes(const IndexShape& sh) {
+    const int64_t per_pool = sh.dtype == DSA_BF16 ? 2LL * sh.d_idx * 2 : sh.d_idx + 4;
+    return round_up(sh.n_pools * per_pool, 256);
+}
+
+int64_t score_ld(const IndexShape& sh) { return round_up(sh.n_pools > 0 ? sh.n_pools : 1, 64); }
+
+dsa_status resolve_chunk(const IndexShape& sh, int64_t chunk_q, int64_t* out) {
+    if (chunk_q < 0) return fail(DSA_ERR_INVALID_ARG, "chunk_q %lld < 0", (long long)chunk_q);
+    if (chunk_q == 0) {
+        chunk_q = kDefaultChunk;
+    } else if (chunk_q % 64 != 0 || chunk_q > kMaxChunk) {
+        return fail(DSA_ERR_UNSUPPORTED, "chunk_q %lld must be a multiple of 64 up to %lld",
+                    (long long)chunk_q, (long long)kMaxChunk);
+    }
+    if (chunk_q * score_ld(sh) * 4 > kScoreBufferCap)
+        return fail(DSA_ERR_UNSUPPORTED,
+                    "chunk_q %lld x %lld pools x 4 B exceeds the 2 GiB per-chunk buffer cap",
+                    (long long)chunk_q, (long long)sh.n_pools);
+    *out = chunk_q;
+    return DSA_OK;
+}
+
+dsa_status index_workspace(const IndexShape& sh, int64_t chunk_q, size_t* bytes) {
+    const int64_t buf = chunk_q * score_ld(sh) * 4;
+    *bytes = (size_t)(kbar_bytes(sh) + round_up(buf, 256));
+    return DSA_OK;
+}
+
+dsa_status check_index_ptrs(const void* q_idx, const void* k_idx, const float* q_scale,
+                            const float* k_scale, const float* w, int64_t w_stride,
+                            const IndexShape& sh) {
+    if (sh.s_q > 0 && (!q_idx || !w))
+        return fail(DSA_ERR_INVALID_ARG, "q_idx and w must be non-null");
+    if (sh.n_pools > 0 && !k_idx) return fail(DSA_ERR_INVALID_ARG, "k_idx must be non-null");
+    if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w))
+        return fail(DSA_ERR_INVALID_ARG, "q_idx, k_idx and w must be 16-byte aligned");
+    if (w_stride < 0 || (w_stride != 0 && w_stride < sh.h_idx))
+        return fail(DSA_ERR_INVALID_ARG, "w_stride_q %lld must be 0 or >= h_idx",
+                    (long long)w_stride);
+    if (sh.dtype == DSA_BF16 && (q_scale || k_scale))
+        return fail(DSA_ERR_INVALID_ARG, "q_scale/k_scale apply to the fp8 indexer only");
+    return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_version(void) { return 100; }
+
+const char* dsa_last_error(void) { return g_err; }
+
+dsa_status dsa_index_workspace_size(int64_t s_q, int64_t s_k, int h_idx, int d_idx, int k_pools,
+                                    int pool_size, int64_t chunk_q, int dtype, size_t* bytes,
+                                    int64_t* chunk_q_used) {
+    g_err[0] = 0;
+    if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes must be non-null");
+    IndexShape sh{s_q, s_k, 0, h_idx, d_idx, pool_size, k_pools, dtype, s_k / 4};
+    dsa_status st = check_index_shape(sh, true);
+    if (st != DSA_OK) return st;
+    int64_t cq = 0;
+    if ((st = resolve_chunk(sh, chunk_q, &cq)) != DSA_OK) return st;
+    if (chunk_q_used) *chunk_q_used = cq;
+    return index_workspace(sh, cq, bytes);
+}
+
+dsa_status dsa_index_score_topk(const void* q_idx, const void* k_idx, const float* q_scale,
+                                const float* k_scale, const float* w, int64_t w_stride_q,
+                                int64_t s_q, int64_t s_k, int64_t q_pos0, int h_idx, int d_idx,
+                                int pool_size, int k_pools, int64_t chunk_q, int dtype,
+                                int32_t* idx_out, float* score_out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    IndexShape sh{s_q, s_k, q_pos0, h_idx, d_idx, pool_size, k_pools, dtype, s_k / 4};
+    dsa_status st = check_index_shape(sh, true);
+    if (st != DSA_OK) return st;
+    if ((st = check_index_ptrs(q_idx, k_idx, q_scale, k_scale, w, w_stride_q, sh)) != DSA_OK)
+        return st;
+    if (s_q > 0 && !idx_out) return fail(DSA_ERR_INVALID_ARG, "idx_out must be non-null");
+    if (!aligned16(idx_out) || !aligned16(score_out))
+        return fail(DSA_ERR_INVALID_ARG, "idx_out and score_out must be 16-byte aligned");
+    int64_t cq = 0;
+    if ((st = resolve_chunk(sh, chunk_q, &cq)) != DSA_OK) return st;
+    size_t need = 0;
+    index_workspace(sh, cq, &need);
+    if (s_q == 0) return DSA_OK;
+    if (!workspace || workspace_bytes < need)
+        return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    uint16_t* kbar = reinterpret_cast<uint16_t*>(ws);
+    float* buf = reinterpret_cast<float*>(ws + kbar_bytes(sh));
+    const int64_t ld = score_ld(sh);
+    hipError_t e;
+    if (sh.n_pools > 0) {
+        Timed tm(K_POOL, s);
+        e = dsa::launch_pool_keys_bf16(static_cast<const uint16_t*>(k_idx), sh.n_pools, d_idx,
+                                       kbar, s);
+        if (e != hipSuccess) return hip_fail(e, "pool_keys launch");
+    }
+    for (int64_t c0 = 0; c0 < s_q; c0 += cq) {
+        const int rows = (int)(s_q - c0 < cq ? s_q - c0 : cq);
+        const int64_t t_last = q_pos0 + c0 + rows - 1;
+        const int64_t n_chunk = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
+        if (n_chunk > 0 && (n_chunk > k_pools || score_out)) {
+            dsa::ScoreArgs a{};
+            a.q_idx = q_idx;
+            a.kbar = kbar;
+            a.w = w;
+            a.w_stride = w_stride_q;
+            a.s_q = s_q;
+            a.row0 = c0;
+            a.rows = rows;
+            a.q_pos0 = q_pos0;
+            a.n_pools = sh.n_pools;
+            a.n_chunk = n_chunk;
+            a.h_idx = h_idx;
+            a.d_idx = d_idx;
+            a.fp8 = 0;
+            a.buf = buf;
+            a.ld = ld;
+            Timed tm(K_SCORE, s);
+            e = dsa::launch_index_score(a, s);
+            if (e != hipSuccess) return hip_fail(e, "index_score launch");
+        }
+        dsa::SelectArgs b{};
+        b.buf = buf;
+        b.ld = ld;
+        b.row0 = c0;
+        b.rows = rows;
+        b.q_pos0 = q_pos0;
+        b.n_pools = sh.n_pools;
+        b.k_pools = k_pools;
+        b.idx_out = idx_out;
+        b.score_out = score_out;
+        Timed tm(K_SELECT, s);
+        e = dsa::launch_topk_select(b, s);
+        if (e != hipSuccess) return hip_fail(e, "topk_select launch");
+    }
+    return DSA_OK;
+}
+
+dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const float* q_scale,
+                            const float* k_scale, const float* w, int64_t w_stride_q,
+                            int64_t s_q, int64_t s_k, int64_t q_pos0, int h_idx, int d_idx,
+                            int pool_size, int dtype, int64_t row0, int64_t n_rows,
+                            float* scores_out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    g_err[0] = 0;
+    IndexShape sh{s_q, s_k, q_pos0, h_idx, d_idx, pool_size, 1, dtype, s_k / 4};
+    dsa_status st = check_index_shape(sh, false);
+    if (st != DSA_OK) return st;
+    if ((st = check_index_ptrs(q_idx, k_idx, q_scale, k_scale, w, w_stride_q, sh)) != DSA_OK)
+        return st;
+    if (row0 < 0 || n_rows < 0 || row0 + n_rows > s_q)
+        return fail(DSA_ERR_INVALID_ARG, "rows [%lld, %lld) outside [0, %lld)", (long long)row0,
+                    (long long)(row0 + n_rows), (long long)s_q);
+    if (n_rows > (int64_t(1) << 20))
+        return fail(DSA_ERR_UNSUPPORTED, "at most 2^20 rows per call");
+    if (n_rows > 0 && !scores_out) return fail(DSA_ERR_INVALID_ARG, "scores_out must be non-null");
+    if (!aligned16(scores_out)) return fail(DSA_ERR_INVALID_ARG, "scores_out must be 16-byte aligned");
+    const size_t need = (size_t)kbar_bytes(sh);
+    if (n_rows == 0 || sh.n_pools == 0) {
+        if (n_rows > 0 && sh.n_pools == 0) return DSA_OK;  // [n_rows, 0]
+        return DSA_OK;
+    }
+    if (!workspace || workspace_bytes < need)
+        return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint16_t* kbar = static_cast<uint16_t*>(workspace);
+    hipError_t e = dsa::launch_fill_f32(scores_out, n_rows * sh.n_pools, -INFINITY, s);
+    if (e != hipSuccess) return hip_fail(e, "fill launch");
+    {
+        Timed tm(K_POOL, s);
+        e = dsa::launch_pool_keys_bf16(static_cast<const uint16_t*>(k_idx), sh.n_pools, d_idx,
+                                       kbar, s);
+        if (e != hipSuccess) return hip_fail(e, "pool_keys launch");
+    }
+    const int64_t t_last = q_pos0 + row0 + n_rows - 1;
+    const int64_t n_chunk = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
+    if (n_chunk > 0) {
+        dsa::ScoreArgs a{};
+        a.q_idx = q_idx;
+        a.kbar = kbar;
+        a.w = w;
+        a.w_stride = w_stride_q;
+        a.s_q = s_q;
+        a.row0 = row0;
+        a.rows = (int)n_rows;
+        a.q_pos0 = q_pos0;
+        a.n_pools = sh.n_pools;
+        a.n_chunk = n_chunk;
+        a.h_idx = h_idx;
+        a.d_idx = d_idx;
+        a.fp8 = 0;
+        a.buf = scores_out;
+        a.ld = sh.n_pools;
+        Timed tm(K_SCORE, s);
+        e = dsa::launch_index_score(a, s);
+        if (e != hipSuccess) return hip_fail(e, "index_score launch");
+    }
+    return DSA_OK;
+}
+
+dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
+                               int64_t s_q, int64_t s_k, int64_t q_pos0, int h, int d, int dv,
+                               int k_pools, int pool_size, int n_tail, float softmax_scale,
+                               void* out, float* lse, void* stream) {
+    g_err[0] = 0;
+    if (s_q < 0 || s_k < 0 || q_pos0 < 0)
+        return fail(DSA_ERR_INVALID_ARG, "negative size or position");
+    if (s_k >= (int64_t(1) << 31) || s_q >= (int64_t(1) << 31))
+        return fail(DSA_ERR_UNSUPPORTED, "s_q and s_k must be below 2^31");
+    if (pool_size != 4) return fail(DSA_ERR_UNSUPPORTED, "pool_size %d: only 4 is supported", pool_size);
+    if (h < 1 || h > 16)
+        return fail(DSA_ERR_UNSUPPORTED, "h %d: 1..16 query heads per key/value head", h);
+    if ((d != 64 && d != 96 && d != 128) || (dv != 64 && dv != 96 && dv != 128))
+        return fail(DSA_ERR_UNSUPPORTED, "d %d / dv %d: supported head dims are 64, 96, 128", d, dv);
+    if (k_pools < 1 || k_pools > kMaxKPools)
+        return fail(DSA_ERR_UNSUPPORTED, "k_pools %d: supported range is 1..%lld", k_pools,
+                    (long long)kMaxKPools);
+    if (n_tail < 0 || n_tail >= pool_size)
+        return fail(DSA_ERR_INVALID_ARG, "n_tail %d outside 0..%d", n_tail, pool_size - 1);
+    if (!(softmax_scale == softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "softmax_scale is NaN");
+    if (s_q > 0 && (!q || !idx || !out))
+        return fail(DSA_ERR_INVALID_ARG, "q, idx and out must be non-null");
+    if (s_k > 0 && s_q > 0 && (!k || !v)) return fail(DSA_ERR_INVALID_ARG, "k and v must be non-null");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(idx) || !aligned16(out) ||
+        !aligned16(lse))
+        return fail(DSA_ERR_INVALID_ARG, "all buffers must be 16-byte aligned");
+    if (s_q == 0) return DSA_OK;
+    const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)d);
+    dsa::AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.idx = idx;
+    a.s_q = s_q;
+    a.s_k = s_k;
+    a.q_pos0 = q_pos0;
+    a.h = h;
+    a.d = d;
+    a.dv = dv;
+    a.k_pools = k_pools;
+    a.n_tail = n_tail;
+    a.scale = scale;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Timed tm(K_ATTN, s);
+    hipError_t e = dsa::launch_sparse_attn(a, s);
+    if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
+    return DSA_OK;
+}
+
+dsa_status dsa_profile_enable(int on) {
+    g_err[0] = 0;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.on = on != 0;
+    return DSA_OK;
+}
+
+dsa_status dsa_profile_read(dsa_kernel_stat* stats, int max_stats, int* n_stats) {
+    g_err[0] = 0;
+    if (!n_stats || (max_stats > 0 && !stats) || max_stats < 0)
+        return fail(DSA_ERR_INVALID_ARG, "bad output arguments");
+    std::vector<Rec> recs;
+    {
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        recs.swap(g_prof.recs);
+    }
+    int64_t launches[K_COUNT] = {0};
+    double total[K_COUNT] = {0};
+    dsa_status st = DSA_OK;
+    for (const Rec& r : recs) {
+        float ms = 0.0f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess && st == DSA_OK) st = hip_fail(e, "profile event");
+        launches[r.kind] += 1;
+        total[r.kind] += ms;
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        for (const Rec& r : recs) {
+            g_prof.pool.push_back(r.a);
+            g_prof.pool.push_back(r.b);
+        }
+    }
+    int n = 0;
+    for (int kd = 0; kd < K_COUNT; ++kd) {
+        if (launches[kd] == 0) continue;
+        if (n < max_stats) {
+            memset(&stats[n], 0, sizeof stats[n]);
+            strncpy(stats[n].name, kKindName[kd], sizeof stats[n].name - 1);
+            stats[n].launches = launches[kd];
+            stats[n].total_ms = total[kd];
+        }
+        ++n;
+    }
+    *n_stats = n < max_stats ? n : max_stats;
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,340 @@
+// Pooling of the indexer keys and chunked lightning-indexer scoring.
+//
+// SkyRL blog "Scaling Training to 1M Token Context on GLM-5.3-Flash",
+// section "DeepSeek Sparse Attention (DSA) Optimizations": every query is
+// scored against every earlier pool of 4 tokens; section "Over Time:
+// Chunking": scores are fp32 and are produced a chunk of queries at a time
+// into a buffer whose size does not grow with the sequence.
+//
+// Score (no formula is printed on the page; the standard lightning-indexer
+// form): s(t,p) = sum_h w[t,h] * relu(q_idx[t,h,:] . kbar_p), kbar_p the mean
+// of key rows 4p..4p+3, for pools with 4p+3 < t.
+//
+// GEMM view of one chunk: rows = (query, head) pairs, columns = pools,
+// contraction = d_idx.  Each workgroup keeps a block of pooled keys resident
+// in registers as the MFMA B operand and streams the chunk's queries through
+// LDS as the A operand; the head-weighted ReLU reduction runs on the MFMA
+// accumulators before anything is stored, so only [query, pool] fp32 scores
+// reach memory.
+//
+// bf16 accuracy: a pooled key rounded once to bf16 perturbs scores by ~1e-3
+// relative, enough to move pools across the top-k boundary.  The pooled key
+// is therefore stored as two bf16 terms hi + lo (hi = bf16(mean),
+// lo = bf16(mean - hi)), and each MFMA consumes 8 dims of hi in the lower
+// half-wave and the same 8 dims of lo in the upper half-wave against the same
+// query values, so q.hi + q.lo is accumulated in one instruction stream.
+// Products of two bf16 values are exact in fp32; the remaining error is the
+// 2^-17 relative residual of the split plus fp32 accumulation.
+#include "common.h"
+#include "internal.h"
+
+namespace dsa {
+
+// ---------------------------------------------------------------- pooling
+
+template <int DI>
+__global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __restrict__ k,
+                                                             int64_t n_pools,
+                                                             uint16_t* __restrict__ kbar) {
+    constexpr int G = DI / 8;  // 8-dim groups per row
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t p = gid / G;
+    const int g = (int)(gid % G);
+    if (p >= n_pools) return;
+    const uint16_t* src = k + (p * 4) * DI + g * 8;
+    u32x4 r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = ldg16(src + (int64_t)j * DI);
+    u32x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int word = e >> 1, sh = (e & 1) * 16;
+        float s = bf16_to_f32((r[0][word] >> sh) & 0xFFFFu);
+        s += bf16_to_f32((r[1][word] >> sh) & 0xFFFFu);
+        s += bf16_to_f32((r[2][word] >> sh) & 0xFFFFu);
+        s += bf16_to_f32((r[3][word] >> sh) & 0xFFFFu);
+        const float m = s * 0.25f;
+        const uint32_t h = f32_to_bf16(m);
+        const uint32_t l = f32_to_bf16(m - bf16_to_f32(h));
+        if ((e & 1) == 0) {
+            hi[word] = h;
+            lo[word] = l;
+        } else {
+            hi[word] |= h << 16;
+            lo[word] |= l << 16;
+        }
+    }
+    uint16_t* dst = kbar + p * (2 * DI) + g * 8;
+    *reinterpret_cast<u32x4*>(dst) = hi;
+    *reinterpret_cast<u32x4*>(dst + DI) = lo;
+}
+
+hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, int64_t n_pools, int d_idx,
+                                 uint16_t* kbar, hipStream_t stream) {
+    if (n_pools <= 0) return hipSuccess;
+    const int64_t threads = n_pools * (d_idx / 8);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    switch (d_idx) {
+        case 64: pool_keys_bf16_kernel<64><<<grid, 256, 0, stream>>>(k_idx, n_pools, kbar); break;
+        case 96: pool_keys_bf16_kernel<96><<<grid, 256, 0, stream>>>(k_idx, n_pools, kbar); break;
+        case 128: pool_keys_bf16_kernel<128><<<grid, 256, 0, stream>>>(k_idx, n_pools, kbar); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_keys_fp8(const uint8_t*, int64_t, int, uint8_t*, float*, hipStream_t) {
+    return hipErrorNotSupported;
+}
+
+// ---------------------------------------------------------------- fill
+
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = v;
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    fill_f32_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(p, n, value);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- scoring
+
+struct ScoreK {
+    const uint16_t* q_idx;
+    const uint16_t* kbar;
+    const float* w;
+    int64_t w_stride;
+    int64_t s_q;
+    int64_t row0;
+    int rows;
+    int gq;          // queries per workgroup (multiple of 32 / HI)
+    int64_t q_pos0;
+    int64_t n_pools;
+    float* buf;
+    int64_t ld;
+};
+
+// One 32x32x16 bf16 MFMA: lane l supplies A row (l % 32) and B column
+// (l % 32), each with the 8 contraction elements of half-wave (l / 32); the
+// accumulator element v of lane l is row 8*(v/4) + 4*(l/32) + (v%4), column
+// l % 32.
+//
+// Workgroup = 4 waves; each wave owns NB blocks of 32 consecutive pools
+// (pooled keys resident as B fragments); the workgroup owns 128*NB pools and
+// a range of gq chunk rows, walked one 32-row (query, head) tile at a time.
+template <int HI, int DI, int NB>
+__global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
+    constexpr int QPT = 32 / HI;   // queries per 32-row tile
+    constexpr int NS = DI / 8;     // MFMA steps (8 dims of hi + 8 of lo each)
+    constexpr int PW = 32 * NB;    // pools per wave
+    constexpr int PB = 4 * PW;     // pools per workgroup
+    constexpr int LROW = DI + 8;   // LDS row stride (bf16 elements)
+    constexpr int CHUNKS = 4 * DI; // 16-byte pieces of one 32-row tile
+    constexpr int CPT = (CHUNKS + 255) / 256;
+
+    __shared__ __attribute__((aligned(16))) uint16_t sq[2][32 * LROW];
+    __shared__ __attribute__((aligned(16))) float sw[2][32];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int64_t p_blk = (int64_t)blockIdx.x * PB;
+    const int64_t p_wave = p_blk + wave * PW;
+
+    // rows of this workgroup; skip leading rows that see none of its pools
+    int i_begin = blockIdx.y * a.gq;
+    const int i_end = min(a.rows, i_begin + a.gq);
+    const int64_t first = 4 * (p_blk + 1) - a.q_pos0 - a.row0;
+    if (first > i_begin) i_begin = (int)(first < (int64_t)i_end ? first : (int64_t)i_end);
+    i_begin = (i_begin / QPT) * QPT;
+    if (i_begin >= i_end) return;
+    const int n_tiles = (i_end - i_begin + QPT - 1) / QPT;
+
+    // resident pooled keys: pool p_wave + nb*32 + col, hi (half 0) / lo (half 1)
+    bf16x8 bfr[NB][NS];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t p = p_wave + nb * 32 + col;
+        if (p < a.n_pools) {
+            const uint16_t* src = a.kbar + p * (2 * DI) + half * DI;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) bfr[nb][s] = as_bf16x8(ldg16(src + 8 * s));
+        } else {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) bfr[nb][s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+
+    // tile j covers chunk rows i_begin + j*QPT .. +QPT: a contiguous block of
+    // 32 * DI bf16 in q_idx (rows = query*HI + head)
+    u32x4 pre[CPT];
+    float prew = 0.0f;
+    auto fetch = [&](int j) {
+        const int64_t qrow0 = a.row0 + i_begin + (int64_t)j * QPT;
+        const uint16_t* src = a.q_idx + qrow0 * (HI * DI);
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int ch = tid + u * 256;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (ch < CHUNKS) {
+                const int r = ch / (DI / 8);
+                if (qrow0 + r / HI < a.s_q) v = ldg16(src + (int64_t)ch * 8);
+            }
+            pre[u] = v;
+        }
+        if (tid < 32) {
+            const int64_t qr = qrow0 + tid / HI;
+            prew = qr < a.s_q ? a.w[qr * a.w_stride + (tid % HI)] : 0.0f;
+        }
+    };
+    auto stash = [&](int b) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int ch = tid + u * 256;
+            if (ch < CHUNKS) {
+                const int r = ch / (DI / 8), c8 = ch % (DI / 8);
+                *reinterpret_cast<u32x4*>(&sq[b][r * LROW + c8 * 8]) = pre[u];
+            }
+        }
+        if (tid < 32) sw[b][tid] = prew;
+    };
+
+    fetch(0);
+    stash(0);
+    __syncthreads();
+
+    for (int j = 0; j < n_tiles; ++j) {
+        const int cur = j & 1;
+        const bool has_next = j + 1 < n_tiles;
+        if (has_next) fetch(j + 1);
+
+        f32x16 acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[nb][v] = 0.0f;
+
+        const uint16_t* arow = &sq[cur][col * LROW];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 8 * s));
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[nb][s], acc[nb], 0, 0, 0);
+        }
+
+        // epilogue: weights of the rows this lane holds
+        float wv[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(&sw[cur][8 * g4 + 4 * half]);
+            wv[4 * g4 + 0] = w4[0];
+            wv[4 * g4 + 1] = w4[1];
+            wv[4 * g4 + 2] = w4[2];
+            wv[4 * g4 + 3] = w4[3];
+        }
+        const int tile_i0 = i_begin + j * QPT;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int64_t p = p_wave + nb * 32 + col;
+            float part[4];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                float s = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s += wv[4 * g4 + i] * relu(acc[nb][4 * g4 + i]);
+                part[g4] = s;
+            }
+            // query qi of this tile and its value on this lane
+            float qv[4];
+            int nq;
+            if constexpr (HI == 32) {
+                float s = (part[0] + part[1]) + (part[2] + part[3]);
+                s += __shfl_xor(s, 32);
+                qv[0] = s;
+                nq = 1;
+            } else if constexpr (HI == 16) {
+                float s0 = part[0] + part[1], s1 = part[2] + part[3];
+                s0 += __shfl_xor(s0, 32);
+                s1 += __shfl_xor(s1, 32);
+                qv[0] = s0;
+                qv[1] = s1;
+                nq = 2;
+            } else if constexpr (HI == 8) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) qv[g4] = part[g4] + __shfl_xor(part[g4], 32);
+                nq = 4;
+            } else {  // HI == 4: rows 8*g4 + 4*half + i -> query 2*g4 + half, complete in-lane
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) qv[g4] = part[g4];
+                nq = 4;
+            }
+            if (HI == 4 || half == 0) {
+#pragma unroll
+                for (int u = 0; u < nq; ++u) {
+                    const int qi = (HI == 4) ? (2 * u + half) : u;
+                    const int i = tile_i0 + qi;
+                    if (i < i_end) {
+                        const int64_t t = a.q_pos0 + a.row0 + i;
+                        const int64_t nt = (t >> 2) < a.n_pools ? (t >> 2) : a.n_pools;
+                        if (p < nt) a.buf[(int64_t)i * a.ld + p] = canonical_zero(qv[u]);
+                    }
+                }
+            }
+        }
+
+        if (has_next) stash(cur ^ 1);
+        __syncthreads();
+    }
+}
+
+template <int HI, int DI>
+static hipError_t launch_score_bf16_t(const ScoreArgs& a, hipStream_t stream) {
+    constexpr int NB = 2;
+    constexpr int PB = 128 * NB;
+    constexpr int QPT = 32 / HI;
+    ScoreK k;
+    k.q_idx = static_cast<const uint16_t*>(a.q_idx);
+    k.kbar = static_cast<const uint16_t*>(a.kbar);
+    k.w = a.w;
+    k.w_stride = a.w_stride;
+    k.s_q = a.s_q;
+    k.row0 = a.row0;
+    k.rows = a.rows;
+    k.gq = 64 * QPT;
+    k.q_pos0 = a.q_pos0;
+    k.n_pools = a.n_pools;
+    k.buf = a.buf;
+    k.ld = a.ld;
+    const dim3 grid((unsigned)((a.n_chunk + PB - 1) / PB), (unsigned)((a.rows + k.gq - 1) / k.gq));
+    if (grid.x == 0 || grid.y == 0) return hipSuccess;
+    index_score_bf16_kernel<HI, DI, NB><<<grid, 256, 0, stream>>>(k);
+    return hipGetLastError();
+}
+
+template <int HI>
+static hipError_t launch_score_bf16_h(const ScoreArgs& a, hipStream_t stream) {
+    switch (a.d_idx) {
+        case 64: return launch_score_bf16_t<HI, 64>(a, stream);
+        case 96: return launch_score_bf16_t<HI, 96>(a, stream);
+        case 128: return launch_score_bf16_t<HI, 128>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
+    if (a.fp8) return hipErrorNotSupported;
+    switch (a.h_idx) {
+        case 4: return launch_score_bf16_h<4>(a, stream);
+        case 8: return launch_score_bf16_h<8>(a, stream);
+        case 16: return launch_score_bf16_h<16>(a, stream);
+        case 32: return launch_score_bf16_h<32>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dsa

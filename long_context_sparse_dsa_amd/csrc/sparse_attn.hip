@@ -1,0 +1,280 @@
+// Sparse attention forward over the kept pools, online softmax.
+//
+// SkyRL blog "Scaling Training to 1M Token Context on GLM-5.3-Flash",
+// section "DeepSeek Sparse Attention (DSA) Optimizations": attention reads
+// only the selected tokens (2048 = 512 pools x 4), so its cost is linear in
+// the sequence; section "Making Sparse Attention Actually Sparse": NoPE heads
+// (head dim 96 here, natively, no padding) and 2,051 keys, read as the 512
+// pools plus up to 3 tokens of the query's own unfinished pool before it.
+//
+// One wave per query; all query heads (<= 16) share the single key/value
+// head, so every gathered key/value row serves every head.  Tokens are
+// processed in tiles of 32 slots (8 pools).  Per tile:
+//   S^T[32 tokens x 16 heads] = K_tile . Q^T      2 x (d/32) MFMA 16x16x32 bf16
+//     (key rows gathered straight from global memory into the A operand)
+//   online softmax per head (fp32, exp2 domain)
+//   O^T[dv x 16 heads] += V_tile^T . P^T           dv/16 MFMA 16x16x32 bf16
+//     (P^T comes straight from the S^T accumulators; V goes through a
+//      per-wave LDS tile because its token axis is the contraction axis)
+// The next tile's key/value rows are loaded into registers while the current
+// tile is computed.
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace dsa {
+
+namespace {
+
+struct AttnK {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* idx;
+    int64_t s_q, s_k, q_pos0, n_pools;
+    int h, k_pools, n_tail;
+    float scale_log2;  // softmax scale * log2(e)
+    uint16_t* out;
+    float* lse;
+};
+
+// 16x16x32 bf16 MFMA: lane l supplies A row (l % 16) and B column (l % 16),
+// each with 8 contraction elements of group (l / 16); accumulator element i
+// of lane l is row 4*(l/16) + i, column l % 16.
+template <int D, int DV>
+__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
+    constexpr int KS = D / 32;             // QK contraction steps
+    constexpr int MT = DV / 16;            // O^T row tiles
+    constexpr int VCH = DV / 8;            // 16-byte pieces per value row
+    constexpr int VPL = 32 * VCH / 64;     // value pieces per lane per tile
+    constexpr int VROW = DV + 4;           // LDS row stride (bf16), 8-byte pad
+    __shared__ __attribute__((aligned(16))) uint16_t sv_all[4][32 * VROW];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t qi = (int64_t)blockIdx.x * 4 + wave;
+    if (qi >= a.s_q) return;  // waves are independent: no workgroup barrier below
+    uint16_t* sv = sv_all[wave];
+    const int col = lane & 15, grp = lane >> 4;
+    const int64_t t = a.q_pos0 + qi;
+    const int n_tail_t = (int)min((int64_t)a.n_tail, t & 3);
+    const int n_pool_slots = 4 * a.k_pools;
+    const int n_slots = n_pool_slots + n_tail_t;
+    const int n_tiles = (n_slots + 31) / 32;
+    const int32_t* irow = a.idx + qi * a.k_pools;
+
+    // Q^T fragments: head = col, dims 32*s + 8*grp .. +8
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (col < a.h) v = ldg16(a.q + (qi * a.h + col) * D + 32 * s + 8 * grp);
+        qf[s] = as_bf16x8(v);
+    }
+
+    // token of a slot of tile `tile`; pid holds pool ids of the tile's 8 pools
+    // in lanes 0..7 (and repeats); every lane must call this (shuffle inside).
+    auto token_of = [&](int slot_in_tile, int tile, int32_t pid) -> int64_t {
+        const int slot = tile * 32 + slot_in_tile;
+        const int32_t p = __shfl(pid, (slot_in_tile >> 2) & 7);
+        if (slot < n_pool_slots) {
+            if (p >= 0 && (int64_t)p < a.n_pools) return 4 * (int64_t)p + (slot & 3);
+            return -1;
+        }
+        const int j = slot - n_pool_slots;
+        if (j < n_tail_t) {
+            const int64_t tok = t - n_tail_t + j;
+            if (tok >= 0 && tok < a.s_k) return tok;
+        }
+        return -1;
+    };
+
+    u32x4 kc[2][KS], vc[VPL];
+    uint32_t valid_c = 0;
+    auto load_tile = [&](int tile, u32x4 (&kr)[2][KS], u32x4 (&vr)[VPL], uint32_t& valid) {
+        const int pi = tile * 8 + (lane & 7);
+        const int32_t pid = pi < a.k_pools ? irow[pi] : -1;
+        const int64_t vt = token_of(lane & 31, tile, pid);
+        valid = (uint32_t)__ballot(vt >= 0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t tok = token_of(16 * u + col, tile, pid);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (tok >= 0) v = ldg16(a.k + tok * D + 32 * s + 8 * grp);
+                kr[u][s] = v;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < VPL; ++r) {
+            const int piece = lane + 64 * r;
+            const int64_t tok = token_of(piece / VCH, tile, pid);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (tok >= 0) v = ldg16(a.v + tok * DV + 8 * (piece % VCH));
+            vr[r] = v;
+        }
+    };
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 oacc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) oacc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (n_tiles > 0) load_tile(0, kc, vc, valid_c);
+
+    for (int tile = 0; tile < n_tiles; ++tile) {
+        // value tile -> LDS (row-major [slot][dv])
+#pragma unroll
+        for (int r = 0; r < VPL; ++r) {
+            const int piece = lane + 64 * r;
+            uint16_t* dst = sv + (piece / VCH) * VROW + 8 * (piece % VCH);
+            reinterpret_cast<u32x2*>(dst)[0] = u32x2{vc[r][0], vc[r][1]};
+            reinterpret_cast<u32x2*>(dst)[1] = u32x2{vc[r][2], vc[r][3]};
+        }
+        const uint32_t valid = valid_c;
+
+        // S^T for the two 16-slot halves
+        f32x4 sacc[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            sacc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[u][s]), qf[s],
+                                                                  sacc[u], 0, 0, 0);
+        }
+
+        // prefetch the next tile while this one is finished
+        u32x4 kn[2][KS], vn[VPL];
+        uint32_t valid_n = 0;
+        if (tile + 1 < n_tiles) load_tile(tile + 1, kn, vn, valid_n);
+
+        // online softmax; this lane holds slots 16u + 4*grp + i of head col
+        float x[2][4];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int slot = 16 * u + 4 * grp + i;
+                x[u][i] = ((valid >> slot) & 1u) ? sacc[u][i] * a.scale_log2 : -INFINITY;
+                mt = fmaxf(mt, x[u][i]);
+            }
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m_run, mt);
+        float alpha = 1.0f;
+        float p[2][4];
+        if (m_new == -INFINITY) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[u][i] = 0.0f;
+        } else {
+            alpha = exp2f(m_run - m_new);
+            float ps = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[u][i] = exp2f(x[u][i] - m_new);
+                    ps += p[u][i];
+                }
+            l_run = l_run * alpha + ps;
+            m_run = m_new;
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) oacc[m] *= alpha;
+
+        // P^T fragment: contraction slots {4g..4g+3, 16+4g..16+4g+3}
+        u32x4 pw;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float lo = p[j >> 1][(j & 1) * 2];
+            const float hi = p[j >> 1][(j & 1) * 2 + 1];
+            pw[j] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+        }
+        const bf16x8 pf = as_bf16x8(pw);
+
+        // V^T fragments from LDS: row = dim 16m + col, same contraction slots
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint16_t* base = sv + 16 * m + col;
+            u32x4 vw;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int s0 = (j >> 1) * 16 + 4 * grp + (j & 1) * 2;
+                vw[j] = (uint32_t)base[s0 * VROW] | ((uint32_t)base[(s0 + 1) * VROW] << 16);
+            }
+            oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw), pf, oacc[m], 0, 0, 0);
+        }
+
+        if (tile + 1 < n_tiles) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int s = 0; s < KS; ++s) kc[u][s] = kn[u][s];
+#pragma unroll
+            for (int r = 0; r < VPL; ++r) vc[r] = vn[r];
+            valid_c = valid_n;
+        }
+    }
+
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (col < a.h) {
+        uint16_t* orow = a.out + (qi * a.h + col) * DV;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint32_t w0 = f32_to_bf16(oacc[m][0] * inv) | (f32_to_bf16(oacc[m][1] * inv) << 16);
+            const uint32_t w1 = f32_to_bf16(oacc[m][2] * inv) | (f32_to_bf16(oacc[m][3] * inv) << 16);
+            *reinterpret_cast<u32x2*>(orow + 16 * m + 4 * grp) = u32x2{w0, w1};
+        }
+        if (a.lse && grp == 0)
+            a.lse[qi * a.h + col] =
+                l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
+template <int D>
+hipError_t launch_d(const AttnK& k, int dv, dim3 grid, hipStream_t stream) {
+    switch (dv) {
+        case 64: sparse_attn_kernel<D, 64><<<grid, 256, 0, stream>>>(k); break;
+        case 96: sparse_attn_kernel<D, 96><<<grid, 256, 0, stream>>>(k); break;
+        case 128: sparse_attn_kernel<D, 128><<<grid, 256, 0, stream>>>(k); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
+    if (a.s_q <= 0) return hipSuccess;
+    AttnK k;
+    k.q = a.q;
+    k.k = a.k;
+    k.v = a.v;
+    k.idx = a.idx;
+    k.s_q = a.s_q;
+    k.s_k = a.s_k;
+    k.q_pos0 = a.q_pos0;
+    k.n_pools = a.s_k / 4;
+    k.h = a.h;
+    k.k_pools = a.k_pools;
+    k.n_tail = a.n_tail;
+    k.scale_log2 = a.scale * 1.4426950408889634f;
+    k.out = a.out;
+    k.lse = a.lse;
+    const dim3 grid((unsigned)((a.s_q + 3) / 4));
+    switch (a.d) {
+        case 64: return launch_d<64>(k, a.dv, grid, stream);
+        case 96: return launch_d<96>(k, a.dv, grid, stream);
+        case 128: return launch_d<128>(k, a.dv, grid, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dsa

@@ -1,0 +1,383 @@
+// Per-query top-k pool selection over one chunk's fp32 score rows.
+//
+// SkyRL blog "Scaling Training to 1M Token Context on GLM-5.3-Flash",
+// section "DeepSeek Sparse Attention (DSA) Optimizations": each query keeps
+// its best pools (512 pools = 2048 tokens); section "Over Time: Chunking":
+// pools are scored and selected a chunk of queries at a time; section
+// "Across GPUs: Sharding": the kept pool ids are int32.
+//
+// Rule: keep the k largest fp32 scores among the n(t) eligible pools, ties
+// broken towards the lower pool id; emit the ids in ascending order, padded
+// with -1 when n(t) < k.  Exact and deterministic: every decision is taken on
+// the 32-bit order key of the fp32 score (larger float <=> larger key), with
+// integer counting only.
+//
+// One workgroup (4 waves) per query row:
+//   n <= k       every eligible pool, no scores read;
+//   n <= CAP     the whole row goes to an LDS list (key, id) in id order;
+//   n >  CAP     a 2048-element sample of the row (128 cache-line blocks)
+//                gives a threshold tau that about 2-4x k elements exceed;
+//                one coalesced pass compacts {key >= tau} into the LDS list,
+//                keeping id order; if fewer than k or more than CAP elements
+//                qualify, an exact multi-pass radix over the row in global
+//                memory takes over (slow path, still exact).
+// On a list, a radix-16 refinement narrows a key range [lo, hi] until the
+// elements above hi plus the in-range ones are exactly decided: everything
+// above hi is kept, and in-range elements are kept in id order while fewer
+// than `remaining` have been kept.  Counting uses per-thread LDS counters
+// (one slot per digit and thread) so that skewed score distributions cause
+// no atomic contention.
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int NT = 256;
+constexpr int CAP = 4096;
+constexpr int SAMPLE_BLOCKS = 128;
+constexpr int SAMPLE_LEN = 16;
+constexpr int SAMPLE_N = SAMPLE_BLOCKS * SAMPLE_LEN;
+
+struct SelShared {
+    uint32_t key[CAP];
+    int32_t id[CAP];
+    uint32_t cnt[16 * NT];
+    uint32_t hist[16];
+    uint32_t tmp[8];
+};
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t n = __shfl_up(v, off);
+        if (lane >= off) v += n;
+    }
+    return v;
+}
+
+// Exclusive prefix over the workgroup; *total receives the sum.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SelShared& sh, uint32_t* total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t inc = wave_incl_scan(v, lane);
+    if (lane == 63) sh.tmp[wave] = inc;
+    __syncthreads();
+    uint32_t base = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const uint32_t x = sh.tmp[w];
+        if (w < wave) base += x;
+        tot += x;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + inc - v;
+}
+
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, SelShared& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor(mn, off));
+        mx = max(mx, (uint32_t)__shfl_xor(mx, off));
+    }
+    if (lane == 0) {
+        sh.tmp[wave] = mn;
+        sh.tmp[4 + wave] = mx;
+    }
+    __syncthreads();
+    mn = min(min(sh.tmp[0], sh.tmp[1]), min(sh.tmp[2], sh.tmp[3]));
+    mx = max(max(sh.tmp[4], sh.tmp[5]), max(sh.tmp[6], sh.tmp[7]));
+    __syncthreads();
+}
+
+// Initial range [lo, hi] from the extreme keys: the aligned block of the
+// lowest nibble boundary above their highest differing bit; returns the
+// first digit shift (or -1 when all keys are equal).
+__device__ __forceinline__ int start_range(uint32_t mn, uint32_t mx, uint32_t& lo, uint32_t& hi) {
+    const uint32_t diff = mn ^ mx;
+    if (diff == 0) {
+        lo = hi = mn;
+        return -1;
+    }
+    const int top = 31 - __clz(diff);
+    const int shift = (top / 4) * 4;
+    const uint32_t mask = (shift + 4 >= 32) ? 0u : (0xFFFFFFFFu << (shift + 4));
+    lo = mn & mask;
+    hi = lo | ~mask;
+    return shift;
+}
+
+// Radix-16 refinement.  Precondition: at least `remaining` keys lie in
+// [lo, hi] and every key above hi is already kept.  On return the kept set is
+// {key > hi} plus the first `remaining` in-range keys in id order.
+template <class KeyAt>
+__device__ void refine(KeyAt key_at, int64_t n, int shift, uint32_t& lo, uint32_t& hi,
+                       uint32_t& remaining, SelShared& sh) {
+    const int tid = threadIdx.x;
+    for (; shift >= 0 && lo != hi; shift -= 4) {
+#pragma unroll
+        for (int d = 0; d < 16; ++d) sh.cnt[d * NT + tid] = 0;
+        for (int64_t e = tid; e < n; e += NT) {
+            const uint32_t k = key_at(e);
+            if (k >= lo && k <= hi) sh.cnt[((k >> shift) & 15u) * NT + tid] += 1;
+        }
+        __syncthreads();
+        uint32_t s = 0;
+        const uint32_t* c = &sh.cnt[(tid >> 4) * NT + (tid & 15) * 16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s += c[u];
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 8);
+        if ((tid & 15) == 0) sh.hist[tid >> 4] = s;
+        __syncthreads();
+        uint32_t above = 0, hb = 0;
+        int b = 0;
+        for (int d = 15; d >= 0; --d) {
+            const uint32_t h = sh.hist[d];
+            if (above + h >= remaining) {
+                b = d;
+                hb = h;
+                break;
+            }
+            above += h;
+        }
+        remaining -= above;
+        const uint32_t keep = (shift + 4 >= 32) ? 0u : (lo & (0xFFFFFFFFu << (shift + 4)));
+        lo = keep | ((uint32_t)b << shift);
+        hi = lo | ((1u << shift) - 1u);
+        __syncthreads();
+        if (hb == remaining) break;
+    }
+}
+
+// Emit the kept ids of the LDS list (already in id order) to out[0..k).
+__device__ void emit_from_list(int m, uint32_t lo, uint32_t hi, uint32_t remaining,
+                               SelShared& sh, int32_t* out, float* score_out) {
+    const int tid = threadIdx.x;
+    const int seg = (m + NT - 1) / NT;
+    const int e0 = min(m, tid * seg), e1 = min(m, e0 + seg);
+    uint32_t n_in = 0;
+    for (int e = e0; e < e1; ++e) {
+        const uint32_t k = sh.key[e];
+        n_in += (k >= lo && k <= hi);
+    }
+    uint32_t tot;
+    uint32_t rank = block_excl_scan(n_in, sh, &tot);
+    uint32_t n_sel = 0;
+    {
+        uint32_t r = rank;
+        for (int e = e0; e < e1; ++e) {
+            const uint32_t k = sh.key[e];
+            if (k > hi) {
+                ++n_sel;
+            } else if (k >= lo) {
+                n_sel += (r < remaining);
+                ++r;
+            }
+        }
+    }
+    uint32_t pos = block_excl_scan(n_sel, sh, &tot);
+    for (int e = e0; e < e1; ++e) {
+        const uint32_t k = sh.key[e];
+        bool take = false;
+        if (k > hi) {
+            take = true;
+        } else if (k >= lo) {
+            take = rank < remaining;
+            ++rank;
+        }
+        if (take) {
+            out[pos] = sh.id[e];
+            if (score_out) score_out[pos] = key_to_float(k);
+            ++pos;
+        }
+    }
+}
+
+__device__ __forceinline__ f32x4 load_row4(const float* row, int64_t e, int64_t n) {
+    // row is 16-byte aligned and padded to a multiple of 4 elements
+    f32x4 v = *reinterpret_cast<const f32x4*>(row + e);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        if (e + u >= n) v[u] = -INFINITY;
+    return v;
+}
+
+// Exact selection directly over the row in global memory.
+__device__ void select_global(const float* row, int64_t n, int k, SelShared& sh, int32_t* out,
+                              float* score_out) {
+    const int tid = threadIdx.x;
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int64_t e = tid; e < n; e += NT) {
+        const uint32_t kk = order_key(row[e]);
+        mn = min(mn, kk);
+        mx = max(mx, kk);
+    }
+    block_minmax(mn, mx, sh);
+    uint32_t lo, hi, remaining = (uint32_t)k;
+    const int shift = start_range(mn, mx, lo, hi);
+    refine([&](int64_t e) { return order_key(row[e]); }, n, shift, lo, hi, remaining, sh);
+
+    // ordered emission, one 4-element group per thread per tile
+    uint32_t rank_base = 0, pos_base = 0;
+    for (int64_t base = 0; base < n; base += 4 * NT) {
+        const int64_t e0 = base + 4 * tid;
+        uint32_t kk[4];
+        uint32_t n_in = 0;
+        if (e0 < n) {
+            const f32x4 v = load_row4(row, e0, n);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                kk[u] = (e0 + u < n) ? order_key(v[u]) : 0u;
+                n_in += (e0 + u < n) && kk[u] >= lo && kk[u] <= hi;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kk[u] = 0u;
+        }
+        uint32_t tot_in;
+        uint32_t rank = rank_base + block_excl_scan(n_in, sh, &tot_in);
+        bool take[4];
+        uint32_t n_sel = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            take[u] = false;
+            if (e0 + u < n) {
+                if (kk[u] > hi) {
+                    take[u] = true;
+                } else if (kk[u] >= lo) {
+                    take[u] = rank < remaining;
+                    ++rank;
+                }
+            }
+            n_sel += take[u];
+        }
+        uint32_t tot_sel;
+        uint32_t pos = pos_base + block_excl_scan(n_sel, sh, &tot_sel);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (take[u]) {
+                out[pos] = (int32_t)(e0 + u);
+                if (score_out) score_out[pos] = key_to_float(kk[u]);
+                ++pos;
+            }
+        rank_base += tot_in;
+        pos_base += tot_sel;
+    }
+}
+
+__global__ __launch_bounds__(NT) void topk_select_kernel(SelectArgs a) {
+    __shared__ SelShared sh;
+    const int tid = threadIdx.x;
+    const int i = blockIdx.x;
+    const int64_t qrow = a.row0 + i;
+    const int64_t t = a.q_pos0 + qrow;
+    const int64_t n = (t >> 2) < a.n_pools ? (t >> 2) : a.n_pools;
+    const int k = a.k_pools;
+    int32_t* out = a.idx_out + qrow * k;
+    float* sout = a.score_out ? a.score_out + qrow * k : nullptr;
+    const float* row = a.buf + (int64_t)i * a.ld;
+
+    if (n <= k) {
+        for (int j = tid; j < k; j += NT) {
+            out[j] = j < n ? j : -1;
+            if (sout) sout[j] = j < n ? row[j] : -INFINITY;
+        }
+        return;
+    }
+
+    int m = 0;  // list length
+    if (n <= CAP) {
+        for (int e = tid; e < (int)n; e += NT) {
+            sh.key[e] = order_key(row[e]);
+            sh.id[e] = e;
+        }
+        m = (int)n;
+        __syncthreads();
+    } else {
+        // threshold from a sample of SAMPLE_BLOCKS cache-line blocks
+        for (int s = tid; s < SAMPLE_N; s += NT) {
+            const int b = s / SAMPLE_LEN, u = s % SAMPLE_LEN;
+            const int64_t start = ((int64_t)b * n / SAMPLE_BLOCKS) & ~(int64_t)(SAMPLE_LEN - 1);
+            sh.key[s] = order_key(row[start + u]);
+        }
+        __syncthreads();
+        const float mu = (float)k * (float)SAMPLE_N / (float)n;
+        uint32_t r = (uint32_t)ceilf(mu + 4.0f * sqrtf(mu) + 4.0f);
+        if (r > (uint32_t)SAMPLE_N) r = SAMPLE_N;
+        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+        for (int s = tid; s < SAMPLE_N; s += NT) {
+            mn = min(mn, sh.key[s]);
+            mx = max(mx, sh.key[s]);
+        }
+        block_minmax(mn, mx, sh);
+        uint32_t lo, hi, rem = r;
+        const int shift = start_range(mn, mx, lo, hi);
+        refine([&](int64_t e) { return sh.key[e]; }, SAMPLE_N, shift, lo, hi, rem, sh);
+        const uint32_t tau = lo;  // at least r sample keys are >= tau
+        __syncthreads();
+
+        // ordered compaction of {key >= tau}
+        uint32_t count = 0;
+        for (int64_t base = 0; base < n; base += 4 * NT) {
+            const int64_t e0 = base + 4 * tid;
+            uint32_t kk[4];
+            uint32_t c = 0;
+            if (e0 < n) {
+                const f32x4 v = load_row4(row, e0, n);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    kk[u] = order_key(v[u]);
+                    c += (e0 + u < n) && kk[u] >= tau;
+                }
+            }
+            uint32_t tot;
+            uint32_t pos = count + block_excl_scan(c, sh, &tot);
+            if (c) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (e0 + u < n && kk[u] >= tau) {
+                        if (pos < (uint32_t)CAP) {
+                            sh.key[pos] = kk[u];
+                            sh.id[pos] = (int32_t)(e0 + u);
+                        }
+                        ++pos;
+                    }
+            }
+            count += tot;
+        }
+        __syncthreads();
+        if (count < (uint32_t)k || count > (uint32_t)CAP) {
+            select_global(row, n, k, sh, out, sout);
+            return;
+        }
+        m = (int)count;
+    }
+
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int e = tid; e < m; e += NT) {
+        mn = min(mn, sh.key[e]);
+        mx = max(mx, sh.key[e]);
+    }
+    block_minmax(mn, mx, sh);
+    uint32_t lo, hi, remaining = (uint32_t)k;
+    const int shift = start_range(mn, mx, lo, hi);
+    refine([&](int64_t e) { return sh.key[e]; }, m, shift, lo, hi, remaining, sh);
+    emit_from_list(m, lo, hi, remaining, sh, out, sout);
+}
+
+}  // namespace
+
+hipError_t launch_topk_select(const SelectArgs& a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    topk_select_kernel<<<dim3((unsigned)a.rows), NT, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

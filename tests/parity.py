@@ -1,0 +1,97 @@
+"""Parity rules between the GPU path and the CPU oracle.
+
+Index sets (pages: SkyRL blog, section "DeepSeek Sparse Attention (DSA)
+Optimizations" -- keep the best pools; the tolerance below is this build's
+reading of "exact up to the selection boundary"):
+  * rows with n(t) <= k must equal [0 .. n(t)-1] padded with -1, exactly;
+  * other rows must hold k distinct, ascending, eligible ids, and the
+    symmetric difference with the oracle's set may only contain pools whose
+    oracle fp32 score lies in the boundary band
+        |s(p) - s_k| <= 1e-3 |s_k| + 1e-6 max_p s(p)
+    around the oracle's k-th score s_k (counted and reported).
+Scores: |s_gpu - s_ref| <= 1e-2 |s_ref| + 1e-4 max_p |s_ref(t, p)| per row.
+Attention (oracle fed the GPU's ids): |o_gpu - o_ref| <= 2e-2 and
+|lse_gpu - lse_ref| <= 2e-2, absolute, for bf16 inputs/outputs with fp32
+accumulation on the GPU.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BAND_REL = 1e-3
+BAND_ABS_OF_MAX = 1e-6
+SCORE_REL = 1e-2
+SCORE_ABS_OF_MAX = 1e-4
+ATTN_ABS = 2e-2
+
+
+def eligible(t: int, n_pools: int) -> int:
+    return min(t // 4, n_pools)
+
+
+def check_index_rows(gpu_idx: np.ndarray, ora_idx: np.ndarray, ora_scores: np.ndarray,
+                     positions, n_pools: int, k: int) -> dict:
+    """gpu_idx / ora_idx [R, k] int32; ora_scores [R, P] fp32 (dense oracle
+    scores of the same rows); positions [R] sequence positions t."""
+    swaps = 0
+    rows_with_swaps = 0
+    worst = 0
+    for r, t in enumerate(positions):
+        n = eligible(int(t), n_pools)
+        g = gpu_idx[r]
+        o = ora_idx[r]
+        if n <= k:
+            expect = np.concatenate([np.arange(n), -np.ones(k - n)]).astype(np.int32)
+            assert np.array_equal(g, expect), f"row t={t}: trivial row differs"
+            assert np.array_equal(o, expect), f"row t={t}: oracle trivial row differs"
+            continue
+        assert np.all(g >= 0) and np.all(g < n), f"row t={t}: id out of range"
+        assert np.all(np.diff(g) > 0), f"row t={t}: ids not strictly ascending"
+        gs, os_ = set(g.tolist()), set(o.tolist())
+        diff = gs ^ os_
+        if diff:
+            s = ora_scores[r, :n]
+            # oracle k-th score in its own order (descending score, ascending id)
+            s_k = s[o].min()
+            band = BAND_REL * abs(s_k) + BAND_ABS_OF_MAX * s.max()
+            bad = [p for p in diff if abs(float(s[p]) - float(s_k)) > band]
+            assert not bad, (f"row t={t}: pools {bad[:8]} differ outside the boundary band "
+                             f"(s_k={s_k}, scores {[float(s[p]) for p in bad[:8]]})")
+            sw = len(gs - os_)
+            swaps += sw
+            rows_with_swaps += 1
+            worst = max(worst, sw)
+    return {"swaps": swaps, "rows_with_swaps": rows_with_swaps, "worst_row": worst,
+            "rows": len(positions)}
+
+
+def check_scores(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """Dense rows [R, P]; -inf entries must coincide.  Returns the worst
+    error relative to the allowed bound."""
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(gpu)), "eligibility pattern differs"
+    worst = 0.0
+    for r in range(ref.shape[0]):
+        f = fin[r]
+        if not f.any():
+            continue
+        rr = ref[r, f].astype(np.float64)
+        gg = gpu[r, f].astype(np.float64)
+        bound = SCORE_REL * np.abs(rr) + SCORE_ABS_OF_MAX * np.abs(rr).max()
+        err = np.abs(gg - rr)
+        ratio = (err / np.maximum(bound, 1e-30)).max()
+        assert np.all(err <= bound), f"row {r}: score error {err.max()} beyond bound"
+        worst = max(worst, float(ratio))
+    return worst
+
+
+def check_attention(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray,
+                    lse_ref: np.ndarray) -> tuple[float, float]:
+    err_o = np.abs(o_gpu.astype(np.float64) - o_ref)
+    assert err_o.max() <= ATTN_ABS, f"attention output error {err_o.max()}"
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(empty, np.isneginf(lse_gpu)), "empty-row pattern differs"
+    err_l = np.abs(lse_gpu[~empty].astype(np.float64) - lse_ref[~empty]) if (~empty).any() \
+        else np.zeros(1)
+    assert err_l.max() <= ATTN_ABS, f"lse error {err_l.max()}"
+    return float(err_o.max()), float(err_l.max())

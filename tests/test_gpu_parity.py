@@ -1,0 +1,222 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case prints what it runs before touching the GPU.  Small cases check
+every row; the full-size workloads check sampled rows (first and last rows,
+4-aligned boundaries, a strided sweep) in the same launch configuration the
+benchmark times.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_dsa_amd import dsa, inputs
+from oracle import oracle
+import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsa.load_library()
+
+
+def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=None,
+             check_scores=True, x=None):
+    _say(f"[case] {wl.name} s_q={wl.s_q} s_k={wl.s_k} q_pos0={wl.q_pos0} "
+         f"H_I={wl.h_idx} D_I={wl.d_idx} k={wl.k_pools} H={wl.h} D={wl.d} Dv={wl.dv} "
+         f"n_tail={wl.n_tail} chunk_q={chunk_q} seed={seed if seed is not None else wl.seed}")
+    if x is None:
+        x = inputs.make_inputs(wl, seed=seed, attention=attention, w_per_query=w_per_query)
+    dev = torch.device("cuda")
+    q_idx, k_idx, w = (x["q_idx"].to(dev), x["k_idx"].to(dev), x["w"].to(dev))
+    idx_g, sc_g = dsa.dsa_index_score_topk(q_idx, k_idx, w, wl.k_pools, q_pos0=wl.q_pos0,
+                                           chunk_q=chunk_q, want_scores=True)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.s_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    pos = wl.q_pos0 + rows
+    idx_g_rows = idx_g.cpu().numpy()[rows]
+    sc_g_rows = sc_g.cpu().numpy()[rows]
+    idx_o, sc_o = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], wl.k_pools,
+                                    q_pos0=wl.q_pos0, rows=rows)
+    s_o = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0, rows=rows)
+    stats = parity.check_index_rows(idx_g_rows, idx_o, s_o, pos, wl.n_pools, wl.k_pools)
+    _say(f"  index: {stats}")
+    # the kept pools' scores against the oracle's dense scores
+    for r in range(len(rows)):
+        sel = idx_g_rows[r] >= 0
+        ref = s_o[r][idx_g_rows[r][sel]]
+        got = sc_g_rows[r][sel]
+        if sel.any():
+            bound = parity.SCORE_REL * np.abs(ref) + parity.SCORE_ABS_OF_MAX * np.abs(
+                s_o[r][np.isfinite(s_o[r])]).max()
+            assert np.all(np.abs(got - ref) <= bound), f"row {rows[r]}: kept-pool scores differ"
+        assert np.all(np.isneginf(sc_g_rows[r][~sel]))
+    if check_scores:
+        # dense scores of a few contiguous row blocks
+        blocks = sorted(set([0, max(0, wl.s_q // 2 - 8), max(0, wl.s_q - 16)]))
+        worst = 0.0
+        for b0 in blocks:
+            nb = min(16, wl.s_q - b0)
+            g = dsa.dsa_index_scores(q_idx, k_idx, w, row0=b0, n_rows=nb, q_pos0=wl.q_pos0)
+            ref = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0,
+                                      rows=np.arange(b0, b0 + nb))
+            worst = max(worst, parity.check_scores(g.cpu().numpy(), ref))
+        _say(f"  scores: worst error / bound = {worst:.3g}")
+    if attention:
+        q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+        o_g, lse_g = dsa.dsa_sparse_attn_fwd(q, k, v, idx_g, q_pos0=wl.q_pos0,
+                                             n_tail=wl.n_tail, want_lse=True)
+        torch.cuda.synchronize()
+        scale = float(np.float32(1.0 / math.sqrt(wl.d)))
+        o_o, lse_o = oracle.sparse_attn(x["q"], x["k"], x["v"], idx_g_rows, wl.k_pools,
+                                        q_pos0=wl.q_pos0, rows=rows, n_tail=wl.n_tail,
+                                        scale=scale)
+        eo, el = parity.check_attention(o_g.float().cpu().numpy()[rows],
+                                        lse_g.cpu().numpy()[rows], o_o, lse_o)
+        _say(f"  attention: max |do| = {eo:.3g}, max |dlse| = {el:.3g}")
+    return x, idx_g
+
+
+# ---------------------------------------------------------------- small, every row
+
+def test_tiny_workload_all_rows():
+    run_case(inputs.WORKLOADS["tiny_s2048"])
+
+
+@pytest.mark.parametrize("h_idx,d_idx", [(32, 128), (16, 96), (8, 64), (4, 128), (32, 96)])
+def test_indexer_shapes_ragged(h_idx, d_idx):
+    # 3 chunks of 64 queries, a ragged last chunk and several 256-pool blocks
+    wl = inputs.custom(f"ragged_{h_idx}x{d_idx}", s_q=2500, s_k=2500, h_idx=h_idx, d_idx=d_idx,
+                       k_pools=40, h=16, d=d_idx, idx_std=1 / math.sqrt(d_idx),
+                       attn_std=1 / math.sqrt(d_idx), number=200 + h_idx + d_idx)
+    run_case(wl, chunk_q=192)
+
+
+def test_offset_queries_per_query_weights_and_tail():
+    wl = inputs.custom("offset_tail", s_q=700, s_k=3003, q_pos0=2303, h_idx=32, d_idx=128,
+                       k_pools=100, h=12, d=96, dv=64, n_tail=3, idx_std=0.1, number=301)
+    run_case(wl, chunk_q=128, w_per_query=True)
+
+
+@pytest.mark.parametrize("n_tail", [1, 2])
+def test_partial_tails(n_tail):
+    wl = inputs.custom(f"tail{n_tail}", s_q=300, s_k=300, h_idx=8, d_idx=64, k_pools=16, h=5,
+                       d=64, dv=128, n_tail=n_tail, number=310 + n_tail)
+    run_case(wl, chunk_q=64)
+
+
+def test_k_covers_every_pool_equals_dense_attention():
+    # with k >= P the selection is every eligible pool and the attention is
+    # dense masked attention (section "Making Sparse Attention Actually Sparse")
+    wl = inputs.custom("dense_equiv", s_q=520, s_k=520, h_idx=4, d_idx=64, k_pools=200, h=16,
+                       d=128, n_tail=3, number=320)
+    x, idx_g = run_case(wl, chunk_q=64)
+    idx = idx_g.cpu().numpy()
+    for t in range(520):
+        n = min(t // 4, 130)
+        assert np.array_equal(idx[t, :n], np.arange(n))
+
+
+def test_k_equals_one_and_tiny_sequences():
+    wl = inputs.custom("k1", s_q=130, s_k=130, h_idx=4, d_idx=64, k_pools=1, h=1, d=64,
+                       number=330)
+    run_case(wl, chunk_q=64)
+    wl = inputs.custom("s3", s_q=3, s_k=3, h_idx=4, d_idx=64, k_pools=4, h=2, d=64, number=331)
+    run_case(wl, chunk_q=64, check_scores=False)
+
+
+def test_ties_resolve_to_lower_ids():
+    wl = inputs.custom("ties", s_q=1100, s_k=1100, h_idx=8, d_idx=64, k_pools=37, h=4, d=64,
+                       number=340)
+    x = inputs.make_inputs(wl)
+    # all weights zero: every score is +0 and the first k pools are kept
+    x0 = dict(x)
+    x0["w"] = torch.zeros_like(x["w"])
+    _, idx0 = run_case(wl, chunk_q=64, x=x0, attention=False)
+    idx0 = idx0.cpu().numpy()
+    for t in range(wl.s_q):
+        n = min(t // 4, wl.n_pools)
+        m = min(n, wl.k_pools)
+        assert np.array_equal(idx0[t, :m], np.arange(m)) and np.all(idx0[t, m:] == -1)
+    # duplicated pools: pools 10..19 copy pools 0..9, so equal scores straddle the boundary
+    x1 = dict(x)
+    k = x["k_idx"].clone()
+    for r in range(10):
+        k[4 * (10 + r): 4 * (11 + r)] = k[4 * r: 4 * (r + 1)]
+    k[200:1100] = (k[200:1100].float() * 0.25).to(torch.bfloat16)
+    x1["k_idx"] = k
+    run_case(wl, chunk_q=64, x=x1, attention=False)
+
+
+def test_large_row_paths_and_sampling():
+    # rows longer than the LDS candidate list (4096 pools) take the sampled path;
+    # a heavy-tied row forces the exact fallback
+    wl = inputs.custom("long_rows", s_q=256, s_k=40000, q_pos0=39744, h_idx=16, d_idx=64,
+                       k_pools=300, h=4, d=64, number=350)
+    run_case(wl, rows=np.arange(0, 256, 3), chunk_q=128)
+    x = inputs.make_inputs(wl, attention=False)
+    x["w"] = torch.zeros_like(x["w"])
+    _, idx0 = run_case(wl, rows=np.arange(0, 256, 17), chunk_q=128, x=x, attention=False,
+                       check_scores=False)
+    assert np.all(idx0.cpu().numpy() == np.arange(wl.k_pools)[None, :])
+
+
+def test_deterministic_bitwise():
+    wl = inputs.custom("determinism", s_q=1500, s_k=1500, h_idx=32, d_idx=128, k_pools=64,
+                       h=16, d=128, number=360)
+    x = inputs.make_inputs(wl)
+    dev = torch.device("cuda")
+    a = [t.to(dev) for t in (x["q_idx"], x["k_idx"], x["w"], x["q"], x["k"], x["v"])]
+    outs = []
+    for _ in range(2):
+        idx, sc = dsa.dsa_index_score_topk(a[0], a[1], a[2], 64, want_scores=True)
+        o, lse = dsa.dsa_sparse_attn_fwd(a[3], a[4], a[5], idx, want_lse=True)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (idx, sc, o, lse)])
+    for u, v in zip(*outs):
+        assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
+
+
+def test_k_and_v_may_alias():
+    wl = inputs.custom("kv_alias", s_q=400, s_k=400, h_idx=4, d_idx=64, k_pools=20, h=8, d=64,
+                       number=370)
+    x = inputs.make_inputs(wl)
+    x["v"] = x["k"]
+    run_case(wl, chunk_q=64, x=x)
+
+
+# ---------------------------------------------------------------- the page's workloads
+
+def test_workload_s32k_sampled():
+    wl = inputs.WORKLOADS["s32k"]
+    run_case(wl, rows=inputs.sample_rows(wl.s_q, 384))
+
+
+@pytest.mark.slow
+def test_workload_s128k_sampled():
+    wl = inputs.WORKLOADS["s128k"]
+    run_case(wl, rows=inputs.sample_rows(wl.s_q, 160), check_scores=False)
+
+
+@pytest.mark.slow
+def test_workload_nope_s64k_sampled():
+    wl = inputs.WORKLOADS["nope_s64k"]
+    run_case(wl, rows=inputs.sample_rows(wl.s_q, 160), check_scores=False)
+
+
+@pytest.mark.slow
+def test_workload_share_1m_sampled():
+    wl = inputs.WORKLOADS["share_1m"]
+    run_case(wl, rows=inputs.sample_rows(wl.s_q, 40), check_scores=False)
