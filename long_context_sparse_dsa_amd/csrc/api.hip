@@ -33,7 +33,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 constexpr int64_t kMaxKPools = 2048;
-constexpr int64_t kDefaultChunk = 256;
+constexpr int64_t kDefaultChunkMax = 4096;
+constexpr int64_t kDefaultBufferBudget = int64_t(1) << 30;
 constexpr int64_t kMaxChunk = 1 << 16;
 constexpr int64_t kScoreBufferCap = int64_t(2) << 30;  // per chunk, as the page keeps it
 
@@ -133,7 +134,13 @@ int64_t score_ld(const IndexShape& sh) { return round_up(sh.n_pools > 0 ? sh.n_p
 dsa_status resolve_chunk(const IndexShape& sh, int64_t chunk_q, int64_t* out) {
     if (chunk_q < 0) return fail(DSA_ERR_INVALID_ARG, "chunk_q %lld < 0", (long long)chunk_q);
     if (chunk_q == 0) {
-        chunk_q = kDefaultChunk;
+        // the largest multiple of 64 (at most 4096 queries, and no more than
+        // the queries there are) whose score buffer fits a 1 GiB budget
+        chunk_q = kDefaultBufferBudget / (score_ld(sh) * 4);
+        if (chunk_q > kDefaultChunkMax) chunk_q = kDefaultChunkMax;
+        if (chunk_q > round_up(sh.s_q, 64)) chunk_q = round_up(sh.s_q, 64);
+        chunk_q = chunk_q / 64 * 64;
+        if (chunk_q < 64) chunk_q = 64;
     } else if (chunk_q % 64 != 0 || chunk_q > kMaxChunk) {
         return fail(DSA_ERR_UNSUPPORTED, "chunk_q %lld must be a multiple of 64 up to %lld",
                     (long long)chunk_q, (long long)kMaxChunk);

@@ -46,6 +46,17 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 // A zero score is stored as +0.0 so that its order key is unique.
 __device__ __forceinline__ float canonical_zero(float x) { return x == 0.0f ? 0.0f : x; }
 
-__device__ __forceinline__ float relu(float x) { return x > 0.0f ? x : 0.0f; }
+// max(x, 0) as one integer max: a non-negative float's bits are a
+// non-negative int, a negative float's (and -0.0's) a negative one.
+__device__ __forceinline__ float relu(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// x[l] + x[l ^ 32] on every lane l (both halves add low half + high half).
+__device__ __forceinline__ float add_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace dsa

@@ -169,6 +169,11 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
         }
     }
 
+    // The resident fragments are loaded once; make that explicit so that the
+    // tile loop never waits on the memory counter for them (which would also
+    // wait for the next tile's prefetch).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
     // tile j covers chunk rows i_begin + j*QPT .. +QPT: a contiguous block of
     // 32 * DI bf16 in q_idx (rows = query*HI + head)
     u32x4 pre[CPT];
@@ -253,20 +258,15 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
             float qv[4];
             int nq;
             if constexpr (HI == 32) {
-                float s = (part[0] + part[1]) + (part[2] + part[3]);
-                s += __shfl_xor(s, 32);
-                qv[0] = s;
+                qv[0] = add_halves((part[0] + part[1]) + (part[2] + part[3]));
                 nq = 1;
             } else if constexpr (HI == 16) {
-                float s0 = part[0] + part[1], s1 = part[2] + part[3];
-                s0 += __shfl_xor(s0, 32);
-                s1 += __shfl_xor(s1, 32);
-                qv[0] = s0;
-                qv[1] = s1;
+                qv[0] = add_halves(part[0] + part[1]);
+                qv[1] = add_halves(part[2] + part[3]);
                 nq = 2;
             } else if constexpr (HI == 8) {
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) qv[g4] = part[g4] + __shfl_xor(part[g4], 32);
+                for (int g4 = 0; g4 < 4; ++g4) qv[g4] = add_halves(part[g4]);
                 nq = 4;
             } else {  // HI == 4: rows 8*g4 + 4*half + i -> query 2*g4 + half, complete in-lane
 #pragma unroll

@@ -41,21 +41,54 @@ constexpr int CAP = 4096;
 constexpr int SAMPLE_BLOCKS = 128;
 constexpr int SAMPLE_LEN = 16;
 constexpr int SAMPLE_N = SAMPLE_BLOCKS * SAMPLE_LEN;
+// per-thread digit counters, one row of NT per digit, padded so that the
+// transposed reduction (16 digits x 16 partial sums per wave) is free of
+// bank conflicts
+constexpr int CNT_STRIDE = NT + 16;
 
 struct SelShared {
-    uint32_t key[CAP];
-    int32_t id[CAP];
-    uint32_t cnt[16 * NT];
+    alignas(16) uint32_t key[CAP];
+    alignas(16) int32_t id[CAP];
+    uint32_t cnt[16 * CNT_STRIDE];
     uint32_t hist[16];
     uint32_t tmp[8];
+    uint32_t wtot[8 * (NT / 64)];
 };
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t n = __shfl_up(v, off);
-        if (lane >= off) v += n;
-    }
+// Wave-level inclusive scans on DPP: row shifts 1, 2, 4, 8 within each row
+// of 16 lanes, then row broadcasts of lanes 15 and 31 into the later rows.
+// Lanes without a source take the identity `id`.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_incl_scan_op(uint32_t v, uint32_t id, Op op) {
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x111, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x112, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x114, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x118, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x142, 0xA, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x143, 0xC, 0xF, false));
+    return v;
+}
+
+struct AddOp {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct MinOp {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+struct MaxOp {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int /*lane*/) {
+    return wave_incl_scan_op(v, 0u, AddOp{});
+}
+
+// Sum over each row of 16 lanes, valid in lane 15 of the row.
+__device__ __forceinline__ uint32_t row16_sum(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);
     return v;
 }
 
@@ -77,14 +110,44 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SelShared& sh, u
     return base + inc - v;
 }
 
+// Exclusive prefix over the workgroup of VB counts per thread, ordered
+// slot-major: all threads' slot 0, then all threads' slot 1, ...  (the order
+// of elements base + (u*NT + tid)*4 + j).  Returns the offsets in `off` and
+// the grand total.
+template <int VB>
+__device__ __forceinline__ uint32_t block_excl_scan_slots(const uint32_t (&c)[VB],
+                                                          uint32_t (&off)[VB], SelShared& sh,
+                                                          uint32_t* wtot) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t inc[VB];
+#pragma unroll
+    for (int u = 0; u < VB; ++u) {
+        inc[u] = wave_incl_scan(c[u], lane);
+        if (lane == 63) wtot[u * (NT / 64) + wave] = inc[u];
+    }
+    __syncthreads();
+    uint32_t base = 0;
+#pragma unroll
+    for (int u = 0; u < VB; ++u) {
+        uint32_t before = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) {
+            const uint32_t x = wtot[u * (NT / 64) + w];
+            if (w < wave) before += x;
+            tot += x;
+        }
+        off[u] = base + before + inc[u] - c[u];
+        base += tot;
+    }
+    __syncthreads();
+    return base;
+}
+
 __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, SelShared& sh) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        mn = min(mn, (uint32_t)__shfl_xor(mn, off));
-        mx = max(mx, (uint32_t)__shfl_xor(mx, off));
-    }
-    if (lane == 0) {
+    mn = wave_incl_scan_op(mn, 0xFFFFFFFFu, MinOp{});
+    mx = wave_incl_scan_op(mx, 0u, MaxOp{});
+    if (lane == 63) {
         sh.tmp[wave] = mn;
         sh.tmp[4 + wave] = mx;
     }
@@ -120,21 +183,19 @@ __device__ void refine(KeyAt key_at, int64_t n, int shift, uint32_t& lo, uint32_
     const int tid = threadIdx.x;
     for (; shift >= 0 && lo != hi; shift -= 4) {
 #pragma unroll
-        for (int d = 0; d < 16; ++d) sh.cnt[d * NT + tid] = 0;
+        for (int d = 0; d < 16; ++d) sh.cnt[d * CNT_STRIDE + tid] = 0;
         for (int64_t e = tid; e < n; e += NT) {
             const uint32_t k = key_at(e);
-            if (k >= lo && k <= hi) sh.cnt[((k >> shift) & 15u) * NT + tid] += 1;
+            if (k >= lo && k <= hi) sh.cnt[((k >> shift) & 15u) * CNT_STRIDE + tid] += 1;
         }
         __syncthreads();
+        // digit tid/16 summed over threads (tid%16) + 16u, u = 0..15
         uint32_t s = 0;
-        const uint32_t* c = &sh.cnt[(tid >> 4) * NT + (tid & 15) * 16];
+        const uint32_t* c = &sh.cnt[(tid >> 4) * CNT_STRIDE + (tid & 15)];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) s += c[u];
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        if ((tid & 15) == 0) sh.hist[tid >> 4] = s;
+        for (int u = 0; u < 16; ++u) s += c[16 * u];
+        s = row16_sum(s);
+        if ((tid & 15) == 15) sh.hist[tid >> 4] = s;
         __syncthreads();
         uint32_t above = 0, hb = 0;
         int b = 0;
@@ -158,9 +219,11 @@ __device__ void refine(KeyAt key_at, int64_t n, int shift, uint32_t& lo, uint32_
 
 // Emit the kept ids of the LDS list (already in id order) to out[0..k).
 __device__ void emit_from_list(int m, uint32_t lo, uint32_t hi, uint32_t remaining,
-                               SelShared& sh, int32_t* out, float* score_out) {
+                               SelShared& sh, int32_t* out, float* score_out, int k_out) {
     const int tid = threadIdx.x;
-    const int seg = (m + NT - 1) / NT;
+    // contiguous segments of odd length: a wave's lanes then read LDS words
+    // at an odd stride, which touches every bank once
+    const int seg = ((m + NT - 1) / NT) | 1;
     const int e0 = min(m, tid * seg), e1 = min(m, e0 + seg);
     uint32_t n_in = 0;
     for (int e = e0; e < e1; ++e) {
@@ -193,8 +256,10 @@ __device__ void emit_from_list(int m, uint32_t lo, uint32_t hi, uint32_t remaini
             ++rank;
         }
         if (take) {
-            out[pos] = sh.id[e];
-            if (score_out) score_out[pos] = key_to_float(k);
+            if (pos < (uint32_t)k_out) {
+                out[pos] = sh.id[e];
+                if (score_out) score_out[pos] = key_to_float(k);
+            }
             ++pos;
         }
     }
@@ -263,8 +328,10 @@ __device__ void select_global(const float* row, int64_t n, int k, SelShared& sh,
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             if (take[u]) {
-                out[pos] = (int32_t)(e0 + u);
-                if (score_out) score_out[pos] = key_to_float(kk[u]);
+                if (pos < (uint32_t)k) {
+                    out[pos] = (int32_t)(e0 + u);
+                    if (score_out) score_out[pos] = key_to_float(kk[u]);
+                }
                 ++pos;
             }
         rank_base += tot_in;
@@ -272,7 +339,7 @@ __device__ void select_global(const float* row, int64_t n, int k, SelShared& sh,
     }
 }
 
-__global__ __launch_bounds__(NT) void topk_select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
     __shared__ SelShared sh;
     const int tid = threadIdx.x;
     const int i = blockIdx.x;
@@ -294,18 +361,24 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(SelectArgs a) {
 
     int m = 0;  // list length
     if (n <= CAP) {
-        for (int e = tid; e < (int)n; e += NT) {
-            sh.key[e] = order_key(row[e]);
-            sh.id[e] = e;
+        // whole row into the list; rows are 16-byte aligned and padded to 4
+        for (int e = 4 * tid; e < (int)n; e += 4 * NT) {
+            const f32x4 v = load_row4(row, e, n);
+            *reinterpret_cast<u32x4*>(&sh.key[e]) =
+                u32x4{order_key(v[0]), order_key(v[1]), order_key(v[2]), order_key(v[3])};
+            *reinterpret_cast<u32x4*>(&sh.id[e]) =
+                u32x4{(uint32_t)e, (uint32_t)e + 1, (uint32_t)e + 2, (uint32_t)e + 3};
         }
         m = (int)n;
         __syncthreads();
     } else {
         // threshold from a sample of SAMPLE_BLOCKS cache-line blocks
-        for (int s = tid; s < SAMPLE_N; s += NT) {
-            const int b = s / SAMPLE_LEN, u = s % SAMPLE_LEN;
+        for (int s4 = tid; s4 < SAMPLE_N / 4; s4 += NT) {
+            const int b = (4 * s4) / SAMPLE_LEN, u = (4 * s4) % SAMPLE_LEN;
             const int64_t start = ((int64_t)b * n / SAMPLE_BLOCKS) & ~(int64_t)(SAMPLE_LEN - 1);
-            sh.key[s] = order_key(row[start + u]);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(row + start + u);
+            *reinterpret_cast<u32x4*>(&sh.key[4 * s4]) =
+                u32x4{order_key(v[0]), order_key(v[1]), order_key(v[2]), order_key(v[3])};
         }
         __syncthreads();
         const float mu = (float)k * (float)SAMPLE_N / (float)n;
@@ -323,34 +396,53 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(SelectArgs a) {
         const uint32_t tau = lo;  // at least r sample keys are >= tau
         __syncthreads();
 
-        // ordered compaction of {key >= tau}
-        uint32_t count = 0;
-        for (int64_t base = 0; base < n; base += 4 * NT) {
-            const int64_t e0 = base + 4 * tid;
-            uint32_t kk[4];
-            uint32_t c = 0;
-            if (e0 < n) {
-                const f32x4 v = load_row4(row, e0, n);
+        // ordered compaction of {key >= tau}: batches of VB 16-byte loads per
+        // thread, the next batch in flight while the current one is compacted
+        constexpr int VB = 4;
+        constexpr int BATCH = 4 * NT * VB;
+        f32x4 cur[VB], nxt[VB];
+        auto fetch = [&](int64_t base, f32x4 (&v)[VB]) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    kk[u] = order_key(v[u]);
-                    c += (e0 + u < n) && kk[u] >= tau;
-                }
+            for (int u = 0; u < VB; ++u) {
+                const int64_t e = base + (int64_t)(u * NT + tid) * 4;
+                v[u] = e < n ? *reinterpret_cast<const f32x4*>(row + e)
+                             : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             }
-            uint32_t tot;
-            uint32_t pos = count + block_excl_scan(c, sh, &tot);
-            if (c) {
+        };
+        const float tau_f = key_to_float(tau);
+        uint32_t count = 0;
+        fetch(0, cur);
+        for (int64_t base = 0; base < n; base += BATCH) {
+            if (base + BATCH < n) fetch(base + BATCH, nxt);
+            uint32_t c[VB], off[VB];
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (e0 + u < n && kk[u] >= tau) {
+            for (int u = 0; u < VB; ++u) {
+                const int64_t e = base + (int64_t)(u * NT + tid) * 4;
+                uint32_t cc = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) cc += (e + j < n) && cur[u][j] >= tau_f;
+                c[u] = cc;
+            }
+            const uint32_t tot = block_excl_scan_slots<VB>(c, off, sh, sh.wtot);
+#pragma unroll
+            for (int u = 0; u < VB; ++u) {
+                if (!c[u]) continue;
+                const int64_t e = base + (int64_t)(u * NT + tid) * 4;
+                uint32_t pos = count + off[u];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (e + j < n && cur[u][j] >= tau_f) {
                         if (pos < (uint32_t)CAP) {
-                            sh.key[pos] = kk[u];
-                            sh.id[pos] = (int32_t)(e0 + u);
+                            sh.key[pos] = order_key(cur[u][j]);
+                            sh.id[pos] = (int32_t)(e + j);
                         }
                         ++pos;
                     }
+                }
             }
             count += tot;
+#pragma unroll
+            for (int u = 0; u < VB; ++u) cur[u] = nxt[u];
         }
         __syncthreads();
         if (count < (uint32_t)k || count > (uint32_t)CAP) {
@@ -369,7 +461,7 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(SelectArgs a) {
     uint32_t lo, hi, remaining = (uint32_t)k;
     const int shift = start_range(mn, mx, lo, hi);
     refine([&](int64_t e) { return sh.key[e]; }, m, shift, lo, hi, remaining, sh);
-    emit_from_list(m, lo, hi, remaining, sh, out, sout);
+    emit_from_list(m, lo, hi, remaining, sh, out, sout, k);
 }
 
 }  // namespace
