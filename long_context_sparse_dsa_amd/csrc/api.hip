@@ -116,17 +116,21 @@ dsa_status check_index_shape(const IndexShape& sh, bool need_k) {
                     sh.d_idx);
     if (sh.dtype != DSA_BF16 && sh.dtype != DSA_FP8_E4M3)
         return fail(DSA_ERR_INVALID_ARG, "unknown dtype %d", sh.dtype);
-    if (sh.dtype == DSA_FP8_E4M3)
-        return fail(DSA_ERR_UNSUPPORTED, "the fp8 E4M3 indexer is not built in this version");
     if (need_k && (sh.k_pools < 1 || sh.k_pools > kMaxKPools))
         return fail(DSA_ERR_UNSUPPORTED, "k_pools %d: supported range is 1..%lld", sh.k_pools,
                     (long long)kMaxKPools);
     return DSA_OK;
 }
 
+// Pooled key table: bf16 [P][2*d_idx] (hi | lo); fp8 [P][d_idx] codes, then
+// [P] fp32 per-pool scales 2^e at the next 256-byte boundary.
+int64_t kbar_codes_bytes(const IndexShape& sh) {
+    return sh.dtype == DSA_BF16 ? round_up(sh.n_pools * 2LL * sh.d_idx * 2, 256)
+                                : round_up(sh.n_pools * (int64_t)sh.d_idx, 256);
+}
+
 int64_t kbar_bytes(const IndexShape& sh) {
-    const int64_t per_pool = sh.dtype == DSA_BF16 ? 2LL * sh.d_idx * 2 : sh.d_idx + 4;
-    return round_up(sh.n_pools * per_pool, 256);
+    return kbar_codes_bytes(sh) + (sh.dtype == DSA_BF16 ? 0 : round_up(sh.n_pools * 4, 256));
 }
 
 int64_t score_ld(const IndexShape& sh) { return round_up(sh.n_pools > 0 ? sh.n_pools : 1, 64); }
@@ -172,7 +176,41 @@ dsa_status check_index_ptrs(const void* q_idx, const void* k_idx, const float* q
                     (long long)w_stride);
     if (sh.dtype == DSA_BF16 && (q_scale || k_scale))
         return fail(DSA_ERR_INVALID_ARG, "q_scale/k_scale apply to the fp8 indexer only");
+    if ((reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u))
+        return fail(DSA_ERR_INVALID_ARG, "q_scale and k_scale must be 4-byte aligned");
     return DSA_OK;
+}
+
+hipError_t launch_pool(const IndexShape& sh, const void* k_idx, void* table, hipStream_t s) {
+    Timed tm(K_POOL, s);
+    if (sh.dtype == DSA_BF16)
+        return dsa::launch_pool_keys_bf16(static_cast<const uint16_t*>(k_idx), sh.n_pools,
+                                          sh.d_idx, static_cast<uint16_t*>(table), s);
+    char* t = static_cast<char*>(table);
+    return dsa::launch_pool_keys_fp8(static_cast<const uint8_t*>(k_idx), sh.n_pools, sh.d_idx,
+                                     reinterpret_cast<uint8_t*>(t),
+                                     reinterpret_cast<float*>(t + kbar_codes_bytes(sh)), s);
+}
+
+void fill_score_args(dsa::ScoreArgs& a, const IndexShape& sh, const void* q_idx, void* table,
+                     const float* q_scale, const float* k_scale, const float* w,
+                     int64_t w_stride) {
+    a.q_idx = q_idx;
+    a.kbar = table;
+    a.pool_scale = sh.dtype == DSA_BF16
+                       ? nullptr
+                       : reinterpret_cast<const float*>(static_cast<char*>(table) +
+                                                        kbar_codes_bytes(sh));
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.w = w;
+    a.w_stride = w_stride;
+    a.s_q = sh.s_q;
+    a.q_pos0 = sh.q_pos0;
+    a.n_pools = sh.n_pools;
+    a.h_idx = sh.h_idx;
+    a.d_idx = sh.d_idx;
+    a.fp8 = sh.dtype == DSA_FP8_E4M3;
 }
 
 }  // namespace
@@ -224,14 +262,11 @@ dsa_status dsa_index_score_topk(const void* q_idx, const void* k_idx, const floa
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
-    uint16_t* kbar = reinterpret_cast<uint16_t*>(ws);
     float* buf = reinterpret_cast<float*>(ws + kbar_bytes(sh));
     const int64_t ld = score_ld(sh);
     hipError_t e;
     if (sh.n_pools > 0) {
-        Timed tm(K_POOL, s);
-        e = dsa::launch_pool_keys_bf16(static_cast<const uint16_t*>(k_idx), sh.n_pools, d_idx,
-                                       kbar, s);
+        e = launch_pool(sh, k_idx, ws, s);
         if (e != hipSuccess) return hip_fail(e, "pool_keys launch");
     }
     for (int64_t c0 = 0; c0 < s_q; c0 += cq) {
@@ -240,19 +275,10 @@ dsa_status dsa_index_score_topk(const void* q_idx, const void* k_idx, const floa
         const int64_t n_chunk = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
         if (n_chunk > 0 && (n_chunk > k_pools || score_out)) {
             dsa::ScoreArgs a{};
-            a.q_idx = q_idx;
-            a.kbar = kbar;
-            a.w = w;
-            a.w_stride = w_stride_q;
-            a.s_q = s_q;
+            fill_score_args(a, sh, q_idx, ws, q_scale, k_scale, w, w_stride_q);
             a.row0 = c0;
             a.rows = rows;
-            a.q_pos0 = q_pos0;
-            a.n_pools = sh.n_pools;
             a.n_chunk = n_chunk;
-            a.h_idx = h_idx;
-            a.d_idx = d_idx;
-            a.fp8 = 0;
             a.buf = buf;
             a.ld = ld;
             Timed tm(K_SCORE, s);
@@ -296,41 +322,24 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const float* q
     if (n_rows > 0 && !scores_out) return fail(DSA_ERR_INVALID_ARG, "scores_out must be non-null");
     if (!aligned16(scores_out)) return fail(DSA_ERR_INVALID_ARG, "scores_out must be 16-byte aligned");
     const size_t need = (size_t)kbar_bytes(sh);
-    if (n_rows == 0 || sh.n_pools == 0) {
-        if (n_rows > 0 && sh.n_pools == 0) return DSA_OK;  // [n_rows, 0]
-        return DSA_OK;
-    }
+    if (n_rows == 0 || sh.n_pools == 0) return DSA_OK;  // nothing to write
     if (!workspace || workspace_bytes < need)
         return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    uint16_t* kbar = static_cast<uint16_t*>(workspace);
     hipError_t e = dsa::launch_fill_f32(scores_out, n_rows * sh.n_pools, -INFINITY, s);
     if (e != hipSuccess) return hip_fail(e, "fill launch");
-    {
-        Timed tm(K_POOL, s);
-        e = dsa::launch_pool_keys_bf16(static_cast<const uint16_t*>(k_idx), sh.n_pools, d_idx,
-                                       kbar, s);
-        if (e != hipSuccess) return hip_fail(e, "pool_keys launch");
-    }
+    e = launch_pool(sh, k_idx, workspace, s);
+    if (e != hipSuccess) return hip_fail(e, "pool_keys launch");
     const int64_t t_last = q_pos0 + row0 + n_rows - 1;
     const int64_t n_chunk = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
     if (n_chunk > 0) {
         dsa::ScoreArgs a{};
-        a.q_idx = q_idx;
-        a.kbar = kbar;
-        a.w = w;
-        a.w_stride = w_stride_q;
-        a.s_q = s_q;
+        fill_score_args(a, sh, q_idx, workspace, q_scale, k_scale, w, w_stride_q);
         a.row0 = row0;
         a.rows = (int)n_rows;
-        a.q_pos0 = q_pos0;
-        a.n_pools = sh.n_pools;
         a.n_chunk = n_chunk;
-        a.h_idx = h_idx;
-        a.d_idx = d_idx;
-        a.fp8 = 0;
         a.buf = scores_out;
         a.ld = sh.n_pools;
         Timed tm(K_SCORE, s);

@@ -83,8 +83,93 @@ hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, int64_t n_pools, int d_i
     return hipGetLastError();
 }
 
-hipError_t launch_pool_keys_fp8(const uint8_t*, int64_t, int, uint8_t*, float*, hipStream_t) {
-    return hipErrorNotSupported;
+// ---------------------------------------------------------------- fp8 pooling
+//
+// OCP FP8 E4M3 ("e4m3fn"): sign, 4 exponent bits with bias 7, 3 mantissa
+// bits, no infinities, largest finite 448, subnormals m * 2^-9.  A pooled key
+// is the mean of its 4 rows' code values (exact in fp32), re-quantised with a
+// power-of-two scale 2^e, e the smallest integer with max|mean| <= 448 * 2^e:
+// scaling by 2^-e is exact, so the code is the round-to-nearest-even of an
+// exact value and does not depend on the precision used.
+
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+    const uint32_t e = (code >> 3) & 15u, m = code & 7u;
+    const float mag = e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8u + m), (int)e - 10);
+    return (code & 0x80u) ? -mag : mag;
+}
+
+// |x| <= 448; ties to the even mantissa (rintf rounds half to even).
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+    const float a = fabsf(x);
+    uint32_t code;
+    if (a < 0x1p-6f) {
+        code = (uint32_t)rintf(a * 512.0f);  // 8 rounds up into the smallest normal, 0x08
+    } else {
+        const int E = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;
+        uint32_t mm = (uint32_t)rintf(ldexpf(a, 3 - E)) - 8u;  // 0..8
+        uint32_t ee = (uint32_t)(E + 7);
+        if (mm == 8u) {
+            mm = 0u;
+            ++ee;
+        }
+        code = (ee << 3) | mm;
+        if (code > 0x7Eu) code = 0x7Eu;
+    }
+    return code | sign;
+}
+
+template <int DI>
+__global__ __launch_bounds__(256) void pool_keys_fp8_kernel(const uint8_t* __restrict__ k8,
+                                                            int64_t n_pools,
+                                                            uint8_t* __restrict__ kbar8,
+                                                            float* __restrict__ pool_scale) {
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= n_pools) return;
+    float m[DI];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < DI / 16; ++c) {
+        u32x4 r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = ldg16(k8 + (p * 4 + j) * DI + 16 * c);
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+            const int word = b >> 2, sh = (b & 3) * 8;
+            float s = e4m3_value((r[0][word] >> sh) & 0xFFu);
+            s += e4m3_value((r[1][word] >> sh) & 0xFFu);
+            s += e4m3_value((r[2][word] >> sh) & 0xFFu);
+            s += e4m3_value((r[3][word] >> sh) & 0xFFu);
+            m[16 * c + b] = s * 0.25f;
+            amax = fmaxf(amax, fabsf(m[16 * c + b]));
+        }
+    }
+    int e = 0;
+    if (amax > 0.0f) {
+        e = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 10;
+        while (amax > ldexpf(448.0f, e)) ++e;
+    }
+#pragma unroll
+    for (int c = 0; c < DI / 16; ++c) {
+        u32x4 o = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int b = 0; b < 16; ++b) o[b >> 2] |= e4m3_code(ldexpf(m[16 * c + b], -e)) << ((b & 3) * 8);
+        *reinterpret_cast<u32x4*>(kbar8 + p * DI + 16 * c) = o;
+    }
+    pool_scale[p] = ldexpf(1.0f, e);
+}
+
+hipError_t launch_pool_keys_fp8(const uint8_t* k8, int64_t n_pools, int d_idx, uint8_t* kbar8,
+                                float* pool_scale, hipStream_t stream) {
+    if (n_pools <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((n_pools + 255) / 256));
+    switch (d_idx) {
+        case 64: pool_keys_fp8_kernel<64><<<grid, 256, 0, stream>>>(k8, n_pools, kbar8, pool_scale); break;
+        case 96: pool_keys_fp8_kernel<96><<<grid, 256, 0, stream>>>(k8, n_pools, kbar8, pool_scale); break;
+        case 128: pool_keys_fp8_kernel<128><<<grid, 256, 0, stream>>>(k8, n_pools, kbar8, pool_scale); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- fill
@@ -292,6 +377,243 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     }
 }
 
+struct ScoreK8 {
+    const uint8_t* q8;
+    const uint8_t* kbar8;
+    const float* pool_scale;
+    const float* q_scale;
+    const float* k_scale;
+    const float* w;
+    int64_t w_stride;
+    int64_t s_q;
+    int64_t row0;
+    int rows;
+    int gq;
+    int64_t q_pos0;
+    int64_t n_pools;
+    float* buf;
+    int64_t ld;
+};
+
+// fp8 E4M3 scoring with the 32x32x64 f8f6f4 MFMA (unit block scales): lane l
+// supplies A row / B column l % 32 and 32 contraction bytes of half-wave
+// l / 32; the accumulator layout is that of the 32x32 bf16 MFMA.  Products of
+// two E4M3 values are exact in fp32.  The score is
+//   s = sum_h w * relu(c_p * q8_h . kbar8_p),   c_p = q_scale * k_scale * 2^e_p,
+// computed as |c_p| * sum_h w * relu(sign(c) * acc) (the sign of c is the
+// sign of q_scale * k_scale, the same for every pool).
+template <int HI, int DI, int NB>
+__global__ __launch_bounds__(256, 2) void index_score_fp8_kernel(ScoreK8 a) {
+    constexpr int QPT = 32 / HI;
+    constexpr int NS = (DI + 63) / 64;   // MFMA steps of 64 dims
+    constexpr int PW = 32 * NB;
+    constexpr int PB = 4 * PW;
+    constexpr int LROW = DI + 16;        // LDS row stride in bytes
+    constexpr int CHUNKS = 2 * DI;       // 16-byte pieces of a 32-row tile
+    constexpr int CPT = (CHUNKS + 255) / 256;
+
+    __shared__ __attribute__((aligned(16))) uint8_t sq[2][32 * LROW];
+    __shared__ __attribute__((aligned(16))) float sw[2][32];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int64_t p_blk = (int64_t)blockIdx.x * PB;
+    const int64_t p_wave = p_blk + wave * PW;
+
+    int i_begin = blockIdx.y * a.gq;
+    const int i_end = min(a.rows, i_begin + a.gq);
+    const int64_t first = 4 * (p_blk + 1) - a.q_pos0 - a.row0;
+    if (first > i_begin) i_begin = (int)(first < (int64_t)i_end ? first : (int64_t)i_end);
+    i_begin = (i_begin / QPT) * QPT;
+    if (i_begin >= i_end) return;
+    const int n_tiles = (i_end - i_begin + QPT - 1) / QPT;
+
+    const float qk = (a.q_scale ? *a.q_scale : 1.0f) * (a.k_scale ? *a.k_scale : 1.0f);
+    const bool flip = qk < 0.0f;
+
+    // resident pooled keys; contraction bytes 64*s + 32*half .. +32 (zero past DI)
+    i32x8 bfr[NB][NS];
+    float cpool[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t p = p_wave + nb * 32 + col;
+        cpool[nb] = p < a.n_pools ? fabsf(qk) * a.pool_scale[p] : 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            u32x4 lo4 = {0u, 0u, 0u, 0u}, hi4 = {0u, 0u, 0u, 0u};
+            const int d0 = 64 * s + 32 * half;
+            if (p < a.n_pools && d0 < DI) {
+                lo4 = ldg16(a.kbar8 + p * DI + d0);
+                hi4 = ldg16(a.kbar8 + p * DI + d0 + 16);
+            }
+            bfr[nb][s] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                               (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): resident loads done before the tile loop
+
+    u32x4 pre[CPT];
+    float prew = 0.0f;
+    auto fetch = [&](int j) {
+        const int64_t qrow0 = a.row0 + i_begin + (int64_t)j * QPT;
+        const uint8_t* src = a.q8 + qrow0 * (HI * DI);
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int ch = tid + u * 256;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (ch < CHUNKS) {
+                const int r = ch / (DI / 16);
+                if (qrow0 + r / HI < a.s_q) v = ldg16(src + (int64_t)ch * 16);
+            }
+            pre[u] = v;
+        }
+        if (tid < 32) {
+            const int64_t qr = qrow0 + tid / HI;
+            prew = qr < a.s_q ? a.w[qr * a.w_stride + (tid % HI)] : 0.0f;
+        }
+    };
+    auto stash = [&](int b) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int ch = tid + u * 256;
+            if (ch < CHUNKS) {
+                const int r = ch / (DI / 16), c16 = ch % (DI / 16);
+                *reinterpret_cast<u32x4*>(&sq[b][r * LROW + c16 * 16]) = pre[u];
+            }
+        }
+        if (tid < 32) sw[b][tid] = prew;
+    };
+
+    fetch(0);
+    stash(0);
+    __syncthreads();
+
+    for (int j = 0; j < n_tiles; ++j) {
+        const int cur = j & 1;
+        const bool has_next = j + 1 < n_tiles;
+        if (has_next) fetch(j + 1);
+
+        f32x16 acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[nb][v] = 0.0f;
+
+        const uint8_t* arow = &sq[cur][col * LROW];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int d0 = 64 * s + 32 * half;
+            u32x4 lo4 = {0u, 0u, 0u, 0u}, hi4 = {0u, 0u, 0u, 0u};
+            if (d0 < DI) {
+                lo4 = *reinterpret_cast<const u32x4*>(arow + d0);
+                hi4 = *reinterpret_cast<const u32x4*>(arow + d0 + 16);
+            }
+            const i32x8 af = {(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                              (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bfr[nb][s], acc[nb],
+                                                                          0, 0, 0, 127, 0, 127);
+        }
+
+        float wv[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(&sw[cur][8 * g4 + 4 * half]);
+            wv[4 * g4 + 0] = w4[0];
+            wv[4 * g4 + 1] = w4[1];
+            wv[4 * g4 + 2] = w4[2];
+            wv[4 * g4 + 3] = w4[3];
+        }
+        const int tile_i0 = i_begin + j * QPT;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int64_t p = p_wave + nb * 32 + col;
+            float part[4];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                float s = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x = flip ? -acc[nb][4 * g4 + i] : acc[nb][4 * g4 + i];
+                    s += wv[4 * g4 + i] * relu(x);
+                }
+                part[g4] = s;
+            }
+            float qv[4];
+            int nq;
+            if constexpr (HI == 32) {
+                qv[0] = add_halves((part[0] + part[1]) + (part[2] + part[3]));
+                nq = 1;
+            } else if constexpr (HI == 16) {
+                qv[0] = add_halves(part[0] + part[1]);
+                qv[1] = add_halves(part[2] + part[3]);
+                nq = 2;
+            } else if constexpr (HI == 8) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) qv[g4] = add_halves(part[g4]);
+                nq = 4;
+            } else {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) qv[g4] = part[g4];
+                nq = 4;
+            }
+            if (HI == 4 || half == 0) {
+#pragma unroll
+                for (int u = 0; u < nq; ++u) {
+                    const int qi = (HI == 4) ? (2 * u + half) : u;
+                    const int i = tile_i0 + qi;
+                    if (i < i_end) {
+                        const int64_t t = a.q_pos0 + a.row0 + i;
+                        const int64_t nt = (t >> 2) < a.n_pools ? (t >> 2) : a.n_pools;
+                        if (p < nt) a.buf[(int64_t)i * a.ld + p] = canonical_zero(cpool[nb] * qv[u]);
+                    }
+                }
+            }
+        }
+
+        if (has_next) stash(cur ^ 1);
+        __syncthreads();
+    }
+}
+
+template <int HI, int DI>
+static hipError_t launch_score_fp8_t(const ScoreArgs& a, hipStream_t stream) {
+    constexpr int NB = 4;
+    constexpr int PB = 128 * NB;
+    constexpr int QPT = 32 / HI;
+    ScoreK8 k;
+    k.q8 = static_cast<const uint8_t*>(a.q_idx);
+    k.kbar8 = static_cast<const uint8_t*>(a.kbar);
+    k.pool_scale = a.pool_scale;
+    k.q_scale = a.q_scale;
+    k.k_scale = a.k_scale;
+    k.w = a.w;
+    k.w_stride = a.w_stride;
+    k.s_q = a.s_q;
+    k.row0 = a.row0;
+    k.rows = a.rows;
+    k.gq = 64 * QPT;
+    k.q_pos0 = a.q_pos0;
+    k.n_pools = a.n_pools;
+    k.buf = a.buf;
+    k.ld = a.ld;
+    const dim3 grid((unsigned)((a.n_chunk + PB - 1) / PB), (unsigned)((a.rows + k.gq - 1) / k.gq));
+    if (grid.x == 0 || grid.y == 0) return hipSuccess;
+    index_score_fp8_kernel<HI, DI, NB><<<grid, 256, 0, stream>>>(k);
+    return hipGetLastError();
+}
+
+template <int HI>
+static hipError_t launch_score_fp8_h(const ScoreArgs& a, hipStream_t stream) {
+    switch (a.d_idx) {
+        case 64: return launch_score_fp8_t<HI, 64>(a, stream);
+        case 96: return launch_score_fp8_t<HI, 96>(a, stream);
+        case 128: return launch_score_fp8_t<HI, 128>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int HI, int DI>
 static hipError_t launch_score_bf16_t(const ScoreArgs& a, hipStream_t stream) {
     constexpr int NB = 2;
@@ -327,7 +649,15 @@ static hipError_t launch_score_bf16_h(const ScoreArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
-    if (a.fp8) return hipErrorNotSupported;
+    if (a.fp8) {
+        switch (a.h_idx) {
+            case 4: return launch_score_fp8_h<4>(a, stream);
+            case 8: return launch_score_fp8_h<8>(a, stream);
+            case 16: return launch_score_fp8_h<16>(a, stream);
+            case 32: return launch_score_fp8_h<32>(a, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (a.h_idx) {
         case 4: return launch_score_bf16_h<4>(a, stream);
         case 8: return launch_score_bf16_h<8>(a, stream);

@@ -140,6 +140,17 @@ def _indexer_shapes(q_idx, k_idx, w):
     return s_q, s_k, h_idx, d_idx, w_stride, dtype
 
 
+def pooled_table_bytes(n_pools: int, d_idx: int, dtype: int) -> int:
+    """Bytes of the pooled key table the library keeps at the start of the
+    workspace (bf16: two bf16 terms per element; fp8: codes, then fp32
+    per-pool scales), each part rounded up to 256 bytes."""
+    def r(x):
+        return (x + 255) // 256 * 256
+    if dtype == DSA_BF16:
+        return r(n_pools * 2 * d_idx * 2)
+    return r(n_pools * d_idx) + r(n_pools * 4)
+
+
 def new_workspace(nbytes: int, device=None) -> torch.Tensor:
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device or "cuda")
 
@@ -182,8 +193,7 @@ def dsa_index_scores(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, 
     n_rows = s_q - row0 if n_rows is None else n_rows
     dev = q_idx.device
     n_pools = s_k // 4
-    per_pool = 4 * d_idx if dtype == DSA_BF16 else d_idx + 4
-    need = (n_pools * per_pool + 255) // 256 * 256
+    need = pooled_table_bytes(n_pools, d_idx, dtype)
     if workspace is None:
         workspace = new_workspace(need, dev)
     out = torch.empty((n_rows, n_pools), dtype=torch.float32, device=dev)

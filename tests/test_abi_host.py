@@ -152,8 +152,19 @@ def test_index_scores_rejects_rows_out_of_range(lib):
     assert st == dsa.DSA_ERR_INVALID_ARG
 
 
-def test_fp8_reported_unsupported_until_built(lib):
-    assert _call_topk(lib, dtype=1, q_scale=None) == dsa.DSA_ERR_UNSUPPORTED
+def test_fp8_scale_pointers(lib):
+    # scales are fp8-only device scalars; a misaligned one is rejected
+    assert _call_topk(lib, dtype=1, q_scale=0x6002) == dsa.DSA_ERR_INVALID_ARG
+    assert _call_topk(lib, dtype=0, k_scale=0x6000) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_fp8_workspace_layout(lib):
+    # codes P x d_idx, then fp32 scales, each rounded to 256 B, then the buffer
+    nbytes, cq = dsa.dsa_index_workspace_size(65536, 65536, 32, 96, 512, 4, 256, dsa.DSA_FP8_E4M3)
+    assert cq == 256
+    assert nbytes == 16384 * 96 + 16384 * 4 + 256 * 16384 * 4
+    assert dsa.pooled_table_bytes(16384, 96, dsa.DSA_FP8_E4M3) == 16384 * 96 + 16384 * 4
+    assert dsa.pooled_table_bytes(1000, 128, dsa.DSA_BF16) == 1000 * 512
 
 
 def test_profile_read_empty(lib):

@@ -32,24 +32,36 @@ def _lib():
 
 
 def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=None,
-             check_scores=True, x=None):
+             check_scores=True, x=None, fp8=False, scales=(1.0, 1.0)):
     _say(f"[case] {wl.name} s_q={wl.s_q} s_k={wl.s_k} q_pos0={wl.q_pos0} "
          f"H_I={wl.h_idx} D_I={wl.d_idx} k={wl.k_pools} H={wl.h} D={wl.d} Dv={wl.dv} "
-         f"n_tail={wl.n_tail} chunk_q={chunk_q} seed={seed if seed is not None else wl.seed}")
+         f"n_tail={wl.n_tail} chunk_q={chunk_q} fp8={fp8} scales={scales} "
+         f"seed={seed if seed is not None else wl.seed}")
     if x is None:
         x = inputs.make_inputs(wl, seed=seed, attention=attention, w_per_query=w_per_query)
     dev = torch.device("cuda")
-    q_idx, k_idx, w = (x["q_idx"].to(dev), x["k_idx"].to(dev), x["w"].to(dev))
+    qn, kn = ("q_idx8", "k_idx8") if fp8 else ("q_idx", "k_idx")
+    q_idx, k_idx, w = (x[qn].to(dev), x[kn].to(dev), x["w"].to(dev))
+    sc_kw = {}
+    if fp8:
+        sc_kw = dict(q_scale=torch.tensor([scales[0]], dtype=torch.float32, device=dev),
+                     k_scale=torch.tensor([scales[1]], dtype=torch.float32, device=dev))
     idx_g, sc_g = dsa.dsa_index_score_topk(q_idx, k_idx, w, wl.k_pools, q_pos0=wl.q_pos0,
-                                           chunk_q=chunk_q, want_scores=True)
+                                           chunk_q=chunk_q, want_scores=True, **sc_kw)
     torch.cuda.synchronize()
     rows = np.arange(wl.s_q) if rows is None else np.asarray(rows, dtype=np.int64)
     pos = wl.q_pos0 + rows
     idx_g_rows = idx_g.cpu().numpy()[rows]
     sc_g_rows = sc_g.cpu().numpy()[rows]
-    idx_o, sc_o = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], wl.k_pools,
-                                    q_pos0=wl.q_pos0, rows=rows)
-    s_o = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0, rows=rows)
+    if fp8:
+        idx_o, sc_o = oracle.index_topk_fp8(x[qn], x[kn], x["w"], wl.k_pools, q_scale=scales[0],
+                                            k_scale=scales[1], q_pos0=wl.q_pos0, rows=rows)
+        s_o = oracle.index_scores_fp8(x[qn], x[kn], x["w"], q_scale=scales[0],
+                                      k_scale=scales[1], q_pos0=wl.q_pos0, rows=rows)
+    else:
+        idx_o, sc_o = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], wl.k_pools,
+                                        q_pos0=wl.q_pos0, rows=rows)
+        s_o = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0, rows=rows)
     stats = parity.check_index_rows(idx_g_rows, idx_o, s_o, pos, wl.n_pools, wl.k_pools)
     _say(f"  index: {stats}")
     # the kept pools' scores against the oracle's dense scores
@@ -68,9 +80,15 @@ def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=N
         worst = 0.0
         for b0 in blocks:
             nb = min(16, wl.s_q - b0)
-            g = dsa.dsa_index_scores(q_idx, k_idx, w, row0=b0, n_rows=nb, q_pos0=wl.q_pos0)
-            ref = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0,
-                                      rows=np.arange(b0, b0 + nb))
+            g = dsa.dsa_index_scores(q_idx, k_idx, w, row0=b0, n_rows=nb, q_pos0=wl.q_pos0,
+                                     **sc_kw)
+            if fp8:
+                ref = oracle.index_scores_fp8(x[qn], x[kn], x["w"], q_scale=scales[0],
+                                              k_scale=scales[1], q_pos0=wl.q_pos0,
+                                              rows=np.arange(b0, b0 + nb))
+            else:
+                ref = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0,
+                                          rows=np.arange(b0, b0 + nb))
             worst = max(worst, parity.check_scores(g.cpu().numpy(), ref))
         _say(f"  scores: worst error / bound = {worst:.3g}")
     if attention:
@@ -197,6 +215,18 @@ def test_k_and_v_may_alias():
     run_case(wl, chunk_q=64, x=x)
 
 
+@pytest.mark.parametrize("h_idx,d_idx,scales", [
+    (32, 96, (1.0, 1.0)), (32, 128, (0.5, 2.0)), (4, 64, (1.0, 1.0)), (16, 96, (-1.5, 0.25)),
+    (8, 128, (3.0, 1.0)),
+])
+def test_fp8_indexer(h_idx, d_idx, scales):
+    # section "Making Sparse Attention Actually Sparse" (NoPE heads): the E4M3
+    # indexer with per-pool power-of-two re-quantisation of the pooled keys
+    wl = inputs.custom(f"fp8_{h_idx}x{d_idx}", s_q=2100, s_k=2100, h_idx=h_idx, d_idx=d_idx,
+                       k_pools=48, h=16, d=96, n_tail=3, fp8=True, number=400 + h_idx + d_idx)
+    run_case(wl, chunk_q=256, fp8=True, scales=scales, attention=(h_idx == 32))
+
+
 # ---------------------------------------------------------------- the page's workloads
 
 def test_workload_s32k_sampled():
@@ -214,6 +244,12 @@ def test_workload_s128k_sampled():
 def test_workload_nope_s64k_sampled():
     wl = inputs.WORKLOADS["nope_s64k"]
     run_case(wl, rows=inputs.sample_rows(wl.s_q, 160), check_scores=False)
+
+
+@pytest.mark.slow
+def test_workload_nope_s64k_fp8_sampled():
+    wl = inputs.WORKLOADS["nope_s64k"]
+    run_case(wl, rows=inputs.sample_rows(wl.s_q, 160), check_scores=False, fp8=True)
 
 
 @pytest.mark.slow
