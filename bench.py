@@ -15,6 +15,7 @@ sample of the same workload on this host's cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -31,8 +32,52 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "DSA fwd queries/sec at S=128k (indexer+topk+attn); TFLOP/s vs MFMA peak"
 
 
+KERNEL_SOURCES = {
+    "index_score": ["index_score.hip", "common.h"],
+    "topk_select": ["topk_select.hip", "common.h"],
+    "sparse_attn": ["sparse_attn.hip", "common.h"],
+    "pool_keys": ["index_score.hip", "common.h"],
+}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "long_context_sparse_dsa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the kernel source as it is now (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return t["hbm_bytes_per_launch"]
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the FETCH_SIZE and
+    WRITE_SIZE counters: the counter values of this run divided by the bytes
+    copied give the factor."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
+                      "launches": 3}), flush=True)
 
 
 def work_counts(wl):
@@ -90,7 +135,12 @@ def main():
     ap.add_argument("--chunk-q", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -163,6 +213,9 @@ def main():
             a = w["b_pool"] * args.steps / t_s / 1e9
             rl[name] = {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": a / PEAK_HBM_GBS, "traffic": None}
+        if name in rl:
+            rl[name]["traffic"] = measured_traffic(name, wl.name)
+            rl[name]["source_sha256"] = kernel_source_hash(name)
         stages[name].update(rl.get(name, {}))
     dominant = max(stats, key=lambda k: stats[k][1]) if stats else None
 
