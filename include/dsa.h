@@ -72,12 +72,14 @@ int dsa_version(void);
 const char *dsa_last_error(void);
 
 /*
- * Bytes of device workspace dsa_index_score_topk / dsa_index_scores need.
- * Holds the pooled key table (bf16: P x 2*d_idx bf16 as a two-term split;
- * fp8: P x d_idx codes + P exponents) and the per-chunk fp32 score buffer
- * of chunk_q x P entries ("Over Time: Chunking": the buffer is constant in
- * s_q).  chunk_q = 0 picks the library's default for these shapes (the
- * value is returned through *chunk_q_used when that pointer is non-NULL).
+ * Bytes of device workspace dsa_index_score_topk needs.  Holds the pooled
+ * key table (bf16: hi = bf16(mean) plus the residual as E4M3 codes with a
+ * per-pool power-of-two scale; fp8: E4M3 codes plus per-pool factors), the
+ * chunk's queries quantised for the bf16 correction term, and the per-chunk
+ * fp32 score buffer of chunk_q x P entries ("Over Time: Chunking": the
+ * buffer is constant in s_q).  chunk_q = 0 picks the library's default for
+ * these shapes (the value is returned through *chunk_q_used when that
+ * pointer is non-NULL).
  * Pure host computation; valid without a GPU.
  */
 dsa_status dsa_index_workspace_size(int64_t s_q, int64_t s_k, int h_idx, int d_idx,
@@ -113,10 +115,19 @@ dsa_status dsa_index_score_topk(const void *q_idx, const void *k_idx, const floa
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace dsa_index_scores needs for n_rows query rows:
+ * the pooled key table plus, for the bf16 indexer, the rows' queries
+ * quantised for the correction term.  Pure host computation.
+ */
+dsa_status dsa_index_scores_workspace_size(int64_t s_q, int64_t s_k, int h_idx, int d_idx,
+                                           int pool_size, int dtype, int64_t n_rows,
+                                           size_t *bytes);
+
+/*
  * Dense fp32 indexer scores of query rows [row0, row0 + n_rows) against
  * every pool (testing and inspection): scores_out [n_rows, P], -inf where a
  * pool is not eligible.  Same arguments and support as dsa_index_score_topk;
- * the workspace only needs to hold the pooled key table.
+ * the workspace is sized by dsa_index_scores_workspace_size.
  */
 dsa_status dsa_index_scores(const void *q_idx, const void *k_idx, const float *q_scale,
                             const float *k_scale, const float *w, int64_t w_stride_q,
@@ -153,7 +164,7 @@ dsa_status dsa_sparse_attn_fwd(const void *q, const void *k, const void *v, cons
  * by HIP events on its own stream; dsa_profile_read synchronises on those
  * events and reports, per kernel kind, the number of launches and the summed
  * duration in milliseconds, then clears the record.  Kinds: "pool_keys",
- * "index_score", "topk_select", "sparse_attn".
+ * "quantize_queries", "index_score", "topk_select", "sparse_attn".
  */
 typedef struct {
     char name[32];

@@ -40,8 +40,9 @@ constexpr int64_t kScoreBufferCap = int64_t(2) << 30;  // per chunk, as the page
 
 // ------------------------------------------------------------ profiling
 
-enum Kind { K_POOL = 0, K_SCORE, K_SELECT, K_ATTN, K_COUNT };
-const char* kKindName[K_COUNT] = {"pool_keys", "index_score", "topk_select", "sparse_attn"};
+enum Kind { K_POOL = 0, K_QUANT, K_SCORE, K_SELECT, K_ATTN, K_COUNT };
+const char* kKindName[K_COUNT] = {"pool_keys", "quantize_queries", "index_score", "topk_select",
+                                  "sparse_attn"};
 
 struct Rec {
     int kind;
@@ -122,17 +123,6 @@ dsa_status check_index_shape(const IndexShape& sh, bool need_k) {
     return DSA_OK;
 }
 
-// Pooled key table: bf16 [P][2*d_idx] (hi | lo); fp8 [P][d_idx] codes, then
-// [P] fp32 per-pool scales 2^e at the next 256-byte boundary.
-int64_t kbar_codes_bytes(const IndexShape& sh) {
-    return sh.dtype == DSA_BF16 ? round_up(sh.n_pools * 2LL * sh.d_idx * 2, 256)
-                                : round_up(sh.n_pools * (int64_t)sh.d_idx, 256);
-}
-
-int64_t kbar_bytes(const IndexShape& sh) {
-    return kbar_codes_bytes(sh) + (sh.dtype == DSA_BF16 ? 0 : round_up(sh.n_pools * 4, 256));
-}
-
 int64_t score_ld(const IndexShape& sh) { return round_up(sh.n_pools > 0 ? sh.n_pools : 1, 64); }
 
 dsa_status resolve_chunk(const IndexShape& sh, int64_t chunk_q, int64_t* out) {
@@ -157,9 +147,37 @@ dsa_status resolve_chunk(const IndexShape& sh, int64_t chunk_q, int64_t* out) {
     return DSA_OK;
 }
 
+// Workspace layout, every part starting on a 256-byte boundary:
+//   bf16 indexer: hi [P][d] bf16 | lo [P][d] E4M3 | lo scales [P] E8M0 |
+//                 chunk queries [rows][h][d] E4M3 | their scales [rows][h] |
+//                 score buffer [rows][ld] fp32
+//   fp8 indexer:  codes [P][d] | per-pool factors [P] fp32 | score buffer
+struct Layout {
+    int64_t hi = 0, lo = 0, lo_scale = 0, q8 = 0, q8_scale = 0, buf = 0, total = 0;
+};
+
+Layout layout(const IndexShape& sh, int64_t rows, bool with_buffer) {
+    Layout L;
+    const int64_t P = sh.n_pools, d = sh.d_idx;
+    int64_t off = 0;
+    if (sh.dtype == DSA_BF16) {
+        L.hi = off;        off += round_up(P * d * 2, 256);
+        L.lo = off;        off += round_up(P * d, 256);
+        L.lo_scale = off;  off += round_up(P, 256);
+        L.q8 = off;        off += round_up(rows * sh.h_idx * d, 256);
+        L.q8_scale = off;  off += round_up(rows * sh.h_idx, 256);
+    } else {
+        L.hi = off;        off += round_up(P * d, 256);
+        L.lo_scale = off;  off += round_up(P * 4, 256);  // fp32 factors 2^e
+    }
+    L.buf = off;
+    if (with_buffer) off += round_up(rows * score_ld(sh) * 4, 256);
+    L.total = off;
+    return L;
+}
+
 dsa_status index_workspace(const IndexShape& sh, int64_t chunk_q, size_t* bytes) {
-    const int64_t buf = chunk_q * score_ld(sh) * 4;
-    *bytes = (size_t)(kbar_bytes(sh) + round_up(buf, 256));
+    *bytes = (size_t)layout(sh, chunk_q, true).total;
     return DSA_OK;
 }
 
@@ -181,26 +199,47 @@ dsa_status check_index_ptrs(const void* q_idx, const void* k_idx, const float* q
     return DSA_OK;
 }
 
-hipError_t launch_pool(const IndexShape& sh, const void* k_idx, void* table, hipStream_t s) {
+hipError_t launch_pool(const IndexShape& sh, const Layout& L, const void* k_idx, void* ws,
+                       hipStream_t s) {
     Timed tm(K_POOL, s);
+    char* w = static_cast<char*>(ws);
     if (sh.dtype == DSA_BF16)
         return dsa::launch_pool_keys_bf16(static_cast<const uint16_t*>(k_idx), sh.n_pools,
-                                          sh.d_idx, static_cast<uint16_t*>(table), s);
-    char* t = static_cast<char*>(table);
+                                          sh.d_idx, reinterpret_cast<uint16_t*>(w + L.hi),
+                                          reinterpret_cast<uint8_t*>(w + L.lo),
+                                          reinterpret_cast<uint8_t*>(w + L.lo_scale), s);
     return dsa::launch_pool_keys_fp8(static_cast<const uint8_t*>(k_idx), sh.n_pools, sh.d_idx,
-                                     reinterpret_cast<uint8_t*>(t),
-                                     reinterpret_cast<float*>(t + kbar_codes_bytes(sh)), s);
+                                     reinterpret_cast<uint8_t*>(w + L.hi),
+                                     reinterpret_cast<float*>(w + L.lo_scale), s);
 }
 
-void fill_score_args(dsa::ScoreArgs& a, const IndexShape& sh, const void* q_idx, void* table,
-                     const float* q_scale, const float* k_scale, const float* w,
-                     int64_t w_stride) {
+// bf16 indexer: quantise query rows [row0, row0 + rows) for the correction MFMAs.
+hipError_t launch_quantize(const IndexShape& sh, const Layout& L, const void* q_idx,
+                           int64_t row0, int64_t rows, void* ws, hipStream_t s) {
+    if (sh.dtype != DSA_BF16) return hipSuccess;
+    Timed tm(K_QUANT, s);
+    char* w = static_cast<char*>(ws);
+    const uint16_t* q = static_cast<const uint16_t*>(q_idx) + row0 * sh.h_idx * sh.d_idx;
+    return dsa::launch_quantize_queries(q, rows * sh.h_idx, sh.d_idx,
+                                        reinterpret_cast<uint8_t*>(w + L.q8),
+                                        reinterpret_cast<uint8_t*>(w + L.q8_scale), s);
+}
+
+void fill_score_args(dsa::ScoreArgs& a, const IndexShape& sh, const Layout& L,
+                     const void* q_idx, void* ws, const float* q_scale, const float* k_scale,
+                     const float* w, int64_t w_stride) {
+    char* base = static_cast<char*>(ws);
     a.q_idx = q_idx;
-    a.kbar = table;
-    a.pool_scale = sh.dtype == DSA_BF16
-                       ? nullptr
-                       : reinterpret_cast<const float*>(static_cast<char*>(table) +
-                                                        kbar_codes_bytes(sh));
+    a.kbar = base + L.hi;
+    if (sh.dtype == DSA_BF16) {
+        a.klo = reinterpret_cast<const uint8_t*>(base + L.lo);
+        a.klo_scale = reinterpret_cast<const uint8_t*>(base + L.lo_scale);
+        a.q8 = reinterpret_cast<const uint8_t*>(base + L.q8);
+        a.q8_scale = reinterpret_cast<const uint8_t*>(base + L.q8_scale);
+        a.pool_scale = nullptr;
+    } else {
+        a.pool_scale = reinterpret_cast<const float*>(base + L.lo_scale);
+    }
     a.q_scale = q_scale;
     a.k_scale = k_scale;
     a.w = w;
@@ -235,6 +274,19 @@ dsa_status dsa_index_workspace_size(int64_t s_q, int64_t s_k, int h_idx, int d_i
     return index_workspace(sh, cq, bytes);
 }
 
+dsa_status dsa_index_scores_workspace_size(int64_t s_q, int64_t s_k, int h_idx, int d_idx,
+                                           int pool_size, int dtype, int64_t n_rows,
+                                           size_t* bytes) {
+    g_err[0] = 0;
+    if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes must be non-null");
+    IndexShape sh{s_q, s_k, 0, h_idx, d_idx, pool_size, 1, dtype, s_k / 4};
+    dsa_status st = check_index_shape(sh, false);
+    if (st != DSA_OK) return st;
+    if (n_rows < 0 || n_rows > s_q) return fail(DSA_ERR_INVALID_ARG, "n_rows outside [0, s_q]");
+    *bytes = (size_t)layout(sh, n_rows, false).total;
+    return DSA_OK;
+}
+
 dsa_status dsa_index_score_topk(const void* q_idx, const void* k_idx, const float* q_scale,
                                 const float* k_scale, const float* w, int64_t w_stride_q,
                                 int64_t s_q, int64_t s_k, int64_t q_pos0, int h_idx, int d_idx,
@@ -262,11 +314,12 @@ dsa_status dsa_index_score_topk(const void* q_idx, const void* k_idx, const floa
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
-    float* buf = reinterpret_cast<float*>(ws + kbar_bytes(sh));
+    const Layout L = layout(sh, cq, true);
+    float* buf = reinterpret_cast<float*>(ws + L.buf);
     const int64_t ld = score_ld(sh);
     hipError_t e;
     if (sh.n_pools > 0) {
-        e = launch_pool(sh, k_idx, ws, s);
+        e = launch_pool(sh, L, k_idx, ws, s);
         if (e != hipSuccess) return hip_fail(e, "pool_keys launch");
     }
     for (int64_t c0 = 0; c0 < s_q; c0 += cq) {
@@ -274,8 +327,10 @@ dsa_status dsa_index_score_topk(const void* q_idx, const void* k_idx, const floa
         const int64_t t_last = q_pos0 + c0 + rows - 1;
         const int64_t n_chunk = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
         if (n_chunk > 0 && (n_chunk > k_pools || score_out)) {
+            e = launch_quantize(sh, L, q_idx, c0, rows, ws, s);
+            if (e != hipSuccess) return hip_fail(e, "quantize_queries launch");
             dsa::ScoreArgs a{};
-            fill_score_args(a, sh, q_idx, ws, q_scale, k_scale, w, w_stride_q);
+            fill_score_args(a, sh, L, q_idx, ws, q_scale, k_scale, w, w_stride_q);
             a.row0 = c0;
             a.rows = rows;
             a.n_chunk = n_chunk;
@@ -321,7 +376,8 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const float* q
         return fail(DSA_ERR_UNSUPPORTED, "at most 2^20 rows per call");
     if (n_rows > 0 && !scores_out) return fail(DSA_ERR_INVALID_ARG, "scores_out must be non-null");
     if (!aligned16(scores_out)) return fail(DSA_ERR_INVALID_ARG, "scores_out must be 16-byte aligned");
-    const size_t need = (size_t)kbar_bytes(sh);
+    const Layout L = layout(sh, n_rows, false);
+    const size_t need = (size_t)L.total;
     if (n_rows == 0 || sh.n_pools == 0) return DSA_OK;  // nothing to write
     if (!workspace || workspace_bytes < need)
         return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -330,13 +386,15 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const float* q
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = dsa::launch_fill_f32(scores_out, n_rows * sh.n_pools, -INFINITY, s);
     if (e != hipSuccess) return hip_fail(e, "fill launch");
-    e = launch_pool(sh, k_idx, workspace, s);
+    e = launch_pool(sh, L, k_idx, workspace, s);
     if (e != hipSuccess) return hip_fail(e, "pool_keys launch");
     const int64_t t_last = q_pos0 + row0 + n_rows - 1;
     const int64_t n_chunk = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
     if (n_chunk > 0) {
+        e = launch_quantize(sh, L, q_idx, row0, n_rows, workspace, s);
+        if (e != hipSuccess) return hip_fail(e, "quantize_queries launch");
         dsa::ScoreArgs a{};
-        fill_score_args(a, sh, q_idx, workspace, q_scale, k_scale, w, w_stride_q);
+        fill_score_args(a, sh, L, q_idx, workspace, q_scale, k_scale, w, w_stride_q);
         a.row0 = row0;
         a.rows = (int)n_rows;
         a.n_chunk = n_chunk;

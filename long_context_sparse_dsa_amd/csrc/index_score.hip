@@ -19,69 +19,21 @@
 //
 // bf16 accuracy: a pooled key rounded once to bf16 perturbs scores by ~1e-3
 // relative, enough to move pools across the top-k boundary.  The pooled key
-// is therefore stored as two bf16 terms hi + lo (hi = bf16(mean),
-// lo = bf16(mean - hi)), and each MFMA consumes 8 dims of hi in the lower
-// half-wave and the same 8 dims of lo in the upper half-wave against the same
-// query values, so q.hi + q.lo is accumulated in one instruction stream.
-// Products of two bf16 values are exact in fp32; the remaining error is the
-// 2^-17 relative residual of the split plus fp32 accumulation.
+// is therefore split as hi + lo, hi = bf16(mean) and lo = mean - hi (exact in
+// fp32, |lo| <= 2^-9 |mean|).  q . hi runs on bf16 MFMAs (exact products);
+// the small correction q . lo only needs a few bits, so it runs on scaled fp8
+// MFMAs: lo is stored as E4M3 codes with a per-pool power-of-two scale and
+// the chunk's queries as E4M3 codes with a per-(query, head) power-of-two
+// scale, both handed to the MFMA as its E8M0 block scales, so the correction
+// lands in the same accumulators.  The fp8 rounding leaves the correction
+// ~5% off, i.e. ~3e-5 of a typical score, far inside the selection's 1e-3
+// boundary band.
 #include "common.h"
 #include "internal.h"
 
 namespace dsa {
 
 // ---------------------------------------------------------------- pooling
-
-template <int DI>
-__global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __restrict__ k,
-                                                             int64_t n_pools,
-                                                             uint16_t* __restrict__ kbar) {
-    constexpr int G = DI / 8;  // 8-dim groups per row
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t p = gid / G;
-    const int g = (int)(gid % G);
-    if (p >= n_pools) return;
-    const uint16_t* src = k + (p * 4) * DI + g * 8;
-    u32x4 r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = ldg16(src + (int64_t)j * DI);
-    u32x4 hi, lo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int word = e >> 1, sh = (e & 1) * 16;
-        float s = bf16_to_f32((r[0][word] >> sh) & 0xFFFFu);
-        s += bf16_to_f32((r[1][word] >> sh) & 0xFFFFu);
-        s += bf16_to_f32((r[2][word] >> sh) & 0xFFFFu);
-        s += bf16_to_f32((r[3][word] >> sh) & 0xFFFFu);
-        const float m = s * 0.25f;
-        const uint32_t h = f32_to_bf16(m);
-        const uint32_t l = f32_to_bf16(m - bf16_to_f32(h));
-        if ((e & 1) == 0) {
-            hi[word] = h;
-            lo[word] = l;
-        } else {
-            hi[word] |= h << 16;
-            lo[word] |= l << 16;
-        }
-    }
-    uint16_t* dst = kbar + p * (2 * DI) + g * 8;
-    *reinterpret_cast<u32x4*>(dst) = hi;
-    *reinterpret_cast<u32x4*>(dst + DI) = lo;
-}
-
-hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, int64_t n_pools, int d_idx,
-                                 uint16_t* kbar, hipStream_t stream) {
-    if (n_pools <= 0) return hipSuccess;
-    const int64_t threads = n_pools * (d_idx / 8);
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    switch (d_idx) {
-        case 64: pool_keys_bf16_kernel<64><<<grid, 256, 0, stream>>>(k_idx, n_pools, kbar); break;
-        case 96: pool_keys_bf16_kernel<96><<<grid, 256, 0, stream>>>(k_idx, n_pools, kbar); break;
-        case 128: pool_keys_bf16_kernel<128><<<grid, 256, 0, stream>>>(k_idx, n_pools, kbar); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
 
 // ---------------------------------------------------------------- fp8 pooling
 //
@@ -172,6 +124,122 @@ hipError_t launch_pool_keys_fp8(const uint8_t* k8, int64_t n_pools, int d_idx, u
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- bf16 pooling
+
+// Smallest e with amax <= 448 * 2^e (0 for amax == 0); amax finite.
+__device__ __forceinline__ int pow2_scale_exp(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 10;
+    while (amax > ldexpf(448.0f, e)) ++e;
+    return e;
+}
+
+// One thread per pool: hi = bf16(mean) [P][DI], lo = E4M3((mean - hi) / 2^e)
+// [P][DI] with one E8M0 byte (e + 127) per pool.
+template <int DI>
+__global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __restrict__ k,
+                                                             int64_t n_pools,
+                                                             uint16_t* __restrict__ hi_out,
+                                                             uint8_t* __restrict__ lo_out,
+                                                             uint8_t* __restrict__ lo_scale) {
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= n_pools) return;
+    float lo[DI];
+    float amax = 0.0f;
+#pragma unroll
+    for (int g = 0; g < DI / 8; ++g) {
+        u32x4 r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = ldg16(k + (p * 4 + j) * DI + 8 * g);
+        u32x4 hi;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int word = e >> 1, sh = (e & 1) * 16;
+            float sum = bf16_to_f32((r[0][word] >> sh) & 0xFFFFu);
+            sum += bf16_to_f32((r[1][word] >> sh) & 0xFFFFu);
+            sum += bf16_to_f32((r[2][word] >> sh) & 0xFFFFu);
+            sum += bf16_to_f32((r[3][word] >> sh) & 0xFFFFu);
+            const float m = sum * 0.25f;
+            const uint32_t h = f32_to_bf16(m);
+            lo[8 * g + e] = m - bf16_to_f32(h);
+            amax = fmaxf(amax, fabsf(lo[8 * g + e]));
+            if ((e & 1) == 0) hi[word] = h;
+            else hi[word] |= h << 16;
+        }
+        *reinterpret_cast<u32x4*>(hi_out + p * DI + 8 * g) = hi;
+    }
+    const int e = pow2_scale_exp(amax);
+#pragma unroll
+    for (int c = 0; c < DI / 16; ++c) {
+        u32x4 o = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int b = 0; b < 16; ++b) o[b >> 2] |= e4m3_code(ldexpf(lo[16 * c + b], -e)) << ((b & 3) * 8);
+        *reinterpret_cast<u32x4*>(lo_out + p * DI + 16 * c) = o;
+    }
+    lo_scale[p] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, int64_t n_pools, int d_idx,
+                                 uint16_t* hi, uint8_t* lo, uint8_t* lo_scale,
+                                 hipStream_t stream) {
+    if (n_pools <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((n_pools + 255) / 256));
+    switch (d_idx) {
+        case 64: pool_keys_bf16_kernel<64><<<grid, 256, 0, stream>>>(k_idx, n_pools, hi, lo, lo_scale); break;
+        case 96: pool_keys_bf16_kernel<96><<<grid, 256, 0, stream>>>(k_idx, n_pools, hi, lo, lo_scale); break;
+        case 128: pool_keys_bf16_kernel<128><<<grid, 256, 0, stream>>>(k_idx, n_pools, hi, lo, lo_scale); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- query quantisation
+
+// Rows [row0, row0 + rows) of q_idx as E4M3 codes with one E8M0 scale byte
+// per (query, head): the scaled MFMA operand of the q . lo correction.  One
+// thread per (query, head).
+template <int DI>
+__global__ __launch_bounds__(256) void quantize_queries_kernel(const uint16_t* __restrict__ q,
+                                                               int64_t n_vec,
+                                                               uint8_t* __restrict__ q8,
+                                                               uint8_t* __restrict__ q_scale) {
+    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (v >= n_vec) return;
+    float x[DI];
+    float amax = 0.0f;
+#pragma unroll
+    for (int g = 0; g < DI / 8; ++g) {
+        const u32x4 r = ldg16(q + v * DI + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x[8 * g + e] = bf16_to_f32((r[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+            amax = fmaxf(amax, fabsf(x[8 * g + e]));
+        }
+    }
+    const int e = pow2_scale_exp(amax);
+#pragma unroll
+    for (int c = 0; c < DI / 16; ++c) {
+        u32x4 o = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int b = 0; b < 16; ++b) o[b >> 2] |= e4m3_code(ldexpf(x[16 * c + b], -e)) << ((b & 3) * 8);
+        *reinterpret_cast<u32x4*>(q8 + v * DI + 16 * c) = o;
+    }
+    q_scale[v] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_quantize_queries(const uint16_t* q_rows, int64_t n_vec, int d_idx,
+                                   uint8_t* q8, uint8_t* q_scale, hipStream_t stream) {
+    if (n_vec <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((n_vec + 255) / 256));
+    switch (d_idx) {
+        case 64: quantize_queries_kernel<64><<<grid, 256, 0, stream>>>(q_rows, n_vec, q8, q_scale); break;
+        case 96: quantize_queries_kernel<96><<<grid, 256, 0, stream>>>(q_rows, n_vec, q8, q_scale); break;
+        case 128: quantize_queries_kernel<128><<<grid, 256, 0, stream>>>(q_rows, n_vec, q8, q_scale); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- fill
 
 __global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
@@ -190,8 +258,12 @@ hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t stream)
 // ---------------------------------------------------------------- scoring
 
 struct ScoreK {
-    const uint16_t* q_idx;
-    const uint16_t* kbar;
+    const uint16_t* q_idx;      // [s_q][HI][DI] bf16
+    const uint8_t* q8;          // chunk rows [rows][HI][DI] E4M3
+    const uint8_t* q8_scale;    // chunk rows [rows][HI] E8M0
+    const uint16_t* khi;        // [P][DI] bf16
+    const uint8_t* klo;         // [P][DI] E4M3
+    const uint8_t* klo_scale;   // [P] E8M0
     const float* w;
     int64_t w_stride;
     int64_t s_q;
@@ -204,26 +276,35 @@ struct ScoreK {
     int64_t ld;
 };
 
-// One 32x32x16 bf16 MFMA: lane l supplies A row (l % 32) and B column
-// (l % 32), each with the 8 contraction elements of half-wave (l / 32); the
-// accumulator element v of lane l is row 8*(v/4) + 4*(l/32) + (v%4), column
-// l % 32.
+// bf16 32x32x16 MFMA: lane l supplies A row (l % 32) and B column (l % 32),
+// each with 8 contraction elements of half-wave (l / 32); the accumulator
+// element v of lane l is row 8*(v/4) + 4*(l/32) + (v%4), column l % 32.  The
+// scaled fp8 32x32x64 MFMA has the same row/column lanes and accumulator
+// layout with 32 contraction bytes per lane, and takes one E8M0 scale per
+// lane for the row (A) or column (B) block that lane holds.
 //
 // Workgroup = 4 waves; each wave owns NB blocks of 32 consecutive pools
-// (pooled keys resident as B fragments); the workgroup owns 128*NB pools and
-// a range of gq chunk rows, walked one 32-row (query, head) tile at a time.
+// (hi and lo of the pooled keys resident as B fragments); the workgroup owns
+// 128*NB pools and a range of gq chunk rows, walked one 32-row (query, head)
+// tile at a time through double-buffered LDS.
 template <int HI, int DI, int NB>
 __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
-    constexpr int QPT = 32 / HI;   // queries per 32-row tile
-    constexpr int NS = DI / 8;     // MFMA steps (8 dims of hi + 8 of lo each)
-    constexpr int PW = 32 * NB;    // pools per wave
-    constexpr int PB = 4 * PW;     // pools per workgroup
-    constexpr int LROW = DI + 8;   // LDS row stride (bf16 elements)
-    constexpr int CHUNKS = 4 * DI; // 16-byte pieces of one 32-row tile
-    constexpr int CPT = (CHUNKS + 255) / 256;
+    constexpr int QPT = 32 / HI;      // queries per 32-row tile
+    constexpr int NSB = DI / 16;      // bf16 MFMA steps (16 dims each)
+    constexpr int NSF = (DI + 63) / 64;  // fp8 MFMA steps (64 dims each)
+    constexpr int PW = 32 * NB;       // pools per wave
+    constexpr int PB = 4 * PW;        // pools per workgroup
+    constexpr int LROW = DI + 8;      // bf16 LDS row stride (elements)
+    constexpr int LROW8 = DI + 16;    // fp8 LDS row stride (bytes)
+    constexpr int CH16 = 4 * DI;      // 16-byte pieces of the bf16 tile
+    constexpr int CH8 = 2 * DI;       // 16-byte pieces of the fp8 tile
+    constexpr int CHT = CH16 + CH8;
+    constexpr int CPT = (CHT + 255) / 256;
 
     __shared__ __attribute__((aligned(16))) uint16_t sq[2][32 * LROW];
+    __shared__ __attribute__((aligned(16))) uint8_t sq8[2][32 * LROW8];
     __shared__ __attribute__((aligned(16))) float sw[2][32];
+    __shared__ __attribute__((aligned(16))) uint32_t ss[2][32];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, half = lane >> 5;
@@ -239,58 +320,81 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     if (i_begin >= i_end) return;
     const int n_tiles = (i_end - i_begin + QPT - 1) / QPT;
 
-    // resident pooled keys: pool p_wave + nb*32 + col, hi (half 0) / lo (half 1)
-    bf16x8 bfr[NB][NS];
+    // resident pooled keys of pool p_wave + nb*32 + col
+    bf16x8 bhi[NB][NSB];
+    i32x8 blo[NB][NSF];
+    int bsc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int64_t p = p_wave + nb * 32 + col;
-        if (p < a.n_pools) {
-            const uint16_t* src = a.kbar + p * (2 * DI) + half * DI;
+        const bool ok = p < a.n_pools;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) bfr[nb][s] = as_bf16x8(ldg16(src + 8 * s));
-        } else {
+        for (int s = 0; s < NSB; ++s)
+            bhi[nb][s] = as_bf16x8(ok ? ldg16(a.khi + p * DI + 16 * s + 8 * half)
+                                      : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
-            for (int s = 0; s < NS; ++s) bfr[nb][s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        for (int s = 0; s < NSF; ++s) {
+            const int d0 = 64 * s + 32 * half;
+            u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+            if (ok && d0 < DI) {
+                x0 = ldg16(a.klo + p * DI + d0);
+                x1 = ldg16(a.klo + p * DI + d0 + 16);
+            }
+            blo[nb][s] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                               (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
         }
+        bsc[nb] = ok ? (int)a.klo_scale[p] : 127;
     }
-
     // The resident fragments are loaded once; make that explicit so that the
     // tile loop never waits on the memory counter for them (which would also
     // wait for the next tile's prefetch).
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-    // tile j covers chunk rows i_begin + j*QPT .. +QPT: a contiguous block of
-    // 32 * DI bf16 in q_idx (rows = query*HI + head)
+    // tile j covers chunk rows i_begin + j*QPT .. +QPT: contiguous blocks of
+    // 32*DI bf16 in q_idx and 32*DI codes in the chunk's quantised queries
     u32x4 pre[CPT];
     float prew = 0.0f;
+    uint32_t pres = 127u;
     auto fetch = [&](int j) {
-        const int64_t qrow0 = a.row0 + i_begin + (int64_t)j * QPT;
+        const int i0 = i_begin + j * QPT;
+        const int64_t qrow0 = a.row0 + i0;
         const uint16_t* src = a.q_idx + qrow0 * (HI * DI);
+        const uint8_t* src8 = a.q8 + (int64_t)i0 * (HI * DI);
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
             const int ch = tid + u * 256;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (ch < CHUNKS) {
-                const int r = ch / (DI / 8);
-                if (qrow0 + r / HI < a.s_q) v = ldg16(src + (int64_t)ch * 8);
+            if (ch < CH16) {
+                if (i0 + (ch / (DI / 8)) / HI < a.rows) v = ldg16(src + (int64_t)ch * 8);
+            } else if (ch < CHT) {
+                const int c8 = ch - CH16;
+                if (i0 + (c8 / (DI / 16)) / HI < a.rows) v = ldg16(src8 + (int64_t)c8 * 16);
             }
             pre[u] = v;
         }
         if (tid < 32) {
-            const int64_t qr = qrow0 + tid / HI;
-            prew = qr < a.s_q ? a.w[qr * a.w_stride + (tid % HI)] : 0.0f;
+            const bool in = i0 + tid / HI < a.rows;
+            prew = in ? a.w[(qrow0 + tid / HI) * a.w_stride + (tid % HI)] : 0.0f;
+            pres = in ? (uint32_t)a.q8_scale[(int64_t)i0 * HI + tid] : 127u;
         }
     };
     auto stash = [&](int b) {
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
             const int ch = tid + u * 256;
-            if (ch < CHUNKS) {
+            if (ch < CH16) {
                 const int r = ch / (DI / 8), c8 = ch % (DI / 8);
                 *reinterpret_cast<u32x4*>(&sq[b][r * LROW + c8 * 8]) = pre[u];
+            } else if (ch < CHT) {
+                const int c8 = ch - CH16;
+                const int r = c8 / (DI / 16), c16 = c8 % (DI / 16);
+                *reinterpret_cast<u32x4*>(&sq8[b][r * LROW8 + c16 * 16]) = pre[u];
             }
         }
-        if (tid < 32) sw[b][tid] = prew;
+        if (tid < 32) {
+            sw[b][tid] = prew;
+            ss[b][tid] = pres;
+        }
     };
 
     fetch(0);
@@ -308,13 +412,32 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[nb][v] = 0.0f;
 
-        const uint16_t* arow = &sq[cur][col * LROW];
+        // q . hi on bf16 MFMAs
+        const uint16_t* arow = &sq[cur][col * LROW + 8 * half];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 8 * s));
+        for (int s = 0; s < NSB; ++s) {
+            const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 16 * s));
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[nb][s], acc[nb], 0, 0, 0);
+                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bhi[nb][s], acc[nb], 0, 0, 0);
+        }
+        // q . lo on scaled fp8 MFMAs into the same accumulators
+        const uint8_t* arow8 = &sq8[cur][col * LROW8];
+        const int qsc = (int)ss[cur][col];
+#pragma unroll
+        for (int s = 0; s < NSF; ++s) {
+            const int d0 = 64 * s + 32 * half;
+            u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+            if (d0 < DI) {
+                x0 = *reinterpret_cast<const u32x4*>(arow8 + d0);
+                x1 = *reinterpret_cast<const u32x4*>(arow8 + d0 + 16);
+            }
+            const i32x8 af8 = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                               (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    af8, blo[nb][s], acc[nb], 0, 0, 0, qsc, 0, bsc[nb]);
         }
 
         // epilogue: weights of the rows this lane holds
@@ -334,10 +457,10 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
             float part[4];
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                float s = 0.0f;
+                float sacc = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s += wv[4 * g4 + i] * relu(acc[nb][4 * g4 + i]);
-                part[g4] = s;
+                for (int i = 0; i < 4; ++i) sacc += wv[4 * g4 + i] * relu(acc[nb][4 * g4 + i]);
+                part[g4] = sacc;
             }
             // query qi of this tile and its value on this lane
             float qv[4];
@@ -375,6 +498,34 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
         if (has_next) stash(cur ^ 1);
         __syncthreads();
     }
+}
+
+template <int HI, int DI>
+static hipError_t launch_score_bf16_t(const ScoreArgs& a, hipStream_t stream) {
+    constexpr int NB = 2;
+    constexpr int PB = 128 * NB;
+    constexpr int QPT = 32 / HI;
+    ScoreK k;
+    k.q_idx = static_cast<const uint16_t*>(a.q_idx);
+    k.q8 = a.q8;
+    k.q8_scale = a.q8_scale;
+    k.khi = static_cast<const uint16_t*>(a.kbar);
+    k.klo = a.klo;
+    k.klo_scale = a.klo_scale;
+    k.w = a.w;
+    k.w_stride = a.w_stride;
+    k.s_q = a.s_q;
+    k.row0 = a.row0;
+    k.rows = a.rows;
+    k.gq = 64 * QPT;
+    k.q_pos0 = a.q_pos0;
+    k.n_pools = a.n_pools;
+    k.buf = a.buf;
+    k.ld = a.ld;
+    const dim3 grid((unsigned)((a.n_chunk + PB - 1) / PB), (unsigned)((a.rows + k.gq - 1) / k.gq));
+    if (grid.x == 0 || grid.y == 0) return hipSuccess;
+    index_score_bf16_kernel<HI, DI, NB><<<grid, 256, 0, stream>>>(k);
+    return hipGetLastError();
 }
 
 struct ScoreK8 {
@@ -612,30 +763,6 @@ static hipError_t launch_score_fp8_h(const ScoreArgs& a, hipStream_t stream) {
         case 128: return launch_score_fp8_t<HI, 128>(a, stream);
         default: return hipErrorInvalidValue;
     }
-}
-
-template <int HI, int DI>
-static hipError_t launch_score_bf16_t(const ScoreArgs& a, hipStream_t stream) {
-    constexpr int NB = 2;
-    constexpr int PB = 128 * NB;
-    constexpr int QPT = 32 / HI;
-    ScoreK k;
-    k.q_idx = static_cast<const uint16_t*>(a.q_idx);
-    k.kbar = static_cast<const uint16_t*>(a.kbar);
-    k.w = a.w;
-    k.w_stride = a.w_stride;
-    k.s_q = a.s_q;
-    k.row0 = a.row0;
-    k.rows = a.rows;
-    k.gq = 64 * QPT;
-    k.q_pos0 = a.q_pos0;
-    k.n_pools = a.n_pools;
-    k.buf = a.buf;
-    k.ld = a.ld;
-    const dim3 grid((unsigned)((a.n_chunk + PB - 1) / PB), (unsigned)((a.rows + k.gq - 1) / k.gq));
-    if (grid.x == 0 || grid.y == 0) return hipSuccess;
-    index_score_bf16_kernel<HI, DI, NB><<<grid, 256, 0, stream>>>(k);
-    return hipGetLastError();
 }
 
 template <int HI>

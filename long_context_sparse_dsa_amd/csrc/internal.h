@@ -7,10 +7,16 @@
 
 namespace dsa {
 
-// Pooled indexer keys, bf16 two-term split: kbar[p] = [hi(0..d) | lo(0..d)]
-// with hi = bf16(mean), lo = bf16(mean - hi).
+// Pooled indexer keys, split as hi = bf16(mean) [P][d] and lo = mean - hi
+// as E4M3 codes [P][d] with one E8M0 power-of-two scale byte per pool.
 hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, int64_t n_pools, int d_idx,
-                                 uint16_t* kbar, hipStream_t stream);
+                                 uint16_t* hi, uint8_t* lo, uint8_t* lo_scale,
+                                 hipStream_t stream);
+
+// n_vec query vectors (bf16 [n_vec][d]) as E4M3 codes with one E8M0
+// power-of-two scale byte each.
+hipError_t launch_quantize_queries(const uint16_t* q_rows, int64_t n_vec, int d_idx,
+                                   uint8_t* q8, uint8_t* q_scale, hipStream_t stream);
 
 // Pooled fp8 keys: per pool, E4M3 codes of mean/2^e and the factor 2^e.
 hipError_t launch_pool_keys_fp8(const uint8_t* k8, int64_t n_pools, int d_idx, uint8_t* kbar8,
@@ -18,7 +24,11 @@ hipError_t launch_pool_keys_fp8(const uint8_t* k8, int64_t n_pools, int d_idx, u
 
 struct ScoreArgs {
     const void* q_idx;        // [s_q, h_idx, d_idx] bf16 or E4M3
-    const void* kbar;         // pooled table (layout per dtype)
+    const void* kbar;         // bf16: hi [P][d]; fp8: codes [P][d]
+    const uint8_t* klo;       // bf16 only: lo codes [P][d]
+    const uint8_t* klo_scale; // bf16 only: [P] E8M0
+    const uint8_t* q8;        // bf16 only: the chunk's queries as E4M3 [rows][h][d]
+    const uint8_t* q8_scale;  // bf16 only: [rows][h] E8M0
     const float* pool_scale;  // fp8 only: [P] factors 2^e
     const float* q_scale;     // fp8 only: device scalar or null
     const float* k_scale;     // fp8 only: device scalar or null

@@ -63,6 +63,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dsa_index_score_topk.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _i64, _int,
             _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.dsa_index_scores_workspace_size.restype = _int
+        lib.dsa_index_scores_workspace_size.argtypes = [
+            _i64, _i64, _int, _int, _int, _int, _i64, ctypes.POINTER(ctypes.c_size_t)]
         lib.dsa_index_scores.restype = _int
         lib.dsa_index_scores.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _i64, _i64,
@@ -140,15 +143,14 @@ def _indexer_shapes(q_idx, k_idx, w):
     return s_q, s_k, h_idx, d_idx, w_stride, dtype
 
 
-def pooled_table_bytes(n_pools: int, d_idx: int, dtype: int) -> int:
-    """Bytes of the pooled key table the library keeps at the start of the
-    workspace (bf16: two bf16 terms per element; fp8: codes, then fp32
-    per-pool scales), each part rounded up to 256 bytes."""
-    def r(x):
-        return (x + 255) // 256 * 256
-    if dtype == DSA_BF16:
-        return r(n_pools * 2 * d_idx * 2)
-    return r(n_pools * d_idx) + r(n_pools * 4)
+def dsa_index_scores_workspace_size(s_q: int, s_k: int, h_idx: int, d_idx: int,
+                                    n_rows: int, pool_size: int = 4,
+                                    dtype: int = DSA_BF16) -> int:
+    lib = load_library()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.dsa_index_scores_workspace_size(s_q, s_k, h_idx, d_idx, pool_size, dtype, n_rows,
+                                               ctypes.byref(nbytes)))
+    return nbytes.value
 
 
 def new_workspace(nbytes: int, device=None) -> torch.Tensor:
@@ -193,7 +195,7 @@ def dsa_index_scores(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, 
     n_rows = s_q - row0 if n_rows is None else n_rows
     dev = q_idx.device
     n_pools = s_k // 4
-    need = pooled_table_bytes(n_pools, d_idx, dtype)
+    need = dsa_index_scores_workspace_size(s_q, s_k, h_idx, d_idx, n_rows, 4, dtype)
     if workspace is None:
         workspace = new_workspace(need, dev)
     out = torch.empty((n_rows, n_pools), dtype=torch.float32, device=dev)

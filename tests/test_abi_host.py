@@ -29,8 +29,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("dsa_index_score_topk", "dsa_sparse_attn_fwd", "dsa_index_workspace_size",
-              "dsa_index_scores", "dsa_last_error", "dsa_version", "dsa_profile_enable",
-              "dsa_profile_read"):
+              "dsa_index_scores", "dsa_index_scores_workspace_size", "dsa_last_error",
+              "dsa_version", "dsa_profile_enable", "dsa_profile_read"):
         assert n in names
 
 
@@ -45,7 +45,9 @@ def test_workspace_size_matches_layout(lib):
     # plus 256 x 32768 fp32 scores -- the page keeps each chunk under 2 GiB
     nbytes, cq = dsa.dsa_index_workspace_size(131072, 131072, 32, 128, 512, 4, 256)
     assert cq == 256
-    assert nbytes == 32768 * 256 * 2 + 256 * 32768 * 4
+    # hi bf16 + lo E4M3 + lo scales, the chunk's E4M3 queries + scales, the scores
+    assert nbytes == (32768 * 128 * 2 + 32768 * 128 + 32768
+                      + 256 * 32 * 128 + 256 * 32 + 256 * 32768 * 4)
     assert 256 * 32768 * 4 <= 2 ** 31
     # default chunk
     _, cq = dsa.dsa_index_workspace_size(32768, 32768, 32, 128, 512)
@@ -163,8 +165,11 @@ def test_fp8_workspace_layout(lib):
     nbytes, cq = dsa.dsa_index_workspace_size(65536, 65536, 32, 96, 512, 4, 256, dsa.DSA_FP8_E4M3)
     assert cq == 256
     assert nbytes == 16384 * 96 + 16384 * 4 + 256 * 16384 * 4
-    assert dsa.pooled_table_bytes(16384, 96, dsa.DSA_FP8_E4M3) == 16384 * 96 + 16384 * 4
-    assert dsa.pooled_table_bytes(1000, 128, dsa.DSA_BF16) == 1000 * 512
+    assert dsa.dsa_index_scores_workspace_size(65536, 65536, 32, 96, 16, 4,
+                                               dsa.DSA_FP8_E4M3) == 16384 * 96 + 16384 * 4
+    r = lambda x: (x + 255) // 256 * 256
+    assert dsa.dsa_index_scores_workspace_size(5000, 4000, 8, 128, 100) == (
+        r(1000 * 256) + r(1000 * 128) + r(1000) + r(100 * 8 * 128) + r(100 * 8))
 
 
 def test_profile_read_empty(lib):
