@@ -74,10 +74,11 @@ const char *dsa_last_error(void);
 /*
  * Bytes of device workspace dsa_index_score_topk needs.  Holds the pooled
  * key table (bf16: hi = bf16(mean) plus the residual as E4M3 codes with a
- * per-pool power-of-two scale; fp8: E4M3 codes plus per-pool factors), the
- * chunk's queries quantised for the bf16 correction term, and the per-chunk
- * fp32 score buffer of chunk_q x P entries ("Over Time: Chunking": the
- * buffer is constant in s_q).  chunk_q = 0 picks the library's default for
+ * per-pool power-of-two scale; fp8: E4M3 codes plus per-pool factors), for
+ * the bf16 indexer the chunk's queries and head weights packed in scoring
+ * tiles (with E4M3 copies of the queries for the correction term), and the
+ * per-chunk fp32 score buffer of chunk_q x round_up(P, 512) entries ("Over
+ * Time: Chunking": the buffer is constant in s_q).  chunk_q = 0 picks the library's default for
  * these shapes (the value is returned through *chunk_q_used when that
  * pointer is non-NULL).
  * Pure host computation; valid without a GPU.
@@ -116,8 +117,8 @@ dsa_status dsa_index_score_topk(const void *q_idx, const void *k_idx, const floa
 
 /*
  * Bytes of device workspace dsa_index_scores needs for n_rows query rows:
- * the pooled key table plus, for the bf16 indexer, the rows' queries
- * quantised for the correction term.  Pure host computation.
+ * the pooled key table plus, for the bf16 indexer, packed query tiles for up
+ * to 4096 rows (the rows are scored 4096 at a time).  Pure host computation.
  */
 dsa_status dsa_index_scores_workspace_size(int64_t s_q, int64_t s_k, int h_idx, int d_idx,
                                            int pool_size, int dtype, int64_t n_rows,
@@ -164,7 +165,7 @@ dsa_status dsa_sparse_attn_fwd(const void *q, const void *k, const void *v, cons
  * by HIP events on its own stream; dsa_profile_read synchronises on those
  * events and reports, per kernel kind, the number of launches and the summed
  * duration in milliseconds, then clears the record.  Kinds: "pool_keys",
- * "quantize_queries", "index_score", "topk_select", "sparse_attn".
+ * "pack_queries", "index_score", "topk_select", "sparse_attn".
  */
 typedef struct {
     char name[32];

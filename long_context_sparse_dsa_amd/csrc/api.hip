@@ -40,8 +40,8 @@ constexpr int64_t kScoreBufferCap = int64_t(2) << 30;  // per chunk, as the page
 
 // ------------------------------------------------------------ profiling
 
-enum Kind { K_POOL = 0, K_QUANT, K_SCORE, K_SELECT, K_ATTN, K_COUNT };
-const char* kKindName[K_COUNT] = {"pool_keys", "quantize_queries", "index_score", "topk_select",
+enum Kind { K_POOL = 0, K_PACK, K_SCORE, K_SELECT, K_ATTN, K_COUNT };
+const char* kKindName[K_COUNT] = {"pool_keys", "pack_queries", "index_score", "topk_select",
                                   "sparse_attn"};
 
 struct Rec {
@@ -123,7 +123,12 @@ dsa_status check_index_shape(const IndexShape& sh, bool need_k) {
     return DSA_OK;
 }
 
-int64_t score_ld(const IndexShape& sh) { return round_up(sh.n_pools > 0 ? sh.n_pools : 1, 64); }
+// Row stride of the chunk score buffer: a multiple of the pools one scoring
+// workgroup covers, so that its stores never need a column mask.
+int64_t score_ld(const IndexShape& sh) { return round_up(sh.n_pools > 0 ? sh.n_pools : 1, 512); }
+
+// Rows per scoring launch of the dense-score entry point (bounds its workspace).
+constexpr int64_t kDenseRows = 4096;
 
 dsa_status resolve_chunk(const IndexShape& sh, int64_t chunk_q, int64_t* out) {
     if (chunk_q < 0) return fail(DSA_ERR_INVALID_ARG, "chunk_q %lld < 0", (long long)chunk_q);
@@ -149,11 +154,10 @@ dsa_status resolve_chunk(const IndexShape& sh, int64_t chunk_q, int64_t* out) {
 
 // Workspace layout, every part starting on a 256-byte boundary:
 //   bf16 indexer: hi [P][d] bf16 | lo [P][d] E4M3 | lo scales [P] E8M0 |
-//                 chunk queries [rows][h][d] E4M3 | their scales [rows][h] |
-//                 score buffer [rows][ld] fp32
+//                 the chunk's packed query tiles | score buffer [rows][ld] fp32
 //   fp8 indexer:  codes [P][d] | per-pool factors [P] fp32 | score buffer
 struct Layout {
-    int64_t hi = 0, lo = 0, lo_scale = 0, q8 = 0, q8_scale = 0, buf = 0, total = 0;
+    int64_t hi = 0, lo = 0, lo_scale = 0, tiles = 0, buf = 0, total = 0;
 };
 
 Layout layout(const IndexShape& sh, int64_t rows, bool with_buffer) {
@@ -164,8 +168,8 @@ Layout layout(const IndexShape& sh, int64_t rows, bool with_buffer) {
         L.hi = off;        off += round_up(P * d * 2, 256);
         L.lo = off;        off += round_up(P * d, 256);
         L.lo_scale = off;  off += round_up(P, 256);
-        L.q8 = off;        off += round_up(rows * sh.h_idx * d, 256);
-        L.q8_scale = off;  off += round_up(rows * sh.h_idx, 256);
+        L.tiles = off;
+        off += round_up(dsa::query_tiles(rows, sh.h_idx) * dsa::query_tile_geom((int)d).tb, 256);
     } else {
         L.hi = off;        off += round_up(P * d, 256);
         L.lo_scale = off;  off += round_up(P * 4, 256);  // fp32 factors 2^e
@@ -213,16 +217,16 @@ hipError_t launch_pool(const IndexShape& sh, const Layout& L, const void* k_idx,
                                      reinterpret_cast<float*>(w + L.lo_scale), s);
 }
 
-// bf16 indexer: quantise query rows [row0, row0 + rows) for the correction MFMAs.
-hipError_t launch_quantize(const IndexShape& sh, const Layout& L, const void* q_idx,
-                           int64_t row0, int64_t rows, void* ws, hipStream_t s) {
+// bf16 indexer: pack query rows [row0, row0 + rows) and their weights into
+// the tiles the scoring kernel streams.
+hipError_t launch_pack(const IndexShape& sh, const Layout& L, const void* q_idx, const float* w,
+                       int64_t w_stride, int64_t row0, int64_t rows, void* ws, hipStream_t s) {
     if (sh.dtype != DSA_BF16) return hipSuccess;
-    Timed tm(K_QUANT, s);
-    char* w = static_cast<char*>(ws);
-    const uint16_t* q = static_cast<const uint16_t*>(q_idx) + row0 * sh.h_idx * sh.d_idx;
-    return dsa::launch_quantize_queries(q, rows * sh.h_idx, sh.d_idx,
-                                        reinterpret_cast<uint8_t*>(w + L.q8),
-                                        reinterpret_cast<uint8_t*>(w + L.q8_scale), s);
+    Timed tm(K_PACK, s);
+    char* base = static_cast<char*>(ws);
+    return dsa::launch_pack_queries(static_cast<const uint16_t*>(q_idx), w, w_stride, row0,
+                                    (int)rows, sh.h_idx, sh.d_idx,
+                                    reinterpret_cast<uint8_t*>(base + L.tiles), s);
 }
 
 void fill_score_args(dsa::ScoreArgs& a, const IndexShape& sh, const Layout& L,
@@ -234,8 +238,7 @@ void fill_score_args(dsa::ScoreArgs& a, const IndexShape& sh, const Layout& L,
     if (sh.dtype == DSA_BF16) {
         a.klo = reinterpret_cast<const uint8_t*>(base + L.lo);
         a.klo_scale = reinterpret_cast<const uint8_t*>(base + L.lo_scale);
-        a.q8 = reinterpret_cast<const uint8_t*>(base + L.q8);
-        a.q8_scale = reinterpret_cast<const uint8_t*>(base + L.q8_scale);
+        a.tiles = reinterpret_cast<const uint8_t*>(base + L.tiles);
         a.pool_scale = nullptr;
     } else {
         a.pool_scale = reinterpret_cast<const float*>(base + L.lo_scale);
@@ -283,7 +286,7 @@ dsa_status dsa_index_scores_workspace_size(int64_t s_q, int64_t s_k, int h_idx, 
     dsa_status st = check_index_shape(sh, false);
     if (st != DSA_OK) return st;
     if (n_rows < 0 || n_rows > s_q) return fail(DSA_ERR_INVALID_ARG, "n_rows outside [0, s_q]");
-    *bytes = (size_t)layout(sh, n_rows, false).total;
+    *bytes = (size_t)layout(sh, n_rows < kDenseRows ? n_rows : kDenseRows, false).total;
     return DSA_OK;
 }
 
@@ -327,8 +330,8 @@ dsa_status dsa_index_score_topk(const void* q_idx, const void* k_idx, const floa
         const int64_t t_last = q_pos0 + c0 + rows - 1;
         const int64_t n_chunk = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
         if (n_chunk > 0 && (n_chunk > k_pools || score_out)) {
-            e = launch_quantize(sh, L, q_idx, c0, rows, ws, s);
-            if (e != hipSuccess) return hip_fail(e, "quantize_queries launch");
+            e = launch_pack(sh, L, q_idx, w, w_stride_q, c0, rows, ws, s);
+            if (e != hipSuccess) return hip_fail(e, "pack_queries launch");
             dsa::ScoreArgs a{};
             fill_score_args(a, sh, L, q_idx, ws, q_scale, k_scale, w, w_stride_q);
             a.row0 = c0;
@@ -376,7 +379,7 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const float* q
         return fail(DSA_ERR_UNSUPPORTED, "at most 2^20 rows per call");
     if (n_rows > 0 && !scores_out) return fail(DSA_ERR_INVALID_ARG, "scores_out must be non-null");
     if (!aligned16(scores_out)) return fail(DSA_ERR_INVALID_ARG, "scores_out must be 16-byte aligned");
-    const Layout L = layout(sh, n_rows, false);
+    const Layout L = layout(sh, n_rows < kDenseRows ? n_rows : kDenseRows, false);
     const size_t need = (size_t)L.total;
     if (n_rows == 0 || sh.n_pools == 0) return DSA_OK;  // nothing to write
     if (!workspace || workspace_bytes < need)
@@ -388,17 +391,20 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const float* q
     if (e != hipSuccess) return hip_fail(e, "fill launch");
     e = launch_pool(sh, L, k_idx, workspace, s);
     if (e != hipSuccess) return hip_fail(e, "pool_keys launch");
-    const int64_t t_last = q_pos0 + row0 + n_rows - 1;
-    const int64_t n_chunk = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
-    if (n_chunk > 0) {
-        e = launch_quantize(sh, L, q_idx, row0, n_rows, workspace, s);
-        if (e != hipSuccess) return hip_fail(e, "quantize_queries launch");
+    for (int64_t r0 = row0; r0 < row0 + n_rows; r0 += kDenseRows) {
+        const int64_t rows = row0 + n_rows - r0 < kDenseRows ? row0 + n_rows - r0 : kDenseRows;
+        const int64_t t_last = q_pos0 + r0 + rows - 1;
+        const int64_t n_chunk = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
+        if (n_chunk == 0) continue;
+        e = launch_pack(sh, L, q_idx, w, w_stride_q, r0, rows, workspace, s);
+        if (e != hipSuccess) return hip_fail(e, "pack_queries launch");
         dsa::ScoreArgs a{};
         fill_score_args(a, sh, L, q_idx, workspace, q_scale, k_scale, w, w_stride_q);
-        a.row0 = row0;
-        a.rows = (int)n_rows;
+        a.row0 = r0;
+        a.rows = (int)rows;
         a.n_chunk = n_chunk;
-        a.buf = scores_out;
+        a.exact = 1;
+        a.buf = scores_out + (r0 - row0) * sh.n_pools;
         a.ld = sh.n_pools;
         Timed tm(K_SCORE, s);
         e = dsa::launch_index_score(a, s);

@@ -59,4 +59,38 @@ __device__ __forceinline__ float add_halves(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// s_waitcnt immediate that waits until at most n vector memory operations
+// are outstanding (0 <= n < 64), leaving the other counters alone.
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+    return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00;
+}
+
+// Byte address of an LDS object in the LDS aperture.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct global -> LDS loads: lane l of the wave reads `size` bytes at its
+// own global address and writes them to LDS at lds + l * size (lds is
+// wave-uniform).  Issued as inline assembly so that the compiler does not
+// serialise them against later LDS reads and barriers; the caller orders
+// them with explicit memory-counter waits.  M0 takes the LDS base (one
+// wait state between the M0 write and the load).
+__device__ __forceinline__ void lds_load16(const void* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+__device__ __forceinline__ void lds_load4(const void* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// Two half-wave sums at once: lanes 0-31 get x0[l] + x0[l + 32], lanes 32-63
+// get x1[l - 32] + x1[l] (the swap exchanges x0's upper half with x1's lower).
+__device__ __forceinline__ float add_halves2(float x0, float x1) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace dsa

@@ -193,27 +193,55 @@ hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, int64_t n_pools, int d_i
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- query quantisation
+// ---------------------------------------------------------------- query tiles
 
-// Rows [row0, row0 + rows) of q_idx as E4M3 codes with one E8M0 scale byte
-// per (query, head): the scaled MFMA operand of the q . lo correction.  One
-// thread per (query, head).
+// Byte offsets inside a packed query tile (layout in internal.h).
 template <int DI>
-__global__ __launch_bounds__(256) void quantize_queries_kernel(const uint16_t* __restrict__ q,
-                                                               int64_t n_vec,
-                                                               uint8_t* __restrict__ q8,
-                                                               uint8_t* __restrict__ q_scale) {
-    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (v >= n_vec) return;
+struct QTile {
+    static constexpr QueryTileGeom G = query_tile_geom(DI);
+    static constexpr int NPQ = G.qb / 16;           // 16-byte pieces of query data
+    static constexpr int CPT = (NPQ + 255) / 256;   // pieces per thread when staging
+    static constexpr int LDSQ = CPT * 4096;         // LDS bytes for the staged pieces
+    static constexpr int LDS_W = LDSQ;              // LDS: w [32] fp32, then scales [32]
+    static constexpr int LDSB = LDSQ + 1024;        // LDS bytes per tile buffer
+    // piece c (16 bytes) of the bf16 / E4M3 row r
+    __device__ static constexpr int bf16_piece(int r, int c) {
+        return r * G.lb + 16 * (G.swz ? (c ^ (r & 15)) : c);
+    }
+    __device__ static constexpr int fp8_piece(int r, int c) {
+        return G.of8 + r * G.l8 + 16 * (G.swz ? (c ^ ((r & 7) ^ ((r >> 3) & 1))) : c);
+    }
+};
+
+// One thread per tile row (query, head): the bf16 row, its E4M3 codes with
+// the power-of-two scale 2^e (e the smallest with max|q| <= 448 * 2^e), and
+// the row's head weight.  Rows past the chunk are zero with weight 0.
+template <int HI, int DI>
+__global__ __launch_bounds__(256) void pack_queries_kernel(const uint16_t* __restrict__ q,
+                                                           const float* __restrict__ w,
+                                                           int64_t w_stride, int64_t row0,
+                                                           int rows, int64_t n_rows_tiled,
+                                                           uint8_t* __restrict__ tiles) {
+    using T = QTile<DI>;
+    constexpr int QPT = 32 / HI;
+    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;  // tile * 32 + r
+    if (v >= n_rows_tiled) return;
+    const int64_t tile = v >> 5;
+    const int r = (int)(v & 31);
+    const int64_t i = tile * QPT + r / HI;
+    const int h = r % HI;
+    const bool in = i < rows;
+    uint8_t* dst = tiles + tile * T::G.tb;
     float x[DI];
     float amax = 0.0f;
 #pragma unroll
-    for (int g = 0; g < DI / 8; ++g) {
-        const u32x4 r = ldg16(q + v * DI + 8 * g);
+    for (int c = 0; c < DI / 8; ++c) {
+        const u32x4 raw = in ? ldg16(q + ((row0 + i) * HI + h) * DI + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(dst + T::bf16_piece(r, c)) = raw;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            x[8 * g + e] = bf16_to_f32((r[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
-            amax = fmaxf(amax, fabsf(x[8 * g + e]));
+            x[8 * c + e] = bf16_to_f32((raw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+            amax = fmaxf(amax, fabsf(x[8 * c + e]));
         }
     }
     const int e = pow2_scale_exp(amax);
@@ -222,22 +250,37 @@ __global__ __launch_bounds__(256) void quantize_queries_kernel(const uint16_t* _
         u32x4 o = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int b = 0; b < 16; ++b) o[b >> 2] |= e4m3_code(ldexpf(x[16 * c + b], -e)) << ((b & 3) * 8);
-        *reinterpret_cast<u32x4*>(q8 + v * DI + 16 * c) = o;
+        *reinterpret_cast<u32x4*>(dst + T::fp8_piece(r, c)) = o;
     }
-    q_scale[v] = (uint8_t)(e + 127);
+    reinterpret_cast<float*>(dst + T::G.qb)[r] = in ? w[(row0 + i) * w_stride + h] : 0.0f;
+    dst[T::G.qb + 128 + r] = (uint8_t)(e + 127);
 }
 
-hipError_t launch_quantize_queries(const uint16_t* q_rows, int64_t n_vec, int d_idx,
-                                   uint8_t* q8, uint8_t* q_scale, hipStream_t stream) {
-    if (n_vec <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((n_vec + 255) / 256));
+template <int HI>
+static hipError_t launch_pack_h(const uint16_t* q, const float* w, int64_t w_stride, int64_t row0,
+                                int rows, int d_idx, uint8_t* tiles, hipStream_t stream) {
+    const int64_t n = ((int64_t)rows + 32 / HI - 1) / (32 / HI) * 32;
+    const dim3 grid((unsigned)((n + 255) / 256));
     switch (d_idx) {
-        case 64: quantize_queries_kernel<64><<<grid, 256, 0, stream>>>(q_rows, n_vec, q8, q_scale); break;
-        case 96: quantize_queries_kernel<96><<<grid, 256, 0, stream>>>(q_rows, n_vec, q8, q_scale); break;
-        case 128: quantize_queries_kernel<128><<<grid, 256, 0, stream>>>(q_rows, n_vec, q8, q_scale); break;
+        case 64: pack_queries_kernel<HI, 64><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, n, tiles); break;
+        case 96: pack_queries_kernel<HI, 96><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, n, tiles); break;
+        case 128: pack_queries_kernel<HI, 128><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, n, tiles); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_pack_queries(const uint16_t* q_idx, const float* w, int64_t w_stride,
+                               int64_t row0, int rows, int h_idx, int d_idx, uint8_t* tiles,
+                               hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    switch (h_idx) {
+        case 4: return launch_pack_h<4>(q_idx, w, w_stride, row0, rows, d_idx, tiles, stream);
+        case 8: return launch_pack_h<8>(q_idx, w, w_stride, row0, rows, d_idx, tiles, stream);
+        case 16: return launch_pack_h<16>(q_idx, w, w_stride, row0, rows, d_idx, tiles, stream);
+        case 32: return launch_pack_h<32>(q_idx, w, w_stride, row0, rows, d_idx, tiles, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 // ---------------------------------------------------------------- fill
@@ -258,15 +301,10 @@ hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t stream)
 // ---------------------------------------------------------------- scoring
 
 struct ScoreK {
-    const uint16_t* q_idx;      // [s_q][HI][DI] bf16
-    const uint8_t* q8;          // chunk rows [rows][HI][DI] E4M3
-    const uint8_t* q8_scale;    // chunk rows [rows][HI] E8M0
+    const uint8_t* tiles;       // the chunk's packed query tiles
     const uint16_t* khi;        // [P][DI] bf16
     const uint8_t* klo;         // [P][DI] E4M3
     const uint8_t* klo_scale;   // [P] E8M0
-    const float* w;
-    int64_t w_stride;
-    int64_t s_q;
     int64_t row0;
     int rows;
     int gq;          // queries per workgroup (multiple of 32 / HI)
@@ -283,28 +321,32 @@ struct ScoreK {
 // layout with 32 contraction bytes per lane, and takes one E8M0 scale per
 // lane for the row (A) or column (B) block that lane holds.
 //
-// Workgroup = 4 waves; each wave owns NB blocks of 32 consecutive pools
+// Workgroup = 4 waves; each wave owns NB = 2 blocks of 32 consecutive pools
 // (hi and lo of the pooled keys resident as B fragments); the workgroup owns
-// 128*NB pools and a range of gq chunk rows, walked one 32-row (query, head)
-// tile at a time through double-buffered LDS.
-template <int HI, int DI, int NB>
+// 256 pools and a range of gq chunk rows, walked one packed query tile (32
+// (query, head) rows) at a time through double-buffered LDS.  Every thread
+// moves the same 16-byte pieces of every tile, from precomputed offsets, two
+// tiles ahead in registers and one ahead in LDS; the loop issues the same
+// memory operations every tile (prefetches past the last tile read the
+// chunk's spare tiles, stores of a chunk buffer are never masked), so its
+// memory-counter waits cover only the prefetch they need.
+//
+// EXACT = false: the chunk-buffer contract of ScoreArgs (any entry may be
+// written, ineligible pools get -inf).  EXACT = true: only eligible entries of
+// rows [0, rows) are stored.
+template <int HI, int DI, int NB, bool EXACT>
 __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
-    constexpr int QPT = 32 / HI;      // queries per 32-row tile
+    static_assert(NB == 2, "the epilogue pairs the two pool blocks of a wave");
+    using T = QTile<DI>;
+    constexpr int QPT = 32 / HI;      // queries per tile
     constexpr int NSB = DI / 16;      // bf16 MFMA steps (16 dims each)
     constexpr int NSF = (DI + 63) / 64;  // fp8 MFMA steps (64 dims each)
     constexpr int PW = 32 * NB;       // pools per wave
     constexpr int PB = 4 * PW;        // pools per workgroup
-    constexpr int LROW = DI + 8;      // bf16 LDS row stride (elements)
-    constexpr int LROW8 = DI + 16;    // fp8 LDS row stride (bytes)
-    constexpr int CH16 = 4 * DI;      // 16-byte pieces of the bf16 tile
-    constexpr int CH8 = 2 * DI;       // 16-byte pieces of the fp8 tile
-    constexpr int CHT = CH16 + CH8;
-    constexpr int CPT = (CHT + 255) / 256;
+    constexpr int CPT = T::CPT;
+    constexpr int NBUF = 4;           // LDS tile buffers (tiles in flight + 1)
 
-    __shared__ __attribute__((aligned(16))) uint16_t sq[2][32 * LROW];
-    __shared__ __attribute__((aligned(16))) uint8_t sq8[2][32 * LROW8];
-    __shared__ __attribute__((aligned(16))) float sw[2][32];
-    __shared__ __attribute__((aligned(16))) uint32_t ss[2][32];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * T::LDSB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, half = lane >> 5;
@@ -346,65 +388,65 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
         bsc[nb] = ok ? (int)a.klo_scale[p] : 127;
     }
     // The resident fragments are loaded once; make that explicit so that the
-    // tile loop never waits on the memory counter for them (which would also
-    // wait for the next tile's prefetch).
+    // tile loop never waits on the memory counter for them.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-    // tile j covers chunk rows i_begin + j*QPT .. +QPT: contiguous blocks of
-    // 32*DI bf16 in q_idx and 32*DI codes in the chunk's quantised queries
-    u32x4 pre[CPT];
-    float prew = 0.0f;
-    uint32_t pres = 127u;
+    // Query tiles travel global -> LDS by direct loads (no registers), NBUF
+    // buffers deep: the loads for tile j + NBUF - 1 are issued at the start
+    // of tile j.  Thread tid moves 16-byte pieces tid + 256u (loads clamped to
+    // the last piece; LDS slots past the query data are spare) and one dword
+    // of the weights/scales tail (w at dwords 0-31, scale bytes in 32-39).
+    // Lane l of a wave lands at the wave's LDS base + l * size, so each
+    // instruction fills a contiguous 1 KiB (256 B) slice.
+    constexpr int D = NBUF - 1;
+    constexpr int NDMA = CPT + 1;                     // direct loads per tile
+    constexpr int S = HI == 4 ? 8 : QPT;              // score stores per tile
+    const uint8_t* gsrc[CPT + 1];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u)
+        gsrc[u] = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb + 16 * min(tid + 256 * u, T::NPQ - 1);
+    gsrc[CPT] = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb + T::G.qb + 4 * min(tid, 39);
+    const uint32_t lds0 = lds_address(lds) + 1024u * (uint32_t)wave;
     auto fetch = [&](int j) {
-        const int i0 = i_begin + j * QPT;
-        const int64_t qrow0 = a.row0 + i0;
-        const uint16_t* src = a.q_idx + qrow0 * (HI * DI);
-        const uint8_t* src8 = a.q8 + (int64_t)i0 * (HI * DI);
+        const int64_t g = (int64_t)j * T::G.tb;
+        const uint32_t l = lds0 + (uint32_t)((j % NBUF) * T::LDSB);
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int ch = tid + u * 256;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (ch < CH16) {
-                if (i0 + (ch / (DI / 8)) / HI < a.rows) v = ldg16(src + (int64_t)ch * 8);
-            } else if (ch < CHT) {
-                const int c8 = ch - CH16;
-                if (i0 + (c8 / (DI / 16)) / HI < a.rows) v = ldg16(src8 + (int64_t)c8 * 16);
-            }
-            pre[u] = v;
-        }
-        if (tid < 32) {
-            const bool in = i0 + tid / HI < a.rows;
-            prew = in ? a.w[(qrow0 + tid / HI) * a.w_stride + (tid % HI)] : 0.0f;
-            pres = in ? (uint32_t)a.q8_scale[(int64_t)i0 * HI + tid] : 127u;
-        }
+        for (int u = 0; u < CPT; ++u) lds_load16(gsrc[u] + g, l + 4096u * u);
+        lds_load4(gsrc[CPT] + g, l + (uint32_t)T::LDS_W - 768u * (uint32_t)wave);
     };
-    auto stash = [&](int b) {
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int ch = tid + u * 256;
-            if (ch < CH16) {
-                const int r = ch / (DI / 8), c8 = ch % (DI / 8);
-                *reinterpret_cast<u32x4*>(&sq[b][r * LROW + c8 * 8]) = pre[u];
-            } else if (ch < CHT) {
-                const int c8 = ch - CH16;
-                const int r = c8 / (DI / 16), c16 = c8 % (DI / 16);
-                *reinterpret_cast<u32x4*>(&sq8[b][r * LROW8 + c16 * 16]) = pre[u];
-            }
-        }
-        if (tid < 32) {
-            sw[b][tid] = prew;
-            ss[b][tid] = pres;
-        }
+    // Tile j's loads are complete once at most this many later memory
+    // operations are outstanding (loads and stores retire in order): the
+    // loads of the D - 1 tiles issued after it and the stores of up to D
+    // tiles.  With EXACT the stores are conditional and are not counted.
+    auto wait_tile = [&](int j) {
+        constexpr int base = (D - 1) * NDMA;
+        constexpr int full = base + (EXACT ? 0 : D * S);
+        static_assert(full < 64, "vmcnt range");
+        if (j >= D) __builtin_amdgcn_s_waitcnt(vmcnt_imm(full));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(base));
     };
 
-    fetch(0);
-    stash(0);
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < D; ++j) fetch(j);
 
+    const int64_t t_row0 = a.q_pos0 + a.row0;
+    auto put = [&](int i, int p, float v) {
+        const int64_t t = t_row0 + i;
+        const int nt = (int)((t >> 2) < a.n_pools ? (t >> 2) : a.n_pools);
+        float* dst = a.buf + (int64_t)i * a.ld + p;
+        if constexpr (EXACT) {
+            if (i < i_end && p < nt) *dst = canonical_zero(v);
+        } else {
+            *dst = p < nt ? canonical_zero(v) : -INFINITY;
+        }
+    };
     for (int j = 0; j < n_tiles; ++j) {
-        const int cur = j & 1;
-        const bool has_next = j + 1 < n_tiles;
-        if (has_next) fetch(j + 1);
+        wait_tile(j);
+        __syncthreads();
+        // every wave is past tile j - 1: its buffer takes tile j + D (tiles
+        // past the chunk's end read its spare tiles and are never used)
+        fetch(j + D);
+        const uint8_t* L = lds + (j % NBUF) * T::LDSB;
 
         f32x16 acc[NB];
 #pragma unroll
@@ -412,92 +454,93 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[nb][v] = 0.0f;
 
-        // q . hi on bf16 MFMAs
-        const uint16_t* arow = &sq[cur][col * LROW + 8 * half];
-#pragma unroll
-        for (int s = 0; s < NSB; ++s) {
-            const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 16 * s));
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bhi[nb][s], acc[nb], 0, 0, 0);
-        }
+        // all A fragments of the tile first, then q . hi on bf16 MFMAs and
         // q . lo on scaled fp8 MFMAs into the same accumulators
-        const uint8_t* arow8 = &sq8[cur][col * LROW8];
-        const int qsc = (int)ss[cur][col];
+        bf16x8 af[NSB];
+        i32x8 af8[NSF];
+#pragma unroll
+        for (int s = 0; s < NSB; ++s)
+            af[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(L + T::bf16_piece(col, 2 * s + half)));
 #pragma unroll
         for (int s = 0; s < NSF; ++s) {
-            const int d0 = 64 * s + 32 * half;
-            u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-            if (d0 < DI) {
-                x0 = *reinterpret_cast<const u32x4*>(arow8 + d0);
-                x1 = *reinterpret_cast<const u32x4*>(arow8 + d0 + 16);
-            }
-            const i32x8 af8 = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                               (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+            // pieces past d_idx (only with d_idx = 96) read row padding or the
+            // next row and are zeroed
+            const bool in = 64 * s + 32 * half < DI;
+            u32x4 x0 = *reinterpret_cast<const u32x4*>(L + T::fp8_piece(col, 4 * s + 2 * half));
+            u32x4 x1 = *reinterpret_cast<const u32x4*>(L + T::fp8_piece(col, 4 * s + 2 * half + 1));
+            if (!in) x0 = x1 = u32x4{0u, 0u, 0u, 0u};
+            af8[s] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                           (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+        }
+        const int qsc = (int)L[T::LDS_W + 128 + col];
+#pragma unroll
+        for (int s = 0; s < NSB; ++s)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], bhi[nb][s], acc[nb], 0, 0, 0);
+#pragma unroll
+        for (int s = 0; s < NSF; ++s)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
                 acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af8, blo[nb][s], acc[nb], 0, 0, 0, qsc, 0, bsc[nb]);
-        }
+                    af8[s], blo[nb][s], acc[nb], 0, 0, 0, qsc, 0, bsc[nb]);
+        // keep the LDS reads ahead of the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, NSB + 2 * NSF + 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NB * (NSB + NSF), 0);
 
-        // epilogue: weights of the rows this lane holds
+        // epilogue: per-lane partial sums w * relu over the rows this lane
+        // holds (rows 8*g4 + 4*half + i), then the two half-waves' partials of
+        // each column are added
         float wv[16];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 w4 = *reinterpret_cast<const f32x4*>(&sw[cur][8 * g4 + 4 * half]);
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(L + T::LDS_W + 4 * (8 * g4 + 4 * half));
             wv[4 * g4 + 0] = w4[0];
             wv[4 * g4 + 1] = w4[1];
             wv[4 * g4 + 2] = w4[2];
             wv[4 * g4 + 3] = w4[3];
         }
-        const int tile_i0 = i_begin + j * QPT;
+        float part[NB][4];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int64_t p = p_wave + nb * 32 + col;
-            float part[4];
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 float sacc = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sacc += wv[4 * g4 + i] * relu(acc[nb][4 * g4 + i]);
-                part[g4] = sacc;
+                part[nb][g4] = sacc;
             }
-            // query qi of this tile and its value on this lane
-            float qv[4];
-            int nq;
-            if constexpr (HI == 32) {
-                qv[0] = add_halves((part[0] + part[1]) + (part[2] + part[3]));
-                nq = 1;
-            } else if constexpr (HI == 16) {
-                qv[0] = add_halves(part[0] + part[1]);
-                qv[1] = add_halves(part[2] + part[3]);
-                nq = 2;
-            } else if constexpr (HI == 8) {
+        const int tile_i0 = i_begin + j * QPT;
+        if constexpr (HI == 4) {
+            // rows 8*g4 + 4*half + i are the 4 heads of query 2*g4 + half
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) qv[g4] = add_halves(part[g4]);
-                nq = 4;
-            } else {  // HI == 4: rows 8*g4 + 4*half + i -> query 2*g4 + half, complete in-lane
+            for (int g4 = 0; g4 < 4; ++g4)
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) qv[g4] = part[g4];
-                nq = 4;
-            }
-            if (HI == 4 || half == 0) {
+                for (int nb = 0; nb < NB; ++nb)
+                    put(tile_i0 + 2 * g4 + half, (int)p_wave + nb * 32 + col, part[nb][g4]);
+        } else {
+            // lane l < 32 ends with pool block 0, lane l >= 32 with block 1:
+            // one store of 64 consecutive pools per query
 #pragma unroll
-                for (int u = 0; u < nq; ++u) {
-                    const int qi = (HI == 4) ? (2 * u + half) : u;
-                    const int i = tile_i0 + qi;
-                    if (i < i_end) {
-                        const int64_t t = a.q_pos0 + a.row0 + i;
-                        const int64_t nt = (t >> 2) < a.n_pools ? (t >> 2) : a.n_pools;
-                        if (p < nt) a.buf[(int64_t)i * a.ld + p] = canonical_zero(qv[u]);
-                    }
+            for (int u = 0; u < QPT; ++u) {
+                float x0, x1;
+                if constexpr (HI == 32) {
+                    x0 = (part[0][0] + part[0][1]) + (part[0][2] + part[0][3]);
+                    x1 = (part[1][0] + part[1][1]) + (part[1][2] + part[1][3]);
+                } else if constexpr (HI == 16) {
+                    x0 = part[0][2 * u] + part[0][2 * u + 1];
+                    x1 = part[1][2 * u] + part[1][2 * u + 1];
+                } else {
+                    x0 = part[0][u];
+                    x1 = part[1][u];
                 }
+                put(tile_i0 + u, (int)p_wave + lane, add_halves2(x0, x1));
             }
         }
-
-        if (has_next) stash(cur ^ 1);
-        __syncthreads();
     }
+    // the direct loads still in flight (spare tiles) write this workgroup's
+    // LDS: they must land before the workgroup ends
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 template <int HI, int DI>
@@ -506,15 +549,10 @@ static hipError_t launch_score_bf16_t(const ScoreArgs& a, hipStream_t stream) {
     constexpr int PB = 128 * NB;
     constexpr int QPT = 32 / HI;
     ScoreK k;
-    k.q_idx = static_cast<const uint16_t*>(a.q_idx);
-    k.q8 = a.q8;
-    k.q8_scale = a.q8_scale;
+    k.tiles = a.tiles;
     k.khi = static_cast<const uint16_t*>(a.kbar);
     k.klo = a.klo;
     k.klo_scale = a.klo_scale;
-    k.w = a.w;
-    k.w_stride = a.w_stride;
-    k.s_q = a.s_q;
     k.row0 = a.row0;
     k.rows = a.rows;
     k.gq = 64 * QPT;
@@ -524,7 +562,8 @@ static hipError_t launch_score_bf16_t(const ScoreArgs& a, hipStream_t stream) {
     k.ld = a.ld;
     const dim3 grid((unsigned)((a.n_chunk + PB - 1) / PB), (unsigned)((a.rows + k.gq - 1) / k.gq));
     if (grid.x == 0 || grid.y == 0) return hipSuccess;
-    index_score_bf16_kernel<HI, DI, NB><<<grid, 256, 0, stream>>>(k);
+    if (a.exact) index_score_bf16_kernel<HI, DI, NB, true><<<grid, 256, 0, stream>>>(k);
+    else index_score_bf16_kernel<HI, DI, NB, false><<<grid, 256, 0, stream>>>(k);
     return hipGetLastError();
 }
 

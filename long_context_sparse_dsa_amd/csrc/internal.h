@@ -13,26 +13,54 @@ hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, int64_t n_pools, int d_i
                                  uint16_t* hi, uint8_t* lo, uint8_t* lo_scale,
                                  hipStream_t stream);
 
-// n_vec query vectors (bf16 [n_vec][d]) as E4M3 codes with one E8M0
-// power-of-two scale byte each.
-hipError_t launch_quantize_queries(const uint16_t* q_rows, int64_t n_vec, int d_idx,
-                                   uint8_t* q8, uint8_t* q_scale, hipStream_t stream);
+// Packed query tiles of the bf16 indexer.  A tile holds 32 (query, head)
+// rows r = qi * h_idx + h of 32 / h_idx consecutive chunk queries, laid out
+// exactly as the scoring kernel keeps it in LDS:
+//   [0, OF8)        bf16 q rows (row stride LB bytes)
+//   [OF8, QB)       E4M3 codes of q / 2^e_r (row stride L8 bytes)
+//   [QB, QB + 128)  w of each row, fp32
+//   [QB + 128, +32) E8M0 byte e_r + 127 of each row
+// Rows are stored in 16-byte pieces.  With d = 128 the piece order within a
+// row is XOR-swizzled by the row index so that the MFMA operand reads of 16
+// rows at a time hit distinct LDS banks; other widths pad each row by 16
+// bytes instead.  Consecutive tiles are TB bytes apart.
+struct QueryTileGeom {
+    bool swz;
+    int lb, l8, of8, qb, tb;
+};
+inline constexpr QueryTileGeom query_tile_geom(int d) {
+    const bool swz = d == 128;
+    const int lb = swz ? 2 * d : 2 * d + 16;
+    const int l8 = swz ? d : d + 16;
+    const int of8 = 32 * lb;
+    const int qb = of8 + 32 * l8;
+    return QueryTileGeom{swz, lb, l8, of8, qb, (qb + 160 + 127) / 128 * 128};
+}
+// Tiles the scoring kernel may read for a chunk of `rows` queries: the
+// chunk's own plus three beyond its end (prefetched, never used).
+inline constexpr int64_t query_tiles(int64_t rows, int h_idx) {
+    return (rows + 32 / h_idx - 1) / (32 / h_idx) + 3;
+}
+
+// Rows [row0, row0 + rows) of q_idx and w packed into query tiles.
+hipError_t launch_pack_queries(const uint16_t* q_idx, const float* w, int64_t w_stride,
+                               int64_t row0, int rows, int h_idx, int d_idx, uint8_t* tiles,
+                               hipStream_t stream);
 
 // Pooled fp8 keys: per pool, E4M3 codes of mean/2^e and the factor 2^e.
 hipError_t launch_pool_keys_fp8(const uint8_t* k8, int64_t n_pools, int d_idx, uint8_t* kbar8,
                                 float* pool_scale, hipStream_t stream);
 
 struct ScoreArgs {
-    const void* q_idx;        // [s_q, h_idx, d_idx] bf16 or E4M3
+    const void* q_idx;        // fp8: [s_q, h_idx, d_idx] E4M3
+    const uint8_t* tiles;     // bf16: the chunk's packed query tiles
     const void* kbar;         // bf16: hi [P][d]; fp8: codes [P][d]
     const uint8_t* klo;       // bf16 only: lo codes [P][d]
     const uint8_t* klo_scale; // bf16 only: [P] E8M0
-    const uint8_t* q8;        // bf16 only: the chunk's queries as E4M3 [rows][h][d]
-    const uint8_t* q8_scale;  // bf16 only: [rows][h] E8M0
     const float* pool_scale;  // fp8 only: [P] factors 2^e
     const float* q_scale;     // fp8 only: device scalar or null
     const float* k_scale;     // fp8 only: device scalar or null
-    const float* w;
+    const float* w;           // fp8 only (bf16 weights travel in the tiles)
     int64_t w_stride;
     int64_t s_q;
     int64_t row0;             // first query row of the chunk
@@ -42,6 +70,11 @@ struct ScoreArgs {
     int64_t n_chunk;          // pools eligible for the chunk's last query
     int h_idx, d_idx;
     int fp8;
+    // exact = 0: buf is a chunk buffer with at least round_up(rows, 8) rows
+    // and ld >= round_up(n_chunk, 512); the kernel may write any entry of it
+    // (ineligible pools get -inf).  exact = 1: only the eligible entries of
+    // rows [0, rows) are written (a caller's dense [rows, P] layout).
+    int exact;
     float* buf;               // [rows, ld] fp32
     int64_t ld;
 };
