@@ -213,58 +213,63 @@ struct QTile {
     }
 };
 
-// One thread per tile row (query, head): the bf16 row, its E4M3 codes with
-// the power-of-two scale 2^e (e the smallest with max|q| <= 448 * 2^e), and
-// the row's head weight.  Rows past the chunk are zero with weight 0.
+// One workgroup per tile, 8 threads per tile row (query, head), thread c
+// holding dims 16c .. 16c + 15: the bf16 row, its E4M3 codes with the
+// power-of-two scale 2^e (e the smallest with max|q| <= 448 * 2^e, the row
+// maximum combined across the row's 8 threads), and the row's head weight.
+// Rows past the chunk are zero with weight 0.
 template <int HI, int DI>
 __global__ __launch_bounds__(256) void pack_queries_kernel(const uint16_t* __restrict__ q,
                                                            const float* __restrict__ w,
                                                            int64_t w_stride, int64_t row0,
-                                                           int rows, int64_t n_rows_tiled,
-                                                           uint8_t* __restrict__ tiles) {
+                                                           int rows, uint8_t* __restrict__ tiles) {
     using T = QTile<DI>;
     constexpr int QPT = 32 / HI;
-    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;  // tile * 32 + r
-    if (v >= n_rows_tiled) return;
-    const int64_t tile = v >> 5;
-    const int r = (int)(v & 31);
+    const int64_t tile = blockIdx.x;
+    const int r = threadIdx.x >> 3, c = threadIdx.x & 7;
     const int64_t i = tile * QPT + r / HI;
     const int h = r % HI;
-    const bool in = i < rows;
+    const bool in = i < rows, act = c < DI / 16;
     uint8_t* dst = tiles + tile * T::G.tb;
-    float x[DI];
+    u32x4 raw[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    if (in && act) {
+        const uint16_t* src = q + ((row0 + i) * HI + h) * DI + 16 * c;
+        raw[0] = ldg16(src);
+        raw[1] = ldg16(src + 8);
+    }
+    float x[16];
     float amax = 0.0f;
 #pragma unroll
-    for (int c = 0; c < DI / 8; ++c) {
-        const u32x4 raw = in ? ldg16(q + ((row0 + i) * HI + h) * DI + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(dst + T::bf16_piece(r, c)) = raw;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            x[8 * c + e] = bf16_to_f32((raw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
-            amax = fmaxf(amax, fabsf(x[8 * c + e]));
-        }
+    for (int e = 0; e < 16; ++e) {
+        x[e] = bf16_to_f32((raw[e >> 3][(e & 7) >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+        amax = fmaxf(amax, fabsf(x[e]));
     }
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
     const int e = pow2_scale_exp(amax);
-#pragma unroll
-    for (int c = 0; c < DI / 16; ++c) {
+    if (act) {
+        *reinterpret_cast<u32x4*>(dst + T::bf16_piece(r, 2 * c)) = raw[0];
+        *reinterpret_cast<u32x4*>(dst + T::bf16_piece(r, 2 * c + 1)) = raw[1];
         u32x4 o = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int b = 0; b < 16; ++b) o[b >> 2] |= e4m3_code(ldexpf(x[16 * c + b], -e)) << ((b & 3) * 8);
+        for (int b = 0; b < 16; ++b) o[b >> 2] |= e4m3_code(ldexpf(x[b], -e)) << ((b & 3) * 8);
         *reinterpret_cast<u32x4*>(dst + T::fp8_piece(r, c)) = o;
     }
-    reinterpret_cast<float*>(dst + T::G.qb)[r] = in ? w[(row0 + i) * w_stride + h] : 0.0f;
-    dst[T::G.qb + 128 + r] = (uint8_t)(e + 127);
+    if (c == 0) {
+        reinterpret_cast<float*>(dst + T::G.qb)[r] = in ? w[(row0 + i) * w_stride + h] : 0.0f;
+        dst[T::G.qb + 128 + r] = (uint8_t)(e + 127);
+    }
 }
 
 template <int HI>
 static hipError_t launch_pack_h(const uint16_t* q, const float* w, int64_t w_stride, int64_t row0,
                                 int rows, int d_idx, uint8_t* tiles, hipStream_t stream) {
-    const int64_t n = ((int64_t)rows + 32 / HI - 1) / (32 / HI) * 32;
-    const dim3 grid((unsigned)((n + 255) / 256));
+    const dim3 grid((unsigned)(((int64_t)rows + 32 / HI - 1) / (32 / HI)));
     switch (d_idx) {
-        case 64: pack_queries_kernel<HI, 64><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, n, tiles); break;
-        case 96: pack_queries_kernel<HI, 96><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, n, tiles); break;
-        case 128: pack_queries_kernel<HI, 128><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, n, tiles); break;
+        case 64: pack_queries_kernel<HI, 64><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, tiles); break;
+        case 96: pack_queries_kernel<HI, 96><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, tiles); break;
+        case 128: pack_queries_kernel<HI, 128><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, tiles); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
