@@ -116,9 +116,14 @@ def cpu_baseline(wl, x, target_s: float):
     def strided(r):
         return np.linspace(0, wl.s_q - 1, r).round().astype(np.int64)
 
+    # two probes separate the fixed cost (pooling every key) from the
+    # per-row cost, so that the timed sample lands near target_s
     probe = max(threads, 8)
-    t_probe = run(strided(probe))
-    r = int(max(probe, min(wl.s_q, probe * target_s / max(t_probe, 1e-3))))
+    t1 = run(strided(probe))
+    t4 = run(strided(4 * probe))
+    per_row = max((t4 - t1) / (3 * probe), 1e-6)
+    fixed = max(t1 - probe * per_row, 0.0)
+    r = int(max(probe, min(wl.s_q, (target_s - fixed) / per_row)))
     rows = strided(r)
     t = run(rows)
     return {"value": r / t, "unit": "queries/s", "cores": threads, "kind": "oracle",

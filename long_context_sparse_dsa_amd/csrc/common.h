@@ -85,6 +85,21 @@ __device__ __forceinline__ void lds_load4(const void* gptr, uint32_t lds) {
                  :: "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
+// XCD-aware workgroup order.  The dispatcher deals workgroups of a launch to
+// the chip's 8 XCDs round-robin by linear id, and each XCD has its own L2.
+// The logical id returned here makes every XCD walk one contiguous range of
+// the launch (x fastest): workgroups that share input rows (same y) then run
+// on the same XCD and share its L2.  Bijective for any grid size.
+__device__ __forceinline__ void xcd_block(int& bx, int& by) {
+    const int gx = (int)gridDim.x;
+    const int n = gx * (int)gridDim.y;
+    const int h = (int)blockIdx.y * gx + (int)blockIdx.x;
+    const int q = n >> 3, r = n & 7, k = h & 7;
+    const int logical = k * q + min(k, r) + (h >> 3);
+    bx = logical % gx;
+    by = logical / gx;
+}
+
 // Two half-wave sums at once: lanes 0-31 get x0[l] + x0[l + 32], lanes 32-63
 // get x1[l - 32] + x1[l] (the swap exchanges x0's upper half with x1's lower).
 __device__ __forceinline__ float add_halves2(float x0, float x1) {

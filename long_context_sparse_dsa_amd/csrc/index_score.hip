@@ -355,11 +355,13 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, half = lane >> 5;
-    const int64_t p_blk = (int64_t)blockIdx.x * PB;
+    int bx, by;
+    xcd_block(bx, by);
+    const int64_t p_blk = (int64_t)bx * PB;
     const int64_t p_wave = p_blk + wave * PW;
 
     // rows of this workgroup; skip leading rows that see none of its pools
-    int i_begin = blockIdx.y * a.gq;
+    int i_begin = by * a.gq;
     const int i_end = min(a.rows, i_begin + a.gq);
     const int64_t first = 4 * (p_blk + 1) - a.q_pos0 - a.row0;
     if (first > i_begin) i_begin = (int)(first < (int64_t)i_end ? first : (int64_t)i_end);
@@ -612,10 +614,12 @@ __global__ __launch_bounds__(256, 2) void index_score_fp8_kernel(ScoreK8 a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, half = lane >> 5;
-    const int64_t p_blk = (int64_t)blockIdx.x * PB;
+    int bx, by;
+    xcd_block(bx, by);
+    const int64_t p_blk = (int64_t)bx * PB;
     const int64_t p_wave = p_blk + wave * PW;
 
-    int i_begin = blockIdx.y * a.gq;
+    int i_begin = by * a.gq;
     const int i_end = min(a.rows, i_begin + a.gq);
     const int64_t first = 4 * (p_blk + 1) - a.q_pos0 - a.row0;
     if (first > i_begin) i_begin = (int)(first < (int64_t)i_end ? first : (int64_t)i_end);
