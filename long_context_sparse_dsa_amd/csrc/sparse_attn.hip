@@ -15,7 +15,8 @@
 //   online softmax per head (fp32, exp2 domain)
 //   O^T[dv x 16 heads] += V_tile^T . P^T           dv/16 MFMA 16x16x32 bf16
 //     (P^T comes straight from the S^T accumulators; V goes through a
-//      per-wave LDS tile because its token axis is the contraction axis)
+//      per-wave LDS tile because its token axis is the contraction axis, and
+//      comes back transposed by ds_read_b64_tr_b16)
 // The next tile's key/value rows are loaded into registers while the current
 // tile is computed.
 #include <math.h>
@@ -48,7 +49,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
     constexpr int MT = DV / 16;            // O^T row tiles
     constexpr int VCH = DV / 8;            // 16-byte pieces per value row
     constexpr int VPL = 32 * VCH / 64;     // value pieces per lane per tile
-    constexpr int VROW = DV + 4;           // LDS row stride (bf16), 8-byte pad
+    // LDS row stride (bf16): rows stay 16-byte aligned, and 4 consecutive
+    // rows x 32 bytes (one transposed read of a 16-lane group) hit distinct
+    // banks (stride = 8 dwords mod 32)
+    constexpr int VROW = DV + 16;
     __shared__ __attribute__((aligned(16))) uint16_t sv_all[4][32 * VROW];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -128,9 +132,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
 #pragma unroll
         for (int r = 0; r < VPL; ++r) {
             const int piece = lane + 64 * r;
-            uint16_t* dst = sv + (piece / VCH) * VROW + 8 * (piece % VCH);
-            reinterpret_cast<u32x2*>(dst)[0] = u32x2{vc[r][0], vc[r][1]};
-            reinterpret_cast<u32x2*>(dst)[1] = u32x2{vc[r][2], vc[r][3]};
+            *reinterpret_cast<u32x4*>(sv + (piece / VCH) * VROW + 8 * (piece % VCH)) = vc[r];
         }
         const uint32_t valid = valid_c;
 
@@ -197,15 +199,23 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
         }
         const bf16x8 pf = as_bf16x8(pw);
 
-        // V^T fragments from LDS: row = dim 16m + col, same contraction slots
+        // V^T fragments from LDS: row = dim 16m + col, the same contraction
+        // slots.  ds_read_b64_tr_b16: in each 16-lane group, lane r names a
+        // row of 4 bf16 and receives element r % 4 of the rows named by lanes
+        // r/4, r/4 + 4, r/4 + 8, r/4 + 12.  Lane x of group grp names slot
+        // 16u + 4*grp + x/4, dims 16m + 4*(x%4) .. +3, so lane (col, grp)
+        // receives dim 16m + col of slots 16u + 4*grp + 0..3.
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const uint16_t* base = sv + 16 * m + col;
             u32x4 vw;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int s0 = (j >> 1) * 16 + 4 * grp + (j & 1) * 2;
-                vw[j] = (uint32_t)base[s0 * VROW] | ((uint32_t)base[(s0 + 1) * VROW] << 16);
+            for (int u = 0; u < 2; ++u) {
+                const int slot = 16 * u + 4 * grp + (col >> 2);
+                const v4i16 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16*)(sv + slot * VROW + 16 * m + 4 * (col & 3)));
+                const u32x2 w2 = __builtin_bit_cast(u32x2, t4);
+                vw[2 * u] = w2[0];
+                vw[2 * u + 1] = w2[1];
             }
             oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw), pf, oacc[m], 0, 0, 0);
         }
