@@ -32,7 +32,7 @@ struct AttnK {
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* v;
-    const int32_t* idx;
+    const int32_t* __restrict__ idx;
     int64_t s_q, s_k, q_pos0, n_pools;
     int h, k_pools, n_tail;
     float scale_log2;  // softmax scale * log2(e)
@@ -43,6 +43,13 @@ struct AttnK {
 // 16x16x32 bf16 MFMA: lane l supplies A row (l % 16) and B column (l % 16),
 // each with 8 contraction elements of group (l / 16); accumulator element i
 // of lane l is row 4*(l/16) + i, column l % 16.
+// Two fp32 values as packed bf16 (round to nearest even; one instruction).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 template <int D, int DV>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
     constexpr int KS = D / 32;             // QK contraction steps
@@ -55,7 +62,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
     constexpr int VROW = DV + 16;
     __shared__ __attribute__((aligned(16))) uint16_t sv_all[4][32 * VROW];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // wave-uniform: everything derived from the query row stays scalar
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t qi = (int64_t)blockIdx.x * 4 + wave;
     if (qi >= a.s_q) return;  // waves are independent: no workgroup barrier below
     uint16_t* sv = sv_all[wave];
@@ -65,6 +74,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
     const int n_pool_slots = 4 * a.k_pools;
     const int n_slots = n_pool_slots + n_tail_t;
     const int n_tiles = (n_slots + 31) / 32;
+    const int n_full = a.k_pools / 8;      // tiles of 8 whole pools
     const int32_t* irow = a.idx + qi * a.k_pools;
 
     // Q^T fragments: head = col, dims 32*s + 8*grp .. +8
@@ -76,8 +86,56 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
         qf[s] = as_bf16x8(v);
     }
 
-    // token of a slot of tile `tile`; pid holds pool ids of the tile's 8 pools
-    // in lanes 0..7 (and repeats); every lane must call this (shuffle inside).
+    // Tile registers: key rows for the two 16-slot halves (lane (col, grp)
+    // holds slot 16u + col, dims 32s + 8grp .. +8) and value pieces.
+    struct Tile {
+        u32x4 k[2][KS];
+        u32x4 v[VPL];
+        uint32_t valid;   // bit s: slot s holds a real token
+    };
+
+    // A tile of 8 whole pools: the pool ids are wave-uniform scalars.  Ids
+    // outside [0, P) are replaced by pool 0 (a real row, so no load strays)
+    // and their slots are masked out of the softmax.  Value load r moves
+    // piece g = lane + 64r of the tile (slot g / VCH, 16-byte piece g % VCH);
+    // one load spans at most two pools (exactly one when DV = 128, where the
+    // address is then scalar).
+    auto load_full = [&](int tile, Tile& T) {
+        int32_t pid[8];
+        uint32_t valid = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int32_t p = irow[tile * 8 + j];
+            const bool ok = p >= 0 && (int64_t)p < a.n_pools;
+            valid |= ok ? 0xFu << (4 * j) : 0u;
+            pid[j] = ok ? p : 0;
+        }
+        T.valid = valid;
+        // key rows: slot 16u + col lies in pool 4u + col/4, which differs
+        // across the lanes of one load; each lane reads its pool id itself
+        // (the 8 ids share one cache line)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            int32_t p = irow[tile * 8 + 4 * u + (col >> 2)];
+            p = (p >= 0 && (int64_t)p < a.n_pools) ? p : 0;
+            const uint16_t* src = a.k + (4 * (int64_t)p + (col & 3)) * D + 8 * grp;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) T.k[u][s] = ldg16(src + 32 * s);
+        }
+#pragma unroll
+        for (int r = 0; r < VPL; ++r) {
+            constexpr int PPL = 4 * VCH;  // pieces per pool
+            const int g = lane + 64 * r;
+            const int slot = g / VCH;
+            const int p0 = 64 * r / PPL;  // first pool this load touches
+            const int32_t p = (slot >> 2) == p0 ? pid[p0] : pid[p0 + 1 < 8 ? p0 + 1 : p0];
+            T.v[r] = ldg16(a.v + (4 * (int64_t)p + (slot & 3)) * DV + 8 * (g % VCH));
+        }
+    };
+
+    // General tile (a partial last pool tile and/or the unfinished-pool
+    // tail): per-slot tokens; invalid slots load zeros.  Every lane must call
+    // token_of (shuffle inside); pid holds the tile's pool ids in lanes 0..7.
     auto token_of = [&](int slot_in_tile, int tile, int32_t pid) -> int64_t {
         const int slot = tile * 32 + slot_in_tile;
         const int32_t p = __shfl(pid, (slot_in_tile >> 2) & 7);
@@ -92,14 +150,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
         }
         return -1;
     };
-
-    u32x4 kc[2][KS], vc[VPL];
-    uint32_t valid_c = 0;
-    auto load_tile = [&](int tile, u32x4 (&kr)[2][KS], u32x4 (&vr)[VPL], uint32_t& valid) {
+    auto load_general = [&](int tile, Tile& T) {
         const int pi = tile * 8 + (lane & 7);
         const int32_t pid = pi < a.k_pools ? irow[pi] : -1;
         const int64_t vt = token_of(lane & 31, tile, pid);
-        valid = (uint32_t)__ballot(vt >= 0);
+        T.valid = (uint32_t)__ballot(vt >= 0);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int64_t tok = token_of(16 * u + col, tile, pid);
@@ -107,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
             for (int s = 0; s < KS; ++s) {
                 u32x4 v = {0u, 0u, 0u, 0u};
                 if (tok >= 0) v = ldg16(a.k + tok * D + 32 * s + 8 * grp);
-                kr[u][s] = v;
+                T.k[u][s] = v;
             }
         }
 #pragma unroll
@@ -116,8 +171,19 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
             const int64_t tok = token_of(piece / VCH, tile, pid);
             u32x4 v = {0u, 0u, 0u, 0u};
             if (tok >= 0) v = ldg16(a.v + tok * DV + 8 * (piece % VCH));
-            vr[r] = v;
+            T.v[r] = v;
         }
+    };
+    auto stash = [&](const Tile& T) {
+#pragma unroll
+        for (int r = 0; r < VPL; ++r) {
+            const int piece = lane + 64 * r;
+            *reinterpret_cast<u32x4*>(sv + (piece / VCH) * VROW + 8 * (piece % VCH)) = T.v[r];
+        }
+    };
+    auto load_tile = [&](int tile, Tile& T) {
+        if (tile < n_full) load_full(tile, T);
+        else load_general(tile, T);
     };
 
     float m_run = -INFINITY, l_run = 0.0f;
@@ -125,16 +191,16 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) oacc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    if (n_tiles > 0) load_tile(0, kc, vc, valid_c);
+    // One set of tile registers: tile j's values go to LDS and its keys into
+    // the S MFMAs before tile j + 1 is loaded over them, so the next tile's
+    // loads overlap this tile's softmax and PV products.
+    Tile cur;
+    if (n_tiles > 0) load_tile(0, cur);
 
     for (int tile = 0; tile < n_tiles; ++tile) {
         // value tile -> LDS (row-major [slot][dv])
-#pragma unroll
-        for (int r = 0; r < VPL; ++r) {
-            const int piece = lane + 64 * r;
-            *reinterpret_cast<u32x4*>(sv + (piece / VCH) * VROW + 8 * (piece % VCH)) = vc[r];
-        }
-        const uint32_t valid = valid_c;
+        stash(cur);
+        const uint32_t valid = cur.valid;
 
         // S^T for the two 16-slot halves
         f32x4 sacc[2];
@@ -143,14 +209,12 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
             sacc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < KS; ++s)
-                sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[u][s]), qf[s],
+                sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.k[u][s]), qf[s],
                                                                   sacc[u], 0, 0, 0);
         }
 
         // prefetch the next tile while this one is finished
-        u32x4 kn[2][KS], vn[VPL];
-        uint32_t valid_n = 0;
-        if (tile + 1 < n_tiles) load_tile(tile + 1, kn, vn, valid_n);
+        if (tile + 1 < n_tiles) load_tile(tile + 1, cur);
 
         // online softmax; this lane holds slots 16u + 4*grp + i of head col
         float x[2][4];
@@ -165,38 +229,37 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
             }
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
+        // Lazy rescaling: the running maximum moves only when the tile's
+        // maximum exceeds it by more than 2^8, so probabilities stay <= 256
+        // (harmless in fp32 and bf16) and the accumulators are rescaled only
+        // on the rare tiles where some head's maximum jumps.  l and O stay
+        // consistent with the same m_run, so the result is unchanged.
+        const bool jump = mt > m_run + 8.0f;
         float alpha = 1.0f;
-        float p[2][4];
-        if (m_new == -INFINITY) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) p[u][i] = 0.0f;
-        } else {
-            alpha = exp2f(m_run - m_new);
-            float ps = 0.0f;
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[u][i] = exp2f(x[u][i] - m_new);
-                    ps += p[u][i];
-                }
-            l_run = l_run * alpha + ps;
-            m_run = m_new;
+        if (jump) {
+            alpha = __builtin_amdgcn_exp2f(m_run - mt);  // 0 when m_run = -inf
+            m_run = mt;
         }
+        float p[2][4];
+        float ps = 0.0f;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) oacc[m] *= alpha;
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // no valid token seen yet: m_run = -inf, every p is 0
+                p[u][i] = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[u][i] - m_run);
+                ps += p[u][i];
+            }
+        l_run = l_run * alpha + ps;
+        if (__ballot(jump)) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) oacc[m] *= alpha;
+        }
 
         // P^T fragment: contraction slots {4g..4g+3, 16+4g..16+4g+3}
         u32x4 pw;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float lo = p[j >> 1][(j & 1) * 2];
-            const float hi = p[j >> 1][(j & 1) * 2 + 1];
-            pw[j] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-        }
+        for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2(p[j >> 1][(j & 1) * 2], p[j >> 1][(j & 1) * 2 + 1]);
         const bf16x8 pf = as_bf16x8(pw);
 
         // V^T fragments from LDS: row = dim 16m + col, the same contraction
@@ -218,16 +281,6 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
                 vw[2 * u + 1] = w2[1];
             }
             oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw), pf, oacc[m], 0, 0, 0);
-        }
-
-        if (tile + 1 < n_tiles) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int s = 0; s < KS; ++s) kc[u][s] = kn[u][s];
-#pragma unroll
-            for (int r = 0; r < VPL; ++r) vc[r] = vn[r];
-            valid_c = valid_n;
         }
     }
 
