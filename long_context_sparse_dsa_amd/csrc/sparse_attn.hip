@@ -11,14 +11,15 @@
 // head, so every gathered key/value row serves every head.  Tokens are
 // processed in tiles of 32 slots (8 pools).  Per tile:
 //   S^T[32 tokens x 16 heads] = K_tile . Q^T      2 x (d/32) MFMA 16x16x32 bf16
-//     (key rows gathered straight from global memory into the A operand)
+//     (key rows pass through a per-wave LDS tile: an operand load would
+//      touch 16 tokens' half cache lines, a tile load reads whole pools)
 //   online softmax per head (fp32, exp2 domain)
 //   O^T[dv x 16 heads] += V_tile^T . P^T           dv/16 MFMA 16x16x32 bf16
 //     (P^T comes straight from the S^T accumulators; V goes through a
 //      per-wave LDS tile because its token axis is the contraction axis, and
 //      comes back transposed by ds_read_b64_tr_b16)
-// The next tile's key/value rows are loaded into registers while the current
-// tile is computed.
+// The next tile's key/value rows are loaded into registers (whole pools per
+// load) while the current tile is computed.
 #include <math.h>
 
 #include "common.h"
@@ -54,12 +55,17 @@ template <int D, int DV>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
     constexpr int KS = D / 32;             // QK contraction steps
     constexpr int MT = DV / 16;            // O^T row tiles
+    constexpr int KCH = D / 8;             // 16-byte pieces per key row
     constexpr int VCH = DV / 8;            // 16-byte pieces per value row
+    constexpr int KPL = 32 * KCH / 64;     // key pieces per lane per tile
     constexpr int VPL = 32 * VCH / 64;     // value pieces per lane per tile
-    // LDS row stride (bf16): rows stay 16-byte aligned, and 4 consecutive
-    // rows x 32 bytes (one transposed read of a 16-lane group) hit distinct
-    // banks (stride = 8 dwords mod 32)
+    // LDS row strides (bf16).  Keys: D + 8, so the 16-byte operand reads of
+    // 16 consecutive rows fall on distinct banks.  Values: DV + 16, so rows
+    // stay 16-byte aligned and the 4 rows x 32 bytes of one transposed read
+    // of a 16-lane group hit distinct banks (stride = 8 dwords mod 32).
+    constexpr int KROW = D + 8;
     constexpr int VROW = DV + 16;
+    __shared__ __attribute__((aligned(16))) uint16_t sk_all[4][32 * KROW];
     __shared__ __attribute__((aligned(16))) uint16_t sv_all[4][32 * VROW];
 
     const int lane = threadIdx.x & 63;
@@ -67,6 +73,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t qi = (int64_t)blockIdx.x * 4 + wave;
     if (qi >= a.s_q) return;  // waves are independent: no workgroup barrier below
+    uint16_t* sk = sk_all[wave];
     uint16_t* sv = sv_all[wave];
     const int col = lane & 15, grp = lane >> 4;
     const int64_t t = a.q_pos0 + qi;
@@ -86,20 +93,20 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
         qf[s] = as_bf16x8(v);
     }
 
-    // Tile registers: key rows for the two 16-slot halves (lane (col, grp)
-    // holds slot 16u + col, dims 32s + 8grp .. +8) and value pieces.
+    // Tile registers: lane L moves 16-byte piece g = L + 64r of the tile's
+    // key rows (slot g / KCH, piece g % KCH) and of its value rows.  Rows of
+    // one pool are contiguous in memory, so every load reads whole cache
+    // lines of at most two pools.
     struct Tile {
-        u32x4 k[2][KS];
+        u32x4 k[KPL];
         u32x4 v[VPL];
         uint32_t valid;   // bit s: slot s holds a real token
     };
 
     // A tile of 8 whole pools: the pool ids are wave-uniform scalars.  Ids
     // outside [0, P) are replaced by pool 0 (a real row, so no load strays)
-    // and their slots are masked out of the softmax.  Value load r moves
-    // piece g = lane + 64r of the tile (slot g / VCH, 16-byte piece g % VCH);
-    // one load spans at most two pools (exactly one when DV = 128, where the
-    // address is then scalar).
+    // and their slots are masked out of the softmax.  A load touches one
+    // pool when a row has 16 pieces (then its address is scalar), else two.
     auto load_full = [&](int tile, Tile& T) {
         int32_t pid[8];
         uint32_t valid = 0;
@@ -111,25 +118,19 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
             pid[j] = ok ? p : 0;
         }
         T.valid = valid;
-        // key rows: slot 16u + col lies in pool 4u + col/4, which differs
-        // across the lanes of one load; each lane reads its pool id itself
-        // (the 8 ids share one cache line)
+        auto pool_of = [&](int r, int ch, int slot) -> int32_t {
+            const int p0 = 64 * r / (4 * ch);  // first pool load r touches
+            return (slot >> 2) == p0 ? pid[p0] : pid[p0 + 1 < 8 ? p0 + 1 : p0];
+        };
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            int32_t p = irow[tile * 8 + 4 * u + (col >> 2)];
-            p = (p >= 0 && (int64_t)p < a.n_pools) ? p : 0;
-            const uint16_t* src = a.k + (4 * (int64_t)p + (col & 3)) * D + 8 * grp;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) T.k[u][s] = ldg16(src + 32 * s);
+        for (int r = 0; r < KPL; ++r) {
+            const int g = lane + 64 * r, slot = g / KCH;
+            T.k[r] = ldg16(a.k + (4 * (int64_t)pool_of(r, KCH, slot) + (slot & 3)) * D + 8 * (g % KCH));
         }
 #pragma unroll
         for (int r = 0; r < VPL; ++r) {
-            constexpr int PPL = 4 * VCH;  // pieces per pool
-            const int g = lane + 64 * r;
-            const int slot = g / VCH;
-            const int p0 = 64 * r / PPL;  // first pool this load touches
-            const int32_t p = (slot >> 2) == p0 ? pid[p0] : pid[p0 + 1 < 8 ? p0 + 1 : p0];
-            T.v[r] = ldg16(a.v + (4 * (int64_t)p + (slot & 3)) * DV + 8 * (g % VCH));
+            const int g = lane + 64 * r, slot = g / VCH;
+            T.v[r] = ldg16(a.v + (4 * (int64_t)pool_of(r, VCH, slot) + (slot & 3)) * DV + 8 * (g % VCH));
         }
     };
 
@@ -156,34 +157,37 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
         const int64_t vt = token_of(lane & 31, tile, pid);
         T.valid = (uint32_t)__ballot(vt >= 0);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int64_t tok = token_of(16 * u + col, tile, pid);
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (tok >= 0) v = ldg16(a.k + tok * D + 32 * s + 8 * grp);
-                T.k[u][s] = v;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < VPL; ++r) {
-            const int piece = lane + 64 * r;
-            const int64_t tok = token_of(piece / VCH, tile, pid);
+        for (int r = 0; r < KPL; ++r) {
+            const int g = lane + 64 * r;
+            const int64_t tok = token_of(g / KCH, tile, pid);
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (tok >= 0) v = ldg16(a.v + tok * DV + 8 * (piece % VCH));
-            T.v[r] = v;
+            if (tok >= 0) v = ldg16(a.k + tok * D + 8 * (g % KCH));
+            T.k[r] = v;
         }
-    };
-    auto stash = [&](const Tile& T) {
 #pragma unroll
         for (int r = 0; r < VPL; ++r) {
-            const int piece = lane + 64 * r;
-            *reinterpret_cast<u32x4*>(sv + (piece / VCH) * VROW + 8 * (piece % VCH)) = T.v[r];
+            const int g = lane + 64 * r;
+            const int64_t tok = token_of(g / VCH, tile, pid);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (tok >= 0) v = ldg16(a.v + tok * DV + 8 * (g % VCH));
+            T.v[r] = v;
         }
     };
     auto load_tile = [&](int tile, Tile& T) {
         if (tile < n_full) load_full(tile, T);
         else load_general(tile, T);
+    };
+    auto stash = [&](const Tile& T) {
+#pragma unroll
+        for (int r = 0; r < KPL; ++r) {
+            const int g = lane + 64 * r;
+            *reinterpret_cast<u32x4*>(sk + (g / KCH) * KROW + 8 * (g % KCH)) = T.k[r];
+        }
+#pragma unroll
+        for (int r = 0; r < VPL; ++r) {
+            const int g = lane + 64 * r;
+            *reinterpret_cast<u32x4*>(sv + (g / VCH) * VROW + 8 * (g % VCH)) = T.v[r];
+        }
     };
 
     float m_run = -INFINITY, l_run = 0.0f;
@@ -191,30 +195,29 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnK a) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) oacc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // One set of tile registers: tile j's values go to LDS and its keys into
-    // the S MFMAs before tile j + 1 is loaded over them, so the next tile's
-    // loads overlap this tile's softmax and PV products.
+    // One set of tile registers: tile j goes to LDS before tile j + 1 is
+    // loaded over it, so the next tile's loads overlap this tile's MFMAs and
+    // softmax.
     Tile cur;
     if (n_tiles > 0) load_tile(0, cur);
 
     for (int tile = 0; tile < n_tiles; ++tile) {
-        // value tile -> LDS (row-major [slot][dv])
         stash(cur);
         const uint32_t valid = cur.valid;
+        if (tile + 1 < n_tiles) load_tile(tile + 1, cur);
 
-        // S^T for the two 16-slot halves
+        // S^T for the two 16-slot halves; A = key rows from LDS: lane
+        // (col, grp) reads slot 16u + col, dims 32s + 8grp .. +8
         f32x4 sacc[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             sacc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-                sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.k[u][s]), qf[s],
-                                                                  sacc[u], 0, 0, 0);
+            for (int s = 0; s < KS; ++s) {
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + (16 * u + col) * KROW + 32 * s + 8 * grp);
+                sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), qf[s], sacc[u], 0, 0, 0);
+            }
         }
-
-        // prefetch the next tile while this one is finished
-        if (tile + 1 < n_tiles) load_tile(tile + 1, cur);
 
         // online softmax; this lane holds slots 16u + 4*grp + i of head col
         float x[2][4];
