@@ -130,6 +130,23 @@ def make_inputs(wl: Workload, seed: int | None = None, *, attention: bool = True
     return out
 
 
+def make_gates(wl: Workload, seed: int | None = None) -> torch.Tensor:
+    """Per-token k-pool gate scores [S_k] fp32 for gated pooling.
+
+    Drawn U(0, 1) from an eighth sub-stream of the same seed (the first seven
+    are those of ``make_inputs``), then normalised so that the 4 gates of each
+    pool sum to 1: the caller supplies normalised gates.  Keys past the last
+    whole pool get gate 0."""
+    seed = wl.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(8)[7]))
+    u = rng.random(size=(wl.s_k,), dtype=np.float32) + np.float32(1e-3)
+    g = np.zeros_like(u)
+    n = wl.n_pools * 4
+    pools = u[:n].reshape(-1, 4)
+    g[:n] = (pools / pools.sum(axis=1, keepdims=True, dtype=np.float32)).reshape(-1)
+    return torch.from_numpy(g)
+
+
 def sample_rows(s_q: int, n: int, extra=()) -> np.ndarray:
     """Rows for sampled checks: the first and last rows, rows around every
     4-aligned boundary near the ends, a strided sweep, plus ``extra``."""

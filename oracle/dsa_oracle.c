@@ -46,7 +46,13 @@
  *     E4M3 with a power-of-two scale 2^e, e the smallest integer with
  *     max_d |mean code value| <= 448 * 2^e, so that the quantisation is a
  *     round-to-nearest-even of an exactly scaled value and no precision
- *     choice can change a code.
+ *     choice can change a code;
+ *   - gated pooling (section "DSA: Gather by Token Position" names k-pool
+ *     gate scores that weight each key within a pool; no normalisation is
+ *     printed): with a per-token gate array g the pooled key is the plain
+ *     gate-weighted sum kbar_p = sum_r g[4p+r] * k[4p+r], the caller
+ *     supplying normalised gates.  Without gates the mean is used, which is
+ *     the gated sum with every gate equal to 1/4.
  *
  * Everything is accumulated in fp64 in plain loops; no blocking, fusion or
  * reordering beyond the definitions above.
@@ -131,34 +137,40 @@ static float canonical_f32(double s)
     return f == 0.0f ? 0.0f : f;
 }
 
-/* Pooled keys in fp64 from bf16 keys: kbar[p][d] = mean of the pool's rows. */
-static void pool_keys_bf16(const uint16_t *k_idx, int64_t n_pools, int d_idx,
-                           int pool, double *kbar)
+/* Pooled keys in fp64 from bf16 keys: kbar[p][d] = mean of the pool's rows,
+ * or, with gates, sum_r gate[p*pool + r] * k[p*pool + r][d]. */
+static void pool_keys_bf16(const uint16_t *k_idx, const float *gate, int64_t n_pools,
+                           int d_idx, int pool, double *kbar)
 {
     for (int64_t p = 0; p < n_pools; ++p)
         for (int d = 0; d < d_idx; ++d) {
             double sum = 0.0;
-            for (int r = 0; r < pool; ++r)
-                sum += dsa_oracle_bf16_value(k_idx[(p * pool + r) * d_idx + d]);
-            kbar[p * d_idx + d] = sum / pool;
+            for (int r = 0; r < pool; ++r) {
+                double x = dsa_oracle_bf16_value(k_idx[(p * pool + r) * d_idx + d]);
+                sum += gate ? (double)gate[p * pool + r] * x : x;
+            }
+            kbar[p * d_idx + d] = gate ? sum : sum / pool;
         }
 }
 
-/* fp8 pooled keys: mean of the pool's code values, re-quantised per pool to
- * E4M3 with a power-of-two scale.  kbar8 receives the fp64 value of the
- * re-quantised codes times 2^e (the per-tensor k scale is applied by the
- * caller); codes and exponents are returned for inspection when non-NULL. */
-static void pool_keys_fp8(const uint8_t *k8, int64_t n_pools, int d_idx, int pool,
-                          double *kbar8, uint8_t *codes, int32_t *exps)
+/* fp8 pooled keys: mean (or gate-weighted sum) of the pool's code values,
+ * re-quantised per pool to E4M3 with a power-of-two scale.  kbar8 receives
+ * the fp64 value of the re-quantised codes times 2^e (the per-tensor k scale
+ * is applied by the caller); codes and exponents are returned for
+ * inspection when non-NULL. */
+static void pool_keys_fp8(const uint8_t *k8, const float *gate, int64_t n_pools, int d_idx,
+                          int pool, double *kbar8, uint8_t *codes, int32_t *exps)
 {
     double *m = (double *)malloc(sizeof(double) * (size_t)d_idx);
     for (int64_t p = 0; p < n_pools; ++p) {
         double amax = 0.0;
         for (int d = 0; d < d_idx; ++d) {
             double sum = 0.0;
-            for (int r = 0; r < pool; ++r)
-                sum += dsa_oracle_e4m3_value(k8[(p * pool + r) * d_idx + d]);
-            m[d] = sum / pool;
+            for (int r = 0; r < pool; ++r) {
+                double x = dsa_oracle_e4m3_value(k8[(p * pool + r) * d_idx + d]);
+                sum += gate ? (double)gate[p * pool + r] * x : x;
+            }
+            m[d] = gate ? sum : sum / pool;
             if (fabs(m[d]) > amax)
                 amax = fabs(m[d]);
         }
@@ -286,18 +298,20 @@ static int check_index_args(int64_t s_q, int64_t s_k, int64_t q_pos0, int h_idx,
 /* Public entry points (bf16 indexer)                                 */
 /* ------------------------------------------------------------------ */
 
-/* Pooled keys in fp64, [floor(s_k/pool), d_idx]. */
-int dsa_oracle_pool_keys(const uint16_t *k_idx, int64_t s_k, int d_idx, int pool, double *kbar)
+/* Pooled keys in fp64, [floor(s_k/pool), d_idx]; gate [s_k] or NULL (mean). */
+int dsa_oracle_pool_keys(const uint16_t *k_idx, const float *gate, int64_t s_k, int d_idx,
+                         int pool, double *kbar)
 {
     if (s_k < 0 || d_idx <= 0 || pool <= 0 || !kbar)
         return ORACLE_ERR_ARG;
-    pool_keys_bf16(k_idx, s_k / pool, d_idx, pool, kbar);
+    pool_keys_bf16(k_idx, gate, s_k / pool, d_idx, pool, kbar);
     return ORACLE_OK;
 }
 
 /* Dense fp32 scores for the listed rows: out[r][p], p < P; -inf where the
  * pool is not eligible for that row's query. */
-int dsa_oracle_index_scores(const uint16_t *q_idx, const uint16_t *k_idx, const float *w,
+int dsa_oracle_index_scores(const uint16_t *q_idx, const uint16_t *k_idx, const float *gate,
+                            const float *w,
                             int64_t w_stride, int64_t s_q, int64_t s_k, int64_t q_pos0,
                             int h_idx, int d_idx, int pool, const int64_t *rows,
                             int64_t n_rows, float *out)
@@ -308,7 +322,7 @@ int dsa_oracle_index_scores(const uint16_t *q_idx, const uint16_t *k_idx, const 
     double *kbar = (double *)malloc(sizeof(double) * (size_t)(n_pools > 0 ? n_pools : 1) * d_idx);
     if (!kbar)
         return ORACLE_ERR_MEM;
-    pool_keys_bf16(k_idx, n_pools, d_idx, pool, kbar);
+    pool_keys_bf16(k_idx, gate, n_pools, d_idx, pool, kbar);
     int rc = score_and_select(q_idx, NULL, 1.0, kbar, 1.0, w, w_stride, s_q, q_pos0, n_pools,
                               h_idx, d_idx, pool, 1, rows, n_rows, out, NULL, NULL);
     free(kbar);
@@ -318,7 +332,8 @@ int dsa_oracle_index_scores(const uint16_t *q_idx, const uint16_t *k_idx, const 
 /* Top-k pool selection for the listed rows: idx_out[r][0..k) ascending
  * pool ids, -1 padded; sel_scores_out (optional) the matching fp32 scores,
  * -inf for padding. */
-int dsa_oracle_index_topk(const uint16_t *q_idx, const uint16_t *k_idx, const float *w,
+int dsa_oracle_index_topk(const uint16_t *q_idx, const uint16_t *k_idx, const float *gate,
+                          const float *w,
                           int64_t w_stride, int64_t s_q, int64_t s_k, int64_t q_pos0,
                           int h_idx, int d_idx, int pool, int k_pools, const int64_t *rows,
                           int64_t n_rows, int32_t *idx_out, float *sel_scores_out)
@@ -329,7 +344,7 @@ int dsa_oracle_index_topk(const uint16_t *q_idx, const uint16_t *k_idx, const fl
     double *kbar = (double *)malloc(sizeof(double) * (size_t)(n_pools > 0 ? n_pools : 1) * d_idx);
     if (!kbar)
         return ORACLE_ERR_MEM;
-    pool_keys_bf16(k_idx, n_pools, d_idx, pool, kbar);
+    pool_keys_bf16(k_idx, gate, n_pools, d_idx, pool, kbar);
     int rc = score_and_select(q_idx, NULL, 1.0, kbar, 1.0, w, w_stride, s_q, q_pos0, n_pools,
                               h_idx, d_idx, pool, k_pools, rows, n_rows, NULL, idx_out,
                               sel_scores_out);
@@ -342,8 +357,8 @@ int dsa_oracle_index_topk(const uint16_t *q_idx, const uint16_t *k_idx, const fl
 /* ------------------------------------------------------------------ */
 
 /* Re-quantised pooled keys: codes [P, d_idx] and per-pool exponents [P]. */
-int dsa_oracle_pool_keys_fp8(const uint8_t *k8, int64_t s_k, int d_idx, int pool,
-                             uint8_t *codes, int32_t *exps)
+int dsa_oracle_pool_keys_fp8(const uint8_t *k8, const float *gate, int64_t s_k, int d_idx,
+                             int pool, uint8_t *codes, int32_t *exps)
 {
     if (s_k < 0 || d_idx <= 0 || pool <= 0 || !codes || !exps)
         return ORACLE_ERR_ARG;
@@ -351,13 +366,14 @@ int dsa_oracle_pool_keys_fp8(const uint8_t *k8, int64_t s_k, int d_idx, int pool
     double *kbar8 = (double *)malloc(sizeof(double) * (size_t)(n_pools > 0 ? n_pools : 1) * d_idx);
     if (!kbar8)
         return ORACLE_ERR_MEM;
-    pool_keys_fp8(k8, n_pools, d_idx, pool, kbar8, codes, exps);
+    pool_keys_fp8(k8, gate, n_pools, d_idx, pool, kbar8, codes, exps);
     free(kbar8);
     return ORACLE_OK;
 }
 
 /* fp8 scores: s = sum_h w * relu(q_scale * k_scale * q8 . (2^e_p * kbar8_p)). */
-int dsa_oracle_index_scores_fp8(const uint8_t *q8, const uint8_t *k8, float q_scale,
+int dsa_oracle_index_scores_fp8(const uint8_t *q8, const uint8_t *k8, const float *gate,
+                                float q_scale,
                                 float k_scale, const float *w, int64_t w_stride, int64_t s_q,
                                 int64_t s_k, int64_t q_pos0, int h_idx, int d_idx, int pool,
                                 const int64_t *rows, int64_t n_rows, float *out)
@@ -368,7 +384,7 @@ int dsa_oracle_index_scores_fp8(const uint8_t *q8, const uint8_t *k8, float q_sc
     double *kbar8 = (double *)malloc(sizeof(double) * (size_t)(n_pools > 0 ? n_pools : 1) * d_idx);
     if (!kbar8)
         return ORACLE_ERR_MEM;
-    pool_keys_fp8(k8, n_pools, d_idx, pool, kbar8, NULL, NULL);
+    pool_keys_fp8(k8, gate, n_pools, d_idx, pool, kbar8, NULL, NULL);
     int rc = score_and_select(NULL, q8, (double)q_scale, kbar8, (double)k_scale, w, w_stride, s_q,
                               q_pos0, n_pools, h_idx, d_idx, pool, 1, rows, n_rows, out, NULL,
                               NULL);
@@ -376,7 +392,8 @@ int dsa_oracle_index_scores_fp8(const uint8_t *q8, const uint8_t *k8, float q_sc
     return rc;
 }
 
-int dsa_oracle_index_topk_fp8(const uint8_t *q8, const uint8_t *k8, float q_scale, float k_scale,
+int dsa_oracle_index_topk_fp8(const uint8_t *q8, const uint8_t *k8, const float *gate,
+                              float q_scale, float k_scale,
                               const float *w, int64_t w_stride, int64_t s_q, int64_t s_k,
                               int64_t q_pos0, int h_idx, int d_idx, int pool, int k_pools,
                               const int64_t *rows, int64_t n_rows, int32_t *idx_out,
@@ -388,7 +405,7 @@ int dsa_oracle_index_topk_fp8(const uint8_t *q8, const uint8_t *k8, float q_scal
     double *kbar8 = (double *)malloc(sizeof(double) * (size_t)(n_pools > 0 ? n_pools : 1) * d_idx);
     if (!kbar8)
         return ORACLE_ERR_MEM;
-    pool_keys_fp8(k8, n_pools, d_idx, pool, kbar8, NULL, NULL);
+    pool_keys_fp8(k8, gate, n_pools, d_idx, pool, kbar8, NULL, NULL);
     int rc = score_and_select(NULL, q8, (double)q_scale, kbar8, (double)k_scale, w, w_stride, s_q,
                               q_pos0, n_pools, h_idx, d_idx, pool, k_pools, rows, n_rows, NULL,
                               idx_out, sel_scores_out);

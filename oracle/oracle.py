@@ -59,23 +59,23 @@ def _load():
         lib.dsa_oracle_e4m3_encode.restype = ctypes.c_uint8
         lib.dsa_oracle_e4m3_encode.argtypes = [ctypes.c_double]
         lib.dsa_oracle_pool_keys.restype = _int
-        lib.dsa_oracle_pool_keys.argtypes = [_ptr, _i64, _int, _int, _ptr]
+        lib.dsa_oracle_pool_keys.argtypes = [_ptr, _ptr, _i64, _int, _int, _ptr]
         lib.dsa_oracle_pool_keys_fp8.restype = _int
-        lib.dsa_oracle_pool_keys_fp8.argtypes = [_ptr, _i64, _int, _int, _ptr, _ptr]
+        lib.dsa_oracle_pool_keys_fp8.argtypes = [_ptr, _ptr, _i64, _int, _int, _ptr, _ptr]
         lib.dsa_oracle_index_scores.restype = _int
         lib.dsa_oracle_index_scores.argtypes = [
-            _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _int, _int, _int, _ptr, _i64, _ptr]
+            _ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _int, _int, _int, _ptr, _i64, _ptr]
         lib.dsa_oracle_index_topk.restype = _int
         lib.dsa_oracle_index_topk.argtypes = [
-            _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _ptr, _i64,
+            _ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _ptr, _i64,
             _ptr, _ptr]
         lib.dsa_oracle_index_scores_fp8.restype = _int
         lib.dsa_oracle_index_scores_fp8.argtypes = [
-            _ptr, _ptr, ctypes.c_float, ctypes.c_float, _ptr, _i64, _i64, _i64, _i64, _int,
+            _ptr, _ptr, _ptr, ctypes.c_float, ctypes.c_float, _ptr, _i64, _i64, _i64, _i64, _int,
             _int, _int, _ptr, _i64, _ptr]
         lib.dsa_oracle_index_topk_fp8.restype = _int
         lib.dsa_oracle_index_topk_fp8.argtypes = [
-            _ptr, _ptr, ctypes.c_float, ctypes.c_float, _ptr, _i64, _i64, _i64, _i64, _int,
+            _ptr, _ptr, _ptr, ctypes.c_float, ctypes.c_float, _ptr, _i64, _i64, _i64, _i64, _int,
             _int, _int, _int, _ptr, _i64, _ptr, _ptr]
         lib.dsa_oracle_sparse_attn.restype = _int
         lib.dsa_oracle_sparse_attn.argtypes = [
@@ -156,27 +156,46 @@ def e4m3_encode(x: float) -> int:
 
 # ---------------------------------------------------------------- indexer
 
-def pool_keys(k_idx, pool: int = 4) -> np.ndarray:
-    """fp64 pooled keys [floor(S_k/pool), D_I] from bf16 keys [S_k, D_I]."""
+def _gate(gate, s_k):
+    """Per-token gates as contiguous fp32 [s_k], or None (mean pooling)."""
+    if gate is None:
+        return None
+    g = np.ascontiguousarray(_f32(gate)).reshape(-1)
+    if g.shape[0] != s_k:
+        raise ValueError(f"gate has {g.shape[0]} entries for {s_k} keys")
+    return g
+
+
+def _pg(g):
+    return None if g is None else _p(g)
+
+
+def pool_keys(k_idx, pool: int = 4, gate=None) -> np.ndarray:
+    """fp64 pooled keys [floor(S_k/pool), D_I] from bf16 keys [S_k, D_I]: the
+    mean of each pool's rows, or with per-token gates [S_k] their gate-weighted
+    sum."""
     kb = _bits16(k_idx)
     s_k, d = kb.shape
+    g = _gate(gate, s_k)
     out = np.zeros((s_k // pool, d), dtype=np.float64)
-    _check(_load().dsa_oracle_pool_keys(_p(kb), s_k, d, pool, _p(out)), "pool_keys")
+    _check(_load().dsa_oracle_pool_keys(_p(kb), _pg(g), s_k, d, pool, _p(out)), "pool_keys")
     return out
 
 
-def pool_keys_fp8(k8, pool: int = 4):
+def pool_keys_fp8(k8, pool: int = 4, gate=None):
     """Re-quantised fp8 pooled keys: (codes [P, D_I] uint8, exponents [P] int32)."""
     kc = _codes8(k8)
     s_k, d = kc.shape
+    g = _gate(gate, s_k)
     codes = np.zeros((s_k // pool, d), dtype=np.uint8)
     exps = np.zeros((s_k // pool,), dtype=np.int32)
-    _check(_load().dsa_oracle_pool_keys_fp8(_p(kc), s_k, d, pool, _p(codes), _p(exps)),
+    _check(_load().dsa_oracle_pool_keys_fp8(_p(kc), _pg(g), s_k, d, pool, _p(codes), _p(exps)),
            "pool_keys_fp8")
     return codes, exps
 
 
-def index_scores(q_idx, k_idx, w, q_pos0: int = 0, rows=None, pool: int = 4) -> np.ndarray:
+def index_scores(q_idx, k_idx, w, q_pos0: int = 0, rows=None, pool: int = 4,
+                 gate=None) -> np.ndarray:
     """fp32 scores [len(rows), P] (-inf where a pool is not eligible).
 
     q_idx [S_q, H_I, D_I] bf16, k_idx [S_k, D_I] bf16, w [H_I] or [S_q, H_I]."""
@@ -185,53 +204,58 @@ def index_scores(q_idx, k_idx, w, q_pos0: int = 0, rows=None, pool: int = 4) -> 
     s_k = kb.shape[0]
     w32, ws = _w_args(w, h_idx)
     r = _rows(rows, s_q)
+    g = _gate(gate, s_k)
     out = np.zeros((len(r), s_k // pool), dtype=np.float32)
     _check(_load().dsa_oracle_index_scores(
-        _p(qb), _p(kb), _p(w32), ws, s_q, s_k, q_pos0, h_idx, d_idx, pool, _p(r), len(r),
+        _p(qb), _p(kb), _pg(g), _p(w32), ws, s_q, s_k, q_pos0, h_idx, d_idx, pool, _p(r), len(r),
         _p(out)), "index_scores")
     return out
 
 
-def index_topk(q_idx, k_idx, w, k_pools: int, q_pos0: int = 0, rows=None, pool: int = 4):
+def index_topk(q_idx, k_idx, w, k_pools: int, q_pos0: int = 0, rows=None, pool: int = 4,
+               gate=None):
     """(idx int32 [len(rows), k_pools], selected fp32 scores [len(rows), k_pools])."""
     qb, kb = _bits16(q_idx), _bits16(k_idx)
     s_q, h_idx, d_idx = qb.shape
     s_k = kb.shape[0]
     w32, ws = _w_args(w, h_idx)
     r = _rows(rows, s_q)
+    g = _gate(gate, s_k)
     idx = np.zeros((len(r), k_pools), dtype=np.int32)
     sc = np.zeros((len(r), k_pools), dtype=np.float32)
     _check(_load().dsa_oracle_index_topk(
-        _p(qb), _p(kb), _p(w32), ws, s_q, s_k, q_pos0, h_idx, d_idx, pool, k_pools, _p(r),
+        _p(qb), _p(kb), _pg(g), _p(w32), ws, s_q, s_k, q_pos0, h_idx, d_idx, pool, k_pools, _p(r),
         len(r), _p(idx), _p(sc)), "index_topk")
     return idx, sc
 
 
 def index_scores_fp8(q8, k8, w, q_scale: float = 1.0, k_scale: float = 1.0, q_pos0: int = 0,
-                     rows=None, pool: int = 4) -> np.ndarray:
+                     rows=None, pool: int = 4, gate=None) -> np.ndarray:
     qc, kc = _codes8(q8), _codes8(k8)
     s_q, h_idx, d_idx = qc.shape
     s_k = kc.shape[0]
     w32, ws = _w_args(w, h_idx)
     r = _rows(rows, s_q)
+    g = _gate(gate, s_k)
     out = np.zeros((len(r), s_k // pool), dtype=np.float32)
     _check(_load().dsa_oracle_index_scores_fp8(
-        _p(qc), _p(kc), q_scale, k_scale, _p(w32), ws, s_q, s_k, q_pos0, h_idx, d_idx, pool,
+        _p(qc), _p(kc), _pg(g), q_scale, k_scale, _p(w32), ws, s_q, s_k, q_pos0, h_idx, d_idx, pool,
         _p(r), len(r), _p(out)), "index_scores_fp8")
     return out
 
 
 def index_topk_fp8(q8, k8, w, k_pools: int, q_scale: float = 1.0, k_scale: float = 1.0,
-                   q_pos0: int = 0, rows=None, pool: int = 4):
+                   q_pos0: int = 0, rows=None, pool: int = 4, gate=None):
     qc, kc = _codes8(q8), _codes8(k8)
     s_q, h_idx, d_idx = qc.shape
     s_k = kc.shape[0]
     w32, ws = _w_args(w, h_idx)
     r = _rows(rows, s_q)
+    g = _gate(gate, s_k)
     idx = np.zeros((len(r), k_pools), dtype=np.int32)
     sc = np.zeros((len(r), k_pools), dtype=np.float32)
     _check(_load().dsa_oracle_index_topk_fp8(
-        _p(qc), _p(kc), q_scale, k_scale, _p(w32), ws, s_q, s_k, q_pos0, h_idx, d_idx, pool,
+        _p(qc), _p(kc), _pg(g), q_scale, k_scale, _p(w32), ws, s_q, s_k, q_pos0, h_idx, d_idx, pool,
         k_pools, _p(r), len(r), _p(idx), _p(sc)), "index_topk_fp8")
     return idx, sc
 

@@ -5,7 +5,8 @@ that a slip in the oracle (an index, a sign, a dropped term, a transposed
 operand) shows up as a mismatch:
 
 * scores through the raw tokens, using the linearity of the pooled dot
-  product (q . mean_r k_r = mean_r q . k_r) rather than a pooled key table;
+  product (q . mean_r k_r = mean_r q . k_r, and likewise for a gate-weighted
+  sum) rather than a pooled key table;
 * selection by counting ranks (p is kept iff fewer than k pools beat it,
   where beating means a larger fp32 score or an equal one at a lower id),
   not by sorting;
@@ -22,10 +23,13 @@ def bf16_to_f64(x: torch.Tensor) -> np.ndarray:
     return x.to(torch.float64).numpy()
 
 
-def raw_token_scores(q_idx, k_idx, w, q_pos0=0, rows=None, pool=4) -> np.ndarray:
-    """fp32 scores [len(rows), P] via raw tokens; -inf for ineligible pools."""
+def raw_token_scores(q_idx, k_idx, w, q_pos0=0, rows=None, pool=4, gate=None) -> np.ndarray:
+    """fp32 scores [len(rows), P] via raw tokens; -inf for ineligible pools.
+    With per-token gates [S_k] the pooled dot is sum_r g_r (q . k_r) instead of
+    the mean."""
     q = bf16_to_f64(q_idx)              # [S_q, H, D]
     k = bf16_to_f64(k_idx)              # [S_k, D]
+    gv = None if gate is None else np.asarray(gate, dtype=np.float32).astype(np.float64)
     wv = w.to(torch.float64).numpy()
     s_q = q.shape[0]
     n_pools = k.shape[0] // pool
@@ -38,7 +42,10 @@ def raw_token_scores(q_idx, k_idx, w, q_pos0=0, rows=None, pool=4) -> np.ndarray
             continue
         toks = k[: n * pool]                       # [n*pool, D]
         per_tok = q[i] @ toks.T                    # [H, n*pool]
-        pooled = per_tok.reshape(q.shape[1], n, pool).mean(axis=2)   # [H, n]
+        if gv is None:
+            pooled = per_tok.reshape(q.shape[1], n, pool).mean(axis=2)   # [H, n]
+        else:
+            pooled = (per_tok * gv[None, : n * pool]).reshape(q.shape[1], n, pool).sum(axis=2)
         wr = wv if wv.ndim == 1 else wv[i]
         s = (wr[:, None] * np.maximum(pooled, 0.0)).sum(axis=0)
         s32 = s.astype(np.float32)

@@ -372,6 +372,92 @@ def test_fp8_scores_close_to_exact_scores():
     assert err.max() < 0.06
 
 
+# ---------------------------------------------------------------- gated pooling
+# section "DSA: Gather by Token Position": k-pool gate scores weight each key
+# within a pool.  Reading: kbar_p = sum_r g[4p+r] k[4p+r] with caller-normalised
+# gates; no gates means the mean.
+
+def test_gated_pooling_with_quarter_gates_is_the_mean():
+    wl = inputs.custom(s_q=96, s_k=96, h_idx=8, d_idx=64, k_pools=4, fp8=True)
+    x = inputs.make_inputs(wl, seed=31, attention=False)
+    g = np.full(wl.s_k, 0.25, dtype=np.float32)
+    assert np.array_equal(oracle.pool_keys(x["k_idx"], gate=g), oracle.pool_keys(x["k_idx"]))
+    c0, e0 = oracle.pool_keys_fp8(x["k_idx8"])
+    c1, e1 = oracle.pool_keys_fp8(x["k_idx8"], gate=g)
+    assert np.array_equal(c0, c1) and np.array_equal(e0, e1)
+    i0, s0 = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], 4)
+    i1, s1 = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], 4, gate=g)
+    assert np.array_equal(i0, i1) and np.array_equal(s0, s1)
+
+
+def test_gated_pooling_hand_example():
+    # pool 0 rows of HAND_K with gates [0.5, 0.25, 0.125, 0.125]
+    k = bf(HAND_K)
+    g = np.array([0.5, 0.25, 0.125, 0.125] + [0.25] * 8, dtype=np.float32)
+    kb = oracle.pool_keys(k, gate=g)
+    rows = np.array(HAND_K[:4], dtype=np.float64)
+    assert np.array_equal(kb[0], (g[:4, None] * rows).sum(axis=0))
+    assert np.array_equal(kb[1:], oracle.pool_keys(k)[1:])
+
+
+def test_gated_pooling_one_hot_gates_pick_a_token():
+    wl = inputs.custom(s_q=64, s_k=64, h_idx=4, d_idx=64, k_pools=2, fp8=True)
+    x = inputs.make_inputs(wl, seed=33, attention=False)
+    for r0 in range(4):
+        g = np.zeros(wl.s_k, dtype=np.float32)
+        g[r0::4] = 1.0
+        kb = oracle.pool_keys(x["k_idx"], gate=g)
+        assert np.array_equal(kb, x["k_idx"][r0::4].to(torch.float64).numpy())
+        # fp8: the pooled value is the token's own code value; re-quantising
+        # it with a power-of-two scale reproduces it exactly
+        codes, exps = oracle.pool_keys_fp8(x["k_idx8"], gate=g)
+        vals = np.array([[oracle.e4m3_value(int(c)) for c in row] for row in codes])
+        got = vals * np.exp2(exps.astype(np.float64))[:, None]
+        assert np.array_equal(got, x["k_idx8"][r0::4].to(torch.float64).numpy())
+
+
+@pytest.mark.parametrize("s,h_idx,d_idx,k_pools,q_pos0", [(64, 4, 64, 4, 0), (301, 8, 96, 8, 40)])
+def test_gated_scores_and_selection_match_brute_force(s, h_idx, d_idx, k_pools, q_pos0):
+    wl = inputs.custom(s_q=s - q_pos0, s_k=s, q_pos0=q_pos0, h_idx=h_idx, d_idx=d_idx,
+                       k_pools=k_pools, idx_std=0.125)
+    x = inputs.make_inputs(wl, seed=41 + s, attention=False, w_per_query=True)
+    g = inputs.make_gates(wl, seed=41 + s)
+    got = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=q_pos0, gate=g)
+    ref = brute.raw_token_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=q_pos0, gate=g)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(got))
+    assert np.all(np.abs(got[fin] - ref[fin]) <= np.spacing(np.abs(ref[fin])) + 1e-30)
+    # the gates matter: mean pooling gives different scores
+    mean = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=q_pos0)
+    assert not np.array_equal(mean[fin], got[fin])
+    idx, _ = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], k_pools, q_pos0=q_pos0, gate=g)
+    for r in range(wl.s_q):
+        n = min((q_pos0 + r) // 4, wl.n_pools)
+        assert np.array_equal(idx[r], brute.rank_select(got[r], n, k_pools)), r
+
+
+def test_gated_scores_scale_with_the_gates():
+    wl = inputs.custom(s_q=128, s_k=128, h_idx=8, d_idx=64, k_pools=4, fp8=True)
+    x = inputs.make_inputs(wl, seed=43, attention=False)
+    g = inputs.make_gates(wl, seed=43)
+    rows = [60, 127]
+    s1 = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], rows=rows, gate=g)
+    s2 = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], rows=rows, gate=2 * g.numpy())
+    assert np.array_equal(np.where(np.isfinite(s1), 2 * s1, s1), s2)
+    # fp8: doubling the gates doubles the pooled values; the power-of-two
+    # re-quantisation keeps the codes and moves the exponent by one
+    c1, e1 = oracle.pool_keys_fp8(x["k_idx8"], gate=g)
+    c2, e2 = oracle.pool_keys_fp8(x["k_idx8"], gate=2 * g.numpy())
+    assert np.array_equal(c1, c2) and np.array_equal(e2, e1 + 1)
+
+
+def test_gates_are_normalised_per_pool():
+    wl = inputs.custom(s_q=40, s_k=42, h_idx=4, d_idx=64, k_pools=2)
+    g = inputs.make_gates(wl, seed=5).numpy()
+    sums = g[:40].reshape(-1, 4).sum(axis=1, dtype=np.float64)
+    assert np.all(np.abs(sums - 1.0) < 1e-6) and np.all(g[:40] > 0) and np.all(g[40:] == 0)
+
+
 # ---------------------------------------------------------------- memory model
 
 def test_unchunked_indexer_memory_matches_the_page():
