@@ -100,7 +100,7 @@ def work_counts(wl):
                 b_select=b_select, b_pool=b_pool)
 
 
-def cpu_baseline(wl, x, target_s: float):
+def cpu_baseline(wl, x, target_s: float, gate=None):
     """The oracle as it stands, on a strided sample of query rows."""
     from oracle import oracle
     threads = os.cpu_count() or 1
@@ -108,7 +108,7 @@ def cpu_baseline(wl, x, target_s: float):
     def run(rows):
         t0 = time.perf_counter()
         idx, _ = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], wl.k_pools, q_pos0=wl.q_pos0,
-                                   rows=rows)
+                                   rows=rows, gate=gate)
         oracle.sparse_attn(x["q"], x["k"], x["v"], idx, wl.k_pools, q_pos0=wl.q_pos0, rows=rows,
                            n_tail=wl.n_tail, scale=float(np.float32(1 / math.sqrt(wl.d))))
         return time.perf_counter() - t0
@@ -140,6 +140,8 @@ def main():
     ap.add_argument("--chunk-q", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gated", action="store_true",
+                    help="gated pooling: per-token k-pool gates weight each key of a pool")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -163,6 +165,7 @@ def main():
     x = inputs.make_inputs(wl)
     log(f"inputs generated in {time.time() - t0:.1f} s")
     g = {k: v.to(dev) for k, v in x.items() if not k.endswith("8")}
+    gate = inputs.make_gates(wl).to(dev) if args.gated else None
     ws_bytes, chunk_q = dsa.dsa_index_workspace_size(wl.s_q, wl.s_k, wl.h_idx, wl.d_idx,
                                                      wl.k_pools, 4, args.chunk_q)
     ws = dsa.new_workspace(ws_bytes, dev)
@@ -171,8 +174,14 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        dsa.dsa_index_score_topk(g["q_idx"], g["k_idx"], g["w"], wl.k_pools, q_pos0=wl.q_pos0,
-                                 chunk_q=chunk_q, idx_out=idx, workspace=ws, stream=stream)
+        if gate is None:
+            dsa.dsa_index_score_topk(g["q_idx"], g["k_idx"], g["w"], wl.k_pools,
+                                     q_pos0=wl.q_pos0, chunk_q=chunk_q, idx_out=idx,
+                                     workspace=ws, stream=stream)
+        else:
+            dsa.dsa_index_score_topk_gated(g["q_idx"], g["k_idx"], gate, g["w"], wl.k_pools,
+                                           q_pos0=wl.q_pos0, chunk_q=chunk_q, idx_out=idx,
+                                           workspace=ws, stream=stream)
         dsa.dsa_sparse_attn_fwd(g["q"], g["k"], g["v"], idx, q_pos0=wl.q_pos0,
                                 n_tail=wl.n_tail, out=out, stream=stream)
 
@@ -232,7 +241,7 @@ def main():
         "config": {"workload": wl.name, "s_q": wl.s_q, "s_k": wl.s_k, "q_pos0": wl.q_pos0,
                    "indexer": f"{wl.h_idx}x{wl.d_idx}", "pool": 4, "k_pools": wl.k_pools,
                    "attention": f"{wl.h}x{wl.d}", "kv_heads": 1, "n_tail": wl.n_tail,
-                   "chunk_q": chunk_q},
+                   "chunk_q": chunk_q, "pooling": "gated" if args.gated else "mean"},
         "tflops": tflops, "tflops_frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "roofline": dict(rl[dominant], kernel=dominant) if dominant in rl else None,
         "stages": stages,
@@ -242,7 +251,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds,
+                                              None if gate is None else gate.cpu().numpy())
     print(json.dumps(result), flush=True)
 
 

@@ -116,6 +116,27 @@ dsa_status dsa_index_score_topk(const void *q_idx, const void *k_idx, const floa
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * dsa_index_score_topk with gated pooling (section "DSA: Gather by Token
+ * Position": per-token k-pool gate scores weight each key within its pool).
+ * The pooled key is the gate-weighted sum
+ *     kbar_p = sum_{r<4} k_gate[4p + r] * k_idx[4p + r]
+ * instead of the mean; the caller supplies normalised gates (gates of 1/4
+ * give the mean).
+ *   k_gate   [s_k] fp32, device memory, 16-byte aligned; must be non-NULL
+ *            when s_k >= 4 (entries past the last whole pool are not read)
+ * Every other argument, the workspace size and the error behaviour are those
+ * of dsa_index_score_topk.  With the fp8 indexer the gated sum of the code
+ * values is formed in fp64 before the per-pool requantisation.
+ */
+dsa_status dsa_index_score_topk_gated(const void *q_idx, const void *k_idx, const float *k_gate,
+                                      const float *q_scale, const float *k_scale, const float *w,
+                                      int64_t w_stride_q, int64_t s_q, int64_t s_k,
+                                      int64_t q_pos0, int h_idx, int d_idx, int pool_size,
+                                      int k_pools, int64_t chunk_q, int dtype, int32_t *idx_out,
+                                      float *score_out, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
+/*
  * Bytes of device workspace dsa_index_scores needs for n_rows query rows:
  * the pooled key table plus, for the bf16 indexer, packed query tiles for up
  * to 4096 rows (the rows are scored 4096 at a time).  Pure host computation.
@@ -136,6 +157,17 @@ dsa_status dsa_index_scores(const void *q_idx, const void *k_idx, const float *q
                             int pool_size, int dtype, int64_t row0, int64_t n_rows,
                             float *scores_out, void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/*
+ * dsa_index_scores with gated pooled keys, as in dsa_index_score_topk_gated
+ * (k_gate [s_k] fp32, non-NULL when s_k >= 4).  Same workspace size.
+ */
+dsa_status dsa_index_scores_gated(const void *q_idx, const void *k_idx, const float *k_gate,
+                                  const float *q_scale, const float *k_scale, const float *w,
+                                  int64_t w_stride_q, int64_t s_q, int64_t s_k, int64_t q_pos0,
+                                  int h_idx, int d_idx, int pool_size, int dtype, int64_t row0,
+                                  int64_t n_rows, float *scores_out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /*
  * Sparse attention forward over the kept pools (sections "DeepSeek Sparse

@@ -203,17 +203,22 @@ dsa_status check_index_ptrs(const void* q_idx, const void* k_idx, const float* q
     return DSA_OK;
 }
 
-hipError_t launch_pool(const IndexShape& sh, const Layout& L, const void* k_idx, void* ws,
-                       hipStream_t s) {
+dsa_status check_gate(const float* k_gate) {
+    if (!aligned16(k_gate)) return fail(DSA_ERR_INVALID_ARG, "k_gate must be 16-byte aligned");
+    return DSA_OK;
+}
+
+hipError_t launch_pool(const IndexShape& sh, const Layout& L, const void* k_idx,
+                       const float* k_gate, void* ws, hipStream_t s) {
     Timed tm(K_POOL, s);
     char* w = static_cast<char*>(ws);
     if (sh.dtype == DSA_BF16)
-        return dsa::launch_pool_keys_bf16(static_cast<const uint16_t*>(k_idx), sh.n_pools,
+        return dsa::launch_pool_keys_bf16(static_cast<const uint16_t*>(k_idx), k_gate, sh.n_pools,
                                           sh.d_idx, reinterpret_cast<uint16_t*>(w + L.hi),
                                           reinterpret_cast<uint8_t*>(w + L.lo),
                                           reinterpret_cast<uint8_t*>(w + L.lo_scale), s);
-    return dsa::launch_pool_keys_fp8(static_cast<const uint8_t*>(k_idx), sh.n_pools, sh.d_idx,
-                                     reinterpret_cast<uint8_t*>(w + L.hi),
+    return dsa::launch_pool_keys_fp8(static_cast<const uint8_t*>(k_idx), k_gate, sh.n_pools,
+                                     sh.d_idx, reinterpret_cast<uint8_t*>(w + L.hi),
                                      reinterpret_cast<float*>(w + L.lo_scale), s);
 }
 
@@ -290,18 +295,20 @@ dsa_status dsa_index_scores_workspace_size(int64_t s_q, int64_t s_k, int h_idx, 
     return DSA_OK;
 }
 
-dsa_status dsa_index_score_topk(const void* q_idx, const void* k_idx, const float* q_scale,
-                                const float* k_scale, const float* w, int64_t w_stride_q,
-                                int64_t s_q, int64_t s_k, int64_t q_pos0, int h_idx, int d_idx,
-                                int pool_size, int k_pools, int64_t chunk_q, int dtype,
-                                int32_t* idx_out, float* score_out, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+static dsa_status index_score_topk(const void* q_idx, const void* k_idx, const float* k_gate,
+                                   const float* q_scale, const float* k_scale, const float* w,
+                                   int64_t w_stride_q, int64_t s_q, int64_t s_k, int64_t q_pos0,
+                                   int h_idx, int d_idx, int pool_size, int k_pools,
+                                   int64_t chunk_q, int dtype, int32_t* idx_out,
+                                   float* score_out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
     g_err[0] = 0;
     IndexShape sh{s_q, s_k, q_pos0, h_idx, d_idx, pool_size, k_pools, dtype, s_k / 4};
     dsa_status st = check_index_shape(sh, true);
     if (st != DSA_OK) return st;
     if ((st = check_index_ptrs(q_idx, k_idx, q_scale, k_scale, w, w_stride_q, sh)) != DSA_OK)
         return st;
+    if ((st = check_gate(k_gate)) != DSA_OK) return st;
     if (s_q > 0 && !idx_out) return fail(DSA_ERR_INVALID_ARG, "idx_out must be non-null");
     if (!aligned16(idx_out) || !aligned16(score_out))
         return fail(DSA_ERR_INVALID_ARG, "idx_out and score_out must be 16-byte aligned");
@@ -322,7 +329,7 @@ dsa_status dsa_index_score_topk(const void* q_idx, const void* k_idx, const floa
     const int64_t ld = score_ld(sh);
     hipError_t e;
     if (sh.n_pools > 0) {
-        e = launch_pool(sh, L, k_idx, ws, s);
+        e = launch_pool(sh, L, k_idx, k_gate, ws, s);
         if (e != hipSuccess) return hip_fail(e, "pool_keys launch");
     }
     for (int64_t c0 = 0; c0 < s_q; c0 += cq) {
@@ -360,18 +367,19 @@ dsa_status dsa_index_score_topk(const void* q_idx, const void* k_idx, const floa
     return DSA_OK;
 }
 
-dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const float* q_scale,
-                            const float* k_scale, const float* w, int64_t w_stride_q,
-                            int64_t s_q, int64_t s_k, int64_t q_pos0, int h_idx, int d_idx,
-                            int pool_size, int dtype, int64_t row0, int64_t n_rows,
-                            float* scores_out, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+static dsa_status index_scores(const void* q_idx, const void* k_idx, const float* k_gate,
+                               const float* q_scale, const float* k_scale, const float* w,
+                               int64_t w_stride_q, int64_t s_q, int64_t s_k, int64_t q_pos0,
+                               int h_idx, int d_idx, int pool_size, int dtype, int64_t row0,
+                               int64_t n_rows, float* scores_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     IndexShape sh{s_q, s_k, q_pos0, h_idx, d_idx, pool_size, 1, dtype, s_k / 4};
     dsa_status st = check_index_shape(sh, false);
     if (st != DSA_OK) return st;
     if ((st = check_index_ptrs(q_idx, k_idx, q_scale, k_scale, w, w_stride_q, sh)) != DSA_OK)
         return st;
+    if ((st = check_gate(k_gate)) != DSA_OK) return st;
     if (row0 < 0 || n_rows < 0 || row0 + n_rows > s_q)
         return fail(DSA_ERR_INVALID_ARG, "rows [%lld, %lld) outside [0, %lld)", (long long)row0,
                     (long long)(row0 + n_rows), (long long)s_q);
@@ -389,7 +397,7 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const float* q
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = dsa::launch_fill_f32(scores_out, n_rows * sh.n_pools, -INFINITY, s);
     if (e != hipSuccess) return hip_fail(e, "fill launch");
-    e = launch_pool(sh, L, k_idx, workspace, s);
+    e = launch_pool(sh, L, k_idx, k_gate, workspace, s);
     if (e != hipSuccess) return hip_fail(e, "pool_keys launch");
     for (int64_t r0 = row0; r0 < row0 + n_rows; r0 += kDenseRows) {
         const int64_t rows = row0 + n_rows - r0 < kDenseRows ? row0 + n_rows - r0 : kDenseRows;
@@ -411,6 +419,59 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const float* q
         if (e != hipSuccess) return hip_fail(e, "index_score launch");
     }
     return DSA_OK;
+}
+
+dsa_status dsa_index_score_topk(const void* q_idx, const void* k_idx, const float* q_scale,
+                                const float* k_scale, const float* w, int64_t w_stride_q,
+                                int64_t s_q, int64_t s_k, int64_t q_pos0, int h_idx, int d_idx,
+                                int pool_size, int k_pools, int64_t chunk_q, int dtype,
+                                int32_t* idx_out, float* score_out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return index_score_topk(q_idx, k_idx, nullptr, q_scale, k_scale, w, w_stride_q, s_q, s_k,
+                            q_pos0, h_idx, d_idx, pool_size, k_pools, chunk_q, dtype, idx_out,
+                            score_out, workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_index_score_topk_gated(const void* q_idx, const void* k_idx, const float* k_gate,
+                                      const float* q_scale, const float* k_scale, const float* w,
+                                      int64_t w_stride_q, int64_t s_q, int64_t s_k,
+                                      int64_t q_pos0, int h_idx, int d_idx, int pool_size,
+                                      int k_pools, int64_t chunk_q, int dtype, int32_t* idx_out,
+                                      float* score_out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+    if (!k_gate && s_k / 4 > 0) {
+        g_err[0] = 0;
+        return fail(DSA_ERR_INVALID_ARG, "k_gate must be non-null");
+    }
+    return index_score_topk(q_idx, k_idx, k_gate, q_scale, k_scale, w, w_stride_q, s_q, s_k,
+                            q_pos0, h_idx, d_idx, pool_size, k_pools, chunk_q, dtype, idx_out,
+                            score_out, workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const float* q_scale,
+                            const float* k_scale, const float* w, int64_t w_stride_q,
+                            int64_t s_q, int64_t s_k, int64_t q_pos0, int h_idx, int d_idx,
+                            int pool_size, int dtype, int64_t row0, int64_t n_rows,
+                            float* scores_out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    return index_scores(q_idx, k_idx, nullptr, q_scale, k_scale, w, w_stride_q, s_q, s_k, q_pos0,
+                        h_idx, d_idx, pool_size, dtype, row0, n_rows, scores_out, workspace,
+                        workspace_bytes, stream);
+}
+
+dsa_status dsa_index_scores_gated(const void* q_idx, const void* k_idx, const float* k_gate,
+                                  const float* q_scale, const float* k_scale, const float* w,
+                                  int64_t w_stride_q, int64_t s_q, int64_t s_k, int64_t q_pos0,
+                                  int h_idx, int d_idx, int pool_size, int dtype, int64_t row0,
+                                  int64_t n_rows, float* scores_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    if (!k_gate && s_k / 4 > 0) {
+        g_err[0] = 0;
+        return fail(DSA_ERR_INVALID_ARG, "k_gate must be non-null");
+    }
+    return index_scores(q_idx, k_idx, k_gate, q_scale, k_scale, w, w_stride_q, s_q, s_k, q_pos0,
+                        h_idx, d_idx, pool_size, dtype, row0, n_rows, scores_out, workspace,
+                        workspace_bytes, stream);
 }
 
 dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx,

@@ -71,6 +71,77 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
     return code | sign;
 }
 
+// The same rounding from an fp64 value: |x| <= 448, ties to even.
+__device__ __forceinline__ uint32_t e4m3_code_f64(double x) {
+    const uint32_t sign = x < 0.0 ? 0x80u : 0u;
+    const double a = fabs(x);
+    uint32_t code;
+    if (a < 0x1p-6) {
+        code = (uint32_t)rint(a * 512.0);
+    } else {
+        int E;
+        (void)frexp(a, &E);  // a = f * 2^E, f in [0.5, 1)
+        E -= 1;              // a in [2^E, 2^(E+1))
+        uint32_t mm = (uint32_t)rint(ldexp(a, 3 - E)) - 8u;
+        uint32_t ee = (uint32_t)(E + 7);
+        if (mm == 8u) {
+            mm = 0u;
+            ++ee;
+        }
+        code = (ee << 3) | mm;
+        if (code > 0x7Eu) code = 0x7Eu;
+    }
+    return code | sign;
+}
+
+// Gated fp8 pooling: m = sum_r g_r * value(code_r), summed in fp64 in row
+// order.  Each product of an fp32 gate and an E4M3 value is exact in fp64,
+// so m, the power-of-two scale and the round-to-nearest-even code below do
+// not depend on the order of evaluation beyond that of the sum.
+template <int DI>
+__global__ __launch_bounds__(256) void pool_keys_fp8_gated_kernel(const uint8_t* __restrict__ k8,
+                                                                  const float* __restrict__ gate,
+                                                                  int64_t n_pools,
+                                                                  uint8_t* __restrict__ kbar8,
+                                                                  float* __restrict__ pool_scale) {
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= n_pools) return;
+    const f32x4 g = *reinterpret_cast<const f32x4*>(gate + 4 * p);
+    double m[DI];
+    double amax = 0.0;
+#pragma unroll
+    for (int c = 0; c < DI / 16; ++c) {
+        u32x4 r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = ldg16(k8 + (p * 4 + j) * DI + 16 * c);
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+            const int word = b >> 2, sh = (b & 3) * 8;
+            double s = 0.0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                s = __dadd_rn(s, __dmul_rn((double)g[j], (double)e4m3_value((r[j][word] >> sh) & 0xFFu)));
+            m[16 * c + b] = s;
+            amax = fmax(amax, fabs(s));
+        }
+    }
+    int e = 0;
+    if (amax > 0.0) {
+        int E;
+        (void)frexp(amax / 448.0, &E);
+        e = E - 3;
+        while (amax > ldexp(448.0, e)) ++e;
+    }
+#pragma unroll
+    for (int c = 0; c < DI / 16; ++c) {
+        u32x4 o = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int b = 0; b < 16; ++b) o[b >> 2] |= e4m3_code_f64(ldexp(m[16 * c + b], -e)) << ((b & 3) * 8);
+        *reinterpret_cast<u32x4*>(kbar8 + p * DI + 16 * c) = o;
+    }
+    pool_scale[p] = ldexpf(1.0f, e);
+}
+
 template <int DI>
 __global__ __launch_bounds__(256) void pool_keys_fp8_kernel(const uint8_t* __restrict__ k8,
                                                             int64_t n_pools,
@@ -111,10 +182,19 @@ __global__ __launch_bounds__(256) void pool_keys_fp8_kernel(const uint8_t* __res
     pool_scale[p] = ldexpf(1.0f, e);
 }
 
-hipError_t launch_pool_keys_fp8(const uint8_t* k8, int64_t n_pools, int d_idx, uint8_t* kbar8,
-                                float* pool_scale, hipStream_t stream) {
+hipError_t launch_pool_keys_fp8(const uint8_t* k8, const float* gate, int64_t n_pools, int d_idx,
+                                uint8_t* kbar8, float* pool_scale, hipStream_t stream) {
     if (n_pools <= 0) return hipSuccess;
     const dim3 grid((unsigned)((n_pools + 255) / 256));
+    if (gate) {
+        switch (d_idx) {
+            case 64: pool_keys_fp8_gated_kernel<64><<<grid, 256, 0, stream>>>(k8, gate, n_pools, kbar8, pool_scale); break;
+            case 96: pool_keys_fp8_gated_kernel<96><<<grid, 256, 0, stream>>>(k8, gate, n_pools, kbar8, pool_scale); break;
+            case 128: pool_keys_fp8_gated_kernel<128><<<grid, 256, 0, stream>>>(k8, gate, n_pools, kbar8, pool_scale); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (d_idx) {
         case 64: pool_keys_fp8_kernel<64><<<grid, 256, 0, stream>>>(k8, n_pools, kbar8, pool_scale); break;
         case 96: pool_keys_fp8_kernel<96><<<grid, 256, 0, stream>>>(k8, n_pools, kbar8, pool_scale); break;
@@ -134,16 +214,20 @@ __device__ __forceinline__ int pow2_scale_exp(float amax) {
     return e;
 }
 
-// One thread per pool: hi = bf16(mean) [P][DI], lo = E4M3((mean - hi) / 2^e)
-// [P][DI] with one E8M0 byte (e + 127) per pool.
-template <int DI>
+// One thread per pool: hi = bf16(kbar) [P][DI], lo = E4M3((kbar - hi) / 2^e)
+// [P][DI] with one E8M0 byte (e + 127) per pool.  kbar is the mean of the
+// pool's 4 rows, or with GATED their gate-weighted sum (fp32).
+template <int DI, bool GATED>
 __global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __restrict__ k,
+                                                             const float* __restrict__ gate,
                                                              int64_t n_pools,
                                                              uint16_t* __restrict__ hi_out,
                                                              uint8_t* __restrict__ lo_out,
                                                              uint8_t* __restrict__ lo_scale) {
     const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (p >= n_pools) return;
+    f32x4 gw = {0.25f, 0.25f, 0.25f, 0.25f};
+    if constexpr (GATED) gw = *reinterpret_cast<const f32x4*>(gate + 4 * p);
     float lo[DI];
     float amax = 0.0f;
 #pragma unroll
@@ -155,11 +239,18 @@ __global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __r
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int word = e >> 1, sh = (e & 1) * 16;
-            float sum = bf16_to_f32((r[0][word] >> sh) & 0xFFFFu);
-            sum += bf16_to_f32((r[1][word] >> sh) & 0xFFFFu);
-            sum += bf16_to_f32((r[2][word] >> sh) & 0xFFFFu);
-            sum += bf16_to_f32((r[3][word] >> sh) & 0xFFFFu);
-            const float m = sum * 0.25f;
+            float m;
+            if constexpr (GATED) {
+                m = gw[0] * bf16_to_f32((r[0][word] >> sh) & 0xFFFFu);
+#pragma unroll
+                for (int j = 1; j < 4; ++j) m = fmaf(gw[j], bf16_to_f32((r[j][word] >> sh) & 0xFFFFu), m);
+            } else {
+                float sum = bf16_to_f32((r[0][word] >> sh) & 0xFFFFu);
+                sum += bf16_to_f32((r[1][word] >> sh) & 0xFFFFu);
+                sum += bf16_to_f32((r[2][word] >> sh) & 0xFFFFu);
+                sum += bf16_to_f32((r[3][word] >> sh) & 0xFFFFu);
+                m = sum * 0.25f;
+            }
             const uint32_t h = f32_to_bf16(m);
             lo[8 * g + e] = m - bf16_to_f32(h);
             amax = fmaxf(amax, fabsf(lo[8 * g + e]));
@@ -179,18 +270,26 @@ __global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __r
     lo_scale[p] = (uint8_t)(e + 127);
 }
 
-hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, int64_t n_pools, int d_idx,
-                                 uint16_t* hi, uint8_t* lo, uint8_t* lo_scale,
-                                 hipStream_t stream) {
-    if (n_pools <= 0) return hipSuccess;
+template <bool GATED>
+static hipError_t launch_pool_bf16_g(const uint16_t* k_idx, const float* gate, int64_t n_pools,
+                                     int d_idx, uint16_t* hi, uint8_t* lo, uint8_t* lo_scale,
+                                     hipStream_t stream) {
     const dim3 grid((unsigned)((n_pools + 255) / 256));
     switch (d_idx) {
-        case 64: pool_keys_bf16_kernel<64><<<grid, 256, 0, stream>>>(k_idx, n_pools, hi, lo, lo_scale); break;
-        case 96: pool_keys_bf16_kernel<96><<<grid, 256, 0, stream>>>(k_idx, n_pools, hi, lo, lo_scale); break;
-        case 128: pool_keys_bf16_kernel<128><<<grid, 256, 0, stream>>>(k_idx, n_pools, hi, lo, lo_scale); break;
+        case 64: pool_keys_bf16_kernel<64, GATED><<<grid, 256, 0, stream>>>(k_idx, gate, n_pools, hi, lo, lo_scale); break;
+        case 96: pool_keys_bf16_kernel<96, GATED><<<grid, 256, 0, stream>>>(k_idx, gate, n_pools, hi, lo, lo_scale); break;
+        case 128: pool_keys_bf16_kernel<128, GATED><<<grid, 256, 0, stream>>>(k_idx, gate, n_pools, hi, lo, lo_scale); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, const float* gate, int64_t n_pools,
+                                 int d_idx, uint16_t* hi, uint8_t* lo, uint8_t* lo_scale,
+                                 hipStream_t stream) {
+    if (n_pools <= 0) return hipSuccess;
+    return gate ? launch_pool_bf16_g<true>(k_idx, gate, n_pools, d_idx, hi, lo, lo_scale, stream)
+                : launch_pool_bf16_g<false>(k_idx, gate, n_pools, d_idx, hi, lo, lo_scale, stream);
 }
 
 // ---------------------------------------------------------------- query tiles

@@ -7,10 +7,12 @@
 
 namespace dsa {
 
-// Pooled indexer keys, split as hi = bf16(mean) [P][d] and lo = mean - hi
-// as E4M3 codes [P][d] with one E8M0 power-of-two scale byte per pool.
-hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, int64_t n_pools, int d_idx,
-                                 uint16_t* hi, uint8_t* lo, uint8_t* lo_scale,
+// Pooled indexer keys kbar (the mean of each pool's 4 rows, or with
+// per-token gates [4 * n_pools] fp32 their gate-weighted sum), split as
+// hi = bf16(kbar) [P][d] and lo = kbar - hi as E4M3 codes [P][d] with one
+// E8M0 power-of-two scale byte per pool.
+hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, const float* gate, int64_t n_pools,
+                                 int d_idx, uint16_t* hi, uint8_t* lo, uint8_t* lo_scale,
                                  hipStream_t stream);
 
 // Packed query tiles of the bf16 indexer.  A tile holds 32 (query, head)
@@ -47,9 +49,10 @@ hipError_t launch_pack_queries(const uint16_t* q_idx, const float* w, int64_t w_
                                int64_t row0, int rows, int h_idx, int d_idx, uint8_t* tiles,
                                hipStream_t stream);
 
-// Pooled fp8 keys: per pool, E4M3 codes of mean/2^e and the factor 2^e.
-hipError_t launch_pool_keys_fp8(const uint8_t* k8, int64_t n_pools, int d_idx, uint8_t* kbar8,
-                                float* pool_scale, hipStream_t stream);
+// Pooled fp8 keys: per pool, E4M3 codes of kbar/2^e and the factor 2^e
+// (kbar the mean of the code values, or with gates their gate-weighted sum).
+hipError_t launch_pool_keys_fp8(const uint8_t* k8, const float* gate, int64_t n_pools, int d_idx,
+                                uint8_t* kbar8, float* pool_scale, hipStream_t stream);
 
 struct ScoreArgs {
     const void* q_idx;        // fp8: [s_q, h_idx, d_idx] E4M3

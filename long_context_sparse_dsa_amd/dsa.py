@@ -63,6 +63,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dsa_index_score_topk.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _i64, _int,
             _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.dsa_index_score_topk_gated.restype = _int
+        lib.dsa_index_score_topk_gated.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _i64,
+            _int, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         lib.dsa_index_scores_workspace_size.restype = _int
         lib.dsa_index_scores_workspace_size.argtypes = [
             _i64, _i64, _int, _int, _int, _int, _i64, ctypes.POINTER(ctypes.c_size_t)]
@@ -70,6 +74,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dsa_index_scores.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _i64, _i64,
             _vp, _vp, ctypes.c_size_t, _vp]
+        lib.dsa_index_scores_gated.restype = _int
+        lib.dsa_index_scores_gated.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _i64,
+            _i64, _vp, _vp, ctypes.c_size_t, _vp]
         lib.dsa_sparse_attn_fwd.restype = _int
         lib.dsa_sparse_attn_fwd.argtypes = [
             _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int, _int, _int, _f, _vp,
@@ -157,17 +165,16 @@ def new_workspace(nbytes: int, device=None) -> torch.Tensor:
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device or "cuda")
 
 
-def dsa_index_score_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
-                         k_pools: int, *, q_pos0: int = 0, chunk_q: int = 0,
-                         q_scale: torch.Tensor | None = None,
-                         k_scale: torch.Tensor | None = None,
-                         idx_out: torch.Tensor | None = None,
-                         score_out: torch.Tensor | None = None,
-                         want_scores: bool = False,
-                         workspace: torch.Tensor | None = None, stream=None):
-    """Pool, score in chunks and keep the top ``k_pools`` pools per query.
+def _gate_ptr(k_gate, k_idx):
+    if k_gate is None:
+        return None
+    _need(k_gate.dtype == torch.float32 and k_gate.dim() == 1 and k_gate.is_contiguous()
+          and k_gate.shape[0] == k_idx.shape[0], "k_gate must be contiguous fp32 [S_k]")
+    return _ptr(k_gate)
 
-    Returns (idx [S_q, k_pools] int32, scores [S_q, k_pools] fp32 or None)."""
+
+def _score_topk(fn, q_idx, k_idx, k_gate, w, k_pools, q_pos0, chunk_q, q_scale, k_scale,
+                idx_out, score_out, want_scores, workspace, stream):
     lib = load_library()
     s_q, s_k, h_idx, d_idx, w_stride, dtype = _indexer_shapes(q_idx, k_idx, w)
     dev = q_idx.device
@@ -178,18 +185,47 @@ def dsa_index_score_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tens
         idx_out = torch.empty((s_q, k_pools), dtype=torch.int32, device=dev)
     if score_out is None and want_scores:
         score_out = torch.empty((s_q, k_pools), dtype=torch.float32, device=dev)
-    _check(lib.dsa_index_score_topk(
-        _ptr(q_idx), _ptr(k_idx), _ptr(q_scale), _ptr(k_scale), _ptr(w), w_stride, s_q, s_k,
-        q_pos0, h_idx, d_idx, 4, k_pools, chunk_q, dtype, _ptr(idx_out), _ptr(score_out),
+    gate = [] if fn == "dsa_index_score_topk" else [_gate_ptr(k_gate, k_idx)]
+    _check(getattr(lib, fn)(
+        _ptr(q_idx), _ptr(k_idx), *gate, _ptr(q_scale), _ptr(k_scale), _ptr(w), w_stride, s_q,
+        s_k, q_pos0, h_idx, d_idx, 4, k_pools, chunk_q, dtype, _ptr(idx_out), _ptr(score_out),
         _ptr(workspace), workspace.numel(), _stream(stream)))
     return idx_out, score_out
 
 
-def dsa_index_scores(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, *,
-                     row0: int = 0, n_rows: int | None = None, q_pos0: int = 0,
-                     q_scale: torch.Tensor | None = None, k_scale: torch.Tensor | None = None,
-                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Dense fp32 scores [n_rows, P] of rows [row0, row0+n_rows); -inf = not eligible."""
+def dsa_index_score_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
+                         k_pools: int, *, q_pos0: int = 0, chunk_q: int = 0,
+                         q_scale: torch.Tensor | None = None,
+                         k_scale: torch.Tensor | None = None,
+                         idx_out: torch.Tensor | None = None,
+                         score_out: torch.Tensor | None = None,
+                         want_scores: bool = False,
+                         workspace: torch.Tensor | None = None, stream=None):
+    """Pool (mean of 4 keys), score in chunks and keep the top ``k_pools``
+    pools per query.
+
+    Returns (idx [S_q, k_pools] int32, scores [S_q, k_pools] fp32 or None)."""
+    return _score_topk("dsa_index_score_topk", q_idx, k_idx, None, w, k_pools, q_pos0, chunk_q,
+                       q_scale, k_scale, idx_out, score_out, want_scores, workspace, stream)
+
+
+def dsa_index_score_topk_gated(q_idx: torch.Tensor, k_idx: torch.Tensor, k_gate: torch.Tensor,
+                               w: torch.Tensor, k_pools: int, *, q_pos0: int = 0,
+                               chunk_q: int = 0, q_scale: torch.Tensor | None = None,
+                               k_scale: torch.Tensor | None = None,
+                               idx_out: torch.Tensor | None = None,
+                               score_out: torch.Tensor | None = None,
+                               want_scores: bool = False,
+                               workspace: torch.Tensor | None = None, stream=None):
+    """As dsa_index_score_topk, with each pooled key the gate-weighted sum of
+    its 4 keys (k_gate: per-token gates [S_k] fp32)."""
+    return _score_topk("dsa_index_score_topk_gated", q_idx, k_idx, k_gate, w, k_pools, q_pos0,
+                       chunk_q, q_scale, k_scale, idx_out, score_out, want_scores, workspace,
+                       stream)
+
+
+def _scores(fn, q_idx, k_idx, k_gate, w, row0, n_rows, q_pos0, q_scale, k_scale, workspace,
+            stream):
     lib = load_library()
     s_q, s_k, h_idx, d_idx, w_stride, dtype = _indexer_shapes(q_idx, k_idx, w)
     n_rows = s_q - row0 if n_rows is None else n_rows
@@ -199,11 +235,31 @@ def dsa_index_scores(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, 
     if workspace is None:
         workspace = new_workspace(need, dev)
     out = torch.empty((n_rows, n_pools), dtype=torch.float32, device=dev)
-    _check(lib.dsa_index_scores(
-        _ptr(q_idx), _ptr(k_idx), _ptr(q_scale), _ptr(k_scale), _ptr(w), w_stride, s_q, s_k,
-        q_pos0, h_idx, d_idx, 4, dtype, row0, n_rows, _ptr(out), _ptr(workspace),
+    gate = [] if fn == "dsa_index_scores" else [_gate_ptr(k_gate, k_idx)]
+    _check(getattr(lib, fn)(
+        _ptr(q_idx), _ptr(k_idx), *gate, _ptr(q_scale), _ptr(k_scale), _ptr(w), w_stride, s_q,
+        s_k, q_pos0, h_idx, d_idx, 4, dtype, row0, n_rows, _ptr(out), _ptr(workspace),
         workspace.numel(), _stream(stream)))
     return out
+
+
+def dsa_index_scores(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, *,
+                     row0: int = 0, n_rows: int | None = None, q_pos0: int = 0,
+                     q_scale: torch.Tensor | None = None, k_scale: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Dense fp32 scores [n_rows, P] of rows [row0, row0+n_rows); -inf = not eligible."""
+    return _scores("dsa_index_scores", q_idx, k_idx, None, w, row0, n_rows, q_pos0, q_scale,
+                   k_scale, workspace, stream)
+
+
+def dsa_index_scores_gated(q_idx: torch.Tensor, k_idx: torch.Tensor, k_gate: torch.Tensor,
+                           w: torch.Tensor, *, row0: int = 0, n_rows: int | None = None,
+                           q_pos0: int = 0, q_scale: torch.Tensor | None = None,
+                           k_scale: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """As dsa_index_scores, with gate-weighted pooled keys (k_gate [S_k] fp32)."""
+    return _scores("dsa_index_scores_gated", q_idx, k_idx, k_gate, w, row0, n_rows, q_pos0,
+                   q_scale, k_scale, workspace, stream)
 
 
 def dsa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, *,

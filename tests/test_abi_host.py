@@ -178,5 +178,18 @@ def test_fp8_workspace_layout(lib):
         r(1000 * 256) + r(1000 * 128) + r(1000) + r(1027 * 12544))
 
 
+def test_gated_entry_points_check_the_gate(lib):
+    a = [0x1000, 0x2000]
+    rest = [None, None, 0x3000, 0, 64, 64, 0, 32, 128, 4, 8, 0, 0, 0x4000, None, 0x5000, 1 << 30,
+            None]
+    # a missing or misaligned gate is rejected before anything is launched
+    assert lib.dsa_index_score_topk_gated(*a, None, *rest) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_index_score_topk_gated(*a, 0x6004, *rest) == dsa.DSA_ERR_INVALID_ARG
+    assert "k_gate" in lib.dsa_last_error().decode()
+    st = lib.dsa_index_scores_gated(0x1000, 0x2000, 0x6008, None, None, 0x3000, 0, 64, 64, 0, 32,
+                                    128, 4, 0, 0, 8, 0x4000, 0x5000, 1 << 20, None)
+    assert st == dsa.DSA_ERR_INVALID_ARG
+
+
 def test_profile_read_empty(lib):
     assert dsa.dsa_profile_read() == {}

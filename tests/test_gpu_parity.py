@@ -32,11 +32,11 @@ def _lib():
 
 
 def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=None,
-             check_scores=True, x=None, fp8=False, scales=(1.0, 1.0)):
+             check_scores=True, x=None, fp8=False, scales=(1.0, 1.0), gate=None):
     _say(f"[case] {wl.name} s_q={wl.s_q} s_k={wl.s_k} q_pos0={wl.q_pos0} "
          f"H_I={wl.h_idx} D_I={wl.d_idx} k={wl.k_pools} H={wl.h} D={wl.d} Dv={wl.dv} "
          f"n_tail={wl.n_tail} chunk_q={chunk_q} fp8={fp8} scales={scales} "
-         f"seed={seed if seed is not None else wl.seed}")
+         f"gated={gate is not None} seed={seed if seed is not None else wl.seed}")
     if x is None:
         x = inputs.make_inputs(wl, seed=seed, attention=attention, w_per_query=w_per_query)
     dev = torch.device("cuda")
@@ -46,8 +46,15 @@ def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=N
     if fp8:
         sc_kw = dict(q_scale=torch.tensor([scales[0]], dtype=torch.float32, device=dev),
                      k_scale=torch.tensor([scales[1]], dtype=torch.float32, device=dev))
-    idx_g, sc_g = dsa.dsa_index_score_topk(q_idx, k_idx, w, wl.k_pools, q_pos0=wl.q_pos0,
-                                           chunk_q=chunk_q, want_scores=True, **sc_kw)
+    g_dev = None if gate is None else gate.to(dev)
+    g_np = None if gate is None else gate.numpy()
+    if gate is None:
+        idx_g, sc_g = dsa.dsa_index_score_topk(q_idx, k_idx, w, wl.k_pools, q_pos0=wl.q_pos0,
+                                               chunk_q=chunk_q, want_scores=True, **sc_kw)
+    else:
+        idx_g, sc_g = dsa.dsa_index_score_topk_gated(q_idx, k_idx, g_dev, w, wl.k_pools,
+                                                     q_pos0=wl.q_pos0, chunk_q=chunk_q,
+                                                     want_scores=True, **sc_kw)
     torch.cuda.synchronize()
     rows = np.arange(wl.s_q) if rows is None else np.asarray(rows, dtype=np.int64)
     pos = wl.q_pos0 + rows
@@ -55,13 +62,15 @@ def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=N
     sc_g_rows = sc_g.cpu().numpy()[rows]
     if fp8:
         idx_o, sc_o = oracle.index_topk_fp8(x[qn], x[kn], x["w"], wl.k_pools, q_scale=scales[0],
-                                            k_scale=scales[1], q_pos0=wl.q_pos0, rows=rows)
+                                            k_scale=scales[1], q_pos0=wl.q_pos0, rows=rows,
+                                            gate=g_np)
         s_o = oracle.index_scores_fp8(x[qn], x[kn], x["w"], q_scale=scales[0],
-                                      k_scale=scales[1], q_pos0=wl.q_pos0, rows=rows)
+                                      k_scale=scales[1], q_pos0=wl.q_pos0, rows=rows, gate=g_np)
     else:
         idx_o, sc_o = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], wl.k_pools,
-                                        q_pos0=wl.q_pos0, rows=rows)
-        s_o = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0, rows=rows)
+                                        q_pos0=wl.q_pos0, rows=rows, gate=g_np)
+        s_o = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0, rows=rows,
+                                  gate=g_np)
     stats = parity.check_index_rows(idx_g_rows, idx_o, s_o, pos, wl.n_pools, wl.k_pools)
     _say(f"  index: {stats}")
     # the kept pools' scores against the oracle's dense scores
@@ -80,15 +89,19 @@ def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=N
         worst = 0.0
         for b0 in blocks:
             nb = min(16, wl.s_q - b0)
-            g = dsa.dsa_index_scores(q_idx, k_idx, w, row0=b0, n_rows=nb, q_pos0=wl.q_pos0,
-                                     **sc_kw)
+            if gate is None:
+                g = dsa.dsa_index_scores(q_idx, k_idx, w, row0=b0, n_rows=nb, q_pos0=wl.q_pos0,
+                                         **sc_kw)
+            else:
+                g = dsa.dsa_index_scores_gated(q_idx, k_idx, g_dev, w, row0=b0, n_rows=nb,
+                                               q_pos0=wl.q_pos0, **sc_kw)
             if fp8:
                 ref = oracle.index_scores_fp8(x[qn], x[kn], x["w"], q_scale=scales[0],
                                               k_scale=scales[1], q_pos0=wl.q_pos0,
-                                              rows=np.arange(b0, b0 + nb))
+                                              rows=np.arange(b0, b0 + nb), gate=g_np)
             else:
                 ref = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0,
-                                          rows=np.arange(b0, b0 + nb))
+                                          rows=np.arange(b0, b0 + nb), gate=g_np)
             worst = max(worst, parity.check_scores(g.cpu().numpy(), ref))
         _say(f"  scores: worst error / bound = {worst:.3g}")
     if attention:
@@ -104,6 +117,39 @@ def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=N
                                         lse_g.cpu().numpy()[rows], o_o, lse_o)
         _say(f"  attention: max |do| = {eo:.3g}, max |dlse| = {el:.3g}")
     return x, idx_g
+
+
+# ---------------------------------------------------------------- gated pooling
+# section "DSA: Gather by Token Position": per-token k-pool gate scores weight
+# each key within its pool.
+
+@pytest.mark.parametrize("h_idx,d_idx,fp8", [(32, 128, False), (16, 96, False), (4, 64, False),
+                                             (32, 96, True), (8, 128, True)])
+def test_gated_pooling(h_idx, d_idx, fp8):
+    wl = inputs.custom(f"gated_{h_idx}x{d_idx}{'_fp8' if fp8 else ''}", s_q=1300, s_k=1303,
+                       h_idx=h_idx, d_idx=d_idx, k_pools=48, h=16, d=d_idx,
+                       idx_std=1.0 if fp8 else 1 / math.sqrt(d_idx),
+                       attn_std=1 / math.sqrt(d_idx), fp8=fp8, number=400 + h_idx + d_idx)
+    gate = inputs.make_gates(wl)
+    run_case(wl, chunk_q=192, w_per_query=True, fp8=fp8, gate=gate,
+             attention=not fp8)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_quarter_gates_reproduce_mean_pooling_bitwise(fp8):
+    wl = inputs.custom("quarter_gates", s_q=900, s_k=900, h_idx=16, d_idx=128, k_pools=40,
+                       idx_std=1.0 if fp8 else 0.1, fp8=fp8, number=420)
+    _say(f"[case] quarter gates fp8={fp8}")
+    x = inputs.make_inputs(wl, attention=False)
+    dev = torch.device("cuda")
+    qn, kn = ("q_idx8", "k_idx8") if fp8 else ("q_idx", "k_idx")
+    q_idx, k_idx, w = x[qn].to(dev), x[kn].to(dev), x["w"].to(dev)
+    gate = torch.full((wl.s_k,), 0.25, dtype=torch.float32, device=dev)
+    i0, s0 = dsa.dsa_index_score_topk(q_idx, k_idx, w, wl.k_pools, chunk_q=256, want_scores=True)
+    i1, s1 = dsa.dsa_index_score_topk_gated(q_idx, k_idx, gate, w, wl.k_pools, chunk_q=256,
+                                            want_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(i0, i1) and torch.equal(s0, s1)
 
 
 # ---------------------------------------------------------------- small, every row
@@ -238,6 +284,21 @@ def test_workload_s32k_sampled():
 def test_workload_s128k_sampled():
     wl = inputs.WORKLOADS["s128k"]
     run_case(wl, rows=inputs.sample_rows(wl.s_q, 160), check_scores=False)
+
+
+@pytest.mark.slow
+def test_workload_s128k_gated_sampled():
+    # the headline shape with per-token k-pool gates (bf16 indexer)
+    wl = inputs.WORKLOADS["s128k"]
+    run_case(wl, rows=inputs.sample_rows(wl.s_q, 120), check_scores=False, attention=False,
+             gate=inputs.make_gates(wl))
+
+
+@pytest.mark.slow
+def test_workload_nope_s64k_fp8_gated_sampled():
+    wl = inputs.WORKLOADS["nope_s64k"]
+    run_case(wl, rows=inputs.sample_rows(wl.s_q, 120), check_scores=False, attention=False,
+             fp8=True, gate=inputs.make_gates(wl))
 
 
 @pytest.mark.slow
