@@ -217,6 +217,134 @@ __device__ void refine(KeyAt key_at, int64_t n, int shift, uint32_t& lo, uint32_
     }
 }
 
+// A key tau with at least r of the SAMPLE_N sample keys (sh.key) >= tau,
+// and not many more: a 256-bin histogram linear in the scores' values (not
+// in their bit patterns, which would lump the upper tail into one bin) gives
+// the highest bin b whose suffix holds r keys; tau is the smallest sample key
+// in bins >= b.  Any tau that leaves between k and CAP row elements above it
+// serves the compaction; the selection after it is exact.
+__device__ uint32_t sample_threshold(uint32_t r, SelShared& sh) {
+    constexpr int NBIN = 256;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int e = tid; e < SAMPLE_N; e += NT) {
+        mn = min(mn, sh.key[e]);
+        mx = max(mx, sh.key[e]);
+    }
+    block_minmax(mn, mx, sh);
+    if (mn == mx) return mn;
+    const float vmin = key_to_float(mn), vmax = key_to_float(mx);
+    const float scale = (float)NBIN / (vmax - vmin);
+    auto bin_of = [&](uint32_t key) {
+        const float b = (key_to_float(key) - vmin) * scale;
+        return b >= (float)(NBIN - 1) ? NBIN - 1 : (b > 0.0f ? (int)b : 0);
+    };
+    uint32_t* hist = sh.cnt;  // NBIN counters
+    for (int b = tid; b < NBIN; b += NT) hist[b] = 0;
+    __syncthreads();
+    for (int e = tid; e < SAMPLE_N; e += NT) atomicAdd(&hist[bin_of(sh.key[e])], 1u);
+    __syncthreads();
+    if (wave == 0) {
+        // lane l holds bins 4l .. 4l+3; suffix sums from the top bin down
+        uint32_t h[4], tot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            h[j] = hist[4 * lane + j];
+            tot += h[j];
+        }
+        // inclusive scan over lanes in reverse order gives the suffix sum
+        const uint32_t rev = wave_incl_scan((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (63 - lane), (int)tot), lane);
+        const uint32_t suffix = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (63 - lane), (int)rev);
+        // bins of this lane: suffix(4l + j) = suffix - sum of h[0..j)
+        uint32_t s_j = suffix;
+        int found = -1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (s_j >= r) found = 4 * lane + j;
+            s_j -= h[j];
+        }
+        // the highest bin whose suffix reaches r
+        const uint32_t best = wave_incl_scan_op(found < 0 ? 0u : (uint32_t)found + 1u, 0u, MaxOp{});
+        if (lane == 63) sh.tmp[0] = best - 1u;
+    }
+    __syncthreads();
+    const int b_min = (int)sh.tmp[0];
+    __syncthreads();
+    uint32_t kmin = 0xFFFFFFFFu, dummy = 0u;
+    for (int e = tid; e < SAMPLE_N; e += NT) {
+        const uint32_t key = sh.key[e];
+        if (bin_of(key) >= b_min) kmin = min(kmin, key);
+    }
+    block_minmax(kmin, dummy, sh);
+    return kmin;
+}
+
+// Radix-256 refinement of a list in LDS: the same contract as refine, with
+// 8-bit digits counted by LDS atomics (integer, so the counts do not depend
+// on their order) and the digit found by one wave's suffix scan: at most 4
+// passes instead of 8.
+__device__ void refine256(int m, uint32_t& lo, uint32_t& hi, uint32_t& remaining,
+                          SelShared& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t* hist = sh.cnt;
+    const uint32_t diff = lo ^ hi;
+    if (diff == 0) return;
+    // highest differing bit of the range -> first 8-bit digit
+    int shift = ((31 - __clz(diff)) / 8) * 8;
+    for (; shift >= 0 && lo != hi; shift -= 8) {
+        for (int b = tid; b < 256; b += NT) hist[b] = 0;
+        __syncthreads();
+        for (int e = tid; e < m; e += NT) {
+            const uint32_t k = sh.key[e];
+            if (k >= lo && k <= hi) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            uint32_t h[4], tot = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h[j] = hist[4 * lane + j];
+                tot += h[j];
+            }
+            const uint32_t rev = wave_incl_scan((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (63 - lane), (int)tot), lane);
+            const uint32_t suffix = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (63 - lane), (int)rev);
+            // digit d: count of in-range keys with digit > d is suffix(d + 1)
+            uint32_t s_j = suffix;
+            int found = -1;
+            uint32_t above_f = 0, h_f = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t above = s_j - h[j];  // keys with a larger digit
+                if (above < remaining && s_j >= remaining) {
+                    found = 4 * lane + j;
+                    above_f = above;
+                    h_f = h[j];
+                }
+                s_j = above;
+            }
+            // exactly one lane finds the digit
+            const uint64_t who = __ballot(found >= 0);
+            const int src = (int)__ffsll((unsigned long long)who) - 1;
+            const int d = __shfl(found, src);
+            const uint32_t ab = (uint32_t)__shfl((int)above_f, src);
+            const uint32_t hd = (uint32_t)__shfl((int)h_f, src);
+            if (lane == 0) {
+                sh.tmp[0] = (uint32_t)d;
+                sh.tmp[1] = ab;
+                sh.tmp[2] = hd;
+            }
+        }
+        __syncthreads();
+        const uint32_t d = sh.tmp[0], above = sh.tmp[1], hd = sh.tmp[2];
+        __syncthreads();
+        remaining -= above;
+        const uint32_t keep = (shift + 8 >= 32) ? 0u : (lo & (0xFFFFFFFFu << (shift + 8)));
+        lo = keep | (d << shift);
+        hi = lo | ((shift == 0) ? 0u : ((1u << shift) - 1u));
+        if (hd == remaining) break;
+    }
+}
+
 // Emit the kept ids of the LDS list (already in id order) to out[0..k).
 __device__ void emit_from_list(int m, uint32_t lo, uint32_t hi, uint32_t remaining,
                                SelShared& sh, int32_t* out, float* score_out, int k_out) {
@@ -384,16 +512,7 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
         const float mu = (float)k * (float)SAMPLE_N / (float)n;
         uint32_t r = (uint32_t)ceilf(mu + 4.0f * sqrtf(mu) + 4.0f);
         if (r > (uint32_t)SAMPLE_N) r = SAMPLE_N;
-        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-        for (int s = tid; s < SAMPLE_N; s += NT) {
-            mn = min(mn, sh.key[s]);
-            mx = max(mx, sh.key[s]);
-        }
-        block_minmax(mn, mx, sh);
-        uint32_t lo, hi, rem = r;
-        const int shift = start_range(mn, mx, lo, hi);
-        refine([&](int64_t e) { return sh.key[e]; }, SAMPLE_N, shift, lo, hi, rem, sh);
-        const uint32_t tau = lo;  // at least r sample keys are >= tau
+        const uint32_t tau = sample_threshold(r, sh);  // at least r sample keys are >= tau
         __syncthreads();
 
         // ordered compaction of {key >= tau}: batches of VB 16-byte loads per
@@ -458,9 +577,8 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
         mx = max(mx, sh.key[e]);
     }
     block_minmax(mn, mx, sh);
-    uint32_t lo, hi, remaining = (uint32_t)k;
-    const int shift = start_range(mn, mx, lo, hi);
-    refine([&](int64_t e) { return sh.key[e]; }, m, shift, lo, hi, remaining, sh);
+    uint32_t lo = mn, hi = mx, remaining = (uint32_t)k;
+    refine256(m, lo, hi, remaining, sh);
     emit_from_list(m, lo, hi, remaining, sh, out, sout, k);
 }
 
