@@ -147,6 +147,15 @@ def make_gates(wl: Workload, seed: int | None = None) -> torch.Tensor:
     return torch.from_numpy(g)
 
 
+def make_dout(wl: Workload, seed: int | None = None) -> torch.Tensor:
+    """Upstream gradient of the attention output, dout [S_q, H, Dv] bf16,
+    N(0, 1) from a ninth sub-stream of the same seed (the first eight are
+    those of ``make_inputs`` and ``make_gates``)."""
+    seed = wl.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(9)[8]))
+    return torch.from_numpy(_normal(rng, (wl.s_q, wl.h, wl.dv), 1.0)).to(torch.bfloat16)
+
+
 def sample_rows(s_q: int, n: int, extra=()) -> np.ndarray:
     """Rows for sampled checks: the first and last rows, rows around every
     4-aligned boundary near the ends, a strided sweep, plus ``extra``."""

@@ -54,6 +54,10 @@
  *     supplying normalised gates.  Without gates the mean is used, which is
  *     the gated sum with every gate equal to 1/4.
  *
+ *   - backward of the attention (the pages' setting is training; they print
+ *     no backward): the exact gradient of the forward's definition for the
+ *     loss sum dout . o, D taken from the exact fp64 forward.
+ *
  * Everything is accumulated in fp64 in plain loops; no blocking, fusion or
  * reordering beyond the definitions above.
  */
@@ -417,6 +421,42 @@ int dsa_oracle_index_topk_fp8(const uint8_t *q8, const uint8_t *k8, const float 
 /* Sparse attention                                                   */
 /* ------------------------------------------------------------------ */
 
+/* The token set T(t) of the query at position t (see the attention section
+ * below): the tokens of every pool listed in idx row `row` (strictly
+ * ascending ids in [0, n), then only -1), followed, when n_tail > 0, by the
+ * up to n_tail tokens of t's own pool that precede t.  Writes the token
+ * positions to tok (room for k_pools * pool + pool entries) and their number
+ * to *n_tok; returns ORACLE_ERR_IDX for a malformed row. */
+static int token_set(const int32_t *row, int k_pools, int pool, int64_t n, int64_t t,
+                     int n_tail, int64_t s_k, int64_t *tok, int64_t *n_tok)
+{
+    int64_t cnt = 0, prev = -1;
+    int ended = 0;
+    for (int j = 0; j < k_pools; ++j) {
+        int64_t p = row[j];
+        if (p < 0) {
+            if (p != -1)
+                return ORACLE_ERR_IDX;
+            ended = 1;
+            continue;
+        }
+        if (ended || p <= prev || p >= n)
+            return ORACLE_ERR_IDX;
+        prev = p;
+        for (int u = 0; u < pool; ++u)
+            tok[cnt++] = p * pool + u;
+    }
+    if (n_tail > 0) {
+        int64_t start = (t / pool) * pool;
+        if (t - n_tail > start)
+            start = t - n_tail;
+        for (int64_t j = start; j < t && j < s_k; ++j)
+            tok[cnt++] = j;
+    }
+    *n_tok = cnt;
+    return ORACLE_OK;
+}
+
 /* For each listed row r (query position t = q_pos0 + rows[r]) and head h:
  *   T(t)  = tokens {pool*p .. pool*p+pool-1} of every pool p >= 0 in
  *           idx[r][0..k_pools) (which must be strictly ascending, eligible,
@@ -451,30 +491,7 @@ int dsa_oracle_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t 
         const int32_t *row = idx + r * k_pools;
         int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(k_pools * pool + pool));
         int64_t n_tok = 0;
-        int ended = 0, row_bad = 0;
-        int64_t prev = -1;
-        for (int j = 0; j < k_pools; ++j) {
-            int64_t p = row[j];
-            if (p < 0) {
-                if (p != -1) row_bad = 1;
-                ended = 1;
-                continue;
-            }
-            if (ended || p <= prev || p >= n) {
-                row_bad = 1;
-                break;
-            }
-            prev = p;
-            for (int u = 0; u < pool; ++u)
-                tok[n_tok++] = p * pool + u;
-        }
-        if (!row_bad && n_tail > 0) {
-            int64_t start = (t / pool) * pool;
-            if (t - n_tail > start)
-                start = t - n_tail;
-            for (int64_t j = start; j < t && j < s_k; ++j)
-                tok[n_tok++] = j;
-        }
+        int row_bad = token_set(row, k_pools, pool, n, t, n_tail, s_k, tok, &n_tok);
         if (row_bad) {
 #pragma omp atomic write
             bad = ORACLE_ERR_IDX;
@@ -515,6 +532,165 @@ int dsa_oracle_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t 
         free(tok);
     }
     return bad;
+}
+
+/* Gradients of the sparse attention above.  The pages' setting is training
+ * (section "Activation Recompute": each layer's forward is rerun in the
+ * backward pass); the page prints no backward, so this is the gradient of
+ * the forward's definition written out.  For the loss L = sum dout . o over
+ * the listed rows (equivalently: dout set to zero on every other row), per
+ * listed row r (position t, query row i = rows[r]) and head h, with P_j the
+ * softmax weights of T(t):
+ *   dP_j = dout[i,h,:] . v[j,:]
+ *   D    = sum_j P_j dP_j                  (= dout[i,h,:] . o[i,h,:])
+ *   dS_j = P_j (dP_j - D)                  (gradient of L wrt logit l_j)
+ *   dq[r,h,:]  = scale * sum_j dS_j k[j,:]
+ *   dk[j,:]   += scale * dS_j q[i,h,:]     for every j in T(t)
+ *   dv[j,:]   += P_j dout[i,h,:]
+ * dq is [n_rows, h, d]; dk [s_k, d] and dv [s_k, dv] cover every key row
+ * (rows no listed query attends stay 0).  All fp64.
+ *
+ * Optional magnitudes (any of dq_mag, dk_mag, dv_mag may be NULL), the same
+ * sums over absolute values, from which a floating-point error bound of an
+ * implementation that rounds the weights or the stored output follows:
+ *   Dabs  = sum_e |dout[i,h,e]| sum_j P_j |v[j,e]|
+ *   m_j   = |dS_j| + P_j Dabs
+ *   dq_mag[r,h,:] = scale * sum_j m_j |k[j,:]|
+ *   dk_mag[j,:]  += scale * m_j |q[i,h,:]|
+ *   dv_mag[j,:]  += P_j |dout[i,h,:]|
+ * Rows are processed in the listed order, heads and tokens in increasing
+ * order.  Returns ORACLE_ERR_IDX for a malformed idx row (outputs are then
+ * incomplete). */
+int dsa_oracle_sparse_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               const int32_t *idx, const uint16_t *dout, int64_t s_q,
+                               int64_t s_k, int64_t q_pos0, int h, int d, int dv, int k_pools,
+                               int pool, int n_tail, double scale, const int64_t *rows,
+                               int64_t n_rows, double *dq, double *dk, double *dvv,
+                               double *dq_mag, double *dk_mag, double *dv_mag)
+{
+    if (s_q < 0 || s_k < 0 || q_pos0 < 0 || h <= 0 || d <= 0 || dv <= 0 || k_pools <= 0 ||
+        pool <= 0 || n_tail < 0 || n_tail >= pool || n_rows < 0 || !dq || !dk || !dvv)
+        return ORACLE_ERR_ARG;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= s_q)
+            return ORACLE_ERR_ARG;
+    int64_t n_pools = s_k / pool;
+    memset(dk, 0, sizeof(double) * (size_t)(s_k * d));
+    memset(dvv, 0, sizeof(double) * (size_t)(s_k * dv));
+    if (dk_mag)
+        memset(dk_mag, 0, sizeof(double) * (size_t)(s_k * d));
+    if (dv_mag)
+        memset(dv_mag, 0, sizeof(double) * (size_t)(s_k * dv));
+    int64_t cap = (int64_t)k_pools * pool + pool;
+    int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
+    /* per head: P_j, dS_j, m_j of the current row */
+    double *pw = (double *)malloc(sizeof(double) * (size_t)(h * cap));
+    double *ds = (double *)malloc(sizeof(double) * (size_t)(h * cap));
+    double *mj = (double *)malloc(sizeof(double) * (size_t)(h * cap));
+    if (!tok || !pw || !ds || !mj) {
+        free(tok);
+        free(pw);
+        free(ds);
+        free(mj);
+        return ORACLE_ERR_MEM;
+    }
+    int rc = ORACLE_OK;
+    for (int64_t r = 0; r < n_rows && rc == ORACLE_OK; ++r) {
+        int64_t i = rows[r];
+        int64_t t = q_pos0 + i;
+        int64_t n_tok = 0;
+        if (token_set(idx + r * k_pools, k_pools, pool, eligible_pools(t, pool, n_pools), t,
+                      n_tail, s_k, tok, &n_tok)) {
+            rc = ORACLE_ERR_IDX;
+            break;
+        }
+        /* per head: softmax weights, dS, magnitudes and dq (heads are
+         * independent; each writes only its own slices) */
+#pragma omp parallel for schedule(static)
+        for (int hh = 0; hh < h; ++hh) {
+            const uint16_t *q_th = q + (i * h + hh) * d;
+            const uint16_t *do_th = dout + (i * h + hh) * dv;
+            double *P = pw + (int64_t)hh * cap, *dS = ds + (int64_t)hh * cap;
+            double *M = mj + (int64_t)hh * cap;
+            double *dq_th = dq + (r * h + hh) * d;
+            for (int e = 0; e < d; ++e) {
+                dq_th[e] = 0.0;
+                if (dq_mag)
+                    dq_mag[(r * h + hh) * d + e] = 0.0;
+            }
+            if (n_tok == 0)
+                continue;
+            double m = -INFINITY;
+            for (int64_t a = 0; a < n_tok; ++a) {
+                double dot = 0.0;
+                for (int e = 0; e < d; ++e)
+                    dot += dsa_oracle_bf16_value(q_th[e]) * dsa_oracle_bf16_value(k[tok[a] * d + e]);
+                P[a] = scale * dot;
+                if (P[a] > m)
+                    m = P[a];
+            }
+            double z = 0.0;
+            for (int64_t a = 0; a < n_tok; ++a)
+                z += exp(P[a] - m);
+            for (int64_t a = 0; a < n_tok; ++a)
+                P[a] = exp(P[a] - m) / z;
+            double D = 0.0;
+            for (int64_t a = 0; a < n_tok; ++a) {
+                double dp = 0.0;
+                for (int e = 0; e < dv; ++e)
+                    dp += dsa_oracle_bf16_value(do_th[e]) * dsa_oracle_bf16_value(v[tok[a] * dv + e]);
+                dS[a] = dp;  /* dP_j for now */
+                D += P[a] * dp;
+            }
+            for (int64_t a = 0; a < n_tok; ++a)
+                dS[a] = P[a] * (dS[a] - D);
+            double dabs = 0.0;
+            for (int e = 0; e < dv; ++e) {
+                double pv = 0.0;
+                for (int64_t a = 0; a < n_tok; ++a)
+                    pv += P[a] * fabs(dsa_oracle_bf16_value(v[tok[a] * dv + e]));
+                dabs += fabs(dsa_oracle_bf16_value(do_th[e])) * pv;
+            }
+            for (int64_t a = 0; a < n_tok; ++a)
+                M[a] = fabs(dS[a]) + P[a] * dabs;
+            for (int e = 0; e < d; ++e) {
+                double acc = 0.0, mag = 0.0;
+                for (int64_t a = 0; a < n_tok; ++a) {
+                    double kv = dsa_oracle_bf16_value(k[tok[a] * d + e]);
+                    acc += dS[a] * kv;
+                    mag += M[a] * fabs(kv);
+                }
+                dq_th[e] = scale * acc;
+                if (dq_mag)
+                    dq_mag[(r * h + hh) * d + e] = scale * mag;
+            }
+        }
+        /* key and value gradients: each element's sum runs over rows, then
+         * tokens, then heads, in that order; columns are independent */
+#pragma omp parallel for schedule(static)
+        for (int e = 0; e < d; ++e)
+            for (int64_t a = 0; a < n_tok; ++a)
+                for (int hh = 0; hh < h; ++hh) {
+                    double qv = dsa_oracle_bf16_value(q[(i * h + hh) * d + e]);
+                    dk[tok[a] * d + e] += scale * ds[(int64_t)hh * cap + a] * qv;
+                    if (dk_mag)
+                        dk_mag[tok[a] * d + e] += scale * mj[(int64_t)hh * cap + a] * fabs(qv);
+                }
+#pragma omp parallel for schedule(static)
+        for (int e = 0; e < dv; ++e)
+            for (int64_t a = 0; a < n_tok; ++a)
+                for (int hh = 0; hh < h; ++hh) {
+                    double g = dsa_oracle_bf16_value(dout[(i * h + hh) * dv + e]);
+                    dvv[tok[a] * dv + e] += pw[(int64_t)hh * cap + a] * g;
+                    if (dv_mag)
+                        dv_mag[tok[a] * dv + e] += pw[(int64_t)hh * cap + a] * fabs(g);
+                }
+    }
+    free(tok);
+    free(pw);
+    free(ds);
+    free(mj);
+    return rc;
 }
 
 /* Token count |T(t)| for each listed row given its idx row (used to size

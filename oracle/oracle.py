@@ -81,6 +81,10 @@ def _load():
         lib.dsa_oracle_sparse_attn.argtypes = [
             _ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _int, _int, _int, _int, _int, _int,
             ctypes.c_double, _ptr, _i64, _ptr, _ptr]
+        lib.dsa_oracle_sparse_attn_bwd.restype = _int
+        lib.dsa_oracle_sparse_attn_bwd.argtypes = [
+            _ptr, _ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _int, _int, _int, _int, _int, _int,
+            ctypes.c_double, _ptr, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr]
         lib.dsa_oracle_token_count.restype = _i64
         lib.dsa_oracle_token_count.argtypes = [_ptr, _i64, _i64, _int, _int, _int, _ptr, _i64]
         _lib = lib
@@ -283,6 +287,38 @@ def sparse_attn(q, k, v, idx_rows, k_pools: int, q_pos0: int = 0, rows=None, n_t
         _p(qb), _p(kb), _p(vb), _p(ix), s_q, s_k, q_pos0, h, d, dv, k_pools, pool, n_tail,
         float(scale), _p(r), len(r), _p(o), _p(lse)), "sparse_attn")
     return o, lse
+
+
+def sparse_attn_bwd(q, k, v, idx_rows, dout, k_pools: int, q_pos0: int = 0, rows=None,
+                    n_tail: int = 0, scale: float | None = None, pool: int = 4,
+                    magnitudes: bool = False):
+    """Gradients of ``sparse_attn`` for the loss sum(dout . o) over the listed
+    rows (dout of every other row taken as zero).
+
+    q [S_q, H, D], k [S_k, D], v [S_k, Dv], dout [S_q, H, Dv] bf16; idx_rows
+    int32 [len(rows), k_pools].  Returns dict with fp64 arrays dq
+    [len(rows), H, D], dk [S_k, D], dv [S_k, Dv] and, with magnitudes=True,
+    dq_mag, dk_mag, dv_mag of the same shapes (sums of absolute values the C
+    file defines)."""
+    qb, kb, vb, gb = _bits16(q), _bits16(k), _bits16(v), _bits16(dout)
+    s_q, h, d = qb.shape
+    s_k, dv = vb.shape
+    assert kb.shape == (s_k, d) and gb.shape == (s_q, h, dv)
+    r = _rows(rows, s_q)
+    ix = np.ascontiguousarray(np.asarray(idx_rows, dtype=np.int32))
+    assert ix.shape == (len(r), k_pools), (ix.shape, len(r), k_pools)
+    if scale is None:
+        scale = float(np.float32(1.0 / np.sqrt(d)))
+    out = {"dq": np.zeros((len(r), h, d)), "dk": np.zeros((s_k, d)), "dv": np.zeros((s_k, dv))}
+    if magnitudes:
+        out.update(dq_mag=np.zeros((len(r), h, d)), dk_mag=np.zeros((s_k, d)),
+                   dv_mag=np.zeros((s_k, dv)))
+    m = (lambda n: _p(out[n]) if magnitudes else None)
+    _check(_load().dsa_oracle_sparse_attn_bwd(
+        _p(qb), _p(kb), _p(vb), _p(ix), _p(gb), s_q, s_k, q_pos0, h, d, dv, k_pools, pool,
+        n_tail, float(scale), _p(r), len(r), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]),
+        m("dq_mag"), m("dk_mag"), m("dv_mag")), "sparse_attn_bwd")
+    return out
 
 
 def token_count(idx_rows, q_pos0: int, s_k: int, k_pools: int, rows, n_tail: int = 0,

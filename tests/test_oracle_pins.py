@@ -467,3 +467,193 @@ def test_unchunked_indexer_memory_matches_the_page():
         return 2 * 4 * s * (s // 4) * 32
     assert unchunked(32768) == 64 * 2 ** 30
     assert unchunked(131072) == 2 ** 40
+
+
+# ---------------------------------------------------------------- attention backward
+# The pages' setting is training (section "Activation Recompute" reruns each
+# layer's forward in the backward pass); the oracle's backward is the exact
+# gradient of its forward, pinned here against torch's float64 autograd of
+# masked dense attention, central finite differences and invariants.
+
+def _visible(t, row_ids, n_tail, s_k, pool=4):
+    """Key positions query t attends: the listed pools' tokens plus up to
+    n_tail tokens of its own pool before it."""
+    toks = [pool * p + u for p in row_ids if p >= 0 for u in range(pool)]
+    start = max((t // pool) * pool, t - n_tail)
+    toks += [j for j in range(start, t) if j < s_k]
+    return toks
+
+
+def _torch_grads(x, dout, idx, rows, q_pos0, n_tail, scale):
+    """float64 autograd of softmax attention with the visibility mask of each
+    listed row; rows that see no key have o = 0 and no gradient."""
+    q = x["q"].double()[rows].clone().requires_grad_(True)
+    k = x["k"].double().clone().requires_grad_(True)
+    v = x["v"].double().clone().requires_grad_(True)
+    s_k = k.shape[0]
+    mask = torch.zeros(len(rows), s_k, dtype=torch.bool)
+    for r, i in enumerate(rows):
+        mask[r, _visible(q_pos0 + int(i), idx[r], n_tail, s_k)] = True
+    live = mask.any(1)
+    lg = torch.einsum("rhd,jd->rhj", q, k) * scale
+    lg = lg.masked_fill(~mask[:, None, :], float("-inf"))
+    lg = torch.where(live[:, None, None], lg, torch.zeros_like(lg))
+    o = torch.softmax(lg, dim=-1) @ v
+    o = torch.where(live[:, None, None], o, torch.zeros_like(o))
+    (o * dout.double()[rows]).sum().backward()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+def _random_idx(rng, rows, q_pos0, n_pools, k_pools):
+    idx = np.full((len(rows), k_pools), -1, dtype=np.int32)
+    for r, i in enumerate(rows):
+        n = min((q_pos0 + int(i)) // 4, n_pools)
+        m = min(n, k_pools)
+        idx[r, :m] = np.sort(rng.choice(n, size=m, replace=False))
+    return idx
+
+
+@pytest.mark.parametrize("n_tail", [0, 3])
+def test_attention_backward_with_every_pool_equals_dense_autograd(n_tail):
+    # k >= P: the selection is every earlier pool, so T(t) is dense causal
+    # attention (strictly before t with n_tail = 3)
+    wl, x = _attn_case(61, h=3, d=32, dv=24, seed=11)
+    dout = inputs.make_dout(wl, seed=11)
+    P = wl.n_pools
+    rows = np.arange(wl.s_q)
+    idx = np.full((len(rows), P), -1, dtype=np.int32)
+    for r in rows:
+        idx[r, :min(r // 4, P)] = np.arange(min(r // 4, P))
+    scale = 0.2
+    g = oracle.sparse_attn_bwd(x["q"], x["k"], x["v"], idx, dout, P, rows=rows, n_tail=n_tail,
+                               scale=scale)
+    dq, dk, dv = _torch_grads(x, dout, idx, rows, 0, n_tail, scale)
+    np.testing.assert_allclose(g["dq"], dq, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(g["dk"], dk, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(g["dv"], dv, rtol=0, atol=1e-11)
+    assert np.abs(dk).max() > 0.1 and np.abs(dq).max() > 0.1
+
+
+@pytest.mark.parametrize("n_tail,q_pos0", [(0, 0), (2, 13), (1, 40)])
+def test_attention_backward_sparse_selection_matches_autograd(n_tail, q_pos0):
+    wl, x = _attn_case(97, h=2, d=16, dv=40, q_pos0=q_pos0, seed=12 + q_pos0)
+    dout = inputs.make_dout(wl, seed=5)
+    rng = np.random.default_rng(q_pos0)
+    rows = np.arange(wl.s_q)
+    idx = _random_idx(rng, rows, q_pos0, wl.n_pools, 5)
+    g = oracle.sparse_attn_bwd(x["q"], x["k"], x["v"], idx, dout, 5, q_pos0=q_pos0, rows=rows,
+                               n_tail=n_tail, scale=0.3)
+    dq, dk, dv = _torch_grads(x, dout, idx, rows, q_pos0, n_tail, 0.3)
+    np.testing.assert_allclose(g["dq"], dq, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(g["dk"], dk, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(g["dv"], dv, rtol=0, atol=1e-11)
+
+
+def test_attention_backward_central_differences():
+    # the gradient of L = sum dout . o against the function's own values,
+    # o evaluated in float64 by a direct softmax over the visible keys
+    wl, x = _attn_case(24, h=2, d=8, dv=6, seed=13)
+    dout = inputs.make_dout(wl, seed=13)
+    rows = np.array([9, 14, 23])
+    idx = np.array([[0, -1], [0, 2], [1, 4]], dtype=np.int32)
+    scale, n_tail = 0.5, 3
+    g = oracle.sparse_attn_bwd(x["q"], x["k"], x["v"], idx, dout, 2, rows=rows, n_tail=n_tail,
+                               scale=scale)
+    q0, k0, v0 = (x[n].double().numpy() for n in ("q", "k", "v"))
+    do = dout.double().numpy()
+
+    def loss(q, k, v):
+        tot = 0.0
+        for r, i in enumerate(rows):
+            toks = _visible(int(i), idx[r], n_tail, k.shape[0])
+            for hh in range(q.shape[1]):
+                lg = scale * (k[toks] @ q[i, hh])
+                p = np.exp(lg - lg.max())
+                tot += do[i, hh] @ (p @ v[toks] / p.sum())
+        return tot
+
+    eps = 1e-6
+    rng = np.random.default_rng(0)
+    for name, arr, grad, sel in (
+            ("q", q0, g["dq"], None), ("k", k0, g["dk"], None), ("v", v0, g["dv"], None)):
+        for _ in range(12):
+            if name == "q":
+                r = int(rng.integers(len(rows)))
+                pos = (int(rows[r]), int(rng.integers(2)), int(rng.integers(8)))
+                gpos = (r,) + pos[1:]
+            else:
+                j = int(rng.choice(_visible(int(rows[-1]), idx[-1], n_tail, 24)))
+                pos = (j, int(rng.integers(arr.shape[1])))
+                gpos = pos
+            hi, lo = arr.copy(), arr.copy()
+            hi[pos] += eps
+            lo[pos] -= eps
+            args_hi = {"q": (hi, k0, v0), "k": (q0, hi, v0), "v": (q0, k0, hi)}[name]
+            args_lo = {"q": (lo, k0, v0), "k": (q0, lo, v0), "v": (q0, k0, lo)}[name]
+            fd = (loss(*args_hi) - loss(*args_lo)) / (2 * eps)
+            assert abs(fd - grad[gpos]) <= 1e-7 * max(1.0, abs(fd)), (name, pos, fd, grad[gpos])
+
+
+def test_attention_backward_invariants():
+    wl, x = _attn_case(130, h=4, d=32, dv=32, seed=14)
+    dout = inputs.make_dout(wl, seed=14)
+    rng = np.random.default_rng(3)
+    rows = np.arange(wl.s_q)
+    idx = _random_idx(rng, rows, 0, wl.n_pools, 6)
+    g = oracle.sparse_attn_bwd(x["q"], x["k"], x["v"], idx, dout, 6, rows=rows, n_tail=3,
+                               scale=0.25, magnitudes=True)
+    do = dout.double().numpy()
+    # the softmax weights of each (row, head) sum to 1: sum_j dv[j] = sum of dout
+    # over the rows that see any key (row 0 sees none)
+    np.testing.assert_allclose(g["dv"].sum(0), do[1:].sum((0, 1)), rtol=0, atol=1e-10)
+    # sum_j dS_j = 0 for every (row, head): the key gradients sum to zero
+    np.testing.assert_allclose(g["dk"].sum(0), 0.0, rtol=0, atol=1e-10)
+    # row 0 sees nothing: no query gradient
+    assert np.all(g["dq"][0] == 0)
+    # the magnitudes bound the values
+    for n in ("dq", "dk", "dv"):
+        assert np.all(np.abs(g[n]) <= g[n + "_mag"] * (1 + 1e-12) + 1e-300)
+    assert g["dq_mag"].max() > 0 and g["dk_mag"].max() > 0
+
+
+def test_attention_backward_single_key_closed_form():
+    # one visible key: the softmax weight is 1 whatever the logit, so dq = 0,
+    # dk = 0, and dv of that key is the sum of dout over the heads
+    wl, x = _attn_case(16, h=3, d=8, dv=8, seed=15)
+    dout = inputs.make_dout(wl, seed=15)
+    rows = [1, 5]                         # t = 1: tail {0}; t = 5: tail {4}
+    idx = np.full((2, 1), -1, dtype=np.int32)
+    g = oracle.sparse_attn_bwd(x["q"], x["k"], x["v"], idx, dout, 1, rows=rows, n_tail=1,
+                               scale=0.5)
+    do = dout.double().numpy()
+    assert np.all(g["dq"] == 0) and np.all(g["dk"] == 0)
+    np.testing.assert_allclose(g["dv"][0], do[1].sum(0), rtol=1e-15)
+    np.testing.assert_allclose(g["dv"][4], do[5].sum(0), rtol=1e-15)
+    assert np.all(g["dv"][[1, 2, 3] + list(range(5, 16))] == 0)
+
+
+def test_attention_backward_listed_rows_equal_zero_dout_elsewhere():
+    wl, x = _attn_case(80, h=2, d=16, seed=16)
+    dout = inputs.make_dout(wl, seed=16)
+    rng = np.random.default_rng(4)
+    rows = np.arange(wl.s_q)
+    idx = _random_idx(rng, rows, 0, wl.n_pools, 4)
+    pick = np.array([7, 30, 31, 79])
+    part = oracle.sparse_attn_bwd(x["q"], x["k"], x["v"], idx[pick], dout, 4, rows=pick,
+                                  n_tail=2)
+    d0 = torch.zeros_like(dout)
+    d0[pick] = dout[pick]
+    full = oracle.sparse_attn_bwd(x["q"], x["k"], x["v"], idx, d0, 4, rows=rows, n_tail=2)
+    np.testing.assert_array_equal(part["dq"], full["dq"][pick])
+    np.testing.assert_array_equal(part["dk"], full["dk"])
+    np.testing.assert_array_equal(part["dv"], full["dv"])
+    assert np.all(full["dq"][np.setdiff1d(rows, pick)] == 0)
+
+
+def test_attention_backward_rejects_malformed_rows():
+    wl, x = _attn_case(64, seed=17)
+    dout = inputs.make_dout(wl, seed=17)
+    for bad in ([3, 1, -1, -1], [0, 0, -1, -1], [0, 15, -1, -1]):
+        with pytest.raises(RuntimeError):
+            oracle.sparse_attn_bwd(x["q"], x["k"], x["v"], np.array([bad], dtype=np.int32),
+                                   dout, 4, rows=[60])
