@@ -193,11 +193,58 @@ dsa_status dsa_sparse_attn_fwd(const void *q, const void *k, const void *v, cons
                                void *out, float *lse, void *stream);
 
 /*
+ * Bytes of device workspace dsa_sparse_attn_bwd needs: delta = dout . out
+ * per query and head (fp32 [s_q, h], rounded up to 256 bytes), then the
+ * bitmap that transposes one chunk of queries' selections,
+ * ceil(s_k / 4) x chunk_q / 32 32-bit words.  chunk_q = 0 picks the default
+ * (min(16384, s_q rounded up to 64)), returned through *chunk_q_used when
+ * that pointer is non-NULL; otherwise a multiple of 64 up to 65536 whose
+ * bitmap stays within 2 GiB.  Pure host computation.
+ */
+dsa_status dsa_sparse_attn_bwd_workspace_size(int64_t s_q, int64_t s_k, int h, int64_t chunk_q,
+                                              size_t *bytes, int64_t *chunk_q_used);
+
+/*
+ * Backward of dsa_sparse_attn_fwd (the pages' setting is training: section
+ * "Activation Recompute" reruns the forward inside the backward pass, so the
+ * softmax weights are recomputed from the forward's lse rather than stored).
+ * Gradients of L = sum dout . out, per query row, head h and attended token j:
+ *     D_h  = dout_h . out_h,   P_j = exp(scale q_h . k_j - lse_h),
+ *     dS_j = P_j (dout_h . v_j - D_h),
+ *     dq_h = scale sum_j dS_j k_j,  dk_j += scale dS_j q_h,  dv_j += P_j dout_h.
+ *   q, k, v, idx, s_q .. softmax_scale   as passed to dsa_sparse_attn_fwd;
+ *                      every valid id of an idx row must be distinct (as
+ *                      dsa_index_score_topk produces them), else the
+ *                      gradients are unspecified
+ *   out  [s_q, h, dv]  bf16, the forward's output
+ *   dout [s_q, h, dv]  bf16, the gradient of L with respect to out
+ *   lse  [s_q, h]      fp32, the forward's lse (required)
+ *   chunk_q            queries per transposition chunk (0 = default)
+ *   dq      [s_q, h, d]  fp32 output
+ *   dk      [s_k, d]     fp32 output (every row written; 0 where no query
+ *                        attends)
+ *   dv_grad [s_k, dv]    fp32 output
+ *   workspace          >= dsa_sparse_attn_bwd_workspace_size(...) bytes
+ * The key and value gradients are sums over the queries that attend each
+ * token; they are formed one chunk of queries at a time, each token's sum in
+ * increasing query order, so the results are deterministic.  The products
+ * that feed the matrix cores take P and dS rounded to bf16; everything else
+ * is fp32.  Supported shapes are those of dsa_sparse_attn_fwd.
+ */
+dsa_status dsa_sparse_attn_bwd(const void *q, const void *k, const void *v, const int32_t *idx,
+                               const void *out, const void *dout, const float *lse, int64_t s_q,
+                               int64_t s_k, int64_t q_pos0, int h, int d, int dv, int k_pools,
+                               int pool_size, int n_tail, float softmax_scale, int64_t chunk_q,
+                               float *dq, float *dk, float *dv_grad, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * Per-kernel GPU timing.  While enabled, every kernel launch is bracketed
  * by HIP events on its own stream; dsa_profile_read synchronises on those
  * events and reports, per kernel kind, the number of launches and the summed
  * duration in milliseconds, then clears the record.  Kinds: "pool_keys",
- * "pack_queries", "index_score", "topk_select", "sparse_attn".
+ * "pack_queries", "index_score", "topk_select", "sparse_attn",
+ * "attn_bwd_dq", "attn_bwd_select", "attn_bwd_dkv".
  */
 typedef struct {
     char name[32];

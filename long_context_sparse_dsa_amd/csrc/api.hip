@@ -40,9 +40,12 @@ constexpr int64_t kScoreBufferCap = int64_t(2) << 30;  // per chunk, as the page
 
 // ------------------------------------------------------------ profiling
 
-enum Kind { K_POOL = 0, K_PACK, K_SCORE, K_SELECT, K_ATTN, K_COUNT };
+enum Kind {
+    K_POOL = 0, K_PACK, K_SCORE, K_SELECT, K_ATTN, K_BWD_DQ, K_BWD_BITS, K_BWD_DKV, K_COUNT
+};
 const char* kKindName[K_COUNT] = {"pool_keys", "pack_queries", "index_score", "topk_select",
-                                  "sparse_attn"};
+                                  "sparse_attn", "attn_bwd_dq", "attn_bwd_select",
+                                  "attn_bwd_dkv"};
 
 struct Rec {
     int kind;
@@ -258,6 +261,54 @@ void fill_score_args(dsa::ScoreArgs& a, const IndexShape& sh, const Layout& L,
     a.h_idx = sh.h_idx;
     a.d_idx = sh.d_idx;
     a.fp8 = sh.dtype == DSA_FP8_E4M3;
+}
+
+// Shape checks shared by the attention forward and backward.
+dsa_status check_attn_shape(int64_t s_q, int64_t s_k, int64_t q_pos0, int h, int d, int dv,
+                            int k_pools, int pool_size, int n_tail, float softmax_scale) {
+    if (s_q < 0 || s_k < 0 || q_pos0 < 0)
+        return fail(DSA_ERR_INVALID_ARG, "negative size or position");
+    if (s_k >= (int64_t(1) << 31) || s_q >= (int64_t(1) << 31))
+        return fail(DSA_ERR_UNSUPPORTED, "s_q and s_k must be below 2^31");
+    if (pool_size != 4) return fail(DSA_ERR_UNSUPPORTED, "pool_size %d: only 4 is supported", pool_size);
+    if (h < 1 || h > 16)
+        return fail(DSA_ERR_UNSUPPORTED, "h %d: 1..16 query heads per key/value head", h);
+    if ((d != 64 && d != 96 && d != 128) || (dv != 64 && dv != 96 && dv != 128))
+        return fail(DSA_ERR_UNSUPPORTED, "d %d / dv %d: supported head dims are 64, 96, 128", d, dv);
+    if (k_pools < 1 || k_pools > kMaxKPools)
+        return fail(DSA_ERR_UNSUPPORTED, "k_pools %d: supported range is 1..%lld", k_pools,
+                    (long long)kMaxKPools);
+    if (n_tail < 0 || n_tail >= pool_size)
+        return fail(DSA_ERR_INVALID_ARG, "n_tail %d outside 0..%d", n_tail, pool_size - 1);
+    if (!(softmax_scale == softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "softmax_scale is NaN");
+    return DSA_OK;
+}
+
+// Backward: queries per transposition chunk (a multiple of 64), and the
+// workspace: delta [s_q, h] fp32, then the chunk bitmap
+// [ceil(s_k / 4)][chunk / 32] words.
+constexpr int64_t kBwdChunkDefault = 16384;
+constexpr int64_t kBwdBitmapCap = int64_t(2) << 30;
+
+dsa_status bwd_layout(int64_t s_q, int64_t s_k, int h, int64_t chunk_q, int64_t* chunk_used,
+                      int64_t* delta_bytes, int64_t* bits_bytes) {
+    if (chunk_q < 0) return fail(DSA_ERR_INVALID_ARG, "chunk_q %lld < 0", (long long)chunk_q);
+    if (chunk_q == 0) {
+        chunk_q = round_up(s_q > 0 ? s_q : 1, 64);
+        if (chunk_q > kBwdChunkDefault) chunk_q = kBwdChunkDefault;
+    }
+    if (chunk_q % 64 != 0 || chunk_q > kMaxChunk)
+        return fail(DSA_ERR_UNSUPPORTED, "chunk_q %lld: must be a multiple of 64 up to %lld",
+                    (long long)chunk_q, (long long)kMaxChunk);
+    const int64_t slots = (s_k + 3) / 4;
+    const int64_t bits = slots * (chunk_q / 32) * 4;
+    if (bits > kBwdBitmapCap)
+        return fail(DSA_ERR_UNSUPPORTED, "chunk_q %lld: the chunk bitmap (%lld bytes) exceeds 2 GiB",
+                    (long long)chunk_q, (long long)bits);
+    *chunk_used = chunk_q;
+    *delta_bytes = round_up(s_q * h * 4, 256);
+    *bits_bytes = bits;
+    return DSA_OK;
 }
 
 }  // namespace
@@ -479,21 +530,9 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
                                int k_pools, int pool_size, int n_tail, float softmax_scale,
                                void* out, float* lse, void* stream) {
     g_err[0] = 0;
-    if (s_q < 0 || s_k < 0 || q_pos0 < 0)
-        return fail(DSA_ERR_INVALID_ARG, "negative size or position");
-    if (s_k >= (int64_t(1) << 31) || s_q >= (int64_t(1) << 31))
-        return fail(DSA_ERR_UNSUPPORTED, "s_q and s_k must be below 2^31");
-    if (pool_size != 4) return fail(DSA_ERR_UNSUPPORTED, "pool_size %d: only 4 is supported", pool_size);
-    if (h < 1 || h > 16)
-        return fail(DSA_ERR_UNSUPPORTED, "h %d: 1..16 query heads per key/value head", h);
-    if ((d != 64 && d != 96 && d != 128) || (dv != 64 && dv != 96 && dv != 128))
-        return fail(DSA_ERR_UNSUPPORTED, "d %d / dv %d: supported head dims are 64, 96, 128", d, dv);
-    if (k_pools < 1 || k_pools > kMaxKPools)
-        return fail(DSA_ERR_UNSUPPORTED, "k_pools %d: supported range is 1..%lld", k_pools,
-                    (long long)kMaxKPools);
-    if (n_tail < 0 || n_tail >= pool_size)
-        return fail(DSA_ERR_INVALID_ARG, "n_tail %d outside 0..%d", n_tail, pool_size - 1);
-    if (!(softmax_scale == softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "softmax_scale is NaN");
+    dsa_status st = check_attn_shape(s_q, s_k, q_pos0, h, d, dv, k_pools, pool_size, n_tail,
+                                     softmax_scale);
+    if (st != DSA_OK) return st;
     if (s_q > 0 && (!q || !idx || !out))
         return fail(DSA_ERR_INVALID_ARG, "q, idx and out must be non-null");
     if (s_k > 0 && s_q > 0 && (!k || !v)) return fail(DSA_ERR_INVALID_ARG, "k and v must be non-null");
@@ -522,6 +561,98 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
     Timed tm(K_ATTN, s);
     hipError_t e = dsa::launch_sparse_attn(a, s);
     if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
+    return DSA_OK;
+}
+
+dsa_status dsa_sparse_attn_bwd_workspace_size(int64_t s_q, int64_t s_k, int h, int64_t chunk_q,
+                                              size_t* bytes, int64_t* chunk_q_used) {
+    g_err[0] = 0;
+    if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes must be non-null");
+    if (s_q < 0 || s_k < 0) return fail(DSA_ERR_INVALID_ARG, "negative size");
+    if (h < 1 || h > 16)
+        return fail(DSA_ERR_UNSUPPORTED, "h %d: 1..16 query heads per key/value head", h);
+    int64_t cq, db, bb;
+    dsa_status st = bwd_layout(s_q, s_k, h, chunk_q, &cq, &db, &bb);
+    if (st != DSA_OK) return st;
+    *bytes = (size_t)(db + bb);
+    if (chunk_q_used) *chunk_q_used = cq;
+    return DSA_OK;
+}
+
+dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const int32_t* idx,
+                               const void* out, const void* dout, const float* lse, int64_t s_q,
+                               int64_t s_k, int64_t q_pos0, int h, int d, int dv, int k_pools,
+                               int pool_size, int n_tail, float softmax_scale, int64_t chunk_q,
+                               float* dq, float* dk, float* dv_grad, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    dsa_status st = check_attn_shape(s_q, s_k, q_pos0, h, d, dv, k_pools, pool_size, n_tail,
+                                     softmax_scale);
+    if (st != DSA_OK) return st;
+    if (s_q > 0 && (!q || !idx || !out || !dout || !lse || !dq))
+        return fail(DSA_ERR_INVALID_ARG, "q, idx, out, dout, lse and dq must be non-null");
+    if (s_k > 0 && (!dk || !dv_grad)) return fail(DSA_ERR_INVALID_ARG, "dk and dv must be non-null");
+    if (s_k > 0 && s_q > 0 && (!k || !v)) return fail(DSA_ERR_INVALID_ARG, "k and v must be non-null");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(idx) || !aligned16(out) ||
+        !aligned16(dout) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv_grad) || !aligned16(workspace))
+        return fail(DSA_ERR_INVALID_ARG, "all buffers must be 16-byte aligned");
+    int64_t cq, db, bb;
+    st = bwd_layout(s_q, s_k, h, chunk_q, &cq, &db, &bb);
+    if (st != DSA_OK) return st;
+    if (s_q > 0 && (!workspace || workspace_bytes < (size_t)(db + bb)))
+        return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %lld needed",
+                    workspace_bytes, (long long)(db + bb));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (s_q == 0) {
+        // no query: the key and value gradients are zero
+        hipError_t e = dsa::launch_fill_f32(dk, s_k * d, 0.0f, s);
+        if (e == hipSuccess) e = dsa::launch_fill_f32(dv_grad, s_k * dv, 0.0f, s);
+        if (e != hipSuccess) return hip_fail(e, "fill launch");
+        return DSA_OK;
+    }
+    dsa::AttnBwdArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.out = static_cast<const uint16_t*>(out);
+    a.dout = static_cast<const uint16_t*>(dout);
+    a.idx = idx;
+    a.lse = lse;
+    a.s_q = s_q;
+    a.s_k = s_k;
+    a.q_pos0 = q_pos0;
+    a.h = h;
+    a.d = d;
+    a.dv = dv;
+    a.k_pools = k_pools;
+    a.n_tail = n_tail;
+    a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)d);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv_grad = dv_grad;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    a.delta = reinterpret_cast<float*>(ws);
+    a.bits = reinterpret_cast<uint32_t*>(ws + db);
+    a.words = cq / 32;
+    {
+        Timed tm(K_BWD_DQ, s);
+        hipError_t e = dsa::launch_attn_bwd_dq(a, s);
+        if (e != hipSuccess) return hip_fail(e, "attn_bwd_dq launch");
+    }
+    if (s_k == 0) return DSA_OK;
+    for (int64_t r0 = 0, c = 0; r0 < s_q; r0 += cq, ++c) {
+        const int rows = (int)(s_q - r0 < cq ? s_q - r0 : cq);
+        {
+            Timed tm(K_BWD_BITS, s);
+            hipError_t e = dsa::launch_fill_f32(reinterpret_cast<float*>(a.bits), bb / 4, 0.0f, s);
+            if (e == hipSuccess) e = dsa::launch_attn_bwd_bits(a, r0, rows, s);
+            if (e != hipSuccess) return hip_fail(e, "attn_bwd_select launch");
+        }
+        Timed tm(K_BWD_DKV, s);
+        hipError_t e = dsa::launch_attn_bwd_dkv(a, r0, rows, c > 0 ? 1 : 0, s);
+        if (e != hipSuccess) return hip_fail(e, "attn_bwd_dkv launch");
+    }
     return DSA_OK;
 }
 

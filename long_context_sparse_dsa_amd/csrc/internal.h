@@ -111,4 +111,30 @@ struct AttnArgs {
 };
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
 
+struct AttnBwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* out;      // forward output [s_q, h, dv]
+    const uint16_t* dout;     // its gradient [s_q, h, dv]
+    const int32_t* idx;
+    const float* lse;         // forward log-sum-exp [s_q, h]
+    int64_t s_q, s_k, q_pos0;
+    int h, d, dv, k_pools, n_tail;
+    float scale;
+    float* dq;                // [s_q, h, d]
+    float* dk;                // [s_k, d]
+    float* dv_grad;           // [s_k, dv]
+    float* delta;             // workspace: dout . out per query and head [s_q, h]
+    uint32_t* bits;           // workspace: chunk bitmap [ceil(s_k / 4)][words]
+    int64_t words;            // words per bitmap row (chunk queries / 32)
+};
+// dq and delta (query-major pass).
+hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t stream);
+// ORs the selections of query rows [row0, row0 + rows) into a cleared bitmap.
+hipError_t launch_attn_bwd_bits(const AttnBwdArgs& a, int64_t row0, int rows, hipStream_t stream);
+// dk, dv of the chunk's queries: stored (accumulate = 0) or added.
+hipError_t launch_attn_bwd_dkv(const AttnBwdArgs& a, int64_t row0, int rows, int accumulate,
+                               hipStream_t stream);
+
 }  // namespace dsa

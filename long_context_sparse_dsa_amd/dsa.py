@@ -82,6 +82,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dsa_sparse_attn_fwd.argtypes = [
             _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int, _int, _int, _f, _vp,
             _vp, _vp]
+        lib.dsa_sparse_attn_bwd_workspace_size.restype = _int
+        lib.dsa_sparse_attn_bwd_workspace_size.argtypes = [
+            _i64, _i64, _int, _i64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(_i64)]
+        lib.dsa_sparse_attn_bwd.restype = _int
+        lib.dsa_sparse_attn_bwd.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int, _int,
+            _int, ctypes.c_float, _i64, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         lib.dsa_profile_enable.restype = _int
         lib.dsa_profile_enable.argtypes = [_int]
         lib.dsa_profile_read.restype = _int
@@ -288,6 +295,55 @@ def dsa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: 
     return out, lse
 
 
+def dsa_sparse_attn_bwd_workspace_size(s_q: int, s_k: int, h: int, chunk_q: int = 0):
+    """(bytes, chunk_q used) of the backward's workspace."""
+    nb = ctypes.c_size_t(0)
+    cq = _i64(0)
+    _check(load_library().dsa_sparse_attn_bwd_workspace_size(s_q, s_k, h, chunk_q,
+                                                              ctypes.byref(nb), ctypes.byref(cq)))
+    return nb.value, cq.value
+
+
+def dsa_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                        out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, *,
+                        q_pos0: int = 0, n_tail: int = 0, softmax_scale: float = 0.0,
+                        chunk_q: int = 0, dq: torch.Tensor | None = None,
+                        dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None):
+    """Gradients of the attention over the kept pools for the upstream
+    gradient dout.  Returns (dq [S_q,H,D], dk [S_k,D], dv [S_k,Dv]), fp32."""
+    lib = load_library()
+    _need(q.dim() == 3 and k.dim() == 2 and v.dim() == 2 and idx.dim() == 2,
+          "q [S_q,H,D], k [S_k,D], v [S_k,Dv], idx [S_q,k_pools]")
+    _need(q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype == torch.bfloat16,
+          "q, k, v, out, dout must be bfloat16")
+    _need(idx.dtype == torch.int32 and lse.dtype == torch.float32, "idx int32, lse fp32")
+    _need(all(t.is_contiguous() for t in (q, k, v, idx, out, dout, lse)),
+          "inputs must be contiguous")
+    s_q, h, d = q.shape
+    s_k, dvd = v.shape
+    _need(k.shape == (s_k, d), "k must be [S_k, D]")
+    _need(idx.shape[0] == s_q, "idx must have one row per query")
+    _need(out.shape == (s_q, h, dvd) and dout.shape == out.shape, "out, dout [S_q, H, Dv]")
+    _need(lse.shape == (s_q, h), "lse [S_q, H]")
+    k_pools = idx.shape[1]
+    dev = q.device
+    if dq is None:
+        dq = torch.empty((s_q, h, d), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty((s_k, d), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty((s_k, dvd), dtype=torch.float32, device=dev)
+    nbytes, _ = dsa_sparse_attn_bwd_workspace_size(s_q, s_k, h, chunk_q)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.dsa_sparse_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out), _ptr(dout), _ptr(lse), s_q, s_k,
+        q_pos0, h, d, dvd, k_pools, 4, n_tail, float(softmax_scale), chunk_q, _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dk, dv
+
+
 def dsa_profile_enable(on: bool = True):
     _check(load_library().dsa_profile_enable(1 if on else 0))
 
@@ -295,7 +351,7 @@ def dsa_profile_enable(on: bool = True):
 def dsa_profile_read() -> dict:
     """{kernel kind: (launches, total_ms)} since the last read."""
     lib = load_library()
-    arr = (KernelStat * 8)()
+    arr = (KernelStat * 16)()
     n = _int(0)
-    _check(lib.dsa_profile_read(arr, 8, ctypes.byref(n)))
+    _check(lib.dsa_profile_read(arr, 16, ctypes.byref(n)))
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}

@@ -13,6 +13,16 @@ Scores: |s_gpu - s_ref| <= 1e-2 |s_ref| + 1e-4 max_p |s_ref(t, p)| per row.
 Attention (oracle fed the GPU's ids): |o_gpu - o_ref| <= 2e-2 and
 |lse_gpu - lse_ref| <= 2e-2, absolute, for bf16 inputs/outputs with fp32
 accumulation on the GPU.
+Attention backward (no tolerance is given by the pages; this one follows
+from the arithmetic): every gradient element is a sum of terms
+c_a * x_a (dS_a k_a, dS_a q, P_a dout), and the GPU rounds P_a and dS_a to
+bf16 for the matrix cores (relative 2^-9) and takes D from the stored bf16
+forward output, whose error is at most 2^-8 sum_a P_a |v_a| per element, so
+|dD| <= 2^-8 Dabs.  Each term's error is then at most 2^-8 m_a |x_a| with
+m_a = |dS_a| + P_a Dabs (the oracle's magnitude sums), and fp32 summation
+over the chains the kernels use (at most a few thousand partial sums) adds
+far less than another 2^-8.  The bound is
+    |g_gpu - g_ref| <= 2^-6 * mag   elementwise,  and g_gpu == 0 where mag == 0.
 """
 from __future__ import annotations
 
@@ -95,3 +105,22 @@ def check_attention(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray,
         else np.zeros(1)
     assert err_l.max() <= ATTN_ABS, f"lse error {err_l.max()}"
     return float(err_o.max()), float(err_l.max())
+
+
+BWD_MAG_REL = 2.0 ** -6
+
+
+def check_grad(name: str, gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray) -> float:
+    """Returns the worst error relative to the bound (<= 1 passes)."""
+    g = gpu.astype(np.float64)
+    err = np.abs(g - ref)
+    zero = mag == 0
+    assert np.all(g[zero] == 0), f"{name}: nonzero where no term contributes"
+    bound = BWD_MAG_REL * mag
+    ratio = np.where(zero, 0.0, err / np.where(zero, 1.0, bound))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    if worst > 1.0:
+        i = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+        raise AssertionError(f"{name}: error {err[i]:.3g} at {i} beyond the bound {bound[i]:.3g} "
+                             f"(gpu {g[i]:.6g}, ref {ref[i]:.6g})")
+    return worst

@@ -193,3 +193,51 @@ def test_gated_entry_points_check_the_gate(lib):
 
 def test_profile_read_empty(lib):
     assert dsa.dsa_profile_read() == {}
+
+
+def _call_bwd(lib, **over):
+    a = dict(q=0x1000, k=0x2000, v=0x3000, idx=0x4000, out=0x5000, dout=0x6000, lse=0x7000,
+             s_q=16, s_k=64, q_pos0=0, h=16, d=128, dv=128, k_pools=8, pool=4, n_tail=0,
+             scale=0.0, chunk=0, dq=0x8000, dk=0x9000, dv_grad=0xA000, ws=0xB000,
+             ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return lib.dsa_sparse_attn_bwd(
+        a["q"], a["k"], a["v"], a["idx"], a["out"], a["dout"], a["lse"], a["s_q"], a["s_k"],
+        a["q_pos0"], a["h"], a["d"], a["dv"], a["k_pools"], a["pool"], a["n_tail"], a["scale"],
+        a["chunk"], a["dq"], a["dk"], a["dv_grad"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(h=17), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(d=80), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(n_tail=4), dsa.DSA_ERR_INVALID_ARG),
+    (dict(lse=None), dsa.DSA_ERR_INVALID_ARG),        # the forward's lse is required
+    (dict(dout=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(dk=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(dq=0x8004), dsa.DSA_ERR_INVALID_ARG),       # misaligned
+    (dict(chunk=100), dsa.DSA_ERR_UNSUPPORTED),       # not a multiple of 64
+    (dict(chunk=-64), dsa.DSA_ERR_INVALID_ARG),
+    (dict(ws=None), dsa.DSA_ERR_WORKSPACE),
+    (dict(ws_bytes=100), dsa.DSA_ERR_WORKSPACE),
+])
+def test_sparse_attn_bwd_rejects_before_launch(lib, over, status):
+    assert _call_bwd(lib, **over) == status
+    assert lib.dsa_last_error().decode() != ""
+
+
+def test_sparse_attn_bwd_workspace_layout(lib):
+    # delta [s_q, h] fp32 rounded to 256 B, then the chunk bitmap
+    # ceil(s_k / 4) rows x chunk / 32 words
+    nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(131072, 131072, 16)
+    assert cq == 16384
+    assert nbytes == 131072 * 16 * 4 + 32768 * 512 * 4
+    nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(100, 203, 5, 64)
+    assert cq == 64 and nbytes == 2048 + 51 * 2 * 4
+    nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(100, 203, 5)
+    assert cq == 128
+    # one GPU's share of 1M keys: 262144 pool rows; 65536 queries per chunk
+    # would need a 2 GiB bitmap, which is the cap
+    dsa.dsa_sparse_attn_bwd_workspace_size(131072, 1 << 20, 16, 65536)
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.dsa_sparse_attn_bwd_workspace_size(131072, (1 << 20) + 4, 16, 65536)
+    assert e.value.status == dsa.DSA_ERR_UNSUPPORTED
