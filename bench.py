@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "DSA fwd queries/sec at S=128k (indexer+topk+attn); TFLOP/s vs MFMA peak"
 
@@ -37,6 +38,8 @@ KERNEL_SOURCES = {
     "topk_select": ["topk_select.hip", "common.h"],
     "sparse_attn": ["sparse_attn.hip", "common.h"],
     "pool_keys": ["index_score.hip", "common.h"],
+    "attn_bwd_dq": ["sparse_attn_bwd.hip", "common.h"],
+    "attn_bwd_dkv": ["sparse_attn_bwd.hip", "common.h"],
 }
 
 
@@ -96,19 +99,33 @@ def work_counts(wl):
               + wl.s_q * wl.k_pools * 4)
     b_select = pairs * 4 + wl.s_q * wl.k_pools * 4
     b_pool = wl.n_pools * 4 * wl.d_idx * 2 + wl.n_pools * 4 * wl.d_idx * 2
+    # attention backward, per token visit: the query-major pass recomputes
+    # S = q k^T and dP = dout v^T and forms dq += dS k; the key-major pass
+    # recomputes S and dP and forms dk += dS^T q and dv += P^T dout
+    f_bwd_dq = 2.0 * wl.h * (2 * wl.d + wl.dv) * tokens
+    f_bwd_dkv = 2.0 * wl.h * (2 * wl.d + 2 * wl.dv) * tokens
+    # query-major pass bytes: the gathered key and value rows, q, out, dout,
+    # lse, ids, and dq written in fp32
+    b_bwd_dq = (tokens * (wl.d + wl.dv) * 2 + wl.s_q * wl.h * (wl.d + 2 * wl.dv) * 2
+                + wl.s_q * wl.h * 4 + wl.s_q * wl.k_pools * 4 + wl.s_q * wl.h * wl.d * 4)
     return dict(pairs=pairs, tokens=tokens, f_score=f_score, f_attn=f_attn, b_attn=b_attn,
-                b_select=b_select, b_pool=b_pool)
+                b_select=b_select, b_pool=b_pool, f_bwd_dq=f_bwd_dq, f_bwd_dkv=f_bwd_dkv,
+                b_bwd_dq=b_bwd_dq)
 
 
-def cpu_baseline(wl, x, target_s: float, gate=None):
+def cpu_baseline(wl, x, target_s: float, gate=None, fp8=False):
     """The oracle as it stands, on a strided sample of query rows."""
     from oracle import oracle
     threads = os.cpu_count() or 1
 
     def run(rows):
         t0 = time.perf_counter()
-        idx, _ = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], wl.k_pools, q_pos0=wl.q_pos0,
-                                   rows=rows, gate=gate)
+        if fp8:
+            idx, _ = oracle.index_topk_fp8(x["q_idx8"], x["k_idx8"], x["w"], wl.k_pools,
+                                           q_pos0=wl.q_pos0, rows=rows, gate=gate)
+        else:
+            idx, _ = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], wl.k_pools,
+                                       q_pos0=wl.q_pos0, rows=rows, gate=gate)
         oracle.sparse_attn(x["q"], x["k"], x["v"], idx, wl.k_pools, q_pos0=wl.q_pos0, rows=rows,
                            n_tail=wl.n_tail, scale=float(np.float32(1 / math.sqrt(wl.d))))
         return time.perf_counter() - t0
@@ -131,6 +148,88 @@ def cpu_baseline(wl, x, target_s: float, gate=None):
                       f"(pooling of all keys included), {t:.1f} s"}
 
 
+def backward(args, wl, x, g, gate, chunk_q, ws, idx, out, stream):
+    """Times dsa_sparse_attn_bwd on the ids, output and lse of one forward
+    pass of the same workload (made before the timed region)."""
+    import torch
+    from long_context_sparse_dsa_amd import dsa, inputs
+    if gate is None:
+        dsa.dsa_index_score_topk(g["q_idx"], g["k_idx"], g["w"], wl.k_pools, q_pos0=wl.q_pos0,
+                                 chunk_q=chunk_q, idx_out=idx, workspace=ws, stream=stream)
+    else:
+        dsa.dsa_index_score_topk_gated(g["q_idx"], g["k_idx"], gate, g["w"], wl.k_pools,
+                                       q_pos0=wl.q_pos0, chunk_q=chunk_q, idx_out=idx,
+                                       workspace=ws, stream=stream)
+    o, lse = dsa.dsa_sparse_attn_fwd(g["q"], g["k"], g["v"], idx, q_pos0=wl.q_pos0,
+                                     n_tail=wl.n_tail, out=out, want_lse=True, stream=stream)
+    dout = inputs.make_dout(wl).to(o.device)
+    del ws
+    dev = o.device
+    dq = torch.empty((wl.s_q, wl.h, wl.d), dtype=torch.float32, device=dev)
+    dk = torch.empty((wl.s_k, wl.d), dtype=torch.float32, device=dev)
+    dv = torch.empty((wl.s_k, wl.dv), dtype=torch.float32, device=dev)
+    nbytes, bwd_chunk = dsa.dsa_sparse_attn_bwd_workspace_size(wl.s_q, wl.s_k, wl.h)
+    bws = dsa.new_workspace(nbytes, dev)
+
+    def step():
+        dsa.dsa_sparse_attn_bwd(g["q"], g["k"], g["v"], idx, o, dout, lse, q_pos0=wl.q_pos0,
+                                n_tail=wl.n_tail, dq=dq, dk=dk, dv=dv, workspace=bws,
+                                stream=stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    dsa.dsa_profile_read()
+    dsa.dsa_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dsa.dsa_profile_enable(False)
+    stats = dsa.dsa_profile_read()
+    ms = (t1 - t0) * 1e3 / args.steps
+    log(f"timed {args.steps} backward steps: {ms:.3f} ms/step; kernels {stats}")
+    w = work_counts(wl)
+    stages = {}
+    for name, (launches, total) in stats.items():
+        st = {"ms_per_step": total / args.steps, "launches_per_step": launches / args.steps}
+        t_s = total / 1e3
+        if name == "attn_bwd_dq":
+            a = w["b_bwd_dq"] * args.steps / t_s / 1e9
+            st.update(bound="hbm", achieved=a, peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=a / PEAK_HBM_GBS, tflops=w["f_bwd_dq"] * args.steps / t_s / 1e12)
+        elif name == "attn_bwd_dkv":
+            a = w["f_bwd_dkv"] * args.steps / t_s / 1e12
+            st.update(bound="mfma", achieved=a, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                      frac=a / PEAK_BF16_TFLOPS)
+        if "bound" in st:
+            st["traffic"] = measured_traffic(name, wl.name)
+            st["source_sha256"] = kernel_source_hash(name)
+        stages[name] = st
+    dominant = max(stats, key=lambda k: stats[k][1]) if stats else None
+    flops = w["f_bwd_dq"] + w["f_bwd_dkv"]
+    result = {
+        "metric": "DSA sparse-attention backward queries/sec (dq, dk, dv)",
+        "value": wl.s_q / (ms / 1e3), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "s_q": wl.s_q, "s_k": wl.s_k, "q_pos0": wl.q_pos0,
+                   "k_pools": wl.k_pools, "attention": f"{wl.h}x{wl.d}", "kv_heads": 1,
+                   "n_tail": wl.n_tail, "bwd_chunk_q": bwd_chunk},
+        "tflops": flops / (ms / 1e3) / 1e12,
+        "roofline": dict(stages[dominant], kernel=dominant) if dominant in stages
+        and "bound" in stages[dominant] else None,
+        "stages": stages,
+        "work": {"tokens": w["tokens"], "f_bwd_dq": w["f_bwd_dq"], "f_bwd_dkv": w["f_bwd_dkv"],
+                 "b_bwd_dq": w["b_bwd_dq"]},
+        "peak_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +241,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gated", action="store_true",
                     help="gated pooling: per-token k-pool gates weight each key of a pool")
+    ap.add_argument("--fp8", action="store_true",
+                    help="the fp8 E4M3 indexer (workloads that carry E4M3 indexer inputs)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the sparse-attention backward (dq, dk, dv) instead of the "
+                         "forward path; the forward's ids, output and lse are made first")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -164,14 +268,24 @@ def main():
     t0 = time.time()
     x = inputs.make_inputs(wl)
     log(f"inputs generated in {time.time() - t0:.1f} s")
+    if args.fp8 and "q_idx8" not in x:
+        print(f"workload {wl.name} has no fp8 indexer inputs", file=sys.stderr)
+        sys.exit(2)
     g = {k: v.to(dev) for k, v in x.items() if not k.endswith("8")}
+    if args.fp8:
+        g["q_idx"], g["k_idx"] = x["q_idx8"].to(dev), x["k_idx8"].to(dev)
     gate = inputs.make_gates(wl).to(dev) if args.gated else None
-    ws_bytes, chunk_q = dsa.dsa_index_workspace_size(wl.s_q, wl.s_k, wl.h_idx, wl.d_idx,
-                                                     wl.k_pools, 4, args.chunk_q)
+    ws_bytes, chunk_q = dsa.dsa_index_workspace_size(
+        wl.s_q, wl.s_k, wl.h_idx, wl.d_idx, wl.k_pools, 4, args.chunk_q,
+        dsa.DSA_FP8_E4M3 if args.fp8 else dsa.DSA_BF16)
     ws = dsa.new_workspace(ws_bytes, dev)
     idx = torch.empty((wl.s_q, wl.k_pools), dtype=torch.int32, device=dev)
     out = torch.empty((wl.s_q, wl.h, wl.dv), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
+
+    if args.backward:
+        backward(args, wl, x, g, gate, chunk_q, ws, idx, out, stream)
+        return
 
     def step():
         if gate is None:
@@ -213,8 +327,9 @@ def main():
         t_s = total / 1e3
         if name == "index_score":
             a = w["f_score"] * args.steps / t_s / 1e12
-            rl[name] = {"bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS,
-                        "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS, "traffic": None}
+            peak = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
+            rl[name] = {"bound": "mfma", "achieved": a, "peak": peak,
+                        "unit": "TFLOP/s", "frac": a / peak, "traffic": None}
         elif name == "sparse_attn":
             a = w["b_attn"] * args.steps / t_s / 1e9
             rl[name] = {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -228,7 +343,8 @@ def main():
             rl[name] = {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": a / PEAK_HBM_GBS, "traffic": None}
         if name in rl:
-            rl[name]["traffic"] = measured_traffic(name, wl.name)
+            rl[name]["traffic"] = None if args.fp8 or args.gated else \
+                measured_traffic(name, wl.name)
             rl[name]["source_sha256"] = kernel_source_hash(name)
         stages[name].update(rl.get(name, {}))
     dominant = max(stats, key=lambda k: stats[k][1]) if stats else None
@@ -241,7 +357,8 @@ def main():
         "config": {"workload": wl.name, "s_q": wl.s_q, "s_k": wl.s_k, "q_pos0": wl.q_pos0,
                    "indexer": f"{wl.h_idx}x{wl.d_idx}", "pool": 4, "k_pools": wl.k_pools,
                    "attention": f"{wl.h}x{wl.d}", "kv_heads": 1, "n_tail": wl.n_tail,
-                   "chunk_q": chunk_q, "pooling": "gated" if args.gated else "mean"},
+                   "chunk_q": chunk_q, "pooling": "gated" if args.gated else "mean",
+                   "indexer_dtype": "e4m3" if args.fp8 else "bf16"},
         "tflops": tflops, "tflops_frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "roofline": dict(rl[dominant], kernel=dominant) if dominant in rl else None,
         "stages": stages,
@@ -252,7 +369,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds,
-                                              None if gate is None else gate.cpu().numpy())
+                                              None if gate is None else gate.cpu().numpy(),
+                                              fp8=args.fp8)
     print(json.dumps(result), flush=True)
 
 

@@ -74,13 +74,14 @@ const char *dsa_last_error(void);
 /*
  * Bytes of device workspace dsa_index_score_topk needs.  Holds the pooled
  * key table (bf16: hi = bf16(mean) plus the residual as E4M3 codes with a
- * per-pool power-of-two scale; fp8: E4M3 codes plus per-pool factors), for
- * the bf16 indexer the chunk's queries and head weights packed in scoring
- * tiles (with E4M3 copies of the queries for the correction term), and the
- * per-chunk fp32 score buffer of chunk_q x round_up(P, 512) entries ("Over
- * Time: Chunking": the buffer is constant in s_q).  chunk_q = 0 picks the library's default for
- * these shapes (the value is returned through *chunk_q_used when that
- * pointer is non-NULL).
+ * per-pool power-of-two scale and a per-pool error-bound factor; fp8: E4M3
+ * codes plus per-pool factors), for the bf16 indexer the chunk's queries and
+ * head weights packed in scoring tiles (with E4M3 copies of the queries for
+ * the correction term) and a per-query error-bound factor, and the per-chunk
+ * fp32 score buffer of chunk_q x round_up(P, 512) entries ("Over Time:
+ * Chunking": the buffer is constant in s_q).  chunk_q = 0 picks the
+ * library's default for these shapes (the value is returned through
+ * *chunk_q_used when that pointer is non-NULL).
  * Pure host computation; valid without a GPU.
  */
 dsa_status dsa_index_workspace_size(int64_t s_q, int64_t s_k, int h_idx, int d_idx,
@@ -107,6 +108,12 @@ dsa_status dsa_index_workspace_size(int64_t s_q, int64_t s_k, int h_idx, int d_i
  *   workspace                      >= dsa_index_workspace_size(...) bytes
  * Supported: h_idx in {4, 8, 16, 32}; d_idx in {64, 96, 128}; s_k < 2^31.
  * The fp32 score of a pool is a +0.0 when zero (never -0.0).
+ * bf16 indexer: the score of a pool is q . hi on bf16 matrix cores plus the
+ * correction q . lo on scaled E4M3 matrix cores, exactly as
+ * dsa_index_scores returns it, and the kept set is exactly the top k_pools
+ * of those scores.  (The chunk is first scored without the correction; a
+ * per-pair error bound then decides every pool it can, and only the pools
+ * near the k-th score are rescored in full.)
  */
 dsa_status dsa_index_score_topk(const void *q_idx, const void *k_idx, const float *q_scale,
                                 const float *k_scale, const float *w, int64_t w_stride_q,

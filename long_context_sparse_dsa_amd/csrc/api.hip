@@ -157,10 +157,11 @@ dsa_status resolve_chunk(const IndexShape& sh, int64_t chunk_q, int64_t* out) {
 
 // Workspace layout, every part starting on a 256-byte boundary:
 //   bf16 indexer: hi [P][d] bf16 | lo [P][d] E4M3 | lo scales [P] E8M0 |
-//                 the chunk's packed query tiles | score buffer [rows][ld] fp32
+//                 bound factors mu [P] fp32 | the chunk's packed query tiles |
+//                 bound factors A [rows] fp32 | score buffer [rows][ld] fp32
 //   fp8 indexer:  codes [P][d] | per-pool factors [P] fp32 | score buffer
 struct Layout {
-    int64_t hi = 0, lo = 0, lo_scale = 0, tiles = 0, buf = 0, total = 0;
+    int64_t hi = 0, lo = 0, lo_scale = 0, mu = 0, tiles = 0, qbound = 0, buf = 0, total = 0;
 };
 
 Layout layout(const IndexShape& sh, int64_t rows, bool with_buffer) {
@@ -171,8 +172,10 @@ Layout layout(const IndexShape& sh, int64_t rows, bool with_buffer) {
         L.hi = off;        off += round_up(P * d * 2, 256);
         L.lo = off;        off += round_up(P * d, 256);
         L.lo_scale = off;  off += round_up(P, 256);
+        L.mu = off;        off += round_up(P * 4, 256);
         L.tiles = off;
         off += round_up(dsa::query_tiles(rows, sh.h_idx) * dsa::query_tile_geom((int)d).tb, 256);
+        L.qbound = off;    off += round_up(rows * 4, 256);
     } else {
         L.hi = off;        off += round_up(P * d, 256);
         L.lo_scale = off;  off += round_up(P * 4, 256);  // fp32 factors 2^e
@@ -219,22 +222,27 @@ hipError_t launch_pool(const IndexShape& sh, const Layout& L, const void* k_idx,
         return dsa::launch_pool_keys_bf16(static_cast<const uint16_t*>(k_idx), k_gate, sh.n_pools,
                                           sh.d_idx, reinterpret_cast<uint16_t*>(w + L.hi),
                                           reinterpret_cast<uint8_t*>(w + L.lo),
-                                          reinterpret_cast<uint8_t*>(w + L.lo_scale), s);
+                                          reinterpret_cast<uint8_t*>(w + L.lo_scale),
+                                          reinterpret_cast<float*>(w + L.mu), s);
     return dsa::launch_pool_keys_fp8(static_cast<const uint8_t*>(k_idx), k_gate, sh.n_pools,
                                      sh.d_idx, reinterpret_cast<uint8_t*>(w + L.hi),
                                      reinterpret_cast<float*>(w + L.lo_scale), s);
 }
 
 // bf16 indexer: pack query rows [row0, row0 + rows) and their weights into
-// the tiles the scoring kernel streams.
+// the tiles the scoring kernel streams (with_bound: and each query's bound
+// factor, for the selection).
 hipError_t launch_pack(const IndexShape& sh, const Layout& L, const void* q_idx, const float* w,
-                       int64_t w_stride, int64_t row0, int64_t rows, void* ws, hipStream_t s) {
+                       int64_t w_stride, int64_t row0, int64_t rows, bool with_bound, void* ws,
+                       hipStream_t s) {
     if (sh.dtype != DSA_BF16) return hipSuccess;
     Timed tm(K_PACK, s);
     char* base = static_cast<char*>(ws);
     return dsa::launch_pack_queries(static_cast<const uint16_t*>(q_idx), w, w_stride, row0,
                                     (int)rows, sh.h_idx, sh.d_idx,
-                                    reinterpret_cast<uint8_t*>(base + L.tiles), s);
+                                    reinterpret_cast<uint8_t*>(base + L.tiles),
+                                    with_bound ? reinterpret_cast<float*>(base + L.qbound) : nullptr,
+                                    s);
 }
 
 void fill_score_args(dsa::ScoreArgs& a, const IndexShape& sh, const Layout& L,
@@ -388,7 +396,7 @@ static dsa_status index_score_topk(const void* q_idx, const void* k_idx, const f
         const int64_t t_last = q_pos0 + c0 + rows - 1;
         const int64_t n_chunk = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
         if (n_chunk > 0 && (n_chunk > k_pools || score_out)) {
-            e = launch_pack(sh, L, q_idx, w, w_stride_q, c0, rows, ws, s);
+            e = launch_pack(sh, L, q_idx, w, w_stride_q, c0, rows, true, ws, s);
             if (e != hipSuccess) return hip_fail(e, "pack_queries launch");
             dsa::ScoreArgs a{};
             fill_score_args(a, sh, L, q_idx, ws, q_scale, k_scale, w, w_stride_q);
@@ -411,6 +419,18 @@ static dsa_status index_score_topk(const void* q_idx, const void* k_idx, const f
         b.k_pools = k_pools;
         b.idx_out = idx_out;
         b.score_out = score_out;
+        b.h_idx = h_idx;
+        b.d_idx = d_idx;
+        if (dtype == DSA_BF16) {
+            // approximate scores (no correction term): the selection rescores
+            // the pools its bound cannot decide
+            b.qbound = reinterpret_cast<const float*>(ws + L.qbound);
+            b.mu = reinterpret_cast<const float*>(ws + L.mu);
+            b.tiles = reinterpret_cast<const uint8_t*>(ws + L.tiles);
+            b.khi = reinterpret_cast<const uint16_t*>(ws + L.hi);
+            b.klo = reinterpret_cast<const uint8_t*>(ws + L.lo);
+            b.klo_scale = reinterpret_cast<const uint8_t*>(ws + L.lo_scale);
+        }
         Timed tm(K_SELECT, s);
         e = dsa::launch_topk_select(b, s);
         if (e != hipSuccess) return hip_fail(e, "topk_select launch");
@@ -455,7 +475,7 @@ static dsa_status index_scores(const void* q_idx, const void* k_idx, const float
         const int64_t t_last = q_pos0 + r0 + rows - 1;
         const int64_t n_chunk = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
         if (n_chunk == 0) continue;
-        e = launch_pack(sh, L, q_idx, w, w_stride_q, r0, rows, workspace, s);
+        e = launch_pack(sh, L, q_idx, w, w_stride_q, r0, rows, false, workspace, s);
         if (e != hipSuccess) return hip_fail(e, "pack_queries launch");
         dsa::ScoreArgs a{};
         fill_score_args(a, sh, L, q_idx, workspace, q_scale, k_scale, w, w_stride_q);

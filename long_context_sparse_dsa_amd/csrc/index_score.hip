@@ -217,19 +217,31 @@ __device__ __forceinline__ int pow2_scale_exp(float amax) {
 // One thread per pool: hi = bf16(kbar) [P][DI], lo = E4M3((kbar - hi) / 2^e)
 // [P][DI] with one E8M0 byte (e + 127) per pool.  kbar is the mean of the
 // pool's 4 rows, or with GATED their gate-weighted sum (fp32).
+//
+// mu (optional) [P] fp32 is the pool's factor of the bound on how far a score
+// taken with hi alone can be from the score with the E4M3 correction:
+//   mu_p = (1 + 2^-6) ||L8_p|| + 2^-14 ||hi_p||   (0 when every lo code is 0)
+// with L8_p the decoded correction vector.  For a query whose factor is
+// A = (1 + 2^-8) sum_h |w_h| max(||q_h||, ||Q8_h||) (see pack_queries_kernel),
+// |score(hi) - score(hi + lo)| <= A mu_p: per head the correction is at most
+// ||Q8_h|| ||L8_p|| (Cauchy-Schwarz), the ReLU is 1-Lipschitz, and the
+// 2^-14 ||hi|| term and the two (1 + ...) factors cover fp32 rounding of the
+// accumulation, the epilogue and of s -/+ A mu_p themselves.  When every lo
+// code is 0 the correction MFMAs add exact zeros, so both scores are equal.
 template <int DI, bool GATED>
 __global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __restrict__ k,
                                                              const float* __restrict__ gate,
                                                              int64_t n_pools,
                                                              uint16_t* __restrict__ hi_out,
                                                              uint8_t* __restrict__ lo_out,
-                                                             uint8_t* __restrict__ lo_scale) {
+                                                             uint8_t* __restrict__ lo_scale,
+                                                             float* __restrict__ mu) {
     const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (p >= n_pools) return;
     f32x4 gw = {0.25f, 0.25f, 0.25f, 0.25f};
     if constexpr (GATED) gw = *reinterpret_cast<const f32x4*>(gate + 4 * p);
     float lo[DI];
-    float amax = 0.0f;
+    float amax = 0.0f, hi2 = 0.0f;
 #pragma unroll
     for (int g = 0; g < DI / 8; ++g) {
         u32x4 r[4];
@@ -252,7 +264,9 @@ __global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __r
                 m = sum * 0.25f;
             }
             const uint32_t h = f32_to_bf16(m);
-            lo[8 * g + e] = m - bf16_to_f32(h);
+            const float hv = bf16_to_f32(h);
+            lo[8 * g + e] = m - hv;
+            hi2 = fmaf(hv, hv, hi2);
             amax = fmaxf(amax, fabsf(lo[8 * g + e]));
             if ((e & 1) == 0) hi[word] = h;
             else hi[word] |= h << 16;
@@ -260,25 +274,34 @@ __global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __r
         *reinterpret_cast<u32x4*>(hi_out + p * DI + 8 * g) = hi;
     }
     const int e = pow2_scale_exp(amax);
+    float lo2 = 0.0f;
 #pragma unroll
     for (int c = 0; c < DI / 16; ++c) {
         u32x4 o = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int b = 0; b < 16; ++b) o[b >> 2] |= e4m3_code(ldexpf(lo[16 * c + b], -e)) << ((b & 3) * 8);
+        for (int b = 0; b < 16; ++b) {
+            const uint32_t code = e4m3_code(ldexpf(lo[16 * c + b], -e));
+            const float v = e4m3_value(code);
+            lo2 = fmaf(v, v, lo2);
+            o[b >> 2] |= code << ((b & 3) * 8);
+        }
         *reinterpret_cast<u32x4*>(lo_out + p * DI + 16 * c) = o;
     }
     lo_scale[p] = (uint8_t)(e + 127);
+    if (mu)
+        mu[p] = lo2 > 0.0f ? fmaf(ldexpf(sqrtf(lo2), e), 1.0f + 0x1p-6f, 0x1p-14f * sqrtf(hi2))
+                           : 0.0f;
 }
 
 template <bool GATED>
 static hipError_t launch_pool_bf16_g(const uint16_t* k_idx, const float* gate, int64_t n_pools,
                                      int d_idx, uint16_t* hi, uint8_t* lo, uint8_t* lo_scale,
-                                     hipStream_t stream) {
+                                     float* mu, hipStream_t stream) {
     const dim3 grid((unsigned)((n_pools + 255) / 256));
     switch (d_idx) {
-        case 64: pool_keys_bf16_kernel<64, GATED><<<grid, 256, 0, stream>>>(k_idx, gate, n_pools, hi, lo, lo_scale); break;
-        case 96: pool_keys_bf16_kernel<96, GATED><<<grid, 256, 0, stream>>>(k_idx, gate, n_pools, hi, lo, lo_scale); break;
-        case 128: pool_keys_bf16_kernel<128, GATED><<<grid, 256, 0, stream>>>(k_idx, gate, n_pools, hi, lo, lo_scale); break;
+        case 64: pool_keys_bf16_kernel<64, GATED><<<grid, 256, 0, stream>>>(k_idx, gate, n_pools, hi, lo, lo_scale, mu); break;
+        case 96: pool_keys_bf16_kernel<96, GATED><<<grid, 256, 0, stream>>>(k_idx, gate, n_pools, hi, lo, lo_scale, mu); break;
+        case 128: pool_keys_bf16_kernel<128, GATED><<<grid, 256, 0, stream>>>(k_idx, gate, n_pools, hi, lo, lo_scale, mu); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -286,30 +309,27 @@ static hipError_t launch_pool_bf16_g(const uint16_t* k_idx, const float* gate, i
 
 hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, const float* gate, int64_t n_pools,
                                  int d_idx, uint16_t* hi, uint8_t* lo, uint8_t* lo_scale,
-                                 hipStream_t stream) {
+                                 float* mu, hipStream_t stream) {
     if (n_pools <= 0) return hipSuccess;
-    return gate ? launch_pool_bf16_g<true>(k_idx, gate, n_pools, d_idx, hi, lo, lo_scale, stream)
-                : launch_pool_bf16_g<false>(k_idx, gate, n_pools, d_idx, hi, lo, lo_scale, stream);
+    return gate ? launch_pool_bf16_g<true>(k_idx, gate, n_pools, d_idx, hi, lo, lo_scale, mu, stream)
+                : launch_pool_bf16_g<false>(k_idx, gate, n_pools, d_idx, hi, lo, lo_scale, mu, stream);
 }
 
 // ---------------------------------------------------------------- query tiles
 
-// Byte offsets inside a packed query tile (layout in internal.h).
-template <int DI>
+// Byte offsets inside a packed query tile (layout in internal.h).  LO: the
+// E4M3 copies are staged too (else only the bf16 rows and the weights).
+template <int DI, bool LO = true>
 struct QTile {
     static constexpr QueryTileGeom G = query_tile_geom(DI);
-    static constexpr int NPQ = G.qb / 16;           // 16-byte pieces of query data
+    static constexpr int NPQ = (LO ? G.qb : G.of8) / 16;  // 16-byte pieces of query data
     static constexpr int CPT = (NPQ + 255) / 256;   // pieces per thread when staging
     static constexpr int LDSQ = CPT * 4096;         // LDS bytes for the staged pieces
     static constexpr int LDS_W = LDSQ;              // LDS: w [32] fp32, then scales [32]
     static constexpr int LDSB = LDSQ + 1024;        // LDS bytes per tile buffer
     // piece c (16 bytes) of the bf16 / E4M3 row r
-    __device__ static constexpr int bf16_piece(int r, int c) {
-        return r * G.lb + 16 * (G.swz ? (c ^ (r & 15)) : c);
-    }
-    __device__ static constexpr int fp8_piece(int r, int c) {
-        return G.of8 + r * G.l8 + 16 * (G.swz ? (c ^ ((r & 7) ^ ((r >> 3) & 1))) : c);
-    }
+    __device__ static constexpr int bf16_piece(int r, int c) { return tile_bf16_piece(G, r, c); }
+    __device__ static constexpr int fp8_piece(int r, int c) { return tile_fp8_piece(G, r, c); }
 };
 
 // One workgroup per tile, 8 threads per tile row (query, head), thread c
@@ -317,13 +337,20 @@ struct QTile {
 // power-of-two scale 2^e (e the smallest with max|q| <= 448 * 2^e, the row
 // maximum combined across the row's 8 threads), and the row's head weight.
 // Rows past the chunk are zero with weight 0.
+//
+// qbound (optional) [rows] fp32 receives each query's factor of the score
+// error bound (see pool_keys_bf16_kernel):
+//   A = (1 + 2^-8) sum_h |w_h| max(||q_h||, ||Q8_h||),
+// Q8_h the decoded E4M3 row; the heads are summed in order.
 template <int HI, int DI>
 __global__ __launch_bounds__(256) void pack_queries_kernel(const uint16_t* __restrict__ q,
                                                            const float* __restrict__ w,
                                                            int64_t w_stride, int64_t row0,
-                                                           int rows, uint8_t* __restrict__ tiles) {
+                                                           int rows, uint8_t* __restrict__ tiles,
+                                                           float* __restrict__ qbound) {
     using T = QTile<DI>;
     constexpr int QPT = 32 / HI;
+    __shared__ float rowbound[32];
     const int64_t tile = blockIdx.x;
     const int r = threadIdx.x >> 3, c = threadIdx.x & 7;
     const int64_t i = tile * QPT + r / HI;
@@ -337,38 +364,63 @@ __global__ __launch_bounds__(256) void pack_queries_kernel(const uint16_t* __res
         raw[1] = ldg16(src + 8);
     }
     float x[16];
-    float amax = 0.0f;
+    float amax = 0.0f, n2 = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         x[e] = bf16_to_f32((raw[e >> 3][(e & 7) >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
         amax = fmaxf(amax, fabsf(x[e]));
+        n2 = fmaf(x[e], x[e], n2);
     }
     amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
     amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
     amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
     const int e = pow2_scale_exp(amax);
+    float n8 = 0.0f;
     if (act) {
         *reinterpret_cast<u32x4*>(dst + T::bf16_piece(r, 2 * c)) = raw[0];
         *reinterpret_cast<u32x4*>(dst + T::bf16_piece(r, 2 * c + 1)) = raw[1];
         u32x4 o = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int b = 0; b < 16; ++b) o[b >> 2] |= e4m3_code(ldexpf(x[b], -e)) << ((b & 3) * 8);
+        for (int b = 0; b < 16; ++b) {
+            const uint32_t code = e4m3_code(ldexpf(x[b], -e));
+            const float v = e4m3_value(code);
+            n8 = fmaf(v, v, n8);
+            o[b >> 2] |= code << ((b & 3) * 8);
+        }
         *reinterpret_cast<u32x4*>(dst + T::fp8_piece(r, c)) = o;
     }
+    float wr = in ? w[(row0 + i) * w_stride + h] : 0.0f;
     if (c == 0) {
-        reinterpret_cast<float*>(dst + T::G.qb)[r] = in ? w[(row0 + i) * w_stride + h] : 0.0f;
+        reinterpret_cast<float*>(dst + T::G.qb)[r] = wr;
         dst[T::G.qb + 128 + r] = (uint8_t)(e + 127);
+    }
+    if (qbound) {
+        n2 += __shfl_xor(n2, 1, 8);
+        n2 += __shfl_xor(n2, 2, 8);
+        n2 += __shfl_xor(n2, 4, 8);
+        n8 += __shfl_xor(n8, 1, 8);
+        n8 += __shfl_xor(n8, 2, 8);
+        n8 += __shfl_xor(n8, 4, 8);
+        if (c == 0) rowbound[r] = fabsf(wr) * fmaxf(sqrtf(n2), ldexpf(sqrtf(n8), e));
+        __syncthreads();
+        if (threadIdx.x < QPT) {
+            const int64_t qi = tile * QPT + threadIdx.x;
+            float a = 0.0f;
+            for (int hh = 0; hh < HI; ++hh) a += rowbound[threadIdx.x * HI + hh];
+            if (qi < rows) qbound[qi] = a * (1.0f + 0x1p-8f);
+        }
     }
 }
 
 template <int HI>
 static hipError_t launch_pack_h(const uint16_t* q, const float* w, int64_t w_stride, int64_t row0,
-                                int rows, int d_idx, uint8_t* tiles, hipStream_t stream) {
+                                int rows, int d_idx, uint8_t* tiles, float* qbound,
+                                hipStream_t stream) {
     const dim3 grid((unsigned)(((int64_t)rows + 32 / HI - 1) / (32 / HI)));
     switch (d_idx) {
-        case 64: pack_queries_kernel<HI, 64><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, tiles); break;
-        case 96: pack_queries_kernel<HI, 96><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, tiles); break;
-        case 128: pack_queries_kernel<HI, 128><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, tiles); break;
+        case 64: pack_queries_kernel<HI, 64><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, tiles, qbound); break;
+        case 96: pack_queries_kernel<HI, 96><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, tiles, qbound); break;
+        case 128: pack_queries_kernel<HI, 128><<<grid, 256, 0, stream>>>(q, w, w_stride, row0, rows, tiles, qbound); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -376,13 +428,13 @@ static hipError_t launch_pack_h(const uint16_t* q, const float* w, int64_t w_str
 
 hipError_t launch_pack_queries(const uint16_t* q_idx, const float* w, int64_t w_stride,
                                int64_t row0, int rows, int h_idx, int d_idx, uint8_t* tiles,
-                               hipStream_t stream) {
+                               float* qbound, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
     switch (h_idx) {
-        case 4: return launch_pack_h<4>(q_idx, w, w_stride, row0, rows, d_idx, tiles, stream);
-        case 8: return launch_pack_h<8>(q_idx, w, w_stride, row0, rows, d_idx, tiles, stream);
-        case 16: return launch_pack_h<16>(q_idx, w, w_stride, row0, rows, d_idx, tiles, stream);
-        case 32: return launch_pack_h<32>(q_idx, w, w_stride, row0, rows, d_idx, tiles, stream);
+        case 4: return launch_pack_h<4>(q_idx, w, w_stride, row0, rows, d_idx, tiles, qbound, stream);
+        case 8: return launch_pack_h<8>(q_idx, w, w_stride, row0, rows, d_idx, tiles, qbound, stream);
+        case 16: return launch_pack_h<16>(q_idx, w, w_stride, row0, rows, d_idx, tiles, qbound, stream);
+        case 32: return launch_pack_h<32>(q_idx, w, w_stride, row0, rows, d_idx, tiles, qbound, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -437,11 +489,14 @@ struct ScoreK {
 //
 // EXACT = false: the chunk-buffer contract of ScoreArgs (any entry may be
 // written, ineligible pools get -inf).  EXACT = true: only eligible entries of
-// rows [0, rows) are stored.
-template <int HI, int DI, int NB, bool EXACT>
+// rows [0, rows) are stored.  LO = false: the correction q . lo is left out
+// (scores from hi alone, within the bound A mu_p of the full score, see
+// pool_keys_bf16_kernel); the selection rescores the pools near its
+// threshold with the full sequence of MFMAs below.
+template <int HI, int DI, int NB, bool EXACT, bool LO>
 __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     static_assert(NB == 2, "the epilogue pairs the two pool blocks of a wave");
-    using T = QTile<DI>;
+    using T = QTile<DI, LO>;
     constexpr int QPT = 32 / HI;      // queries per tile
     constexpr int NSB = DI / 16;      // bf16 MFMA steps (16 dims each)
     constexpr int NSF = (DI + 63) / 64;  // fp8 MFMA steps (64 dims each)
@@ -480,6 +535,7 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
         for (int s = 0; s < NSB; ++s)
             bhi[nb][s] = as_bf16x8(ok ? ldg16(a.khi + p * DI + 16 * s + 8 * half)
                                       : u32x4{0u, 0u, 0u, 0u});
+        if constexpr (!LO) continue;
 #pragma unroll
         for (int s = 0; s < NSF; ++s) {
             const int d0 = 64 * s + 32 * half;
@@ -568,7 +624,7 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
         for (int s = 0; s < NSB; ++s)
             af[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(L + T::bf16_piece(col, 2 * s + half)));
 #pragma unroll
-        for (int s = 0; s < NSF; ++s) {
+        for (int s = 0; s < (LO ? NSF : 0); ++s) {
             // pieces past d_idx (only with d_idx = 96) read row padding or the
             // next row and are zeroed
             const bool in = 64 * s + 32 * half < DI;
@@ -578,21 +634,26 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
             af8[s] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
                            (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
         }
-        const int qsc = (int)L[T::LDS_W + 128 + col];
+        const int qsc = LO ? (int)L[T::LDS_W + 128 + col] : 127;
 #pragma unroll
         for (int s = 0; s < NSB; ++s)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
                 acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], bhi[nb][s], acc[nb], 0, 0, 0);
 #pragma unroll
-        for (int s = 0; s < NSF; ++s)
+        for (int s = 0; s < (LO ? NSF : 0); ++s)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
                 acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     af8[s], blo[nb][s], acc[nb], 0, 0, 0, qsc, 0, bsc[nb]);
         // keep the LDS reads ahead of the MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, NSB + 2 * NSF + 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, NB * (NSB + NSF), 0);
+        if constexpr (LO) {
+            __builtin_amdgcn_sched_group_barrier(0x100, NSB + 2 * NSF + 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NB * (NSB + NSF), 0);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x100, NSB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NB * NSB, 0);
+        }
 
         // epilogue: per-lane partial sums w * relu over the rows this lane
         // holds (rows 8*g4 + 4*half + i), then the two half-waves' partials of
@@ -668,8 +729,10 @@ static hipError_t launch_score_bf16_t(const ScoreArgs& a, hipStream_t stream) {
     k.ld = a.ld;
     const dim3 grid((unsigned)((a.n_chunk + PB - 1) / PB), (unsigned)((a.rows + k.gq - 1) / k.gq));
     if (grid.x == 0 || grid.y == 0) return hipSuccess;
-    if (a.exact) index_score_bf16_kernel<HI, DI, NB, true><<<grid, 256, 0, stream>>>(k);
-    else index_score_bf16_kernel<HI, DI, NB, false><<<grid, 256, 0, stream>>>(k);
+    // the chunk buffer of the selection holds approximate scores; exact
+    // (caller-owned) rows get the full scores
+    if (a.exact) index_score_bf16_kernel<HI, DI, NB, true, true><<<grid, 256, 0, stream>>>(k);
+    else index_score_bf16_kernel<HI, DI, NB, false, false><<<grid, 256, 0, stream>>>(k);
     return hipGetLastError();
 }
 

@@ -10,10 +10,11 @@ namespace dsa {
 // Pooled indexer keys kbar (the mean of each pool's 4 rows, or with
 // per-token gates [4 * n_pools] fp32 their gate-weighted sum), split as
 // hi = bf16(kbar) [P][d] and lo = kbar - hi as E4M3 codes [P][d] with one
-// E8M0 power-of-two scale byte per pool.
+// E8M0 power-of-two scale byte per pool.  mu (optional) [P] fp32: each pool's
+// factor of the bound on the score error of leaving lo out.
 hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, const float* gate, int64_t n_pools,
                                  int d_idx, uint16_t* hi, uint8_t* lo, uint8_t* lo_scale,
-                                 hipStream_t stream);
+                                 float* mu, hipStream_t stream);
 
 // Packed query tiles of the bf16 indexer.  A tile holds 32 (query, head)
 // rows r = qi * h_idx + h of 32 / h_idx consecutive chunk queries, laid out
@@ -38,16 +39,24 @@ inline constexpr QueryTileGeom query_tile_geom(int d) {
     const int qb = of8 + 32 * l8;
     return QueryTileGeom{swz, lb, l8, of8, qb, (qb + 160 + 127) / 128 * 128};
 }
+// Byte offset of 16-byte piece c of the bf16 row r / of the E4M3 row r.
+inline constexpr int tile_bf16_piece(const QueryTileGeom& g, int r, int c) {
+    return r * g.lb + 16 * (g.swz ? (c ^ (r & 15)) : c);
+}
+inline constexpr int tile_fp8_piece(const QueryTileGeom& g, int r, int c) {
+    return g.of8 + r * g.l8 + 16 * (g.swz ? (c ^ ((r & 7) ^ ((r >> 3) & 1))) : c);
+}
 // Tiles the scoring kernel may read for a chunk of `rows` queries: the
 // chunk's own plus three beyond its end (prefetched, never used).
 inline constexpr int64_t query_tiles(int64_t rows, int h_idx) {
     return (rows + 32 / h_idx - 1) / (32 / h_idx) + 3;
 }
 
-// Rows [row0, row0 + rows) of q_idx and w packed into query tiles.
+// Rows [row0, row0 + rows) of q_idx and w packed into query tiles; qbound
+// (optional) [rows] fp32: each query's factor of the same bound.
 hipError_t launch_pack_queries(const uint16_t* q_idx, const float* w, int64_t w_stride,
                                int64_t row0, int rows, int h_idx, int d_idx, uint8_t* tiles,
-                               hipStream_t stream);
+                               float* qbound, hipStream_t stream);
 
 // Pooled fp8 keys: per pool, E4M3 codes of kbar/2^e and the factor 2^e
 // (kbar the mean of the code values, or with gates their gate-weighted sum).
@@ -75,8 +84,10 @@ struct ScoreArgs {
     int fp8;
     // exact = 0: buf is a chunk buffer with at least round_up(rows, 8) rows
     // and ld >= round_up(n_chunk, 512); the kernel may write any entry of it
-    // (ineligible pools get -inf).  exact = 1: only the eligible entries of
-    // rows [0, rows) are written (a caller's dense [rows, P] layout).
+    // (ineligible pools get -inf); with the bf16 indexer the scores leave the
+    // correction q . lo out (the selection rescores the pools near its
+    // threshold).  exact = 1: only the eligible entries of rows [0, rows) are
+    // written (a caller's dense [rows, P] layout), with full scores.
     int exact;
     float* buf;               // [rows, ld] fp32
     int64_t ld;
@@ -86,7 +97,7 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream);
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t stream);
 
 struct SelectArgs {
-    const float* buf;         // [rows, ld] scores of the chunk
+    float* buf;               // [rows, ld] scores of the chunk (rows may be rewritten)
     int64_t ld;
     int64_t row0;
     int rows;
@@ -95,6 +106,17 @@ struct SelectArgs {
     int k_pools;
     int32_t* idx_out;         // [s_q, k_pools]
     float* score_out;         // optional
+    // Approximate scores (bf16 indexer without the correction term): every
+    // score is within qbound[i] * mu[p] of the full score, which the
+    // selection recomputes for the pools it cannot decide from the bound.
+    // qbound == nullptr: the scores are final.
+    const float* qbound;      // [rows] per chunk query
+    const float* mu;          // [n_pools]
+    const uint8_t* tiles;     // the chunk's packed query tiles
+    const uint16_t* khi;      // [P][d_idx] bf16
+    const uint8_t* klo;       // [P][d_idx] E4M3
+    const uint8_t* klo_scale; // [P] E8M0
+    int h_idx, d_idx;
 };
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t stream);
 

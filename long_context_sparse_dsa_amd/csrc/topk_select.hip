@@ -6,27 +6,40 @@
 // pools are scored and selected a chunk of queries at a time; section
 // "Across GPUs: Sharding": the kept pool ids are int32.
 //
-// Rule: keep the k largest fp32 scores among the n(t) eligible pools, ties
-// broken towards the lower pool id; emit the ids in ascending order, padded
-// with -1 when n(t) < k.  Exact and deterministic: every decision is taken on
-// the 32-bit order key of the fp32 score (larger float <=> larger key), with
+// Rule: keep the k largest scores among the n(t) eligible pools, ties broken
+// towards the lower pool id; emit the ids in ascending order, padded with -1
+// when n(t) < k.  Exact and deterministic: every decision is taken on the
+// 32-bit order key of an fp32 value (larger float <=> larger key), with
 // integer counting only.
 //
+// Approximate rows (bf16 indexer): the row holds s~_p, the score taken with
+// the bf16 pooled key hi_p alone, and the selection is made on the full score
+// s_p (hi_p plus the E4M3 correction lo_p) that the scoring kernel would give
+// with the correction.  Every |s~_p - s_p| <= delta_p = A * mu_p (A per query,
+// mu_p per pool; see the pooling and packing kernels), so with
+//   l_p = s~_p - delta_p,  u_p = s~_p + delta_p,
+//   L = k-th largest l,    U = k-th largest u,
+// the k-th largest full score lies in [L, U]: pools with l_p > U are kept for
+// certain, pools with u_p < L are dropped for certain, and only the pools in
+// between (the band, typically about k of them) are rescored, by the same
+// MFMA sequence the scoring kernel uses with the correction, so the result is
+// bit for bit the selection over the full scores.  Pools with delta_p = 0
+// already hold their full score.  Final rows (fp8 indexer) are the case
+// delta = 0: the band is the set of keys equal to the k-th.
+//
 // One workgroup (4 waves) per query row:
-//   n <= k       every eligible pool, no scores read;
-//   n <= CAP     the whole row goes to an LDS list (key, id) in id order;
-//   n >  CAP     a 2048-element sample of the row (128 cache-line blocks)
-//                gives a threshold tau that about 2-4x k elements exceed;
-//                one coalesced pass compacts {key >= tau} into the LDS list,
-//                keeping id order; if fewer than k or more than CAP elements
-//                qualify, an exact multi-pass radix over the row in global
-//                memory takes over (slow path, still exact).
-// On a list, a radix-16 refinement narrows a key range [lo, hi] until the
-// elements above hi plus the in-range ones are exactly decided: everything
-// above hi is kept, and in-range elements are kept in id order while fewer
-// than `remaining` have been kept.  Counting uses per-thread LDS counters
-// (one slot per digit and thread) so that skewed score distributions cause
-// no atomic contention.
+//   n <= k       every eligible pool;
+//   n <= CAP     the whole row goes to an LDS list (id, score, delta);
+//   n >  CAP     a 4096-element sample of the row (256 blocks of 16) gives a
+//                threshold tau on the l keys; one coalesced pass keeps
+//                {u >= tau} in the LDS list, in id order.  The list then holds
+//                every pool that can matter when at least k of its l keys
+//                are >= tau and it fits; otherwise the row is handled in
+//                global memory (slow path, still exact): L and U by radix
+//                over the row, the band rescored in place, and an exact
+//                selection over the row.
+// On a list, L and U come from radix-256 selections, and the kept band
+// members from one more over their full scores.
 #include <math.h>
 
 #include "common.h"
@@ -38,21 +51,33 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int CAP = 4096;
-constexpr int SAMPLE_BLOCKS = 128;
 constexpr int SAMPLE_LEN = 16;
-constexpr int SAMPLE_N = SAMPLE_BLOCKS * SAMPLE_LEN;
-// per-thread digit counters, one row of NT per digit, padded so that the
-// transposed reduction (16 digits x 16 partial sums per wave) is free of
-// bank conflicts
-constexpr int CNT_STRIDE = NT + 16;
+// sample blocks of SAMPLE_LEN: more for long rows, where k is a smaller
+// fraction of the row (the sample lives in the three list arrays)
+constexpr int SAMPLE_BLOCKS_SHORT = 256;
+constexpr int SAMPLE_BLOCKS_LONG = 768;
+constexpr int64_t LONG_ROW = 65536;
+static_assert(SAMPLE_BLOCKS_LONG * SAMPLE_LEN <= 3 * CAP, "the sample lives in the list");
+
+// list entry tags: id in bits 0-28 (ids < 2^29), class in bits 29-30, and
+// bit 31 set when the entry's full score must be computed
+constexpr uint32_t ID_MASK = (1u << 29) - 1u;
+constexpr uint32_t C_OUT = 0u, C_IN = 1u, C_BAND = 2u;
+constexpr uint32_t RESCORE = 1u << 31;
+__device__ __forceinline__ uint32_t cls_of(uint32_t t) { return (t >> 29) & 3u; }
 
 struct SelShared {
-    alignas(16) uint32_t key[CAP];
-    alignas(16) int32_t id[CAP];
-    uint32_t cnt[16 * CNT_STRIDE];
-    uint32_t hist[16];
+    union {
+        struct {
+            alignas(16) uint32_t idc[CAP];  // tagged pool ids
+            alignas(16) float s[CAP];       // scores: approximate, then full where rescored
+            alignas(16) float d[CAP];       // bounds delta; then the entries to rescore
+        };
+        alignas(16) uint32_t sample[3 * CAP];  // sample keys, before the list is built
+    };
+    uint32_t hist[512];
     uint32_t tmp[8];
-    uint32_t wtot[8 * (NT / 64)];
+    uint32_t wtot[4 * (NT / 64)];
 };
 
 // Wave-level inclusive scans on DPP: row shifts 1, 2, 4, 8 within each row
@@ -81,15 +106,6 @@ struct MaxOp {
 
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int /*lane*/) {
     return wave_incl_scan_op(v, 0u, AddOp{});
-}
-
-// Sum over each row of 16 lanes, valid in lane 15 of the row.
-__device__ __forceinline__ uint32_t row16_sum(uint32_t v) {
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);
-    return v;
 }
 
 // Exclusive prefix over the workgroup; *total receives the sum.
@@ -157,79 +173,218 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, SelShar
     __syncthreads();
 }
 
-// Initial range [lo, hi] from the extreme keys: the aligned block of the
-// lowest nibble boundary above their highest differing bit; returns the
-// first digit shift (or -1 when all keys are equal).
-__device__ __forceinline__ int start_range(uint32_t mn, uint32_t mx, uint32_t& lo, uint32_t& hi) {
-    const uint32_t diff = mn ^ mx;
-    if (diff == 0) {
-        lo = hi = mn;
-        return -1;
+
+// Sum over the workgroup.
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, SelShared& sh) {
+    uint32_t tot;
+    (void)block_excl_scan(v, sh, &tot);
+    return tot;
+}
+
+// One wave's search of a 256-bin digit histogram (lane l holds bins
+// 4l .. 4l+3): the digit d whose in-range keys reach `remaining` when counted
+// from the top, with the count of keys above it and in it.  Exactly one lane
+// finds it when at least `remaining` keys are in range.
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t remaining, uint32_t& dg,
+                                           uint32_t& above_out, uint32_t& in_out) {
+    const int lane = threadIdx.x & 63;
+    uint32_t h[4], tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = hist[4 * lane + j];
+        tot += h[j];
     }
+    const uint32_t rev = wave_incl_scan((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (63 - lane), (int)tot), lane);
+    const uint32_t suffix = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (63 - lane), (int)rev);
+    // digit d: the in-range keys with a digit above d number suffix(d + 1)
+    uint32_t s_j = suffix;
+    int found = -1;
+    uint32_t above_f = 0, h_f = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t above = s_j - h[j];
+        if (above < remaining && s_j >= remaining) {
+            found = 4 * lane + j;
+            above_f = above;
+            h_f = h[j];
+        }
+        s_j = above;
+    }
+    const uint64_t who = __ballot(found >= 0);
+    const int src = who ? (int)__ffsll((unsigned long long)who) - 1 : 0;
+    dg = (uint32_t)__shfl(found, src);
+    above_out = (uint32_t)__shfl((int)above_f, src);
+    in_out = (uint32_t)__shfl((int)h_f, src);
+}
+
+// Digit shifts: the first 8-bit digit ends at the highest bit where lo and
+// hi differ (so the keys of one row, which share their top bits, spread over
+// all 256 bins), then 8 bits lower each pass, the last one clipped at bit 0
+// (its bins above the remaining bits are then constant).  -1: done.
+__device__ __forceinline__ int first_shift(uint32_t lo, uint32_t hi) {
+    const uint32_t diff = lo ^ hi;
+    if (diff == 0) return -1;
     const int top = 31 - __clz(diff);
-    const int shift = (top / 4) * 4;
-    const uint32_t mask = (shift + 4 >= 32) ? 0u : (0xFFFFFFFFu << (shift + 4));
-    lo = mn & mask;
-    hi = lo | ~mask;
-    return shift;
+    return top >= 7 ? top - 7 : 0;
+}
+__device__ __forceinline__ int next_shift(int shift) {
+    return shift >= 8 ? shift - 8 : (shift > 0 ? 0 : -1);
 }
 
-// Radix-16 refinement.  Precondition: at least `remaining` keys lie in
-// [lo, hi] and every key above hi is already kept.  On return the kept set is
-// {key > hi} plus the first `remaining` in-range keys in id order.
+// Narrow [lo, hi] to digit dg at `shift` (the bits of lo above the digit
+// are shared by every in-range key).
+__device__ __forceinline__ void narrow(uint32_t& lo, uint32_t& hi, int shift, uint32_t dg) {
+    const uint32_t keep = (shift + 8 >= 32) ? 0u : (lo & (0xFFFFFFFFu << (shift + 8)));
+    lo = keep | (dg << shift);
+    hi = lo | ((shift == 0) ? 0u : ((1u << shift) - 1u));
+}
+
+// Radix-256 narrowing over the keys of the member elements e < n of any
+// source: key_at(e, &key) returns whether e is a member.  Precondition: at
+// least `remaining` member keys lie in [lo, hi] and every member key above hi
+// is kept.  On return the kept set is {key > hi} plus the first `remaining`
+// member keys in [lo, hi] in element order.  With to_end the range is
+// narrowed to a single key (lo == hi, the k-th largest); otherwise it stops
+// as soon as every in-range key is kept.  Digits are counted with LDS
+// atomics (integer, so the counts do not depend on their order) and found by
+// one wave's suffix scan.
 template <class KeyAt>
-__device__ void refine(KeyAt key_at, int64_t n, int shift, uint32_t& lo, uint32_t& hi,
-                       uint32_t& remaining, SelShared& sh) {
-    const int tid = threadIdx.x;
-    for (; shift >= 0 && lo != hi; shift -= 4) {
-#pragma unroll
-        for (int d = 0; d < 16; ++d) sh.cnt[d * CNT_STRIDE + tid] = 0;
+__device__ void radix_narrow(int64_t n, KeyAt key_at, uint32_t& lo, uint32_t& hi,
+                             uint32_t& remaining, bool to_end, SelShared& sh) {
+    const int tid = threadIdx.x, wave = tid >> 6;
+    uint32_t* hist = sh.hist;
+    for (int shift = first_shift(lo, hi); shift >= 0 && lo != hi; shift = next_shift(shift)) {
+        for (int b = tid; b < 256; b += NT) hist[b] = 0;
+        __syncthreads();
         for (int64_t e = tid; e < n; e += NT) {
-            const uint32_t k = key_at(e);
-            if (k >= lo && k <= hi) sh.cnt[((k >> shift) & 15u) * CNT_STRIDE + tid] += 1;
+            uint32_t k;
+            if (key_at(e, k) && k >= lo && k <= hi) atomicAdd(&hist[(k >> shift) & 255u], 1u);
         }
         __syncthreads();
-        // digit tid/16 summed over threads (tid%16) + 16u, u = 0..15
-        uint32_t s = 0;
-        const uint32_t* c = &sh.cnt[(tid >> 4) * CNT_STRIDE + (tid & 15)];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) s += c[16 * u];
-        s = row16_sum(s);
-        if ((tid & 15) == 15) sh.hist[tid >> 4] = s;
-        __syncthreads();
-        uint32_t above = 0, hb = 0;
-        int b = 0;
-        for (int d = 15; d >= 0; --d) {
-            const uint32_t h = sh.hist[d];
-            if (above + h >= remaining) {
-                b = d;
-                hb = h;
-                break;
+        if (wave == 0) {
+            uint32_t dg, ab, hd;
+            find_digit(hist, remaining, dg, ab, hd);
+            if ((tid & 63) == 0) {
+                sh.tmp[0] = dg;
+                sh.tmp[1] = ab;
+                sh.tmp[2] = hd;
             }
-            above += h;
         }
-        remaining -= above;
-        const uint32_t keep = (shift + 4 >= 32) ? 0u : (lo & (0xFFFFFFFFu << (shift + 4)));
-        lo = keep | ((uint32_t)b << shift);
-        hi = lo | ((1u << shift) - 1u);
         __syncthreads();
-        if (hb == remaining) break;
+        const uint32_t dg = sh.tmp[0], above = sh.tmp[1], hd = sh.tmp[2];
+        __syncthreads();
+        remaining -= above;
+        narrow(lo, hi, shift, dg);
+        if (!to_end && hd == remaining) break;
     }
 }
 
-// A key tau with at least r of the SAMPLE_N sample keys (sh.key) >= tau,
-// and not many more: a 256-bin histogram linear in the scores' values (not
+// The highest bin b of a 256-bin histogram (one wave, lane l holding bins
+// 4l .. 4l+3) whose suffix sum (bins b .. 255) reaches r; -1 if none.
+__device__ __forceinline__ int top_bin(const uint32_t* hist, uint32_t r) {
+    const int lane = threadIdx.x & 63;
+    uint32_t h[4], tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = hist[4 * lane + j];
+        tot += h[j];
+    }
+    // inclusive scan over lanes in reverse order gives the suffix sums
+    const uint32_t rev = wave_incl_scan((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (63 - lane), (int)tot), lane);
+    const uint32_t suffix = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (63 - lane), (int)rev);
+    uint32_t s_j = suffix;
+    int found = -1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (s_j >= r) found = 4 * lane + j;
+        s_j -= h[j];
+    }
+    const uint32_t best = wave_incl_scan_op(found < 0 ? 0u : (uint32_t)found + 1u, 0u, MaxOp{});
+    return (int)__shfl((int)best, 63) - 1;
+}
+
+// Bin of a value in a 256-bin histogram linear in value from vmin (scale =
+// 256 / range); monotone non-decreasing in the value.
+__device__ __forceinline__ int value_bin(float x, float vmin, float scale) {
+    const float b = (x - vmin) * scale;
+    return b >= 255.0f ? 255 : (b > 0.0f ? (int)b : 0);
+}
+
+// Safe bounds on the k-th largest l and u keys of the list (at least k
+// entries): Lk <= the k-th largest l and Uk >= the k-th largest u.  One
+// sweep for the value range, one filling a 256-bin histogram of each,
+// linear in value, and one for the smallest l in the bins that hold the k
+// largest l and the largest u in the bins up to the one holding the k-th
+// largest u.  The bins widen the band by at most one bin each way.
+template <class Key2At>
+__device__ void band_bounds(int m, Key2At key2_at, uint32_t k, uint32_t& Lk, uint32_t& Uk,
+                            SelShared& sh) {
+    const int tid = threadIdx.x, wave = tid >> 6;
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int e = tid; e < m; e += NT) {
+        uint32_t lk, uk;
+        key2_at(e, lk, uk);
+        mn = min(mn, lk);
+        mx = max(mx, uk);
+    }
+    block_minmax(mn, mx, sh);
+    const float vmin = key_to_float(mn), vmax = key_to_float(mx);
+    const float scale = 256.0f / (vmax - vmin);
+    for (int b = tid; b < 512; b += NT) sh.hist[b] = 0;
+    __syncthreads();
+    for (int e = tid; e < m; e += NT) {
+        uint32_t lk, uk;
+        key2_at(e, lk, uk);
+        atomicAdd(&sh.hist[value_bin(key_to_float(lk), vmin, scale)], 1u);
+        atomicAdd(&sh.hist[256 + value_bin(key_to_float(uk), vmin, scale)], 1u);
+    }
+    __syncthreads();
+    if (wave < 2) {
+        const int b = top_bin(sh.hist + 256 * wave, k);
+        if ((tid & 63) == 0) sh.tmp[wave] = (uint32_t)b;
+    }
+    __syncthreads();
+    const int bl = (int)sh.tmp[0], bu = (int)sh.tmp[1];
+    __syncthreads();
+    uint32_t lmin = 0xFFFFFFFFu, umax = 0u;
+    for (int e = tid; e < m; e += NT) {
+        uint32_t lk, uk;
+        key2_at(e, lk, uk);
+        if (value_bin(key_to_float(lk), vmin, scale) >= bl) lmin = min(lmin, lk);
+        if (value_bin(key_to_float(uk), vmin, scale) <= bu) umax = max(umax, uk);
+    }
+    block_minmax(lmin, umax, sh);
+    Lk = lmin;
+    Uk = umax;
+}
+
+// Smallest and largest member key (min = 0xFFFFFFFF, max = 0 when none).
+template <class KeyAt>
+__device__ void member_minmax(int64_t n, KeyAt key_at, uint32_t& mn, uint32_t& mx, SelShared& sh) {
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
+    for (int64_t e = threadIdx.x; e < n; e += NT) {
+        uint32_t k;
+        if (key_at(e, k)) {
+            mn = min(mn, k);
+            mx = max(mx, k);
+        }
+    }
+    block_minmax(mn, mx, sh);
+}
+
+// A key tau with at least r of the ns sample keys (sh.sample) >= tau,
+// and not many more: a 256-bin histogram linear in the sampled values (not
 // in their bit patterns, which would lump the upper tail into one bin) gives
 // the highest bin b whose suffix holds r keys; tau is the smallest sample key
-// in bins >= b.  Any tau that leaves between k and CAP row elements above it
-// serves the compaction; the selection after it is exact.
-__device__ uint32_t sample_threshold(uint32_t r, SelShared& sh) {
+// in bins >= b.
+__device__ uint32_t sample_threshold(int ns, uint32_t r, SelShared& sh) {
     constexpr int NBIN = 256;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int e = tid; e < SAMPLE_N; e += NT) {
-        mn = min(mn, sh.key[e]);
-        mx = max(mx, sh.key[e]);
+    for (int e = tid; e < ns; e += NT) {
+        mn = min(mn, sh.sample[e]);
+        mx = max(mx, sh.sample[e]);
     }
     block_minmax(mn, mx, sh);
     if (mn == mx) return mn;
@@ -239,10 +394,10 @@ __device__ uint32_t sample_threshold(uint32_t r, SelShared& sh) {
         const float b = (key_to_float(key) - vmin) * scale;
         return b >= (float)(NBIN - 1) ? NBIN - 1 : (b > 0.0f ? (int)b : 0);
     };
-    uint32_t* hist = sh.cnt;  // NBIN counters
+    uint32_t* hist = sh.hist;
     for (int b = tid; b < NBIN; b += NT) hist[b] = 0;
     __syncthreads();
-    for (int e = tid; e < SAMPLE_N; e += NT) atomicAdd(&hist[bin_of(sh.key[e])], 1u);
+    for (int e = tid; e < ns; e += NT) atomicAdd(&hist[bin_of(sh.sample[e])], 1u);
     __syncthreads();
     if (wave == 0) {
         // lane l holds bins 4l .. 4l+3; suffix sums from the top bin down
@@ -252,10 +407,8 @@ __device__ uint32_t sample_threshold(uint32_t r, SelShared& sh) {
             h[j] = hist[4 * lane + j];
             tot += h[j];
         }
-        // inclusive scan over lanes in reverse order gives the suffix sum
         const uint32_t rev = wave_incl_scan((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (63 - lane), (int)tot), lane);
         const uint32_t suffix = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (63 - lane), (int)rev);
-        // bins of this lane: suffix(4l + j) = suffix - sum of h[0..j)
         uint32_t s_j = suffix;
         int found = -1;
 #pragma unroll
@@ -271,122 +424,209 @@ __device__ uint32_t sample_threshold(uint32_t r, SelShared& sh) {
     const int b_min = (int)sh.tmp[0];
     __syncthreads();
     uint32_t kmin = 0xFFFFFFFFu, dummy = 0u;
-    for (int e = tid; e < SAMPLE_N; e += NT) {
-        const uint32_t key = sh.key[e];
+    for (int e = tid; e < ns; e += NT) {
+        const uint32_t key = sh.sample[e];
         if (bin_of(key) >= b_min) kmin = min(kmin, key);
     }
     block_minmax(kmin, dummy, sh);
     return kmin;
 }
 
-// Radix-256 refinement of a list in LDS: the same contract as refine, with
-// 8-bit digits counted by LDS atomics (integer, so the counts do not depend
-// on their order) and the digit found by one wave's suffix scan: at most 4
-// passes instead of 8.
-__device__ void refine256(int m, uint32_t& lo, uint32_t& hi, uint32_t& remaining,
-                          SelShared& sh) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t* hist = sh.cnt;
-    const uint32_t diff = lo ^ hi;
-    if (diff == 0) return;
-    // highest differing bit of the range -> first 8-bit digit
-    int shift = ((31 - __clz(diff)) / 8) * 8;
-    for (; shift >= 0 && lo != hi; shift -= 8) {
-        for (int b = tid; b < 256; b += NT) hist[b] = 0;
-        __syncthreads();
-        for (int e = tid; e < m; e += NT) {
-            const uint32_t k = sh.key[e];
-            if (k >= lo && k <= hi) atomicAdd(&hist[(k >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (wave == 0) {
-            uint32_t h[4], tot = 0;
+// Ordered compaction: entries with flag(e) for e < n in element order go to
+// slots [0, count) through put(slot, e); returns count.  Thread tid takes a
+// contiguous segment of odd length, so that a wave's LDS reads at that
+// stride touch every bank once.
+template <class Flag, class Put>
+__device__ uint32_t compact(int n, Flag flag, Put put, SelShared& sh) {
+    const int tid = threadIdx.x;
+    const int seg = ((n + NT - 1) / NT) | 1;
+    const int e0 = min(n, tid * seg), e1 = min(n, e0 + seg);
+    uint32_t c = 0;
+    for (int e = e0; e < e1; ++e) c += flag(e);
+    uint32_t tot;
+    uint32_t pos = block_excl_scan(c, sh, &tot);
+    for (int e = e0; e < e1; ++e)
+        if (flag(e)) put(pos++, e);
+    return tot;
+}
+
+// ---------------------------------------------------------------- rescoring
+
+// The full score of pools for one query, with the scoring kernel's MFMA
+// sequence and epilogue (so that the value is bit for bit the one the
+// scoring kernel stores when it includes the correction): per lane
+// (col = lane % 32, half = lane / 32) the A operand is row col of the
+// query's packed tile, the B operand pool cand[col]; 8 (d / 16) bf16 MFMAs
+// with hi, then the scaled E4M3 MFMAs with lo, into one 32 x 32 accumulator;
+// then per query sum_h w_h relu(acc), the rows of the query summed in the
+// scoring kernel's order.  One wave scores 32 pools at a time.
+template <int HI, int DI>
+struct Rescorer {
+    static constexpr QueryTileGeom G = query_tile_geom(DI);
+    static constexpr int QPT = 32 / HI;
+    static constexpr int NSB = DI / 16;
+    static constexpr int NSF = (DI + 63) / 64;
+    bf16x8 af[NSB];
+    i32x8 af8[NSF];
+    float wv[16];
+    int qsc;
+    int qi;
+
+    __device__ void load(const uint8_t* tiles, int64_t i) {
+        const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+        const uint8_t* tile = tiles + (i / QPT) * G.tb;
+        qi = (int)(i % QPT);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                h[j] = hist[4 * lane + j];
-                tot += h[j];
-            }
-            const uint32_t rev = wave_incl_scan((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (63 - lane), (int)tot), lane);
-            const uint32_t suffix = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (63 - lane), (int)rev);
-            // digit d: count of in-range keys with digit > d is suffix(d + 1)
-            uint32_t s_j = suffix;
-            int found = -1;
-            uint32_t above_f = 0, h_f = 0;
+        for (int s = 0; s < NSB; ++s)
+            af[s] = as_bf16x8(ldg16(tile + tile_bf16_piece(G, col, 2 * s + half)));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t above = s_j - h[j];  // keys with a larger digit
-                if (above < remaining && s_j >= remaining) {
-                    found = 4 * lane + j;
-                    above_f = above;
-                    h_f = h[j];
-                }
-                s_j = above;
+        for (int s = 0; s < NSF; ++s) {
+            u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+            if (64 * s + 32 * half < DI) {
+                x0 = ldg16(tile + tile_fp8_piece(G, col, 4 * s + 2 * half));
+                x1 = ldg16(tile + tile_fp8_piece(G, col, 4 * s + 2 * half + 1));
             }
-            // exactly one lane finds the digit
-            const uint64_t who = __ballot(found >= 0);
-            const int src = (int)__ffsll((unsigned long long)who) - 1;
-            const int d = __shfl(found, src);
-            const uint32_t ab = (uint32_t)__shfl((int)above_f, src);
-            const uint32_t hd = (uint32_t)__shfl((int)h_f, src);
-            if (lane == 0) {
-                sh.tmp[0] = (uint32_t)d;
-                sh.tmp[1] = ab;
-                sh.tmp[2] = hd;
-            }
+            af8[s] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                           (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
         }
-        __syncthreads();
-        const uint32_t d = sh.tmp[0], above = sh.tmp[1], hd = sh.tmp[2];
-        __syncthreads();
-        remaining -= above;
-        const uint32_t keep = (shift + 8 >= 32) ? 0u : (lo & (0xFFFFFFFFu << (shift + 8)));
-        lo = keep | (d << shift);
-        hi = lo | ((shift == 0) ? 0u : ((1u << shift) - 1u));
-        if (hd == remaining) break;
+        qsc = (int)tile[G.qb + 128 + col];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(tile + G.qb + 4 * (8 * g4 + 4 * half));
+            wv[4 * g4 + 0] = w4[0];
+            wv[4 * g4 + 1] = w4[1];
+            wv[4 * g4 + 2] = w4[2];
+            wv[4 * g4 + 3] = w4[3];
+        }
+    }
+
+    // Score of pool p (this lane's column); the value is valid on lane
+    // owner() of each column (col or col + 32).
+    __device__ float score(const uint16_t* khi, const uint8_t* klo, const uint8_t* klo_scale,
+                           int64_t p) const {
+        const int lane = threadIdx.x & 63, half = lane >> 5;
+        bf16x8 bhi[NSB];
+        i32x8 blo[NSF];
+#pragma unroll
+        for (int s = 0; s < NSB; ++s) bhi[s] = as_bf16x8(ldg16(khi + p * DI + 16 * s + 8 * half));
+#pragma unroll
+        for (int s = 0; s < NSF; ++s) {
+            const int d0 = 64 * s + 32 * half;
+            u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+            if (d0 < DI) {
+                x0 = ldg16(klo + p * DI + d0);
+                x1 = ldg16(klo + p * DI + d0 + 16);
+            }
+            blo[s] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                           (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+        }
+        const int bsc = (int)klo_scale[p];
+        f32x16 acc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NSB; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], bhi[s], acc, 0, 0, 0);
+#pragma unroll
+        for (int s = 0; s < NSF; ++s)
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af8[s], blo[s], acc, 0, 0, 0, qsc,
+                                                                  0, bsc);
+        float part[4];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            float sacc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc += wv[4 * g4 + i] * relu(acc[4 * g4 + i]);
+            part[g4] = sacc;
+        }
+        // (selects, not an indexed register array)
+        auto pick = [&](int j) {
+            return j == 0 ? part[0] : j == 1 ? part[1] : j == 2 ? part[2] : part[3];
+        };
+        float v;
+        if constexpr (HI == 4) {
+            // rows 8*g4 + 4*half + i are the 4 heads of query 2*g4 + half
+            v = pick(qi >> 1);
+        } else if constexpr (HI == 32) {
+            v = add_halves((part[0] + part[1]) + (part[2] + part[3]));
+        } else if constexpr (HI == 16) {
+            v = add_halves(qi == 0 ? part[0] + part[1] : part[2] + part[3]);
+        } else {
+            v = add_halves(pick(qi));
+        }
+        return canonical_zero(v);
+    }
+
+    // the lane that holds column col's value
+    __device__ int owner(int col) const { return HI == 4 ? col + 32 * (qi & 1) : col; }
+};
+
+// Rescore the entries j < nr whose tag tag_of(j) has the RESCORE bit: the
+// tag's id bits name the pool, and its full score goes to put(j, value).
+// The 4 waves take blocks of 32 entries in turn and skip blocks with nothing
+// to rescore.
+template <int HI, int DI, class TagOf, class Put>
+__device__ void rescore(uint32_t nr, TagOf tag_of, Put put, const SelectArgs& a, int64_t i) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31;
+    const uint32_t nblk = (nr + 31) / 32;
+    if ((uint32_t)wave >= nblk) return;
+    Rescorer<HI, DI> r;
+    bool loaded = false;
+    int own = 0;
+    for (uint32_t b = wave; b < nblk; b += 4) {
+        const uint32_t j = 32 * b + col;
+        // columns past the end score entry 32 b (any valid pool) and are dropped
+        const uint32_t t = tag_of(j < nr ? j : 32 * b);
+        const bool keep = j < nr && (t & RESCORE) != 0u;
+        if (__ballot(keep) == 0) continue;
+        if (!loaded) {
+            r.load(a.tiles, i);
+            own = r.owner(col);
+            loaded = true;
+        }
+        const float v = r.score(a.khi, a.klo, a.klo_scale, (int64_t)(t & ID_MASK));
+        if (lane == own && keep) put(j, v);
     }
 }
 
-// Emit the kept ids of the LDS list (already in id order) to out[0..k).
-__device__ void emit_from_list(int m, uint32_t lo, uint32_t hi, uint32_t remaining,
-                               SelShared& sh, int32_t* out, float* score_out, int k_out) {
+// ---------------------------------------------------------------- emission
+
+// Emit the kept ids of the list (in id order) to out[0..k): every C_IN
+// entry, and the C_BAND entries with key > hi plus the first `remaining`
+// with key in [lo, hi].
+__device__ void emit_list(int m, uint32_t lo, uint32_t hi, uint32_t remaining, SelShared& sh,
+                          int32_t* out, float* score_out, int k_out) {
     const int tid = threadIdx.x;
-    // contiguous segments of odd length: a wave's lanes then read LDS words
-    // at an odd stride, which touches every bank once
     const int seg = ((m + NT - 1) / NT) | 1;
     const int e0 = min(m, tid * seg), e1 = min(m, e0 + seg);
     uint32_t n_in = 0;
     for (int e = e0; e < e1; ++e) {
-        const uint32_t k = sh.key[e];
-        n_in += (k >= lo && k <= hi);
+        const uint32_t k = order_key(sh.s[e]);
+        n_in += cls_of(sh.idc[e]) == C_BAND && k >= lo && k <= hi;
     }
     uint32_t tot;
-    uint32_t rank = block_excl_scan(n_in, sh, &tot);
+    const uint32_t rank0 = block_excl_scan(n_in, sh, &tot);
+    auto take = [&](int e, uint32_t& r) {
+        const uint32_t c = cls_of(sh.idc[e]);
+        if (c == C_IN) return true;
+        if (c != C_BAND) return false;
+        const uint32_t k = order_key(sh.s[e]);
+        if (k > hi) return true;
+        if (k < lo) return false;
+        return r++ < remaining;
+    };
     uint32_t n_sel = 0;
     {
-        uint32_t r = rank;
-        for (int e = e0; e < e1; ++e) {
-            const uint32_t k = sh.key[e];
-            if (k > hi) {
-                ++n_sel;
-            } else if (k >= lo) {
-                n_sel += (r < remaining);
-                ++r;
-            }
-        }
+        uint32_t r = rank0;
+        for (int e = e0; e < e1; ++e) n_sel += take(e, r);
     }
     uint32_t pos = block_excl_scan(n_sel, sh, &tot);
+    uint32_t r = rank0;
     for (int e = e0; e < e1; ++e) {
-        const uint32_t k = sh.key[e];
-        bool take = false;
-        if (k > hi) {
-            take = true;
-        } else if (k >= lo) {
-            take = rank < remaining;
-            ++rank;
-        }
-        if (take) {
+        if (take(e, r)) {
             if (pos < (uint32_t)k_out) {
-                out[pos] = sh.id[e];
-                if (score_out) score_out[pos] = key_to_float(k);
+                out[pos] = (int32_t)(sh.idc[e] & ID_MASK);
+                if (score_out) score_out[pos] = sh.s[e];
             }
             ++pos;
         }
@@ -402,20 +642,17 @@ __device__ __forceinline__ f32x4 load_row4(const float* row, int64_t e, int64_t 
     return v;
 }
 
-// Exact selection directly over the row in global memory.
-__device__ void select_global(const float* row, int64_t n, int k, SelShared& sh, int32_t* out,
-                              float* score_out) {
+// Exact selection directly over a row of final scores in global memory.
+__device__ void select_row(const float* row, int64_t n, int k, SelShared& sh, int32_t* out,
+                           float* score_out) {
     const int tid = threadIdx.x;
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int64_t e = tid; e < n; e += NT) {
-        const uint32_t kk = order_key(row[e]);
-        mn = min(mn, kk);
-        mx = max(mx, kk);
-    }
-    block_minmax(mn, mx, sh);
+    auto key_at = [&](int64_t e, uint32_t& key) {
+        key = order_key(row[e]);
+        return true;
+    };
     uint32_t lo, hi, remaining = (uint32_t)k;
-    const int shift = start_range(mn, mx, lo, hi);
-    refine([&](int64_t e) { return order_key(row[e]); }, n, shift, lo, hi, remaining, sh);
+    member_minmax(n, key_at, lo, hi, sh);
+    radix_narrow(n, key_at, lo, hi, remaining, false, sh);
 
     // ordered emission, one 4-element group per thread per tile
     uint32_t rank_base = 0, pos_base = 0;
@@ -436,26 +673,26 @@ __device__ void select_global(const float* row, int64_t n, int k, SelShared& sh,
         }
         uint32_t tot_in;
         uint32_t rank = rank_base + block_excl_scan(n_in, sh, &tot_in);
-        bool take[4];
+        bool tk[4];
         uint32_t n_sel = 0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            take[u] = false;
+            tk[u] = false;
             if (e0 + u < n) {
                 if (kk[u] > hi) {
-                    take[u] = true;
+                    tk[u] = true;
                 } else if (kk[u] >= lo) {
-                    take[u] = rank < remaining;
+                    tk[u] = rank < remaining;
                     ++rank;
                 }
             }
-            n_sel += take[u];
+            n_sel += tk[u];
         }
         uint32_t tot_sel;
         uint32_t pos = pos_base + block_excl_scan(n_sel, sh, &tot_sel);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            if (take[u]) {
+            if (tk[u]) {
                 if (pos < (uint32_t)k) {
                     out[pos] = (int32_t)(e0 + u);
                     if (score_out) score_out[pos] = key_to_float(kk[u]);
@@ -467,6 +704,47 @@ __device__ void select_global(const float* row, int64_t n, int k, SelShared& sh,
     }
 }
 
+// Slow path for an approximate row that does not fit the list: L and U by
+// radix over the row, every pool that needs its full score rescored in place
+// (the band; with score_out also the certain ones), then the exact selection
+// over the row.  Pools outside the band keep their approximate scores, which
+// lie strictly above U (kept) or below L (dropped) and so cannot change the
+// set.
+template <int HI, int DI>
+__device__ void select_row_bounded(const SelectArgs& a, int64_t i, float* row, int64_t n, float A,
+                                   SelShared& sh, int32_t* out, float* score_out) {
+    const int tid = threadIdx.x;
+    uint32_t Lk, Uk;
+    band_bounds((int)n, [&](int64_t e, uint32_t& lk, uint32_t& uk) {
+        const float x = row[e], dl = A * a.mu[e];
+        lk = order_key(x - dl);
+        uk = order_key(x + dl);
+    }, (uint32_t)a.k_pools, Lk, Uk, sh);
+    uint32_t* ids = reinterpret_cast<uint32_t*>(sh.d);
+    for (int64_t base = 0; base < n; base += CAP) {
+        const int w = (int)min((int64_t)CAP, n - base);
+        // this window's pools in LDS first: the rescoring below writes the row
+        for (int e = tid; e < w; e += NT) {
+            const float x = row[base + e], dl = A * a.mu[base + e];
+            const uint32_t lk = order_key(x - dl), uk = order_key(x + dl);
+            const bool band = uk >= Lk && lk <= Uk;
+            const bool in = lk > Uk;
+            sh.idc[e] = (dl > 0.0f && (band || (in && score_out))) ? 1u : 0u;
+        }
+        __syncthreads();
+        const uint32_t nr = compact(w, [&](int e) { return sh.idc[e] != 0u; },
+                                    [&](uint32_t slot, int e) { ids[slot] = (uint32_t)(base + e); },
+                                    sh);
+        __syncthreads();
+        rescore<HI, DI>(nr, [&](uint32_t j) { return ids[j] | RESCORE; },
+                        [&](uint32_t j, float v) { row[ids[j]] = v; }, a, i);
+        __threadfence_block();
+        __syncthreads();
+    }
+    select_row(row, n, a.k_pools, sh, out, score_out);
+}
+
+template <int HI, int DI, bool BOUNDS>
 __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
     __shared__ SelShared sh;
     const int tid = threadIdx.x;
@@ -477,46 +755,72 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
     const int k = a.k_pools;
     int32_t* out = a.idx_out + qrow * k;
     float* sout = a.score_out ? a.score_out + qrow * k : nullptr;
-    const float* row = a.buf + (int64_t)i * a.ld;
+    float* row = a.buf + (int64_t)i * a.ld;
+    const float A = BOUNDS ? a.qbound[i] : 0.0f;
+    auto delta = [&](int64_t p) { return BOUNDS ? A * a.mu[p] : 0.0f; };
 
     if (n <= k) {
-        for (int j = tid; j < k; j += NT) {
-            out[j] = j < n ? j : -1;
-            if (sout) sout[j] = j < n ? row[j] : -INFINITY;
+        for (int j = tid; j < k; j += NT) out[j] = j < n ? j : -1;
+        if (!sout) return;
+        // the scores of every eligible pool, rescored where they are approximate
+        for (int j = tid; j < (int)n; j += NT) {
+            sh.s[j] = row[j];
+            sh.idc[j] = (BOUNDS && delta(j) > 0.0f) ? 1u : 0u;
         }
+        __syncthreads();
+        if constexpr (BOUNDS) {
+            uint32_t* ids = reinterpret_cast<uint32_t*>(sh.d);
+            const uint32_t nr = compact((int)n, [&](int e) { return sh.idc[e] != 0u; },
+                                        [&](uint32_t slot, int e) { ids[slot] = (uint32_t)e; }, sh);
+            __syncthreads();
+            rescore<HI, DI>(nr, [&](uint32_t j) { return ids[j] | RESCORE; },
+                            [&](uint32_t j, float v) { sh.s[ids[j]] = v; }, a, i);
+            __syncthreads();
+        }
+        for (int j = tid; j < k; j += NT) sout[j] = j < n ? sh.s[j] : -INFINITY;
         return;
     }
 
     int m = 0;  // list length
     if (n <= CAP) {
-        // whole row into the list; rows are 16-byte aligned and padded to 4
+        // the whole row; rows are 16-byte aligned and padded to 4
         for (int e = 4 * tid; e < (int)n; e += 4 * NT) {
             const f32x4 v = load_row4(row, e, n);
-            *reinterpret_cast<u32x4*>(&sh.key[e]) =
-                u32x4{order_key(v[0]), order_key(v[1]), order_key(v[2]), order_key(v[3])};
-            *reinterpret_cast<u32x4*>(&sh.id[e]) =
+            *reinterpret_cast<f32x4*>(&sh.s[e]) = v;
+            *reinterpret_cast<u32x4*>(&sh.idc[e]) =
                 u32x4{(uint32_t)e, (uint32_t)e + 1, (uint32_t)e + 2, (uint32_t)e + 3};
+            if constexpr (BOUNDS) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sh.d[e + u] = e + u < n ? delta(e + u) : 0.0f;
+            } else {
+                *reinterpret_cast<f32x4*>(&sh.d[e]) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
         }
         m = (int)n;
         __syncthreads();
     } else {
-        // threshold from a sample of SAMPLE_BLOCKS cache-line blocks
-        for (int s4 = tid; s4 < SAMPLE_N / 4; s4 += NT) {
+        // threshold on the l keys from nb blocks of SAMPLE_LEN
+        const int nb = n > LONG_ROW ? SAMPLE_BLOCKS_LONG : SAMPLE_BLOCKS_SHORT;
+        const int ns = nb * SAMPLE_LEN;
+        for (int s4 = tid; s4 < ns / 4; s4 += NT) {
             const int b = (4 * s4) / SAMPLE_LEN, u = (4 * s4) % SAMPLE_LEN;
-            const int64_t start = ((int64_t)b * n / SAMPLE_BLOCKS) & ~(int64_t)(SAMPLE_LEN - 1);
-            const f32x4 v = *reinterpret_cast<const f32x4*>(row + start + u);
-            *reinterpret_cast<u32x4*>(&sh.key[4 * s4]) =
-                u32x4{order_key(v[0]), order_key(v[1]), order_key(v[2]), order_key(v[3])};
+            const int64_t e = (((int64_t)b * n / nb) & ~(int64_t)(SAMPLE_LEN - 1)) + u;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(row + e);
+            u32x4 kk;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kk[j] = order_key(v[j] - delta(e + j));
+            *reinterpret_cast<u32x4*>(&sh.sample[4 * s4]) = kk;
         }
         __syncthreads();
-        const float mu = (float)k * (float)SAMPLE_N / (float)n;
-        uint32_t r = (uint32_t)ceilf(mu + 4.0f * sqrtf(mu) + 4.0f);
-        if (r > (uint32_t)SAMPLE_N) r = SAMPLE_N;
-        const uint32_t tau = sample_threshold(r, sh);  // at least r sample keys are >= tau
+        const float mu = (float)k * (float)ns / (float)n;
+        uint32_t r = (uint32_t)ceilf(mu + 5.0f * sqrtf(mu) + 8.0f);
+        if (r > (uint32_t)ns) r = ns;
+        const uint32_t tau = sample_threshold(ns, r, sh);  // at least r sample l keys are >= tau
         __syncthreads();
 
-        // ordered compaction of {key >= tau}: batches of VB 16-byte loads per
-        // thread, the next batch in flight while the current one is compacted
+        // ordered compaction of {u key >= tau}: batches of VB 16-byte loads per
+        // thread, the next batch in flight while the current one is compacted;
+        // cnt_l counts the pools with l key >= tau
         constexpr int VB = 4;
         constexpr int BATCH = 4 * NT * VB;
         f32x4 cur[VB], nxt[VB];
@@ -528,18 +832,29 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
                              : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             }
         };
-        const float tau_f = key_to_float(tau);
-        uint32_t count = 0;
+        uint32_t count = 0, cnt_l = 0;
         fetch(0, cur);
         for (int64_t base = 0; base < n; base += BATCH) {
             if (base + BATCH < n) fetch(base + BATCH, nxt);
             uint32_t c[VB], off[VB];
+            f32x4 dl[VB];
 #pragma unroll
             for (int u = 0; u < VB; ++u) {
                 const int64_t e = base + (int64_t)(u * NT + tid) * 4;
+                if constexpr (BOUNDS) {
+                    const f32x4 mu4 = e < n ? *reinterpret_cast<const f32x4*>(a.mu + e)
+                                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    dl[u] = A * mu4;
+                } else {
+                    dl[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
                 uint32_t cc = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) cc += (e + j < n) && cur[u][j] >= tau_f;
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = e + j < n;
+                    cc += ok && order_key(cur[u][j] + dl[u][j]) >= tau;
+                    if constexpr (BOUNDS) cnt_l += ok && order_key(cur[u][j] - dl[u][j]) >= tau;
+                }
                 c[u] = cc;
             }
             const uint32_t tot = block_excl_scan_slots<VB>(c, off, sh, sh.wtot);
@@ -550,10 +865,11 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
                 uint32_t pos = count + off[u];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    if (e + j < n && cur[u][j] >= tau_f) {
+                    if (e + j < n && order_key(cur[u][j] + dl[u][j]) >= tau) {
                         if (pos < (uint32_t)CAP) {
-                            sh.key[pos] = order_key(cur[u][j]);
-                            sh.id[pos] = (int32_t)(e + j);
+                            sh.s[pos] = cur[u][j];
+                            sh.d[pos] = dl[u][j];
+                            sh.idc[pos] = (uint32_t)(e + j);
                         }
                         ++pos;
                     }
@@ -563,31 +879,103 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
 #pragma unroll
             for (int u = 0; u < VB; ++u) cur[u] = nxt[u];
         }
+        if constexpr (BOUNDS) cnt_l = block_sum(cnt_l, sh);
+        else cnt_l = count;
         __syncthreads();
-        if (count < (uint32_t)k || count > (uint32_t)CAP) {
-            select_global(row, n, k, sh, out, sout);
+        if (count > (uint32_t)CAP || cnt_l < (uint32_t)k) {
+            if constexpr (BOUNDS) {
+                if (A > 0.0f) {
+                    select_row_bounded<HI, DI>(a, i, row, n, A, sh, out, sout);
+                    return;
+                }
+            }
+            select_row(row, n, k, sh, out, sout);
             return;
         }
         m = (int)count;
     }
 
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int e = tid; e < m; e += NT) {
-        mn = min(mn, sh.key[e]);
-        mx = max(mx, sh.key[e]);
+    if constexpr (!BOUNDS) {
+        // final scores: one selection over the whole list
+        for (int e = tid; e < m; e += NT) sh.idc[e] |= C_BAND << 29;
+        __syncthreads();
+        auto key_at = [&](int64_t e, uint32_t& key) {
+            key = order_key(sh.s[e]);
+            return true;
+        };
+        uint32_t lo, hi, remaining = (uint32_t)k;
+        member_minmax(m, key_at, lo, hi, sh);
+        radix_narrow(m, key_at, lo, hi, remaining, false, sh);
+        emit_list(m, lo, hi, remaining, sh, out, sout, k);
+        return;
     }
-    block_minmax(mn, mx, sh);
-    uint32_t lo = mn, hi = mx, remaining = (uint32_t)k;
-    refine256(m, lo, hi, remaining, sh);
-    emit_from_list(m, lo, hi, remaining, sh, out, sout, k);
+    // bounds on L and U over the list
+    uint32_t Lk, Uk;
+    band_bounds(m, [&](int64_t e, uint32_t& lk, uint32_t& uk) {
+        const float x = sh.s[e], dl = sh.d[e];
+        lk = order_key(x - dl);
+        uk = order_key(x + dl);
+    }, (uint32_t)k, Lk, Uk, sh);
+    // classify: certain (l > U), band (u >= L, l <= U), dropped (u < L)
+    uint32_t n_in = 0;
+    for (int e = tid; e < m; e += NT) {
+        const float x = sh.s[e], dl = sh.d[e];
+        const uint32_t lk = order_key(x - dl), uk = order_key(x + dl);
+        const uint32_t c = lk > Uk ? C_IN : (uk >= Lk ? C_BAND : C_OUT);
+        const bool need = dl > 0.0f && (c == C_BAND || (c == C_IN && sout));
+        sh.idc[e] |= (c << 29) | (need ? RESCORE : 0u);
+        n_in += c == C_IN;
+    }
+    n_in = block_sum(n_in, sh);
+    __syncthreads();
+    // the band and the entries to rescore, in list order
+    uint32_t* pos = reinterpret_cast<uint32_t*>(sh.d);
+    const uint32_t np = compact(m, [&](int e) {
+        const uint32_t t = sh.idc[e];
+        return cls_of(t) == C_BAND || (t & RESCORE) != 0u;
+    }, [&](uint32_t slot, int e) { pos[slot] = (uint32_t)e; }, sh);
+    __syncthreads();
+    rescore<HI, DI>(np, [&](uint32_t j) { return sh.idc[pos[j]]; },
+                    [&](uint32_t j, float v) { sh.s[pos[j]] = v; }, a, i);
+    __syncthreads();
+    // the remaining k - n_in from the band, by full score, ties to the lower id
+    auto band_key = [&](int64_t j, uint32_t& key) {
+        key = order_key(sh.s[pos[j]]);
+        return cls_of(sh.idc[pos[j]]) == C_BAND;
+    };
+    uint32_t lo, hi, remaining = (uint32_t)k - n_in;
+    member_minmax(np, band_key, lo, hi, sh);
+    radix_narrow(np, band_key, lo, hi, remaining, false, sh);
+    emit_list(m, lo, hi, remaining, sh, out, sout, k);
+}
+
+template <int HI>
+hipError_t launch_bounded_h(const SelectArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)a.rows);
+    switch (a.d_idx) {
+        case 64: topk_select_kernel<HI, 64, true><<<grid, NT, 0, stream>>>(a); break;
+        case 96: topk_select_kernel<HI, 96, true><<<grid, NT, 0, stream>>>(a); break;
+        case 128: topk_select_kernel<HI, 128, true><<<grid, NT, 0, stream>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
-    topk_select_kernel<<<dim3((unsigned)a.rows), NT, 0, stream>>>(a);
-    return hipGetLastError();
+    if (!a.qbound) {
+        topk_select_kernel<32, 128, false><<<dim3((unsigned)a.rows), NT, 0, stream>>>(a);
+        return hipGetLastError();
+    }
+    switch (a.h_idx) {
+        case 4: return launch_bounded_h<4>(a, stream);
+        case 8: return launch_bounded_h<8>(a, stream);
+        case 16: return launch_bounded_h<16>(a, stream);
+        case 32: return launch_bounded_h<32>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace dsa

@@ -236,6 +236,53 @@ def test_large_row_paths_and_sampling():
     assert np.all(idx0.cpu().numpy() == np.arange(wl.k_pools)[None, :])
 
 
+def _host_topk_ids(scores, n, k):
+    """Exact top-k of one row of fp32 scores by (-score, id), ascending ids,
+    -1 padded: the selection rule restated on the host."""
+    if n <= k:
+        return np.concatenate([np.arange(n), np.full(k - n, -1)]).astype(np.int32)
+    order = np.lexsort((np.arange(n), -scores[:n].astype(np.float64)))
+    return np.sort(order[:k]).astype(np.int32)
+
+
+@pytest.mark.parametrize("near_constant", [False, True])
+def test_selection_equals_exact_topk_of_full_scores(near_constant):
+    # The chunk buffer holds scores taken without the E4M3 correction; the
+    # selection rescores only the pools its error bound cannot decide.  The
+    # kept ids must be exactly the top-k of the full scores, which
+    # dsa_index_scores returns (same MFMA sequence).  Near-constant keys put
+    # nearly every pool within the bound of the threshold, so long rows
+    # overflow the LDS list and take the slow path in global memory.
+    wl = inputs.custom("full_topk", s_q=192, s_k=24576, q_pos0=24384, h_idx=32, d_idx=128,
+                       k_pools=512, h=16, d=128, idx_std=1 / math.sqrt(128),
+                       number=381 if near_constant else 380)
+    x = inputs.make_inputs(wl, attention=False)
+    if near_constant:
+        rng = np.random.default_rng(7)
+        base = rng.standard_normal(wl.d_idx).astype(np.float32) / np.float32(math.sqrt(128))
+        noise = rng.standard_normal((wl.s_k, wl.d_idx)).astype(np.float32)
+        x["k_idx"] = torch.from_numpy(base[None, :] * (1 + np.float32(0.01) * noise)).to(
+            torch.bfloat16)
+    dev = torch.device("cuda")
+    q_idx, k_idx, w = x["q_idx"].to(dev), x["k_idx"].to(dev), x["w"].to(dev)
+    idx, sc = dsa.dsa_index_score_topk(q_idx, k_idx, w, wl.k_pools, q_pos0=wl.q_pos0,
+                                       chunk_q=64, want_scores=True)
+    full = dsa.dsa_index_scores(q_idx, k_idx, w, row0=0, n_rows=wl.s_q, q_pos0=wl.q_pos0)
+    torch.cuda.synchronize()
+    idx, sc, full = idx.cpu().numpy(), sc.cpu().numpy(), full.cpu().numpy()
+    for i in range(wl.s_q):
+        n = min((wl.q_pos0 + i) // 4, wl.n_pools)
+        want = _host_topk_ids(full[i], n, wl.k_pools)
+        assert np.array_equal(idx[i], want), f"row {i}: ids differ from the full-score top-k"
+        sel = want >= 0
+        assert np.array_equal(sc[i][sel].view(np.uint32), full[i][want[sel]].view(np.uint32)), \
+            f"row {i}: selected scores differ from the full scores"
+    if near_constant:
+        # and against the oracle, within the parity rules
+        run_case(wl, rows=np.arange(0, wl.s_q, 16), chunk_q=64, x=x, attention=False,
+                 check_scores=False)
+
+
 def test_deterministic_bitwise():
     wl = inputs.custom("determinism", s_q=1500, s_k=1500, h_idx=32, d_idx=128, k_pools=64,
                        h=16, d=128, number=360)
