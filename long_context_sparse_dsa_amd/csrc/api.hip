@@ -405,6 +405,10 @@ static dsa_status index_score_topk(const void* q_idx, const void* k_idx, const f
             a.n_chunk = n_chunk;
             a.buf = buf;
             a.ld = ld;
+            if (dtype == DSA_BF16) {
+                a.qbound = reinterpret_cast<const float*>(ws + L.qbound);
+                a.mu = reinterpret_cast<const float*>(ws + L.mu);
+            }
             Timed tm(K_SCORE, s);
             e = dsa::launch_index_score(a, s);
             if (e != hipSuccess) return hip_fail(e, "index_score launch");

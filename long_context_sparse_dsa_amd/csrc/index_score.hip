@@ -339,7 +339,7 @@ struct QTile {
 // Rows past the chunk are zero with weight 0.
 //
 // qbound (optional) [rows] fp32 receives each query's factor of the score
-// error bound (see pool_keys_bf16_kernel):
+// error bound (see pool_keys_bf16_kernel), and the tile a copy of it:
 //   A = (1 + 2^-8) sum_h |w_h| max(||q_h||, ||Q8_h||),
 // Q8_h the decoded E4M3 row; the heads are summed in order.
 template <int HI, int DI>
@@ -407,7 +407,9 @@ __global__ __launch_bounds__(256) void pack_queries_kernel(const uint16_t* __res
             const int64_t qi = tile * QPT + threadIdx.x;
             float a = 0.0f;
             for (int hh = 0; hh < HI; ++hh) a += rowbound[threadIdx.x * HI + hh];
-            if (qi < rows) qbound[qi] = a * (1.0f + 0x1p-8f);
+            a *= 1.0f + 0x1p-8f;
+            if (qi < rows) qbound[qi] = a;
+            reinterpret_cast<float*>(dst + T::G.qb + 160)[threadIdx.x] = a;
         }
     }
 }
@@ -468,6 +470,8 @@ struct ScoreK {
     int64_t n_pools;
     float* buf;
     int64_t ld;
+    const float* qbound;        // without the correction: [rows] per-query bound factors
+    const float* mu;            // and [P] per-pool bound factors
 };
 
 // bf16 32x32x16 MFMA: lane l supplies A row (l % 32) and B column (l % 32),
@@ -489,10 +493,13 @@ struct ScoreK {
 //
 // EXACT = false: the chunk-buffer contract of ScoreArgs (any entry may be
 // written, ineligible pools get -inf).  EXACT = true: only eligible entries of
-// rows [0, rows) are stored.  LO = false: the correction q . lo is left out
-// (scores from hi alone, within the bound A mu_p of the full score, see
-// pool_keys_bf16_kernel); the selection rescores the pools near its
-// threshold with the full sequence of MFMAs below.
+// rows [0, rows) are stored.  LO = false: the correction q . lo is left out;
+// the score s~ from hi alone is within A mu_p of the full score (see
+// pool_keys_bf16_kernel), and the buffer receives the upper bound
+// u = fma(A, mu_p, s~), from which the selection takes both bounds
+// (s~ + A mu_p and u - 2 A mu_p) without reading mu for every pool; it
+// rescores the pools near its threshold with the full sequence of MFMAs
+// below.
 template <int HI, int DI, int NB, bool EXACT, bool LO>
 __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     static_assert(NB == 2, "the epilogue pairs the two pool blocks of a wave");
@@ -557,7 +564,8 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     // buffers deep: the loads for tile j + NBUF - 1 are issued at the start
     // of tile j.  Thread tid moves 16-byte pieces tid + 256u (loads clamped to
     // the last piece; LDS slots past the query data are spare) and one dword
-    // of the weights/scales tail (w at dwords 0-31, scale bytes in 32-39).
+    // of the tail (w at dwords 0-31, scale bytes in 32-39, the queries' bound
+    // factors in 40-47).
     // Lane l of a wave lands at the wave's LDS base + l * size, so each
     // instruction fills a contiguous 1 KiB (256 B) slice.
     constexpr int D = NBUF - 1;
@@ -567,7 +575,7 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u)
         gsrc[u] = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb + 16 * min(tid + 256 * u, T::NPQ - 1);
-    gsrc[CPT] = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb + T::G.qb + 4 * min(tid, 39);
+    gsrc[CPT] = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb + T::G.qb + 4 * min(tid, 47);
     const uint32_t lds0 = lds_address(lds) + 1024u * (uint32_t)wave;
     auto fetch = [&](int j) {
         const int64_t g = (int64_t)j * T::G.tb;
@@ -592,13 +600,29 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     for (int j = 0; j < D; ++j) fetch(j);
 
     const int64_t t_row0 = a.q_pos0 + a.row0;
-    auto put = [&](int i, int p, float v) {
+    // pool factors of the bound for the columns this lane stores
+    float mu_st[NB] = {};
+    if constexpr (!LO) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int64_t p = HI == 4 ? p_wave + nb * 32 + col : p_wave + lane;
+            mu_st[nb] = p < a.n_pools ? a.mu[p] : 0.0f;
+        }
+    }
+    const uint8_t* Lw = nullptr;  // the current tile's weights/scales/bounds in LDS
+    int tile_i0 = 0;
+    auto put = [&](int i, int p, float v, float mu) {
         const int64_t t = t_row0 + i;
         const int nt = (int)((t >> 2) < a.n_pools ? (t >> 2) : a.n_pools);
         float* dst = a.buf + (int64_t)i * a.ld + p;
         if constexpr (EXACT) {
             if (i < i_end && p < nt) *dst = canonical_zero(v);
         } else {
+            if constexpr (!LO) {
+                // the query's bound factor, staged in LDS with the tile
+                const float A = reinterpret_cast<const float*>(Lw + 160)[i - tile_i0];
+                v = fmaf(A, mu, canonical_zero(v));
+            }
             *dst = p < nt ? canonical_zero(v) : -INFINITY;
         }
     };
@@ -677,14 +701,16 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
                 for (int i = 0; i < 4; ++i) sacc += wv[4 * g4 + i] * relu(acc[nb][4 * g4 + i]);
                 part[nb][g4] = sacc;
             }
-        const int tile_i0 = i_begin + j * QPT;
+        tile_i0 = i_begin + j * QPT;
+        Lw = L + T::LDS_W;
         if constexpr (HI == 4) {
             // rows 8*g4 + 4*half + i are the 4 heads of query 2*g4 + half
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    put(tile_i0 + 2 * g4 + half, (int)p_wave + nb * 32 + col, part[nb][g4]);
+                    put(tile_i0 + 2 * g4 + half, (int)p_wave + nb * 32 + col, part[nb][g4],
+                        mu_st[nb]);
         } else {
             // lane l < 32 ends with pool block 0, lane l >= 32 with block 1:
             // one store of 64 consecutive pools per query
@@ -701,7 +727,7 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
                     x0 = part[0][u];
                     x1 = part[1][u];
                 }
-                put(tile_i0 + u, (int)p_wave + lane, add_halves2(x0, x1));
+                put(tile_i0 + u, (int)p_wave + lane, add_halves2(x0, x1), mu_st[0]);
             }
         }
     }
@@ -727,6 +753,8 @@ static hipError_t launch_score_bf16_t(const ScoreArgs& a, hipStream_t stream) {
     k.n_pools = a.n_pools;
     k.buf = a.buf;
     k.ld = a.ld;
+    k.qbound = a.qbound;
+    k.mu = a.mu;
     const dim3 grid((unsigned)((a.n_chunk + PB - 1) / PB), (unsigned)((a.rows + k.gq - 1) / k.gq));
     if (grid.x == 0 || grid.y == 0) return hipSuccess;
     // the chunk buffer of the selection holds approximate scores; exact

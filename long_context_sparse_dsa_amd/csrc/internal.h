@@ -23,6 +23,7 @@ hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, const float* gate, int64
 //   [OF8, QB)       E4M3 codes of q / 2^e_r (row stride L8 bytes)
 //   [QB, QB + 128)  w of each row, fp32
 //   [QB + 128, +32) E8M0 byte e_r + 127 of each row
+//   [QB + 160, +32) the error-bound factor of each of the tile's queries, fp32
 // Rows are stored in 16-byte pieces.  With d = 128 the piece order within a
 // row is XOR-swizzled by the row index so that the MFMA operand reads of 16
 // rows at a time hit distinct LDS banks; other widths pad each row by 16
@@ -37,7 +38,7 @@ inline constexpr QueryTileGeom query_tile_geom(int d) {
     const int l8 = swz ? d : d + 16;
     const int of8 = 32 * lb;
     const int qb = of8 + 32 * l8;
-    return QueryTileGeom{swz, lb, l8, of8, qb, (qb + 160 + 127) / 128 * 128};
+    return QueryTileGeom{swz, lb, l8, of8, qb, (qb + 192 + 127) / 128 * 128};
 }
 // Byte offset of 16-byte piece c of the bf16 row r / of the E4M3 row r.
 inline constexpr int tile_bf16_piece(const QueryTileGeom& g, int r, int c) {
@@ -89,6 +90,10 @@ struct ScoreArgs {
     // threshold).  exact = 1: only the eligible entries of rows [0, rows) are
     // written (a caller's dense [rows, P] layout), with full scores.
     int exact;
+    // bf16, exact = 0: bound factors; the buffer receives upper bounds
+    // u = fma(qbound[i], mu[p], score without the correction)
+    const float* qbound;      // [rows]
+    const float* mu;          // [n_pools]
     float* buf;               // [rows, ld] fp32
     int64_t ld;
 };
@@ -106,10 +111,11 @@ struct SelectArgs {
     int k_pools;
     int32_t* idx_out;         // [s_q, k_pools]
     float* score_out;         // optional
-    // Approximate scores (bf16 indexer without the correction term): every
-    // score is within qbound[i] * mu[p] of the full score, which the
-    // selection recomputes for the pools it cannot decide from the bound.
-    // qbound == nullptr: the scores are final.
+    // Bounded rows (bf16 indexer): the buffer holds u = s~ + delta with
+    // delta = qbound[i] * mu[p] and s~ the score without the correction term,
+    // so the full score lies in [u - 2 delta, u]; the selection recomputes it
+    // for the pools it cannot decide from the bounds.  qbound == nullptr: the
+    // buffer holds the final scores.
     const float* qbound;      // [rows] per chunk query
     const float* mu;          // [n_pools]
     const uint8_t* tiles;     // the chunk's packed query tiles

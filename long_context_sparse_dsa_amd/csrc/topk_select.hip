@@ -459,67 +459,55 @@ __device__ uint32_t compact(int n, Flag flag, Put put, SelShared& sh) {
 // query's packed tile, the B operand pool cand[col]; 8 (d / 16) bf16 MFMAs
 // with hi, then the scaled E4M3 MFMAs with lo, into one 32 x 32 accumulator;
 // then per query sum_h w_h relu(acc), the rows of the query summed in the
-// scoring kernel's order.  One wave scores 32 pools at a time.
+// scoring kernel's order.  One wave scores 32 pools at a time.  Both
+// operands are loaded for every block (the tile stays in cache), so that
+// nothing is live across blocks and every load of a block is in flight
+// before its first MFMA: a gather costs one memory latency, not one per
+// MFMA.
 template <int HI, int DI>
 struct Rescorer {
     static constexpr QueryTileGeom G = query_tile_geom(DI);
     static constexpr int QPT = 32 / HI;
     static constexpr int NSB = DI / 16;
     static constexpr int NSF = (DI + 63) / 64;
-    bf16x8 af[NSB];
-    i32x8 af8[NSF];
-    float wv[16];
-    int qsc;
+    const uint8_t* tile;
     int qi;
 
-    __device__ void load(const uint8_t* tiles, int64_t i) {
-        const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
-        const uint8_t* tile = tiles + (i / QPT) * G.tb;
+    __device__ void init(const uint8_t* tiles, int64_t i) {
+        tile = tiles + (i / QPT) * G.tb;
         qi = (int)(i % QPT);
-#pragma unroll
-        for (int s = 0; s < NSB; ++s)
-            af[s] = as_bf16x8(ldg16(tile + tile_bf16_piece(G, col, 2 * s + half)));
-#pragma unroll
-        for (int s = 0; s < NSF; ++s) {
-            u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-            if (64 * s + 32 * half < DI) {
-                x0 = ldg16(tile + tile_fp8_piece(G, col, 4 * s + 2 * half));
-                x1 = ldg16(tile + tile_fp8_piece(G, col, 4 * s + 2 * half + 1));
-            }
-            af8[s] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                           (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-        }
-        qsc = (int)tile[G.qb + 128 + col];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 w4 = *reinterpret_cast<const f32x4*>(tile + G.qb + 4 * (8 * g4 + 4 * half));
-            wv[4 * g4 + 0] = w4[0];
-            wv[4 * g4 + 1] = w4[1];
-            wv[4 * g4 + 2] = w4[2];
-            wv[4 * g4 + 3] = w4[3];
-        }
     }
 
     // Score of pool p (this lane's column); the value is valid on lane
-    // owner() of each column (col or col + 32).
+    // owner() of each column (col or col + 32).  w: the tile's 32 head
+    // weights, staged in LDS.
     __device__ float score(const uint16_t* khi, const uint8_t* klo, const uint8_t* klo_scale,
-                           int64_t p) const {
-        const int lane = threadIdx.x & 63, half = lane >> 5;
-        bf16x8 bhi[NSB];
-        i32x8 blo[NSF];
+                           int64_t p, const float* w) const {
+        const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+        bf16x8 af[NSB], bhi[NSB];
+        i32x8 af8[NSF], blo[NSF];
 #pragma unroll
-        for (int s = 0; s < NSB; ++s) bhi[s] = as_bf16x8(ldg16(khi + p * DI + 16 * s + 8 * half));
+        for (int s = 0; s < NSB; ++s) {
+            af[s] = as_bf16x8(ldg16(tile + tile_bf16_piece(G, col, 2 * s + half)));
+            bhi[s] = as_bf16x8(ldg16(khi + p * DI + 16 * s + 8 * half));
+        }
 #pragma unroll
         for (int s = 0; s < NSF; ++s) {
+            u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+            u32x4 b0 = {0u, 0u, 0u, 0u}, b1 = {0u, 0u, 0u, 0u};
             const int d0 = 64 * s + 32 * half;
-            u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
             if (d0 < DI) {
-                x0 = ldg16(klo + p * DI + d0);
-                x1 = ldg16(klo + p * DI + d0 + 16);
+                a0 = ldg16(tile + tile_fp8_piece(G, col, 4 * s + 2 * half));
+                a1 = ldg16(tile + tile_fp8_piece(G, col, 4 * s + 2 * half + 1));
+                b0 = ldg16(klo + p * DI + d0);
+                b1 = ldg16(klo + p * DI + d0 + 16);
             }
-            blo[s] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                           (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+            af8[s] = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            blo[s] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                           (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
         }
+        const int qsc = (int)tile[G.qb + 128 + col];
         const int bsc = (int)klo_scale[p];
         f32x16 acc;
 #pragma unroll
@@ -531,12 +519,16 @@ struct Rescorer {
         for (int s = 0; s < NSF; ++s)
             acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af8[s], blo[s], acc, 0, 0, 0, qsc,
                                                                   0, bsc);
+        // every load first, then the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 * NSB + 4 * NSF + 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NSB + NSF, 0);
         float part[4];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(w + 8 * g4 + 4 * half);
             float sacc = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sacc += wv[4 * g4 + i] * relu(acc[4 * g4 + i]);
+            for (int i = 0; i < 4; ++i) sacc += w4[i] * relu(acc[4 * g4 + i]);
             part[g4] = sacc;
         }
         // (selects, not an indexed register array)
@@ -564,27 +556,27 @@ struct Rescorer {
 // Rescore the entries j < nr whose tag tag_of(j) has the RESCORE bit: the
 // tag's id bits name the pool, and its full score goes to put(j, value).
 // The 4 waves take blocks of 32 entries in turn and skip blocks with nothing
-// to rescore.
+// to rescore.  Called by the whole workgroup; the head weights of the tile
+// are staged in sh.hist.
 template <int HI, int DI, class TagOf, class Put>
-__device__ void rescore(uint32_t nr, TagOf tag_of, Put put, const SelectArgs& a, int64_t i) {
+__device__ void rescore(uint32_t nr, TagOf tag_of, Put put, const SelectArgs& a, int64_t i,
+                        SelShared& sh) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31;
+    Rescorer<HI, DI> r;
+    r.init(a.tiles, i);
+    float* w = reinterpret_cast<float*>(sh.hist);
+    if (threadIdx.x < 32) w[threadIdx.x] = reinterpret_cast<const float*>(r.tile + r.G.qb)[threadIdx.x];
+    __syncthreads();
     const uint32_t nblk = (nr + 31) / 32;
     if ((uint32_t)wave >= nblk) return;
-    Rescorer<HI, DI> r;
-    bool loaded = false;
-    int own = 0;
+    const int own = r.owner(col);
     for (uint32_t b = wave; b < nblk; b += 4) {
         const uint32_t j = 32 * b + col;
         // columns past the end score entry 32 b (any valid pool) and are dropped
         const uint32_t t = tag_of(j < nr ? j : 32 * b);
         const bool keep = j < nr && (t & RESCORE) != 0u;
         if (__ballot(keep) == 0) continue;
-        if (!loaded) {
-            r.load(a.tiles, i);
-            own = r.owner(col);
-            loaded = true;
-        }
-        const float v = r.score(a.khi, a.klo, a.klo_scale, (int64_t)(t & ID_MASK));
+        const float v = r.score(a.khi, a.klo, a.klo_scale, (int64_t)(t & ID_MASK), w);
         if (lane == own && keep) put(j, v);
     }
 }
@@ -716,9 +708,9 @@ __device__ void select_row_bounded(const SelectArgs& a, int64_t i, float* row, i
     const int tid = threadIdx.x;
     uint32_t Lk, Uk;
     band_bounds((int)n, [&](int64_t e, uint32_t& lk, uint32_t& uk) {
-        const float x = row[e], dl = A * a.mu[e];
-        lk = order_key(x - dl);
-        uk = order_key(x + dl);
+        const float x = row[e];
+        lk = order_key(x - 2.0f * (A * a.mu[e]));
+        uk = order_key(x);
     }, (uint32_t)a.k_pools, Lk, Uk, sh);
     uint32_t* ids = reinterpret_cast<uint32_t*>(sh.d);
     for (int64_t base = 0; base < n; base += CAP) {
@@ -726,7 +718,7 @@ __device__ void select_row_bounded(const SelectArgs& a, int64_t i, float* row, i
         // this window's pools in LDS first: the rescoring below writes the row
         for (int e = tid; e < w; e += NT) {
             const float x = row[base + e], dl = A * a.mu[base + e];
-            const uint32_t lk = order_key(x - dl), uk = order_key(x + dl);
+            const uint32_t lk = order_key(x - 2.0f * dl), uk = order_key(x);
             const bool band = uk >= Lk && lk <= Uk;
             const bool in = lk > Uk;
             sh.idc[e] = (dl > 0.0f && (band || (in && score_out))) ? 1u : 0u;
@@ -737,7 +729,7 @@ __device__ void select_row_bounded(const SelectArgs& a, int64_t i, float* row, i
                                     sh);
         __syncthreads();
         rescore<HI, DI>(nr, [&](uint32_t j) { return ids[j] | RESCORE; },
-                        [&](uint32_t j, float v) { row[ids[j]] = v; }, a, i);
+                        [&](uint32_t j, float v) { row[ids[j]] = v; }, a, i, sh);
         __threadfence_block();
         __syncthreads();
     }
@@ -774,7 +766,7 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
                                         [&](uint32_t slot, int e) { ids[slot] = (uint32_t)e; }, sh);
             __syncthreads();
             rescore<HI, DI>(nr, [&](uint32_t j) { return ids[j] | RESCORE; },
-                            [&](uint32_t j, float v) { sh.s[ids[j]] = v; }, a, i);
+                            [&](uint32_t j, float v) { sh.s[ids[j]] = v; }, a, i, sh);
             __syncthreads();
         }
         for (int j = tid; j < k; j += NT) sout[j] = j < n ? sh.s[j] : -INFINITY;
@@ -808,7 +800,7 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
             const f32x4 v = *reinterpret_cast<const f32x4*>(row + e);
             u32x4 kk;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) kk[j] = order_key(v[j] - delta(e + j));
+            for (int j = 0; j < 4; ++j) kk[j] = order_key(v[j] - 2.0f * delta(e + j));
             *reinterpret_cast<u32x4*>(&sh.sample[4 * s4]) = kk;
         }
         __syncthreads();
@@ -818,9 +810,9 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
         const uint32_t tau = sample_threshold(ns, r, sh);  // at least r sample l keys are >= tau
         __syncthreads();
 
-        // ordered compaction of {u key >= tau}: batches of VB 16-byte loads per
-        // thread, the next batch in flight while the current one is compacted;
-        // cnt_l counts the pools with l key >= tau
+        // ordered compaction of {u key >= tau} (rows hold u): batches of VB
+        // 16-byte loads per thread, the next batch in flight while the
+        // current one is compacted
         constexpr int VB = 4;
         constexpr int BATCH = 4 * NT * VB;
         f32x4 cur[VB], nxt[VB];
@@ -837,24 +829,12 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
         for (int64_t base = 0; base < n; base += BATCH) {
             if (base + BATCH < n) fetch(base + BATCH, nxt);
             uint32_t c[VB], off[VB];
-            f32x4 dl[VB];
 #pragma unroll
             for (int u = 0; u < VB; ++u) {
                 const int64_t e = base + (int64_t)(u * NT + tid) * 4;
-                if constexpr (BOUNDS) {
-                    const f32x4 mu4 = e < n ? *reinterpret_cast<const f32x4*>(a.mu + e)
-                                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                    dl[u] = A * mu4;
-                } else {
-                    dl[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                }
                 uint32_t cc = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool ok = e + j < n;
-                    cc += ok && order_key(cur[u][j] + dl[u][j]) >= tau;
-                    if constexpr (BOUNDS) cnt_l += ok && order_key(cur[u][j] - dl[u][j]) >= tau;
-                }
+                for (int j = 0; j < 4; ++j) cc += e + j < n && order_key(cur[u][j]) >= tau;
                 c[u] = cc;
             }
             const uint32_t tot = block_excl_scan_slots<VB>(c, off, sh, sh.wtot);
@@ -865,10 +845,9 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
                 uint32_t pos = count + off[u];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    if (e + j < n && order_key(cur[u][j] + dl[u][j]) >= tau) {
+                    if (e + j < n && order_key(cur[u][j]) >= tau) {
                         if (pos < (uint32_t)CAP) {
                             sh.s[pos] = cur[u][j];
-                            sh.d[pos] = dl[u][j];
                             sh.idc[pos] = (uint32_t)(e + j);
                         }
                         ++pos;
@@ -879,8 +858,20 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
 #pragma unroll
             for (int u = 0; u < VB; ++u) cur[u] = nxt[u];
         }
-        if constexpr (BOUNDS) cnt_l = block_sum(cnt_l, sh);
-        else cnt_l = count;
+        __syncthreads();
+        // the bounds of the kept entries, and how many have l key >= tau
+        if constexpr (BOUNDS) {
+            const int mm = (int)min(count, (uint32_t)CAP);
+            for (int e = tid; e < mm; e += NT) {
+                const float dl = delta(sh.idc[e]);
+                sh.d[e] = dl;
+                cnt_l += order_key(sh.s[e] - 2.0f * dl) >= tau;
+            }
+            cnt_l = block_sum(cnt_l, sh);
+        } else {
+            for (int e = tid; e < (int)min(count, (uint32_t)CAP); e += NT) sh.d[e] = 0.0f;
+            cnt_l = count;
+        }
         __syncthreads();
         if (count > (uint32_t)CAP || cnt_l < (uint32_t)k) {
             if constexpr (BOUNDS) {
@@ -912,15 +903,15 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
     // bounds on L and U over the list
     uint32_t Lk, Uk;
     band_bounds(m, [&](int64_t e, uint32_t& lk, uint32_t& uk) {
-        const float x = sh.s[e], dl = sh.d[e];
-        lk = order_key(x - dl);
-        uk = order_key(x + dl);
+        const float x = sh.s[e];
+        lk = order_key(x - 2.0f * sh.d[e]);
+        uk = order_key(x);
     }, (uint32_t)k, Lk, Uk, sh);
     // classify: certain (l > U), band (u >= L, l <= U), dropped (u < L)
     uint32_t n_in = 0;
     for (int e = tid; e < m; e += NT) {
         const float x = sh.s[e], dl = sh.d[e];
-        const uint32_t lk = order_key(x - dl), uk = order_key(x + dl);
+        const uint32_t lk = order_key(x - 2.0f * dl), uk = order_key(x);
         const uint32_t c = lk > Uk ? C_IN : (uk >= Lk ? C_BAND : C_OUT);
         const bool need = dl > 0.0f && (c == C_BAND || (c == C_IN && sout));
         sh.idc[e] |= (c << 29) | (need ? RESCORE : 0u);
@@ -936,7 +927,7 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
     }, [&](uint32_t slot, int e) { pos[slot] = (uint32_t)e; }, sh);
     __syncthreads();
     rescore<HI, DI>(np, [&](uint32_t j) { return sh.idc[pos[j]]; },
-                    [&](uint32_t j, float v) { sh.s[pos[j]] = v; }, a, i);
+                    [&](uint32_t j, float v) { sh.s[pos[j]] = v; }, a, i, sh);
     __syncthreads();
     // the remaining k - n_in from the band, by full score, ties to the lower id
     auto band_key = [&](int64_t j, uint32_t& key) {
