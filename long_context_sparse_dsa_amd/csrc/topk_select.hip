@@ -53,7 +53,8 @@ constexpr int NT = 256;
 constexpr int CAP = 4096;
 constexpr int SAMPLE_LEN = 16;
 // sample blocks of SAMPLE_LEN: more for long rows, where k is a smaller
-// fraction of the row (the sample lives in the three list arrays)
+// fraction of the row, and twice as many for bounded rows, whose threshold
+// takes a wider margin (the sample lives in the three list arrays)
 constexpr int SAMPLE_BLOCKS_SHORT = 256;
 constexpr int SAMPLE_BLOCKS_LONG = 768;
 constexpr int64_t LONG_ROW = 65536;
@@ -792,7 +793,7 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
         __syncthreads();
     } else {
         // threshold on the l keys from nb blocks of SAMPLE_LEN
-        const int nb = n > LONG_ROW ? SAMPLE_BLOCKS_LONG : SAMPLE_BLOCKS_SHORT;
+        const int nb = (n > LONG_ROW ? SAMPLE_BLOCKS_LONG : SAMPLE_BLOCKS_SHORT) / (BOUNDS ? 1 : 2);
         const int ns = nb * SAMPLE_LEN;
         for (int s4 = tid; s4 < ns / 4; s4 += NT) {
             const int b = (4 * s4) / SAMPLE_LEN, u = (4 * s4) % SAMPLE_LEN;
@@ -804,8 +805,10 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
             *reinterpret_cast<u32x4*>(&sh.sample[4 * s4]) = kk;
         }
         __syncthreads();
+        // expected sample keys above the k-th; the margin of a bounded row
+        // also covers the l keys' shift below the scores
         const float mu = (float)k * (float)ns / (float)n;
-        uint32_t r = (uint32_t)ceilf(mu + 5.0f * sqrtf(mu) + 8.0f);
+        uint32_t r = (uint32_t)ceilf(BOUNDS ? mu + 5.0f * sqrtf(mu) + 8.0f : mu + 4.0f * sqrtf(mu) + 4.0f);
         if (r > (uint32_t)ns) r = ns;
         const uint32_t tau = sample_threshold(ns, r, sh);  // at least r sample l keys are >= tau
         __syncthreads();
