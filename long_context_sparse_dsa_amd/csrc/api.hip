@@ -130,6 +130,18 @@ dsa_status check_index_shape(const IndexShape& sh, bool need_k) {
 // workgroup covers, so that its stores never need a column mask.
 int64_t score_ld(const IndexShape& sh) { return round_up(sh.n_pools > 0 ? sh.n_pools : 1, 512); }
 
+// bf16 indexer: score a chunk without the correction term and rescore only
+// the pools near each row's k-th score (bounded), or score it in full?  The
+// rescoring costs about k pools per row whatever the row's length, the
+// correction term a share of every pool, so the bounds pay once the rows see
+// more than about 24 k pools (measured on MI355X at k = 512: 16, 24, 32 and
+// 48 k compared at 64k, 128k and the 1M-token share).
+bool bounded_chunk(const IndexShape& sh, int64_t t_first, int64_t t_last) {
+    const int64_t n_first = (t_first / 4) < sh.n_pools ? (t_first / 4) : sh.n_pools;
+    const int64_t n_last = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
+    return n_first + n_last > 2 * 24 * (int64_t)sh.k_pools;
+}
+
 // Rows per scoring launch of the dense-score entry point (bounds its workspace).
 constexpr int64_t kDenseRows = 4096;
 
@@ -395,8 +407,9 @@ static dsa_status index_score_topk(const void* q_idx, const void* k_idx, const f
         const int rows = (int)(s_q - c0 < cq ? s_q - c0 : cq);
         const int64_t t_last = q_pos0 + c0 + rows - 1;
         const int64_t n_chunk = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
+        const bool bounded = dtype == DSA_BF16 && bounded_chunk(sh, q_pos0 + c0, t_last);
         if (n_chunk > 0 && (n_chunk > k_pools || score_out)) {
-            e = launch_pack(sh, L, q_idx, w, w_stride_q, c0, rows, true, ws, s);
+            e = launch_pack(sh, L, q_idx, w, w_stride_q, c0, rows, bounded, ws, s);
             if (e != hipSuccess) return hip_fail(e, "pack_queries launch");
             dsa::ScoreArgs a{};
             fill_score_args(a, sh, L, q_idx, ws, q_scale, k_scale, w, w_stride_q);
@@ -405,7 +418,7 @@ static dsa_status index_score_topk(const void* q_idx, const void* k_idx, const f
             a.n_chunk = n_chunk;
             a.buf = buf;
             a.ld = ld;
-            if (dtype == DSA_BF16) {
+            if (bounded) {
                 a.qbound = reinterpret_cast<const float*>(ws + L.qbound);
                 a.mu = reinterpret_cast<const float*>(ws + L.mu);
             }
@@ -425,9 +438,9 @@ static dsa_status index_score_topk(const void* q_idx, const void* k_idx, const f
         b.score_out = score_out;
         b.h_idx = h_idx;
         b.d_idx = d_idx;
-        if (dtype == DSA_BF16) {
-            // approximate scores (no correction term): the selection rescores
-            // the pools its bound cannot decide
+        if (bounded) {
+            // bounds of the scores without the correction term: the
+            // selection rescores the pools its bound cannot decide
             b.qbound = reinterpret_cast<const float*>(ws + L.qbound);
             b.mu = reinterpret_cast<const float*>(ws + L.mu);
             b.tiles = reinterpret_cast<const uint8_t*>(ws + L.tiles);

@@ -757,9 +757,11 @@ static hipError_t launch_score_bf16_t(const ScoreArgs& a, hipStream_t stream) {
     k.mu = a.mu;
     const dim3 grid((unsigned)((a.n_chunk + PB - 1) / PB), (unsigned)((a.rows + k.gq - 1) / k.gq));
     if (grid.x == 0 || grid.y == 0) return hipSuccess;
-    // the chunk buffer of the selection holds approximate scores; exact
-    // (caller-owned) rows get the full scores
+    // exact (caller-owned) rows get the full scores; the chunk buffer gets
+    // the full scores or, with bound factors, the upper bounds of the
+    // scores without the correction term
     if (a.exact) index_score_bf16_kernel<HI, DI, NB, true, true><<<grid, 256, 0, stream>>>(k);
+    else if (!a.qbound) index_score_bf16_kernel<HI, DI, NB, false, true><<<grid, 256, 0, stream>>>(k);
     else index_score_bf16_kernel<HI, DI, NB, false, false><<<grid, 256, 0, stream>>>(k);
     return hipGetLastError();
 }

@@ -85,13 +85,15 @@ struct ScoreArgs {
     int fp8;
     // exact = 0: buf is a chunk buffer with at least round_up(rows, 8) rows
     // and ld >= round_up(n_chunk, 512); the kernel may write any entry of it
-    // (ineligible pools get -inf); with the bf16 indexer the scores leave the
-    // correction q . lo out (the selection rescores the pools near its
-    // threshold).  exact = 1: only the eligible entries of rows [0, rows) are
-    // written (a caller's dense [rows, P] layout), with full scores.
+    // (ineligible pools get -inf); with the bf16 indexer and bound factors
+    // the scores leave the correction q . lo out (the selection rescores the
+    // pools near its threshold).  exact = 1: only the eligible entries of rows
+    // [0, rows) are written (a caller's dense [rows, P] layout), with full
+    // scores.
     int exact;
     // bf16, exact = 0: bound factors; the buffer receives upper bounds
-    // u = fma(qbound[i], mu[p], score without the correction)
+    // u = fma(qbound[i], mu[p], score without the correction), or the full
+    // scores when qbound is null
     const float* qbound;      // [rows]
     const float* mu;          // [n_pools]
     float* buf;               // [rows, ld] fp32

@@ -586,7 +586,8 @@ __device__ void rescore(uint32_t nr, TagOf tag_of, Put put, const SelectArgs& a,
 
 // Emit the kept ids of the list (in id order) to out[0..k): every C_IN
 // entry, and the C_BAND entries with key > hi plus the first `remaining`
-// with key in [lo, hi].
+// with key in [lo, hi].  ALL_BAND: every entry is a band entry (untagged).
+template <bool ALL_BAND>
 __device__ void emit_list(int m, uint32_t lo, uint32_t hi, uint32_t remaining, SelShared& sh,
                           int32_t* out, float* score_out, int k_out) {
     const int tid = threadIdx.x;
@@ -595,12 +596,12 @@ __device__ void emit_list(int m, uint32_t lo, uint32_t hi, uint32_t remaining, S
     uint32_t n_in = 0;
     for (int e = e0; e < e1; ++e) {
         const uint32_t k = order_key(sh.s[e]);
-        n_in += cls_of(sh.idc[e]) == C_BAND && k >= lo && k <= hi;
+        n_in += (ALL_BAND || cls_of(sh.idc[e]) == C_BAND) && k >= lo && k <= hi;
     }
     uint32_t tot;
     const uint32_t rank0 = block_excl_scan(n_in, sh, &tot);
     auto take = [&](int e, uint32_t& r) {
-        const uint32_t c = cls_of(sh.idc[e]);
+        const uint32_t c = ALL_BAND ? C_BAND : cls_of(sh.idc[e]);
         if (c == C_IN) return true;
         if (c != C_BAND) return false;
         const uint32_t k = order_key(sh.s[e]);
@@ -785,8 +786,6 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
             if constexpr (BOUNDS) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) sh.d[e + u] = e + u < n ? delta(e + u) : 0.0f;
-            } else {
-                *reinterpret_cast<f32x4*>(&sh.d[e]) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
         }
         m = (int)n;
@@ -872,7 +871,6 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
             }
             cnt_l = block_sum(cnt_l, sh);
         } else {
-            for (int e = tid; e < (int)min(count, (uint32_t)CAP); e += NT) sh.d[e] = 0.0f;
             cnt_l = count;
         }
         __syncthreads();
@@ -891,8 +889,6 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
 
     if constexpr (!BOUNDS) {
         // final scores: one selection over the whole list
-        for (int e = tid; e < m; e += NT) sh.idc[e] |= C_BAND << 29;
-        __syncthreads();
         auto key_at = [&](int64_t e, uint32_t& key) {
             key = order_key(sh.s[e]);
             return true;
@@ -900,7 +896,7 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
         uint32_t lo, hi, remaining = (uint32_t)k;
         member_minmax(m, key_at, lo, hi, sh);
         radix_narrow(m, key_at, lo, hi, remaining, false, sh);
-        emit_list(m, lo, hi, remaining, sh, out, sout, k);
+        emit_list<true>(m, lo, hi, remaining, sh, out, sout, k);
         return;
     }
     // bounds on L and U over the list
@@ -940,7 +936,7 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
     uint32_t lo, hi, remaining = (uint32_t)k - n_in;
     member_minmax(np, band_key, lo, hi, sh);
     radix_narrow(np, band_key, lo, hi, remaining, false, sh);
-    emit_list(m, lo, hi, remaining, sh, out, sout, k);
+    emit_list<false>(m, lo, hi, remaining, sh, out, sout, k);
 }
 
 template <int HI>

@@ -126,8 +126,9 @@ def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=N
 @pytest.mark.parametrize("h_idx,d_idx,fp8", [(32, 128, False), (16, 96, False), (4, 64, False),
                                              (32, 96, True), (8, 128, True)])
 def test_gated_pooling(h_idx, d_idx, fp8):
+    # k small against the rows' lengths: most chunks take the bounded path
     wl = inputs.custom(f"gated_{h_idx}x{d_idx}{'_fp8' if fp8 else ''}", s_q=1300, s_k=1303,
-                       h_idx=h_idx, d_idx=d_idx, k_pools=48, h=16, d=d_idx,
+                       h_idx=h_idx, d_idx=d_idx, k_pools=8, h=16, d=d_idx,
                        idx_std=1.0 if fp8 else 1 / math.sqrt(d_idx),
                        attn_std=1 / math.sqrt(d_idx), fp8=fp8, number=400 + h_idx + d_idx)
     gate = inputs.make_gates(wl)
@@ -160,9 +161,11 @@ def test_tiny_workload_all_rows():
 
 @pytest.mark.parametrize("h_idx,d_idx", [(32, 128), (16, 96), (8, 64), (4, 128), (32, 96)])
 def test_indexer_shapes_ragged(h_idx, d_idx):
-    # 3 chunks of 64 queries, a ragged last chunk and several 256-pool blocks
+    # chunks of 192 queries, a ragged last chunk and several 256-pool blocks;
+    # k is small against the rows' lengths, so the early chunks are scored in
+    # full and the later ones with error bounds and rescoring
     wl = inputs.custom(f"ragged_{h_idx}x{d_idx}", s_q=2500, s_k=2500, h_idx=h_idx, d_idx=d_idx,
-                       k_pools=40, h=16, d=d_idx, idx_std=1 / math.sqrt(d_idx),
+                       k_pools=16, h=16, d=d_idx, idx_std=1 / math.sqrt(d_idx),
                        attn_std=1 / math.sqrt(d_idx), number=200 + h_idx + d_idx)
     run_case(wl, chunk_q=192)
 
@@ -253,7 +256,7 @@ def test_selection_equals_exact_topk_of_full_scores(near_constant):
     # dsa_index_scores returns (same MFMA sequence).  Near-constant keys put
     # nearly every pool within the bound of the threshold, so long rows
     # overflow the LDS list and take the slow path in global memory.
-    wl = inputs.custom("full_topk", s_q=192, s_k=24576, q_pos0=24384, h_idx=32, d_idx=128,
+    wl = inputs.custom("full_topk", s_q=192, s_k=65536, q_pos0=65344, h_idx=32, d_idx=128,
                        k_pools=512, h=16, d=128, idx_std=1 / math.sqrt(128),
                        number=381 if near_constant else 380)
     x = inputs.make_inputs(wl, attention=False)
