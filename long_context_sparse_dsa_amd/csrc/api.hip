@@ -34,7 +34,10 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 constexpr int64_t kMaxKPools = 2048;
 constexpr int64_t kDefaultChunkMax = 4096;
-constexpr int64_t kDefaultBufferBudget = int64_t(1) << 30;
+constexpr int64_t kDefaultBufferBudget = int64_t(3) << 29;  // 1.5 GiB
+// Top-k workgroups resident at once on MI355X: 256 CUs x 3.  Default chunks
+// are a multiple of it, so that no selection launch ends on a partial wave.
+constexpr int64_t kSelectWave = 768;
 constexpr int64_t kMaxChunk = 1 << 16;
 constexpr int64_t kScoreBufferCap = int64_t(2) << 30;  // per chunk, as the page keeps it
 
@@ -148,12 +151,16 @@ constexpr int64_t kDenseRows = 4096;
 dsa_status resolve_chunk(const IndexShape& sh, int64_t chunk_q, int64_t* out) {
     if (chunk_q < 0) return fail(DSA_ERR_INVALID_ARG, "chunk_q %lld < 0", (long long)chunk_q);
     if (chunk_q == 0) {
-        // the largest multiple of 64 (at most 4096 queries, and no more than
-        // the queries there are) whose score buffer fits a 1 GiB budget
+        // at most 4096 queries (and no more than the queries there are);
+        // when the 1.5 GiB buffer budget is what limits the chunk (long
+        // rows), the largest multiple of 768 within it, else of 64
         chunk_q = kDefaultBufferBudget / (score_ld(sh) * 4);
+        const bool by_budget = chunk_q < kDefaultChunkMax;
         if (chunk_q > kDefaultChunkMax) chunk_q = kDefaultChunkMax;
         if (chunk_q > round_up(sh.s_q, 64)) chunk_q = round_up(sh.s_q, 64);
-        chunk_q = chunk_q / 64 * 64;
+        chunk_q = by_budget && chunk_q >= kSelectWave && sh.s_q > kSelectWave
+                      ? chunk_q / kSelectWave * kSelectWave
+                      : chunk_q / 64 * 64;
         if (chunk_q < 64) chunk_q = 64;
     } else if (chunk_q % 64 != 0 || chunk_q > kMaxChunk) {
         return fail(DSA_ERR_UNSUPPORTED, "chunk_q %lld must be a multiple of 64 up to %lld",
