@@ -794,14 +794,30 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
         // threshold on the l keys from nb blocks of SAMPLE_LEN
         const int nb = (n > LONG_ROW ? SAMPLE_BLOCKS_LONG : SAMPLE_BLOCKS_SHORT) / (BOUNDS ? 1 : 2);
         const int ns = nb * SAMPLE_LEN;
-        for (int s4 = tid; s4 < ns / 4; s4 += NT) {
-            const int b = (4 * s4) / SAMPLE_LEN, u = (4 * s4) % SAMPLE_LEN;
-            const int64_t e = (((int64_t)b * n / nb) & ~(int64_t)(SAMPLE_LEN - 1)) + u;
-            const f32x4 v = *reinterpret_cast<const f32x4*>(row + e);
-            u32x4 kk;
+        // SU 16-byte pieces per thread in flight at once (ns / 4 is a
+        // multiple of NT; the blocks lie inside the row, n > CAP)
+        constexpr int SU = 6;
+        for (int s0 = 0; s0 < ns / 4; s0 += SU * NT) {
+            f32x4 v[SU], mv[SU];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) kk[j] = order_key(v[j] - 2.0f * delta(e + j));
-            *reinterpret_cast<u32x4*>(&sh.sample[4 * s4]) = kk;
+            for (int u = 0; u < SU; ++u) {
+                const int s4 = s0 + u * NT + tid;
+                if (s4 >= ns / 4) continue;
+                const int b = (4 * s4) / SAMPLE_LEN, o = (4 * s4) % SAMPLE_LEN;
+                const int64_t e = (((int64_t)b * n / nb) & ~(int64_t)(SAMPLE_LEN - 1)) + o;
+                v[u] = *reinterpret_cast<const f32x4*>(row + e);
+                if constexpr (BOUNDS) mv[u] = *reinterpret_cast<const f32x4*>(a.mu + e);
+            }
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int s4 = s0 + u * NT + tid;
+                if (s4 >= ns / 4) continue;
+                u32x4 kk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    kk[j] = order_key(v[u][j] - 2.0f * (BOUNDS ? A * mv[u][j] : 0.0f));
+                *reinterpret_cast<u32x4*>(&sh.sample[4 * s4]) = kk;
+            }
         }
         __syncthreads();
         // expected sample keys above the k-th; the margin of a bounded row
@@ -813,30 +829,29 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
         __syncthreads();
 
         // ordered compaction of {u key >= tau} (rows hold u): batches of VB
-        // 16-byte loads per thread, the next batch in flight while the
-        // current one is compacted
-        constexpr int VB = 4;
+        // 16-byte pieces per thread, all loads of a batch in flight at once
+        // (pieces past the row read its last piece and are masked).  Rows
+        // hold no -0, so order_key(x) >= tau is x >= ftau.
+        constexpr int VB = 8;
         constexpr int BATCH = 4 * NT * VB;
-        f32x4 cur[VB], nxt[VB];
-        auto fetch = [&](int64_t base, f32x4 (&v)[VB]) {
+        const float ftau = key_to_float(tau);
+        const int64_t last = (n - 1) & ~(int64_t)3;
+        uint32_t count = 0, cnt_l = 0;
+        for (int64_t base = 0; base < n; base += BATCH) {
+            f32x4 v[VB];
+            int lim[VB];  // elements of piece u below lim[u] lie in the row
 #pragma unroll
             for (int u = 0; u < VB; ++u) {
                 const int64_t e = base + (int64_t)(u * NT + tid) * 4;
-                v[u] = e < n ? *reinterpret_cast<const f32x4*>(row + e)
-                             : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                v[u] = *reinterpret_cast<const f32x4*>(row + (e < n ? e : last));
+                lim[u] = e + 4 <= n ? 4 : (e < n ? (int)(n - e) : 0);
             }
-        };
-        uint32_t count = 0, cnt_l = 0;
-        fetch(0, cur);
-        for (int64_t base = 0; base < n; base += BATCH) {
-            if (base + BATCH < n) fetch(base + BATCH, nxt);
             uint32_t c[VB], off[VB];
 #pragma unroll
             for (int u = 0; u < VB; ++u) {
-                const int64_t e = base + (int64_t)(u * NT + tid) * 4;
                 uint32_t cc = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) cc += e + j < n && order_key(cur[u][j]) >= tau;
+                for (int j = 0; j < 4; ++j) cc += (j < lim[u]) & (v[u][j] >= ftau);
                 c[u] = cc;
             }
             const uint32_t tot = block_excl_scan_slots<VB>(c, off, sh, sh.wtot);
@@ -847,9 +862,9 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
                 uint32_t pos = count + off[u];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    if (e + j < n && order_key(cur[u][j]) >= tau) {
+                    if ((j < lim[u]) & (v[u][j] >= ftau)) {
                         if (pos < (uint32_t)CAP) {
-                            sh.s[pos] = cur[u][j];
+                            sh.s[pos] = v[u][j];
                             sh.idc[pos] = (uint32_t)(e + j);
                         }
                         ++pos;
@@ -857,17 +872,26 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
                 }
             }
             count += tot;
-#pragma unroll
-            for (int u = 0; u < VB; ++u) cur[u] = nxt[u];
         }
         __syncthreads();
         // the bounds of the kept entries, and how many have l key >= tau
         if constexpr (BOUNDS) {
+            // every gather of the thread in flight at once (mm <= CAP)
             const int mm = (int)min(count, (uint32_t)CAP);
-            for (int e = tid; e < mm; e += NT) {
-                const float dl = delta(sh.idc[e]);
-                sh.d[e] = dl;
-                cnt_l += order_key(sh.s[e] - 2.0f * dl) >= tau;
+            constexpr int GU = CAP / NT;
+            float dl[GU];
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                const int e = u * NT + tid;
+                dl[u] = e < mm ? delta(sh.idc[e]) : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                const int e = u * NT + tid;
+                if (e < mm) {
+                    sh.d[e] = dl[u];
+                    cnt_l += order_key(sh.s[e] - 2.0f * dl[u]) >= tau;
+                }
             }
             cnt_l = block_sum(cnt_l, sh);
         } else {
