@@ -74,10 +74,10 @@ const char *dsa_last_error(void);
 /*
  * Bytes of device workspace dsa_index_score_topk needs.  Holds the pooled
  * key table (bf16: hi = bf16(mean) plus the residual as E4M3 codes with a
- * per-pool power-of-two scale and a per-pool error-bound factor; fp8: E4M3
+ * per-pool power-of-two scale and two per-pool error-bound factors; fp8: E4M3
  * codes plus per-pool factors), for the bf16 indexer the chunk's queries and
  * head weights packed in scoring tiles (with E4M3 copies of the queries for
- * the correction term) and a per-query error-bound factor, and the per-chunk
+ * the correction term) and two per-query error-bound factors, and the per-chunk
  * fp32 score buffer of chunk_q x round_up(P, 512) entries ("Over Time:
  * Chunking": the buffer is constant in s_q).  chunk_q = 0 picks the
  * library's default for these shapes (the value is returned through

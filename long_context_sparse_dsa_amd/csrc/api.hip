@@ -176,8 +176,8 @@ dsa_status resolve_chunk(const IndexShape& sh, int64_t chunk_q, int64_t* out) {
 
 // Workspace layout, every part starting on a 256-byte boundary:
 //   bf16 indexer: hi [P][d] bf16 | lo [P][d] E4M3 | lo scales [P] E8M0 |
-//                 bound factors mu [P] fp32 | the chunk's packed query tiles |
-//                 bound factors A [rows] fp32 | score buffer [rows][ld] fp32
+//                 bound factors mu [P][2] fp32 | the chunk's packed query tiles |
+//                 bound factors A [rows][2] fp32 | score buffer [rows][ld] fp32
 //   fp8 indexer:  codes [P][d] | per-pool factors [P] fp32 | score buffer
 struct Layout {
     int64_t hi = 0, lo = 0, lo_scale = 0, mu = 0, tiles = 0, qbound = 0, buf = 0, total = 0;
@@ -191,10 +191,10 @@ Layout layout(const IndexShape& sh, int64_t rows, bool with_buffer) {
         L.hi = off;        off += round_up(P * d * 2, 256);
         L.lo = off;        off += round_up(P * d, 256);
         L.lo_scale = off;  off += round_up(P, 256);
-        L.mu = off;        off += round_up(P * 4, 256);
+        L.mu = off;        off += round_up(P * 8, 256);
         L.tiles = off;
         off += round_up(dsa::query_tiles(rows, sh.h_idx) * dsa::query_tile_geom((int)d).tb, 256);
-        L.qbound = off;    off += round_up(rows * 4, 256);
+        L.qbound = off;    off += round_up(rows * 8, 256);
     } else {
         L.hi = off;        off += round_up(P * d, 256);
         L.lo_scale = off;  off += round_up(P * 4, 256);  // fp32 factors 2^e

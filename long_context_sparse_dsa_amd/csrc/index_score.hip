@@ -218,16 +218,22 @@ __device__ __forceinline__ int pow2_scale_exp(float amax) {
 // [P][DI] with one E8M0 byte (e + 127) per pool.  kbar is the mean of the
 // pool's 4 rows, or with GATED their gate-weighted sum (fp32).
 //
-// mu (optional) [P] fp32 is the pool's factor of the bound on how far a score
-// taken with hi alone can be from the score with the E4M3 correction:
-//   mu_p = (1 + 2^-6) ||L8_p|| + 2^-14 ||hi_p||   (0 when every lo code is 0)
-// with L8_p the decoded correction vector.  For a query whose factor is
-// A = (1 + 2^-8) sum_h |w_h| max(||q_h||, ||Q8_h||) (see pack_queries_kernel),
-// |score(hi) - score(hi + lo)| <= A mu_p: per head the correction is at most
-// ||Q8_h|| ||L8_p|| (Cauchy-Schwarz), the ReLU is 1-Lipschitz, and the
-// 2^-14 ||hi|| term and the two (1 + ...) factors cover fp32 rounding of the
-// accumulation, the epilogue and of s -/+ A mu_p themselves.  When every lo
-// code is 0 the correction MFMAs add exact zeros, so both scores are equal.
+// mu (optional) [P][2] fp32 holds the pool's two factors of the bound on how
+// far a score taken with hi alone can be from the score with the E4M3
+// correction:
+//   m1_p = (1 + 2^-12) ||L8_p||,  m2_p = 2^-10 ||L8_p|| + 2^-14 ||hi_p||
+// (both 0 when every lo code is 0), L8_p the decoded correction vector.  With
+// the query's factors A1 and A2 (pack_queries_kernel),
+//   |score(hi) - score(hi + lo)| <= A1 m1_p + A2 m2_p.
+// Per head the correction is c_h = Q8_h . L8_p and the ReLU is 1-Lipschitz,
+// so the scores differ by at most sum_h |w_h| |c_h| plus rounding.  That sum
+// is (sum_h s_h |w_h| Q8_h) . L8_p for the signs s_h of c_h, at most
+// ||L8_p|| max over sign vectors of ||sum_h s_h |w_h| Q8_h||, which A1 bounds
+// through the Gram matrix of the query's rows.  A2 = (1 + 2^-8) sum_h |w_h|
+// max(||q_h||, ||Q8_h||) times m2_p covers fp32 rounding: of the correction
+// MFMAs (the 2^-10 term), of the accumulation and the epilogue (the 2^-14
+// term), and of s -/+ the bound themselves.  When every lo code is 0 the
+// correction MFMAs add exact zeros, so both scores are equal.
 template <int DI, bool GATED>
 __global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __restrict__ k,
                                                              const float* __restrict__ gate,
@@ -288,9 +294,12 @@ __global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __r
         *reinterpret_cast<u32x4*>(lo_out + p * DI + 16 * c) = o;
     }
     lo_scale[p] = (uint8_t)(e + 127);
-    if (mu)
-        mu[p] = lo2 > 0.0f ? fmaf(ldexpf(sqrtf(lo2), e), 1.0f + 0x1p-6f, 0x1p-14f * sqrtf(hi2))
-                           : 0.0f;
+    if (mu) {
+        const float nl = ldexpf(sqrtf(lo2), e);
+        f32x2 m = {0.0f, 0.0f};
+        if (lo2 > 0.0f) m = f32x2{nl * (1.0f + 0x1p-12f), fmaf(nl, 0x1p-10f, 0x1p-14f * sqrtf(hi2))};
+        *reinterpret_cast<f32x2*>(mu + 2 * p) = m;
+    }
 }
 
 template <bool GATED>
@@ -338,10 +347,18 @@ struct QTile {
 // maximum combined across the row's 8 threads), and the row's head weight.
 // Rows past the chunk are zero with weight 0.
 //
-// qbound (optional) [rows] fp32 receives each query's factor of the score
-// error bound (see pool_keys_bf16_kernel), and the tile a copy of it:
-//   A = (1 + 2^-8) sum_h |w_h| max(||q_h||, ||Q8_h||),
-// Q8_h the decoded E4M3 row; the heads are summed in order.
+// qbound (optional) [rows][2] fp32 receives each query's two factors of the
+// score error bound (see pool_keys_bf16_kernel), and the tile a copy:
+//   A2 = (1 + 2^-8) sum_h |w_h| max(||q_h||, ||Q8_h||)   (heads in order)
+//   A1 = min(A2, (1 + 2^-8) sqrt(S + 2^-14 A2^2)),  S = sum_{h,g} |w_h| |w_g| |G_hg|
+// with Q8_h the decoded E4M3 row and G = Q8 Q8^T the Gram matrix of the
+// query's rows, taken on the same scaled E4M3 MFMA as the correction term
+// (exact products, fp32 accumulation).  For every sign vector s,
+// ||sum_h s_h |w_h| Q8_h||^2 = sum_{h,g} s_h s_g |w_h| |w_g| G_hg <= S; the
+// 2^-14 A2^2 term covers the accumulation error of G (at most 2^-16
+// ||Q8_h|| ||Q8_g|| per entry) and the (1 + 2^-8) factor the rounding of S,
+// of the square root and of the products.  Queries with a row scale below
+// 2^-48 (products that could leave the fp32 normal range) keep A1 = A2.
 template <int HI, int DI>
 __global__ __launch_bounds__(256) void pack_queries_kernel(const uint16_t* __restrict__ q,
                                                            const float* __restrict__ w,
@@ -350,7 +367,13 @@ __global__ __launch_bounds__(256) void pack_queries_kernel(const uint16_t* __res
                                                            float* __restrict__ qbound) {
     using T = QTile<DI>;
     constexpr int QPT = 32 / HI;
+    constexpr int NSF = (DI + 63) / 64;  // scaled fp8 MFMA steps of the Gram matrix
     __shared__ float rowbound[32];
+    // for the Gram matrix: the rows' E4M3 codes (dims past d_idx zero),
+    // scale bytes, |w| and tiny-scale flags, and one partial sum per lane
+    __shared__ __attribute__((aligned(16))) uint32_t gcode[32][36];
+    __shared__ int gsc[32], gtiny[32];
+    __shared__ float gw[32], gpart[64];
     const int64_t tile = blockIdx.x;
     const int r = threadIdx.x >> 3, c = threadIdx.x & 7;
     const int64_t i = tile * QPT + r / HI;
@@ -376,10 +399,10 @@ __global__ __launch_bounds__(256) void pack_queries_kernel(const uint16_t* __res
     amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
     const int e = pow2_scale_exp(amax);
     float n8 = 0.0f;
+    u32x4 o = {0u, 0u, 0u, 0u};
     if (act) {
         *reinterpret_cast<u32x4*>(dst + T::bf16_piece(r, 2 * c)) = raw[0];
         *reinterpret_cast<u32x4*>(dst + T::bf16_piece(r, 2 * c + 1)) = raw[1];
-        u32x4 o = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int b = 0; b < 16; ++b) {
             const uint32_t code = e4m3_code(ldexpf(x[b], -e));
@@ -401,15 +424,54 @@ __global__ __launch_bounds__(256) void pack_queries_kernel(const uint16_t* __res
         n8 += __shfl_xor(n8, 1, 8);
         n8 += __shfl_xor(n8, 2, 8);
         n8 += __shfl_xor(n8, 4, 8);
-        if (c == 0) rowbound[r] = fabsf(wr) * fmaxf(sqrtf(n2), ldexpf(sqrtf(n8), e));
+        if (c == 0) {
+            rowbound[r] = fabsf(wr) * fmaxf(sqrtf(n2), ldexpf(sqrtf(n8), e));
+            gsc[r] = e + 127;
+            gw[r] = fabsf(wr);
+            gtiny[r] = amax > 0.0f && e < -48;
+        }
+        *reinterpret_cast<u32x4*>(&gcode[r][4 * c]) = o;  // zero for pieces past d_idx
+        __syncthreads();
+        if (threadIdx.x < 64) {
+            // G on one wave: lane l holds column l % 32 of rows
+            // 8*(v/4) + 4*(l/32) + v%4; only pairs of heads of one query count
+            const int lane = threadIdx.x, gr = lane & 31, kb = lane >> 5;
+            f32x16 acc;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+            for (int st = 0; st < NSF; ++st) {
+                const u32x4 x0 = *reinterpret_cast<const u32x4*>(&gcode[gr][16 * st + 8 * kb]);
+                const u32x4 x1 = *reinterpret_cast<const u32x4*>(&gcode[gr][16 * st + 8 * kb + 4]);
+                const i32x8 fr = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                                  (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+                acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr, fr, acc, 0, 0, 0, gsc[gr],
+                                                                      0, gsc[gr]);
+            }
+            float part = 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int hr = 8 * (v / 4) + 4 * kb + (v % 4);
+                if (hr / HI == gr / HI) part = fmaf(gw[hr], fabsf(acc[v]), part);
+            }
+            gpart[lane] = part * gw[gr];
+        }
         __syncthreads();
         if (threadIdx.x < QPT) {
             const int64_t qi = tile * QPT + threadIdx.x;
-            float a = 0.0f;
-            for (int hh = 0; hh < HI; ++hh) a += rowbound[threadIdx.x * HI + hh];
+            float a = 0.0f, S = 0.0f;
+            int tiny = 0;
+            for (int hh = 0; hh < HI; ++hh) {
+                a += rowbound[threadIdx.x * HI + hh];
+                tiny |= gtiny[threadIdx.x * HI + hh];
+            }
             a *= 1.0f + 0x1p-8f;
-            if (qi < rows) qbound[qi] = a;
-            reinterpret_cast<float*>(dst + T::G.qb + 160)[threadIdx.x] = a;
+            for (int l = 0; l < 64; ++l)
+                if ((l & 31) / HI == (int)threadIdx.x) S += gpart[l];
+            const float a1 =
+                tiny ? a : fminf(a, (1.0f + 0x1p-8f) * sqrtf(fmaf(0x1p-14f * a, a, S)));
+            if (qi < rows) *reinterpret_cast<f32x2*>(qbound + 2 * qi) = f32x2{a1, a};
+            reinterpret_cast<f32x2*>(dst + T::G.qb + 160)[threadIdx.x] = f32x2{a1, a};
         }
     }
 }
@@ -470,8 +532,8 @@ struct ScoreK {
     int64_t n_pools;
     float* buf;
     int64_t ld;
-    const float* qbound;        // without the correction: [rows] per-query bound factors
-    const float* mu;            // and [P] per-pool bound factors
+    const float* qbound;        // without the correction: [rows][2] per-query bound factors
+    const float* mu;            // and [P][2] per-pool bound factors
 };
 
 // bf16 32x32x16 MFMA: lane l supplies A row (l % 32) and B column (l % 32),
@@ -499,7 +561,8 @@ struct ScoreK {
 // u = fma(A, mu_p, s~), from which the selection takes both bounds
 // (s~ + A mu_p and u - 2 A mu_p) without reading mu for every pool; it
 // rescores the pools near its threshold with the full sequence of MFMAs
-// below.
+// below.  Here A mu_p stands for A1 m1_p + A2 m2_p, formed as
+// fma(A1, m1, fma(A2, m2, s~)).
 template <int HI, int DI, int NB, bool EXACT, bool LO>
 __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     static_assert(NB == 2, "the epilogue pairs the two pool blocks of a wave");
@@ -565,7 +628,7 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     // of tile j.  Thread tid moves 16-byte pieces tid + 256u (loads clamped to
     // the last piece; LDS slots past the query data are spare) and one dword
     // of the tail (w at dwords 0-31, scale bytes in 32-39, the queries' bound
-    // factors in 40-47).
+    // factor pairs in 40-55).
     // Lane l of a wave lands at the wave's LDS base + l * size, so each
     // instruction fills a contiguous 1 KiB (256 B) slice.
     constexpr int D = NBUF - 1;
@@ -575,7 +638,7 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u)
         gsrc[u] = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb + 16 * min(tid + 256 * u, T::NPQ - 1);
-    gsrc[CPT] = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb + T::G.qb + 4 * min(tid, 47);
+    gsrc[CPT] = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb + T::G.qb + 4 * min(tid, 55);
     const uint32_t lds0 = lds_address(lds) + 1024u * (uint32_t)wave;
     auto fetch = [&](int j) {
         const int64_t g = (int64_t)j * T::G.tb;
@@ -601,17 +664,17 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
 
     const int64_t t_row0 = a.q_pos0 + a.row0;
     // pool factors of the bound for the columns this lane stores
-    float mu_st[NB] = {};
+    f32x2 mu_st[NB] = {};
     if constexpr (!LO) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int64_t p = HI == 4 ? p_wave + nb * 32 + col : p_wave + lane;
-            mu_st[nb] = p < a.n_pools ? a.mu[p] : 0.0f;
+            if (p < a.n_pools) mu_st[nb] = *reinterpret_cast<const f32x2*>(a.mu + 2 * p);
         }
     }
     const uint8_t* Lw = nullptr;  // the current tile's weights/scales/bounds in LDS
     int tile_i0 = 0;
-    auto put = [&](int i, int p, float v, float mu) {
+    auto put = [&](int i, int p, float v, f32x2 mu) {
         const int64_t t = t_row0 + i;
         const int nt = (int)((t >> 2) < a.n_pools ? (t >> 2) : a.n_pools);
         float* dst = a.buf + (int64_t)i * a.ld + p;
@@ -619,9 +682,9 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
             if (i < i_end && p < nt) *dst = canonical_zero(v);
         } else {
             if constexpr (!LO) {
-                // the query's bound factor, staged in LDS with the tile
-                const float A = reinterpret_cast<const float*>(Lw + 160)[i - tile_i0];
-                v = fmaf(A, mu, canonical_zero(v));
+                // the query's bound factors, staged in LDS with the tile
+                const f32x2 A = reinterpret_cast<const f32x2*>(Lw + 160)[i - tile_i0];
+                v = fmaf(A[0], mu[0], fmaf(A[1], mu[1], canonical_zero(v)));
             }
             *dst = p < nt ? canonical_zero(v) : -INFINITY;
         }

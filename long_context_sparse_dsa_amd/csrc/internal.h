@@ -10,8 +10,8 @@ namespace dsa {
 // Pooled indexer keys kbar (the mean of each pool's 4 rows, or with
 // per-token gates [4 * n_pools] fp32 their gate-weighted sum), split as
 // hi = bf16(kbar) [P][d] and lo = kbar - hi as E4M3 codes [P][d] with one
-// E8M0 power-of-two scale byte per pool.  mu (optional) [P] fp32: each pool's
-// factor of the bound on the score error of leaving lo out.
+// E8M0 power-of-two scale byte per pool.  mu (optional) [P][2] fp32: each
+// pool's two factors of the bound on the score error of leaving lo out.
 hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, const float* gate, int64_t n_pools,
                                  int d_idx, uint16_t* hi, uint8_t* lo, uint8_t* lo_scale,
                                  float* mu, hipStream_t stream);
@@ -23,7 +23,7 @@ hipError_t launch_pool_keys_bf16(const uint16_t* k_idx, const float* gate, int64
 //   [OF8, QB)       E4M3 codes of q / 2^e_r (row stride L8 bytes)
 //   [QB, QB + 128)  w of each row, fp32
 //   [QB + 128, +32) E8M0 byte e_r + 127 of each row
-//   [QB + 160, +32) the error-bound factor of each of the tile's queries, fp32
+//   [QB + 160, +64) the two error-bound factors of each of the tile's queries, fp32
 // Rows are stored in 16-byte pieces.  With d = 128 the piece order within a
 // row is XOR-swizzled by the row index so that the MFMA operand reads of 16
 // rows at a time hit distinct LDS banks; other widths pad each row by 16
@@ -38,7 +38,7 @@ inline constexpr QueryTileGeom query_tile_geom(int d) {
     const int l8 = swz ? d : d + 16;
     const int of8 = 32 * lb;
     const int qb = of8 + 32 * l8;
-    return QueryTileGeom{swz, lb, l8, of8, qb, (qb + 192 + 127) / 128 * 128};
+    return QueryTileGeom{swz, lb, l8, of8, qb, (qb + 224 + 127) / 128 * 128};
 }
 // Byte offset of 16-byte piece c of the bf16 row r / of the E4M3 row r.
 inline constexpr int tile_bf16_piece(const QueryTileGeom& g, int r, int c) {
@@ -54,7 +54,7 @@ inline constexpr int64_t query_tiles(int64_t rows, int h_idx) {
 }
 
 // Rows [row0, row0 + rows) of q_idx and w packed into query tiles; qbound
-// (optional) [rows] fp32: each query's factor of the same bound.
+// (optional) [rows][2] fp32: each query's two factors of the same bound.
 hipError_t launch_pack_queries(const uint16_t* q_idx, const float* w, int64_t w_stride,
                                int64_t row0, int rows, int h_idx, int d_idx, uint8_t* tiles,
                                float* qbound, hipStream_t stream);
@@ -92,10 +92,11 @@ struct ScoreArgs {
     // scores.
     int exact;
     // bf16, exact = 0: bound factors; the buffer receives upper bounds
-    // u = fma(qbound[i], mu[p], score without the correction), or the full
-    // scores when qbound is null
-    const float* qbound;      // [rows]
-    const float* mu;          // [n_pools]
+    // u = fma(A1, m1, fma(A2, m2, score without the correction)) with
+    // (A1, A2) = qbound[i] and (m1, m2) = mu[p], or the full scores when
+    // qbound is null
+    const float* qbound;      // [rows][2]
+    const float* mu;          // [n_pools][2]
     float* buf;               // [rows, ld] fp32
     int64_t ld;
 };
@@ -114,12 +115,13 @@ struct SelectArgs {
     int32_t* idx_out;         // [s_q, k_pools]
     float* score_out;         // optional
     // Bounded rows (bf16 indexer): the buffer holds u = s~ + delta with
-    // delta = qbound[i] * mu[p] and s~ the score without the correction term,
-    // so the full score lies in [u - 2 delta, u]; the selection recomputes it
-    // for the pools it cannot decide from the bounds.  qbound == nullptr: the
-    // buffer holds the final scores.
-    const float* qbound;      // [rows] per chunk query
-    const float* mu;          // [n_pools]
+    // delta = A1 m1 + A2 m2, (A1, A2) = qbound[i], (m1, m2) = mu[p], and s~
+    // the score without the correction term, so the full score lies in
+    // [u - 2 delta, u]; the selection recomputes it for the pools it cannot
+    // decide from the bounds.  qbound == nullptr: the buffer holds the final
+    // scores.
+    const float* qbound;      // [rows][2] per chunk query
+    const float* mu;          // [n_pools][2]
     const uint8_t* tiles;     // the chunk's packed query tiles
     const uint16_t* khi;      // [P][d_idx] bf16
     const uint8_t* klo;       // [P][d_idx] E4M3

@@ -698,6 +698,13 @@ __device__ void select_row(const float* row, int64_t n, int k, SelShared& sh, in
     }
 }
 
+// The half-width of pool p's score interval for a query with bound factors
+// A: A1 m1 + A2 m2 (the chunk buffer holds the interval's upper end).
+__device__ __forceinline__ float bound_delta(f32x2 A, const float* mu, int64_t p) {
+    const f32x2 m = *reinterpret_cast<const f32x2*>(mu + 2 * p);
+    return fmaf(A[0], m[0], A[1] * m[1]);
+}
+
 // Slow path for an approximate row that does not fit the list: L and U by
 // radix over the row, every pool that needs its full score rescored in place
 // (the band; with score_out also the certain ones), then the exact selection
@@ -705,13 +712,13 @@ __device__ void select_row(const float* row, int64_t n, int k, SelShared& sh, in
 // lie strictly above U (kept) or below L (dropped) and so cannot change the
 // set.
 template <int HI, int DI>
-__device__ void select_row_bounded(const SelectArgs& a, int64_t i, float* row, int64_t n, float A,
+__device__ void select_row_bounded(const SelectArgs& a, int64_t i, float* row, int64_t n, f32x2 A,
                                    SelShared& sh, int32_t* out, float* score_out) {
     const int tid = threadIdx.x;
     uint32_t Lk, Uk;
     band_bounds((int)n, [&](int64_t e, uint32_t& lk, uint32_t& uk) {
         const float x = row[e];
-        lk = order_key(x - 2.0f * (A * a.mu[e]));
+        lk = order_key(x - 2.0f * bound_delta(A, a.mu, e));
         uk = order_key(x);
     }, (uint32_t)a.k_pools, Lk, Uk, sh);
     uint32_t* ids = reinterpret_cast<uint32_t*>(sh.d);
@@ -719,7 +726,7 @@ __device__ void select_row_bounded(const SelectArgs& a, int64_t i, float* row, i
         const int w = (int)min((int64_t)CAP, n - base);
         // this window's pools in LDS first: the rescoring below writes the row
         for (int e = tid; e < w; e += NT) {
-            const float x = row[base + e], dl = A * a.mu[base + e];
+            const float x = row[base + e], dl = bound_delta(A, a.mu, base + e);
             const uint32_t lk = order_key(x - 2.0f * dl), uk = order_key(x);
             const bool band = uk >= Lk && lk <= Uk;
             const bool in = lk > Uk;
@@ -750,8 +757,8 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
     int32_t* out = a.idx_out + qrow * k;
     float* sout = a.score_out ? a.score_out + qrow * k : nullptr;
     float* row = a.buf + (int64_t)i * a.ld;
-    const float A = BOUNDS ? a.qbound[i] : 0.0f;
-    auto delta = [&](int64_t p) { return BOUNDS ? A * a.mu[p] : 0.0f; };
+    const f32x2 A = BOUNDS ? *reinterpret_cast<const f32x2*>(a.qbound + 2 * i) : f32x2{0.0f, 0.0f};
+    auto delta = [&](int64_t p) { return BOUNDS ? bound_delta(A, a.mu, p) : 0.0f; };
 
     if (n <= k) {
         for (int j = tid; j < k; j += NT) out[j] = j < n ? j : -1;
@@ -798,7 +805,7 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
         // multiple of NT; the blocks lie inside the row, n > CAP)
         constexpr int SU = 6;
         for (int s0 = 0; s0 < ns / 4; s0 += SU * NT) {
-            f32x4 v[SU], mv[SU];
+            f32x4 v[SU], mv[SU][2];
 #pragma unroll
             for (int u = 0; u < SU; ++u) {
                 const int s4 = s0 + u * NT + tid;
@@ -806,7 +813,10 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
                 const int b = (4 * s4) / SAMPLE_LEN, o = (4 * s4) % SAMPLE_LEN;
                 const int64_t e = (((int64_t)b * n / nb) & ~(int64_t)(SAMPLE_LEN - 1)) + o;
                 v[u] = *reinterpret_cast<const f32x4*>(row + e);
-                if constexpr (BOUNDS) mv[u] = *reinterpret_cast<const f32x4*>(a.mu + e);
+                if constexpr (BOUNDS) {
+                    mv[u][0] = *reinterpret_cast<const f32x4*>(a.mu + 2 * e);
+                    mv[u][1] = *reinterpret_cast<const f32x4*>(a.mu + 2 * e + 4);
+                }
             }
 #pragma unroll
             for (int u = 0; u < SU; ++u) {
@@ -814,8 +824,12 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
                 if (s4 >= ns / 4) continue;
                 u32x4 kk;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    kk[j] = order_key(v[u][j] - 2.0f * (BOUNDS ? A * mv[u][j] : 0.0f));
+                for (int j = 0; j < 4; ++j) {
+                    const float dl = BOUNDS ? fmaf(A[0], mv[u][j >> 1][2 * (j & 1)],
+                                                   A[1] * mv[u][j >> 1][2 * (j & 1) + 1])
+                                            : 0.0f;
+                    kk[j] = order_key(v[u][j] - 2.0f * dl);
+                }
                 *reinterpret_cast<u32x4*>(&sh.sample[4 * s4]) = kk;
             }
         }
@@ -900,7 +914,7 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
         __syncthreads();
         if (count > (uint32_t)CAP || cnt_l < (uint32_t)k) {
             if constexpr (BOUNDS) {
-                if (A > 0.0f) {
+                if (A[1] > 0.0f) {
                     select_row_bounded<HI, DI>(a, i, row, n, A, sh, out, sout);
                     return;
                 }

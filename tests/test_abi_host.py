@@ -45,12 +45,12 @@ def test_workspace_size_matches_layout(lib):
     # plus 256 x 32768 fp32 scores -- the page keeps each chunk under 2 GiB
     nbytes, cq = dsa.dsa_index_workspace_size(131072, 131072, 32, 128, 512, 4, 256)
     assert cq == 256
-    # hi bf16 + lo E4M3 + lo scales + per-pool bound factors (fp32), the
+    # hi bf16 + lo E4M3 + lo scales + per-pool bound factors (2 x fp32), the
     # chunk's packed query tiles (one query per tile at 32 heads, three spare;
-    # 12288 query bytes + 160 bytes of weights and scales, rounded to 128),
-    # per-query bound factors (fp32), the scores
-    assert nbytes == (32768 * 128 * 2 + 32768 * 128 + 32768 + 32768 * 4
-                      + (256 + 3) * 12544 + 256 * 4 + 256 * 32768 * 4)
+    # 12288 query bytes + 224 bytes of weights, scales and bound factors,
+    # rounded to 128), per-query bound factors (2 x fp32), the scores
+    assert nbytes == (32768 * 128 * 2 + 32768 * 128 + 32768 + 32768 * 8
+                      + (256 + 3) * 12544 + 256 * 8 + 256 * 32768 * 4)
     assert 256 * 32768 * 4 <= 2 ** 31
     # default chunk
     _, cq = dsa.dsa_index_workspace_size(32768, 32768, 32, 128, 512)
@@ -172,12 +172,12 @@ def test_fp8_workspace_layout(lib):
                                                dsa.DSA_FP8_E4M3) == 16384 * 96 + 16384 * 4
     r = lambda x: (x + 255) // 256 * 256
     # 8 heads: 4 queries per tile, 25 tiles + 3 spare; per-pool and per-query
-    # bound factors (fp32) after the scales and after the tiles
+    # bound factors (2 x fp32) after the scales and after the tiles
     assert dsa.dsa_index_scores_workspace_size(5000, 4000, 8, 128, 100) == (
-        r(1000 * 256) + r(1000 * 128) + r(1000) + r(1000 * 4) + r(28 * 12544) + r(100 * 4))
+        r(1000 * 256) + r(1000 * 128) + r(1000) + r(1000 * 8) + r(28 * 12544) + r(100 * 8))
     # rows are scored 4096 at a time: the tiles stop growing there
     assert dsa.dsa_index_scores_workspace_size(8192, 4000, 8, 128, 8192) == (
-        r(1000 * 256) + r(1000 * 128) + r(1000) + r(1000 * 4) + r(1027 * 12544) + r(4096 * 4))
+        r(1000 * 256) + r(1000 * 128) + r(1000) + r(1000 * 8) + r(1027 * 12544) + r(4096 * 8))
 
 
 def test_gated_entry_points_check_the_gate(lib):
