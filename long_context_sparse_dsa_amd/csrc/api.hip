@@ -33,7 +33,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 constexpr int64_t kMaxKPools = 2048;
-constexpr int64_t kDefaultChunkMax = 4096;
+constexpr int64_t kDefaultChunkMax = 8192;
 constexpr int64_t kDefaultBufferBudget = int64_t(3) << 29;  // 1.5 GiB
 // Top-k workgroups resident at once on MI355X: 256 CUs x 3.  Default chunks
 // are a multiple of it, so that no selection launch ends on a partial wave.
@@ -151,7 +151,7 @@ constexpr int64_t kDenseRows = 4096;
 dsa_status resolve_chunk(const IndexShape& sh, int64_t chunk_q, int64_t* out) {
     if (chunk_q < 0) return fail(DSA_ERR_INVALID_ARG, "chunk_q %lld < 0", (long long)chunk_q);
     if (chunk_q == 0) {
-        // at most 4096 queries (and no more than the queries there are);
+        // at most 8192 queries (and no more than the queries there are);
         // when the 1.5 GiB buffer budget is what limits the chunk (long
         // rows), the largest multiple of 768 within it, else of 64
         chunk_q = kDefaultBufferBudget / (score_ld(sh) * 4);

@@ -577,7 +577,8 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * T::LDSB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
     int bx, by;
     xcd_block(bx, by);
@@ -640,9 +641,9 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
         gsrc[u] = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb + 16 * min(tid + 256 * u, T::NPQ - 1);
     gsrc[CPT] = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb + T::G.qb + 4 * min(tid, 55);
     const uint32_t lds0 = lds_address(lds) + 1024u * (uint32_t)wave;
-    auto fetch = [&](int j) {
+    auto fetch = [&](int j, int b) {  // tile j into LDS buffer b = j % NBUF
         const int64_t g = (int64_t)j * T::G.tb;
-        const uint32_t l = lds0 + (uint32_t)((j % NBUF) * T::LDSB);
+        const uint32_t l = lds0 + (uint32_t)(b * T::LDSB);
 #pragma unroll
         for (int u = 0; u < CPT; ++u) lds_load16(gsrc[u] + g, l + 4096u * u);
         lds_load4(gsrc[CPT] + g, l + (uint32_t)T::LDS_W - 768u * (uint32_t)wave);
@@ -660,7 +661,7 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     };
 
 #pragma unroll
-    for (int j = 0; j < D; ++j) fetch(j);
+    for (int j = 0; j < D; ++j) fetch(j, j);
 
     const int64_t t_row0 = a.q_pos0 + a.row0;
     // pool factors of the bound for the columns this lane stores
@@ -674,6 +675,9 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     }
     const uint8_t* Lw = nullptr;  // the current tile's weights/scales/bounds in LDS
     int tile_i0 = 0;
+    // all_in: every pool of this wave is eligible for every query of the
+    // tile (wave-uniform), so no store needs the -inf mask
+    bool all_in = false;
     auto put = [&](int i, int p, float v, f32x2 mu) {
         const int64_t t = t_row0 + i;
         const int nt = (int)((t >> 2) < a.n_pools ? (t >> 2) : a.n_pools);
@@ -682,115 +686,131 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
             if (i < i_end && p < nt) *dst = canonical_zero(v);
         } else {
             if constexpr (!LO) {
-                // the query's bound factors, staged in LDS with the tile
+                // the query's bound factors, staged in LDS with the tile.  A
+                // and mu are non-negative, so both products are +0 or
+                // positive and u is never -0: it needs no canonicalisation.
                 const f32x2 A = reinterpret_cast<const f32x2*>(Lw + 160)[i - tile_i0];
-                v = fmaf(A[0], mu[0], fmaf(A[1], mu[1], canonical_zero(v)));
+                v = fmaf(A[0], mu[0], fmaf(A[1], mu[1], v));
+            } else {
+                v = canonical_zero(v);
             }
-            *dst = p < nt ? canonical_zero(v) : -INFINITY;
+            if (all_in) *dst = v;
+            else *dst = p < nt ? v : -INFINITY;
         }
     };
-    for (int j = 0; j < n_tiles; ++j) {
-        wait_tile(j);
-        __syncthreads();
-        // every wave is past tile j - 1: its buffer takes tile j + D (tiles
-        // past the chunk's end read its spare tiles and are never used)
-        fetch(j + D);
-        const uint8_t* L = lds + (j % NBUF) * T::LDSB;
+    // unrolled by NBUF, so that every LDS buffer address is a constant
+    // offset from the per-lane operand offsets
+    for (int j0 = 0; j0 < n_tiles; j0 += NBUF) {
+#pragma unroll
+        for (int jj = 0; jj < NBUF; ++jj) {
+            const int j = j0 + jj;
+            if (j >= n_tiles) break;
+            wait_tile(j);
+            __syncthreads();
+            // every wave is past tile j - 1: its buffer takes tile j + D (tiles
+            // past the chunk's end read its spare tiles and are never used)
+            fetch(j + D, (jj + D) % NBUF);
+            const uint8_t* L = lds + jj * T::LDSB;
 
-        f32x16 acc[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[nb][v] = 0.0f;
-
-        // all A fragments of the tile first, then q . hi on bf16 MFMAs and
-        // q . lo on scaled fp8 MFMAs into the same accumulators
-        bf16x8 af[NSB];
-        i32x8 af8[NSF];
-#pragma unroll
-        for (int s = 0; s < NSB; ++s)
-            af[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(L + T::bf16_piece(col, 2 * s + half)));
-#pragma unroll
-        for (int s = 0; s < (LO ? NSF : 0); ++s) {
-            // pieces past d_idx (only with d_idx = 96) read row padding or the
-            // next row and are zeroed
-            const bool in = 64 * s + 32 * half < DI;
-            u32x4 x0 = *reinterpret_cast<const u32x4*>(L + T::fp8_piece(col, 4 * s + 2 * half));
-            u32x4 x1 = *reinterpret_cast<const u32x4*>(L + T::fp8_piece(col, 4 * s + 2 * half + 1));
-            if (!in) x0 = x1 = u32x4{0u, 0u, 0u, 0u};
-            af8[s] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                           (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-        }
-        const int qsc = LO ? (int)L[T::LDS_W + 128 + col] : 127;
-#pragma unroll
-        for (int s = 0; s < NSB; ++s)
+            f32x16 acc[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], bhi[nb][s], acc[nb], 0, 0, 0);
 #pragma unroll
-        for (int s = 0; s < (LO ? NSF : 0); ++s)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af8[s], blo[nb][s], acc[nb], 0, 0, 0, qsc, 0, bsc[nb]);
-        // keep the LDS reads ahead of the MFMAs
-        if constexpr (LO) {
-            __builtin_amdgcn_sched_group_barrier(0x100, NSB + 2 * NSF + 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, NB * (NSB + NSF), 0);
-        } else {
-            __builtin_amdgcn_sched_group_barrier(0x100, NSB, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, NB * NSB, 0);
-        }
+                for (int v = 0; v < 16; ++v) acc[nb][v] = 0.0f;
 
-        // epilogue: per-lane partial sums w * relu over the rows this lane
-        // holds (rows 8*g4 + 4*half + i), then the two half-waves' partials of
-        // each column are added
-        float wv[16];
+            // all A fragments of the tile first, then q . hi on bf16 MFMAs and
+            // q . lo on scaled fp8 MFMAs into the same accumulators
+            bf16x8 af[NSB];
+            i32x8 af8[NSF];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 w4 = *reinterpret_cast<const f32x4*>(L + T::LDS_W + 4 * (8 * g4 + 4 * half));
-            wv[4 * g4 + 0] = w4[0];
-            wv[4 * g4 + 1] = w4[1];
-            wv[4 * g4 + 2] = w4[2];
-            wv[4 * g4 + 3] = w4[3];
-        }
-        float part[NB][4];
+            for (int s = 0; s < NSB; ++s)
+                af[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(L + T::bf16_piece(col, 2 * s + half)));
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                float sacc = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sacc += wv[4 * g4 + i] * relu(acc[nb][4 * g4 + i]);
-                part[nb][g4] = sacc;
+            for (int s = 0; s < (LO ? NSF : 0); ++s) {
+                // pieces past d_idx (only with d_idx = 96) read row padding or the
+                // next row and are zeroed
+                const bool in = 64 * s + 32 * half < DI;
+                u32x4 x0 = *reinterpret_cast<const u32x4*>(L + T::fp8_piece(col, 4 * s + 2 * half));
+                u32x4 x1 = *reinterpret_cast<const u32x4*>(L + T::fp8_piece(col, 4 * s + 2 * half + 1));
+                if (!in) x0 = x1 = u32x4{0u, 0u, 0u, 0u};
+                af8[s] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                               (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
             }
-        tile_i0 = i_begin + j * QPT;
-        Lw = L + T::LDS_W;
-        if constexpr (HI == 4) {
-            // rows 8*g4 + 4*half + i are the 4 heads of query 2*g4 + half
+            const int qsc = LO ? (int)L[T::LDS_W + 128 + col] : 127;
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4)
+            for (int s = 0; s < NSB; ++s)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    put(tile_i0 + 2 * g4 + half, (int)p_wave + nb * 32 + col, part[nb][g4],
-                        mu_st[nb]);
-        } else {
-            // lane l < 32 ends with pool block 0, lane l >= 32 with block 1:
-            // one store of 64 consecutive pools per query
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], bhi[nb][s], acc[nb], 0, 0, 0);
 #pragma unroll
-            for (int u = 0; u < QPT; ++u) {
-                float x0, x1;
-                if constexpr (HI == 32) {
-                    x0 = (part[0][0] + part[0][1]) + (part[0][2] + part[0][3]);
-                    x1 = (part[1][0] + part[1][1]) + (part[1][2] + part[1][3]);
-                } else if constexpr (HI == 16) {
-                    x0 = part[0][2 * u] + part[0][2 * u + 1];
-                    x1 = part[1][2 * u] + part[1][2 * u + 1];
-                } else {
-                    x0 = part[0][u];
-                    x1 = part[1][u];
+            for (int s = 0; s < (LO ? NSF : 0); ++s)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        af8[s], blo[nb][s], acc[nb], 0, 0, 0, qsc, 0, bsc[nb]);
+            // keep the LDS reads ahead of the MFMAs
+            if constexpr (LO) {
+                __builtin_amdgcn_sched_group_barrier(0x100, NSB + 2 * NSF + 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NB * (NSB + NSF), 0);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x100, NSB, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NB * NSB, 0);
+            }
+
+            // epilogue: per-lane partial sums w * relu over the rows this lane
+            // holds (rows 8*g4 + 4*half + i), then the two half-waves' partials of
+            // each column are added
+            float wv[16];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(L + T::LDS_W + 4 * (8 * g4 + 4 * half));
+                wv[4 * g4 + 0] = w4[0];
+                wv[4 * g4 + 1] = w4[1];
+                wv[4 * g4 + 2] = w4[2];
+                wv[4 * g4 + 3] = w4[3];
+            }
+            float part[NB][4];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    float sacc = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sacc += wv[4 * g4 + i] * relu(acc[nb][4 * g4 + i]);
+                    part[nb][g4] = sacc;
                 }
-                put(tile_i0 + u, (int)p_wave + lane, add_halves2(x0, x1), mu_st[0]);
+            tile_i0 = i_begin + j * QPT;
+            Lw = L + T::LDS_W;
+            {
+                const int64_t t0 = t_row0 + tile_i0;
+                all_in = p_wave + PW <= ((t0 >> 2) < a.n_pools ? (t0 >> 2) : a.n_pools);
+            }
+            if constexpr (HI == 4) {
+                // rows 8*g4 + 4*half + i are the 4 heads of query 2*g4 + half
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        put(tile_i0 + 2 * g4 + half, (int)p_wave + nb * 32 + col, part[nb][g4],
+                            mu_st[nb]);
+            } else {
+                // lane l < 32 ends with pool block 0, lane l >= 32 with block 1:
+                // one store of 64 consecutive pools per query
+#pragma unroll
+                for (int u = 0; u < QPT; ++u) {
+                    float x0, x1;
+                    if constexpr (HI == 32) {
+                        x0 = (part[0][0] + part[0][1]) + (part[0][2] + part[0][3]);
+                        x1 = (part[1][0] + part[1][1]) + (part[1][2] + part[1][3]);
+                    } else if constexpr (HI == 16) {
+                        x0 = part[0][2 * u] + part[0][2 * u + 1];
+                        x1 = part[1][2 * u] + part[1][2 * u + 1];
+                    } else {
+                        x0 = part[0][u];
+                        x1 = part[1][u];
+                    }
+                    put(tile_i0 + u, (int)p_wave + lane, add_halves2(x0, x1), mu_st[0]);
+                }
             }
         }
     }

@@ -78,7 +78,7 @@ struct SelShared {
     };
     uint32_t hist[512];
     uint32_t tmp[8];
-    uint32_t wtot[4 * (NT / 64)];
+    uint32_t wtot[8 * (NT / 64)];  // per-slot wave totals of block_excl_scan_slots (<= 8 slots)
 };
 
 // Wave-level inclusive scans on DPP: row shifts 1, 2, 4, 8 within each row
@@ -131,10 +131,11 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SelShared& sh, u
 // slot-major: all threads' slot 0, then all threads' slot 1, ...  (the order
 // of elements base + (u*NT + tid)*4 + j).  Returns the offsets in `off` and
 // the grand total.
-template <int VB>
+template <int VB, int NW>
 __device__ __forceinline__ uint32_t block_excl_scan_slots(const uint32_t (&c)[VB],
                                                           uint32_t (&off)[VB], SelShared& sh,
-                                                          uint32_t* wtot) {
+                                                          uint32_t (&wtot)[NW]) {
+    static_assert(VB * (NT / 64) <= NW, "one wave total per slot and wave");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t inc[VB];
 #pragma unroll

@@ -248,17 +248,23 @@ def _host_topk_ids(scores, n, k):
     return np.sort(order[:k]).astype(np.int32)
 
 
-@pytest.mark.parametrize("near_constant", [False, True])
-def test_selection_equals_exact_topk_of_full_scores(near_constant):
+@pytest.mark.parametrize("s_k,q_pos0,near_constant", [
+    (65536, 65344, False), (65536, 65344, True),      # bounded rows of 16k pools
+    (131072, 130880, False), (131072, 130880, True),  # bounded rows of 32k pools
+    (80192, 80000, False),                            # rows of 20k pools, scored in full
+])
+def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, near_constant):
     # The chunk buffer holds scores taken without the E4M3 correction; the
     # selection rescores only the pools its error bound cannot decide.  The
     # kept ids must be exactly the top-k of the full scores, which
     # dsa_index_scores returns (same MFMA sequence).  Near-constant keys put
     # nearly every pool within the bound of the threshold, so long rows
-    # overflow the LDS list and take the slow path in global memory.
-    wl = inputs.custom("full_topk", s_q=192, s_k=65536, q_pos0=65344, h_idx=32, d_idx=128,
+    # overflow the LDS list and take the slow path in global memory.  At
+    # 80000 the chunk's rows are short enough to be scored in full, so the
+    # selection works on final scores.
+    wl = inputs.custom("full_topk", s_q=192, s_k=s_k, q_pos0=q_pos0, h_idx=32, d_idx=128,
                        k_pools=512, h=16, d=128, idx_std=1 / math.sqrt(128),
-                       number=381 if near_constant else 380)
+                       number=380 + (1 if near_constant else 0) + (s_k - 65536) // 4096)
     x = inputs.make_inputs(wl, attention=False)
     if near_constant:
         rng = np.random.default_rng(7)
