@@ -87,6 +87,17 @@ __device__ __forceinline__ void lds_load4(const void* gptr, uint32_t lds) {
                  :: "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
+// The same with a wave-uniform base address (SGPR pair) and a 32-bit
+// per-lane offset, so that moving to the next tile is scalar arithmetic.
+__device__ __forceinline__ void lds_load16_sv(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+__device__ __forceinline__ void lds_load4_sv(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
 // XCD-aware workgroup order.  The dispatcher deals workgroups of a launch to
 // the chip's 8 XCDs round-robin by linear id, and each XCD has its own L2.
 // The logical id returned here makes every XCD walk one contiguous range of

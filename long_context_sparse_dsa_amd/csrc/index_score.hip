@@ -635,18 +635,19 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     constexpr int D = NBUF - 1;
     constexpr int NDMA = CPT + 1;                     // direct loads per tile
     constexpr int S = HI == 4 ? 8 : QPT;              // score stores per tile
-    const uint8_t* gsrc[CPT + 1];
+    // (wave-uniform tile addresses, per-lane offsets)
+    const uint8_t* tile0 = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb;
+    uint32_t voff[CPT + 1];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u)
-        gsrc[u] = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb + 16 * min(tid + 256 * u, T::NPQ - 1);
-    gsrc[CPT] = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb + T::G.qb + 4 * min(tid, 55);
+    for (int u = 0; u < CPT; ++u) voff[u] = 16u * (uint32_t)min(tid + 256 * u, T::NPQ - 1);
+    voff[CPT] = (uint32_t)T::G.qb + 4u * (uint32_t)min(tid, 55);
     const uint32_t lds0 = lds_address(lds) + 1024u * (uint32_t)wave;
     auto fetch = [&](int j, int b) {  // tile j into LDS buffer b = j % NBUF
-        const int64_t g = (int64_t)j * T::G.tb;
+        const uint8_t* src = tile0 + (int64_t)j * T::G.tb;
         const uint32_t l = lds0 + (uint32_t)(b * T::LDSB);
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) lds_load16(gsrc[u] + g, l + 4096u * u);
-        lds_load4(gsrc[CPT] + g, l + (uint32_t)T::LDS_W - 768u * (uint32_t)wave);
+        for (int u = 0; u < CPT; ++u) lds_load16_sv(src, voff[u], l + 4096u * u);
+        lds_load4_sv(src, voff[CPT], l + (uint32_t)T::LDS_W - 768u * (uint32_t)wave);
     };
     // Tile j's loads are complete once at most this many later memory
     // operations are outstanding (loads and stores retire in order): the
@@ -663,27 +664,30 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
 #pragma unroll
     for (int j = 0; j < D; ++j) fetch(j, j);
 
-    const int64_t t_row0 = a.q_pos0 + a.row0;
     // pool factors of the bound for the columns this lane stores
+    const int64_t t_row0 = a.q_pos0 + a.row0;
     f32x2 mu_st[NB] = {};
-    if constexpr (!LO) {
+    // and the first chunk row for which each of those pools is eligible
+    // (4p + 3 < t, t = t_row0 + i; never for p >= n_pools), as a 32-bit
+    // threshold on the row index: the -inf mask of a store is one compare
+    int e_st[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int64_t p = HI == 4 ? p_wave + nb * 32 + col : p_wave + lane;
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t p = HI == 4 ? p_wave + nb * 32 + col : p_wave + lane;
+        if constexpr (!LO)
             if (p < a.n_pools) mu_st[nb] = *reinterpret_cast<const f32x2*>(a.mu + 2 * p);
-        }
+        const int64_t e = p < a.n_pools ? 4 * p + 4 - t_row0 : (int64_t)INT32_MAX;
+        e_st[nb] = (int)(e < (int64_t)INT32_MIN ? (int64_t)INT32_MIN
+                                                : (e > (int64_t)INT32_MAX ? (int64_t)INT32_MAX : e));
     }
     const uint8_t* Lw = nullptr;  // the current tile's weights/scales/bounds in LDS
     int tile_i0 = 0;
-    // all_in: every pool of this wave is eligible for every query of the
-    // tile (wave-uniform), so no store needs the -inf mask
-    bool all_in = false;
-    auto put = [&](int i, int p, float v, f32x2 mu) {
-        const int64_t t = t_row0 + i;
-        const int nt = (int)((t >> 2) < a.n_pools ? (t >> 2) : a.n_pools);
-        float* dst = a.buf + (int64_t)i * a.ld + p;
+    auto put = [&](int i, int p, float v, f32x2 mu, int e) {
+        // row base (wave-uniform where i is) plus a 32-bit byte offset
+        float* dst = reinterpret_cast<float*>(reinterpret_cast<char*>(a.buf + (int64_t)i * a.ld) +
+                                              (uint32_t)p * 4u);
         if constexpr (EXACT) {
-            if (i < i_end && p < nt) *dst = canonical_zero(v);
+            if (i < i_end && i >= e) *dst = canonical_zero(v);
         } else {
             if constexpr (!LO) {
                 // the query's bound factors, staged in LDS with the tile.  A
@@ -694,8 +698,7 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
             } else {
                 v = canonical_zero(v);
             }
-            if (all_in) *dst = v;
-            else *dst = p < nt ? v : -INFINITY;
+            *dst = i >= e ? v : -INFINITY;
         }
     };
     // unrolled by NBUF, so that every LDS buffer address is a constant
@@ -769,22 +772,24 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
                 wv[4 * g4 + 2] = w4[2];
                 wv[4 * g4 + 3] = w4[3];
             }
+            // (the bound path at 32 heads sums each pool block's 16 rows in
+            // two chains of 8, with fewer additions; its order only has to
+            // stay within the rounding the bound covers, while full scores
+            // keep the order the rescoring reproduces)
+            constexpr bool CHAINS = !LO && HI == 32;
             float part[NB][4];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
+                for (int g4 = 0; g4 < 4; g4 += CHAINS ? 2 : 1) {
                     float sacc = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sacc += wv[4 * g4 + i] * relu(acc[nb][4 * g4 + i]);
+                    for (int i = 0; i < (CHAINS ? 8 : 4); ++i)
+                        sacc += wv[4 * g4 + i] * relu(acc[nb][4 * g4 + i]);
                     part[nb][g4] = sacc;
                 }
             tile_i0 = i_begin + j * QPT;
             Lw = L + T::LDS_W;
-            {
-                const int64_t t0 = t_row0 + tile_i0;
-                all_in = p_wave + PW <= ((t0 >> 2) < a.n_pools ? (t0 >> 2) : a.n_pools);
-            }
             if constexpr (HI == 4) {
                 // rows 8*g4 + 4*half + i are the 4 heads of query 2*g4 + half
 #pragma unroll
@@ -792,14 +797,17 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
                         put(tile_i0 + 2 * g4 + half, (int)p_wave + nb * 32 + col, part[nb][g4],
-                            mu_st[nb]);
+                            mu_st[nb], e_st[nb]);
             } else {
                 // lane l < 32 ends with pool block 0, lane l >= 32 with block 1:
                 // one store of 64 consecutive pools per query
 #pragma unroll
                 for (int u = 0; u < QPT; ++u) {
                     float x0, x1;
-                    if constexpr (HI == 32) {
+                    if constexpr (CHAINS) {
+                        x0 = part[0][0] + part[0][2];
+                        x1 = part[1][0] + part[1][2];
+                    } else if constexpr (HI == 32) {
                         x0 = (part[0][0] + part[0][1]) + (part[0][2] + part[0][3]);
                         x1 = (part[1][0] + part[1][1]) + (part[1][2] + part[1][3]);
                     } else if constexpr (HI == 16) {
@@ -809,7 +817,7 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
                         x0 = part[0][u];
                         x1 = part[1][u];
                     }
-                    put(tile_i0 + u, (int)p_wave + lane, add_halves2(x0, x1), mu_st[0]);
+                    put(tile_i0 + u, (int)p_wave + lane, add_halves2(x0, x1), mu_st[0], e_st[0]);
                 }
             }
         }
