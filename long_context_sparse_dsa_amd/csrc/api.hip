@@ -137,12 +137,13 @@ int64_t score_ld(const IndexShape& sh) { return round_up(sh.n_pools > 0 ? sh.n_p
 // the pools near each row's k-th score (bounded), or score it in full?  The
 // rescoring costs about k pools per row whatever the row's length, the
 // correction term a share of every pool, so the bounds pay once the rows see
-// more than about 24 k pools (measured on MI355X at k = 512: 16, 24, 32 and
-// 48 k compared at 64k, 128k and the 1M-token share).
+// more than about 16 k pools (measured on MI355X at k = 512 with 8192-query
+// chunks: 8, 12, 16 and 24 k per row were within 1% of each other at 32k
+// and 128k, 16 k the fastest at 128k).
 bool bounded_chunk(const IndexShape& sh, int64_t t_first, int64_t t_last) {
     const int64_t n_first = (t_first / 4) < sh.n_pools ? (t_first / 4) : sh.n_pools;
     const int64_t n_last = (t_last / 4) < sh.n_pools ? (t_last / 4) : sh.n_pools;
-    return n_first + n_last > 2 * 24 * (int64_t)sh.k_pools;
+    return n_first + n_last > 2 * 16 * (int64_t)sh.k_pools;
 }
 
 // Rows per scoring launch of the dense-score entry point (bounds its workspace).

@@ -657,3 +657,48 @@ def test_attention_backward_rejects_malformed_rows():
         with pytest.raises(RuntimeError):
             oracle.sparse_attn_bwd(x["q"], x["k"], x["v"], np.array([bad], dtype=np.int32),
                                    dout, 4, rows=[60])
+
+
+# ---------------------------------------------------------------- page figures
+# tests/golden/page_figures.txt holds the figures the blog prints, with their
+# sections; these tests tie the oracle's shapes to them.
+
+def _page_figures():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "page_figures.txt")
+    out = {}
+    with open(path) as fh:
+        for ln in fh:
+            if not ln.strip() or ln.lstrip().startswith("#"):
+                continue
+            name, size, value = ln.split()[:3]
+            out.setdefault(name, {})[size] = int(value)
+    return out
+
+
+def test_page_figures_memory_model_and_selection_size():
+    fig = _page_figures()
+    # the unchunked per-head score buffer: 2 copies x 4 B x S x S/4 pools x 32 heads
+    for size, value in fig["unchunked_indexer_bytes"].items():
+        s = int(size)
+        assert 2 * 4 * s * (s // fig["pool_size"]["-"]) * 32 == value
+    # 512 pools of 4 tokens are the 2048 attended tokens
+    assert 512 * fig["pool_size"]["-"] == fig["selected_tokens"]["-"]
+
+
+def test_page_figures_keys_per_query_from_the_oracle():
+    # With all logits 0 (q = 0) the softmax is uniform over the token set, so
+    # exp(lse) counts the keys a query attends: 512 pools of 4 plus the 3
+    # earlier tokens of its own pool (reading R6) make the page's 2,051.
+    fig = _page_figures()
+    k_pools = fig["selected_tokens"]["-"] // fig["pool_size"]["-"]
+    t = 4 * 1200 + 3                      # t mod 4 = 3: three earlier tokens in its pool
+    s_k = t + 1
+    q = torch.zeros(1, 2, 64, dtype=torch.bfloat16)
+    k = torch.randn(s_k, 64).to(torch.bfloat16)
+    v = torch.randn(s_k, 64).to(torch.bfloat16)
+    ids = np.arange(0, 2 * k_pools, 2, dtype=np.int32)[None, :]   # 512 pools, all before t
+    _, lse = oracle.sparse_attn(q, k, v, ids, k_pools, q_pos0=t, rows=np.array([0]), n_tail=3)
+    assert np.allclose(np.exp(lse), fig["keys_per_query"]["-"], rtol=1e-12)
+    # the chunk buffer cap the ABI enforces is the page's
+    assert fig["chunk_buffer_cap_bytes"]["-"] == 2 ** 31
