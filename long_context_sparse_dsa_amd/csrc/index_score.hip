@@ -28,6 +28,8 @@
 // lands in the same accumulators.  The fp8 rounding leaves the correction
 // ~5% off, i.e. ~3e-5 of a typical score, far inside the selection's 1e-3
 // boundary band.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -881,9 +883,17 @@ struct ScoreK8 {
 // two E4M3 values are exact in fp32.  The score is
 //   s = sum_h w * relu(c_p * q8_h . kbar8_p),   c_p = q_scale * k_scale * 2^e_p,
 // computed as |c_p| * sum_h w * relu(sign(c) * acc) (the sign of c is the
-// sign of q_scale * k_scale, the same for every pool).
-template <int HI, int DI, int NB>
+// sign of q_scale * k_scale, the same for every pool).  With a negative sign
+// w * relu(-x) is taken as (-w) * min(x, 0), one integer min on the bits of
+// x (negative floats are the negative ints), so both signs cost one integer
+// op and one FMA per element; the sign is a uniform branch per tile.
+//
+// EXACT = false: the chunk-buffer contract of ScoreArgs (any entry may be
+// written, ineligible pools get -inf); EXACT = true: only eligible entries
+// of rows [0, rows).
+template <int HI, int DI, int NB, bool EXACT>
 __global__ __launch_bounds__(256, 2) void index_score_fp8_kernel(ScoreK8 a) {
+    static_assert(NB % 2 == 0, "pool blocks are stored in pairs");
     constexpr int QPT = 32 / HI;
     constexpr int NS = (DI + 63) / 64;   // MFMA steps of 64 dims
     constexpr int PW = 32 * NB;
@@ -912,14 +922,26 @@ __global__ __launch_bounds__(256, 2) void index_score_fp8_kernel(ScoreK8 a) {
 
     const float qk = (a.q_scale ? *a.q_scale : 1.0f) * (a.k_scale ? *a.k_scale : 1.0f);
     const bool flip = qk < 0.0f;
+    // pools of the stored columns (block 2m in lanes 0-31, 2m + 1 in lanes
+    // 32-63) and the first chunk row for which each is eligible (4p + 3 < t),
+    // as a 32-bit threshold on the row index
+    const int64_t t_row0 = a.q_pos0 + a.row0;
+    int e_st[NB / 2];
+    float c_st[NB / 2];
+#pragma unroll
+    for (int m = 0; m < NB / 2; ++m) {
+        const int64_t p = p_wave + 64 * m + lane;
+        const int64_t e = p < a.n_pools ? 4 * p + 4 - t_row0 : (int64_t)INT32_MAX;
+        e_st[m] = (int)(e < (int64_t)INT32_MIN ? (int64_t)INT32_MIN
+                                               : (e > (int64_t)INT32_MAX ? (int64_t)INT32_MAX : e));
+        c_st[m] = p < a.n_pools ? fabsf(qk) * a.pool_scale[p] : 0.0f;
+    }
 
     // resident pooled keys; contraction bytes 64*s + 32*half .. +32 (zero past DI)
     i32x8 bfr[NB][NS];
-    float cpool[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int64_t p = p_wave + nb * 32 + col;
-        cpool[nb] = p < a.n_pools ? fabsf(qk) * a.pool_scale[p] : 0.0f;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             u32x4 lo4 = {0u, 0u, 0u, 0u}, hi4 = {0u, 0u, 0u, 0u};
@@ -1008,48 +1030,69 @@ __global__ __launch_bounds__(256, 2) void index_score_fp8_kernel(ScoreK8 a) {
             wv[4 * g4 + 3] = w4[3];
         }
         const int tile_i0 = i_begin + j * QPT;
+        // per-lane partial sums w * relu over the rows this lane holds (rows
+        // 8*g4 + 4*half + i of the accumulator)
+        float part[NB][4];
+        auto head_sums = [&](auto flip_tag) {
+            constexpr bool FL = decltype(flip_tag)::value;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int64_t p = p_wave + nb * 32 + col;
-            float part[4];
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                float s = 0.0f;
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    float sacc = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x = flip ? -acc[nb][4 * g4 + i] : acc[nb][4 * g4 + i];
-                    s += wv[4 * g4 + i] * relu(x);
+                    for (int i = 0; i < 4; ++i) {
+                        const int xb = __float_as_int(acc[nb][4 * g4 + i]);
+                        sacc = FL ? fmaf(-wv[4 * g4 + i], __int_as_float(min(xb, 0)), sacc)
+                                  : fmaf(wv[4 * g4 + i], __int_as_float(max(xb, 0)), sacc);
+                    }
+                    part[nb][g4] = sacc;
                 }
-                part[g4] = s;
+        };
+        if (flip) head_sums(std::true_type{});
+        else head_sums(std::false_type{});
+        auto put = [&](int i, int m, float v) {
+            float* dst = reinterpret_cast<float*>(
+                reinterpret_cast<char*>(a.buf + (int64_t)i * a.ld) +
+                (uint32_t)(p_wave + 64 * m + lane) * 4u);
+            v = canonical_zero(c_st[m] * v);
+            if constexpr (EXACT) {
+                if (i < i_end && i >= e_st[m]) *dst = v;
+            } else {
+                *dst = i >= e_st[m] ? v : -INFINITY;
             }
-            float qv[4];
-            int nq;
-            if constexpr (HI == 32) {
-                qv[0] = add_halves((part[0] + part[1]) + (part[2] + part[3]));
-                nq = 1;
-            } else if constexpr (HI == 16) {
-                qv[0] = add_halves(part[0] + part[1]);
-                qv[1] = add_halves(part[2] + part[3]);
-                nq = 2;
-            } else if constexpr (HI == 8) {
+        };
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) qv[g4] = add_halves(part[g4]);
-                nq = 4;
+        for (int m = 0; m < NB / 2; ++m) {
+            // lanes 0-31 end with pool block 2m, lanes 32-63 with block 2m + 1
+            if constexpr (HI == 4) {
+                // lane half h holds query 2*g4 + h in part[.][g4]; swapping
+                // the upper half of block 2m with the lower half of block
+                // 2m + 1 gives query 2*g4 in r[0] and query 2*g4 + 1 in r[1]
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const auto r = __builtin_amdgcn_permlane32_swap(
+                        __float_as_uint(part[2 * m][g4]), __float_as_uint(part[2 * m + 1][g4]),
+                        false, false);
+                    put(tile_i0 + 2 * g4, m, __uint_as_float(r[0]));
+                    put(tile_i0 + 2 * g4 + 1, m, __uint_as_float(r[1]));
+                }
             } else {
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) qv[g4] = part[g4];
-                nq = 4;
-            }
-            if (HI == 4 || half == 0) {
-#pragma unroll
-                for (int u = 0; u < nq; ++u) {
-                    const int qi = (HI == 4) ? (2 * u + half) : u;
-                    const int i = tile_i0 + qi;
-                    if (i < i_end) {
-                        const int64_t t = a.q_pos0 + a.row0 + i;
-                        const int64_t nt = (t >> 2) < a.n_pools ? (t >> 2) : a.n_pools;
-                        if (p < nt) a.buf[(int64_t)i * a.ld + p] = canonical_zero(cpool[nb] * qv[u]);
+                for (int u = 0; u < QPT; ++u) {
+                    float x0, x1;
+                    if constexpr (HI == 32) {
+                        x0 = (part[2 * m][0] + part[2 * m][1]) + (part[2 * m][2] + part[2 * m][3]);
+                        x1 = (part[2 * m + 1][0] + part[2 * m + 1][1]) +
+                             (part[2 * m + 1][2] + part[2 * m + 1][3]);
+                    } else if constexpr (HI == 16) {
+                        x0 = part[2 * m][2 * u] + part[2 * m][2 * u + 1];
+                        x1 = part[2 * m + 1][2 * u] + part[2 * m + 1][2 * u + 1];
+                    } else {
+                        x0 = part[2 * m][u];
+                        x1 = part[2 * m + 1][u];
                     }
+                    put(tile_i0 + u, m, add_halves2(x0, x1));
                 }
             }
         }
@@ -1082,7 +1125,8 @@ static hipError_t launch_score_fp8_t(const ScoreArgs& a, hipStream_t stream) {
     k.ld = a.ld;
     const dim3 grid((unsigned)((a.n_chunk + PB - 1) / PB), (unsigned)((a.rows + k.gq - 1) / k.gq));
     if (grid.x == 0 || grid.y == 0) return hipSuccess;
-    index_score_fp8_kernel<HI, DI, NB><<<grid, 256, 0, stream>>>(k);
+    if (a.exact) index_score_fp8_kernel<HI, DI, NB, true><<<grid, 256, 0, stream>>>(k);
+    else index_score_fp8_kernel<HI, DI, NB, false><<<grid, 256, 0, stream>>>(k);
     return hipGetLastError();
 }
 
