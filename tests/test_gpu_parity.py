@@ -292,6 +292,37 @@ def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, near_constant):
                  check_scores=False)
 
 
+@pytest.mark.parametrize("h_idx,d_idx,scales", [
+    (32, 96, (1.0, 1.0)), (32, 128, (-0.5, 1.0)), (4, 64, (-2.0, 0.5)), (8, 96, (1.0, 3.0)),
+])
+def test_fp8_selection_equals_exact_topk_of_dense_scores(h_idx, d_idx, scales):
+    # The fp8 indexer selects on final scores: the chunk path's ids and kept
+    # scores must be exactly the top-k of the dense scores (same kernel,
+    # masked stores), for both signs of q_scale * k_scale, with rows longer
+    # than the LDS list (sampled threshold).
+    wl = inputs.custom(f"fp8_topk_{h_idx}x{d_idx}", s_q=192, s_k=20000, q_pos0=19808,
+                       h_idx=h_idx, d_idx=d_idx, k_pools=300, h=16, d=128, fp8=True,
+                       number=440 + h_idx + d_idx)
+    _say(f"[case] {wl.name} scales={scales}")
+    x = inputs.make_inputs(wl, attention=False)
+    dev = torch.device("cuda")
+    q8, k8, w = x["q_idx8"].to(dev), x["k_idx8"].to(dev), x["w"].to(dev)
+    kw = dict(q_scale=torch.tensor([scales[0]], dtype=torch.float32, device=dev),
+              k_scale=torch.tensor([scales[1]], dtype=torch.float32, device=dev))
+    idx, sc = dsa.dsa_index_score_topk(q8, k8, w, wl.k_pools, q_pos0=wl.q_pos0, chunk_q=64,
+                                       want_scores=True, **kw)
+    full = dsa.dsa_index_scores(q8, k8, w, row0=0, n_rows=wl.s_q, q_pos0=wl.q_pos0, **kw)
+    torch.cuda.synchronize()
+    idx, sc, full = idx.cpu().numpy(), sc.cpu().numpy(), full.cpu().numpy()
+    for i in range(wl.s_q):
+        n = min((wl.q_pos0 + i) // 4, wl.n_pools)
+        want = _host_topk_ids(full[i], n, wl.k_pools)
+        assert np.array_equal(idx[i], want), f"row {i}: ids differ from the dense-score top-k"
+        sel = want >= 0
+        assert np.array_equal(sc[i][sel].view(np.uint32), full[i][want[sel]].view(np.uint32)), \
+            f"row {i}: kept scores differ from the dense scores"
+
+
 def test_deterministic_bitwise():
     wl = inputs.custom("determinism", s_q=1500, s_k=1500, h_idx=32, d_idx=128, k_pools=64,
                        h=16, d=128, number=360)
