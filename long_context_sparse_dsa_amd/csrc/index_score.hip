@@ -224,7 +224,7 @@ __device__ __forceinline__ int pow2_scale_exp(float amax) {
 // far a score taken with hi alone can be from the score with the E4M3
 // correction:
 //   m1_p = (1 + 2^-12) ||L8_p||,  m2_p = 2^-10 ||L8_p|| + 2^-14 ||hi_p||
-// (both 0 when every lo code is 0), L8_p the decoded correction vector.  With
+// (both 0 only for a zero pool), L8_p the decoded correction vector.  With
 // the query's factors A1 and A2 (pack_queries_kernel),
 //   |score(hi) - score(hi + lo)| <= A1 m1_p + A2 m2_p.
 // Per head the correction is c_h = Q8_h . L8_p and the ReLU is 1-Lipschitz,
@@ -234,8 +234,8 @@ __device__ __forceinline__ int pow2_scale_exp(float amax) {
 // through the Gram matrix of the query's rows.  A2 = (1 + 2^-8) sum_h |w_h|
 // max(||q_h||, ||Q8_h||) times m2_p covers fp32 rounding: of the correction
 // MFMAs (the 2^-10 term), of the accumulation and the epilogue (the 2^-14
-// term), and of s -/+ the bound themselves.  When every lo code is 0 the
-// correction MFMAs add exact zeros, so both scores are equal.
+// term, which also covers the chunk path's different order of summing the
+// heads), and of s -/+ the bound themselves.  A zero pool scores +0 either way.
 template <int DI, bool GATED>
 __global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __restrict__ k,
                                                              const float* __restrict__ gate,
@@ -298,8 +298,11 @@ __global__ __launch_bounds__(256) void pool_keys_bf16_kernel(const uint16_t* __r
     lo_scale[p] = (uint8_t)(e + 127);
     if (mu) {
         const float nl = ldexpf(sqrtf(lo2), e);
-        f32x2 m = {0.0f, 0.0f};
-        if (lo2 > 0.0f) m = f32x2{nl * (1.0f + 0x1p-12f), fmaf(nl, 0x1p-10f, 0x1p-14f * sqrtf(hi2))};
+        // m2 > 0 whenever hi is not zero, even with every lo code 0: the
+        // chunk path sums the heads in another order than the full score,
+        // so its score differs from the full one by rounding (a zero pool
+        // scores +0 in every order)
+        const f32x2 m = {nl * (1.0f + 0x1p-12f), fmaf(nl, 0x1p-10f, 0x1p-14f * sqrtf(hi2))};
         *reinterpret_cast<f32x2*>(mu + 2 * p) = m;
     }
 }

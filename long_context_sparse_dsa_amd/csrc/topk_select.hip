@@ -24,7 +24,7 @@
 // between (the band, typically about k of them) are rescored, by the same
 // MFMA sequence the scoring kernel uses with the correction, so the result is
 // bit for bit the selection over the full scores.  Pools with delta_p = 0
-// already hold their full score.  Final rows (fp8 indexer) are the case
+// (zero pools only) already hold their full score, +0.  Final rows (fp8 indexer) are the case
 // delta = 0: the band is the set of keys equal to the k-th.
 //
 // One workgroup (4 waves) per query row:

@@ -248,12 +248,13 @@ def _host_topk_ids(scores, n, k):
     return np.sort(order[:k]).astype(np.int32)
 
 
-@pytest.mark.parametrize("s_k,q_pos0,near_constant", [
-    (65536, 65344, False), (65536, 65344, True),      # bounded rows of 16k pools
-    (131072, 130880, False), (131072, 130880, True),  # bounded rows of 32k pools
-    (80192, 80000, False),                            # rows of 20k pools, scored in full
+@pytest.mark.parametrize("s_k,q_pos0,keys", [
+    (65536, 65344, "random"), (65536, 65344, "near_constant"),    # bounded rows of 16k pools
+    (131072, 130880, "random"), (131072, 130880, "near_constant"),  # bounded rows of 32k pools
+    (80192, 80000, "random"),                                       # rows of 20k pools, scored in full
+    (65536, 65344, "pool_constant"),  # every pooled key exactly bf16: no correction term at all
 ])
-def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, near_constant):
+def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, keys):
     # The chunk buffer holds scores taken without the E4M3 correction; the
     # selection rescores only the pools its error bound cannot decide.  The
     # kept ids must be exactly the top-k of the full scores, which
@@ -261,10 +262,15 @@ def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, near_constant):
     # nearly every pool within the bound of the threshold, so long rows
     # overflow the LDS list and take the slow path in global memory.  At
     # 80000 the chunk's rows are short enough to be scored in full, so the
-    # selection works on final scores.
+    # selection works on final scores.  With the 4 keys of every pool equal,
+    # each pooled key is exactly bf16 and every correction code is 0; the
+    # chunk's scores still differ from the full ones by the rounding of a
+    # different summation order, which the bound must cover.
+    near_constant = keys == "near_constant"
     wl = inputs.custom("full_topk", s_q=192, s_k=s_k, q_pos0=q_pos0, h_idx=32, d_idx=128,
                        k_pools=512, h=16, d=128, idx_std=1 / math.sqrt(128),
-                       number=380 + (1 if near_constant else 0) + (s_k - 65536) // 4096)
+                       number=380 + {"random": 0, "near_constant": 1, "pool_constant": 2}[keys]
+                       + (s_k - 65536) // 4096)
     x = inputs.make_inputs(wl, attention=False)
     if near_constant:
         rng = np.random.default_rng(7)
@@ -272,6 +278,8 @@ def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, near_constant):
         noise = rng.standard_normal((wl.s_k, wl.d_idx)).astype(np.float32)
         x["k_idx"] = torch.from_numpy(base[None, :] * (1 + np.float32(0.01) * noise)).to(
             torch.bfloat16)
+    if keys == "pool_constant":
+        x["k_idx"] = x["k_idx"][0::4].repeat_interleave(4, dim=0)[:wl.s_k].contiguous()
     dev = torch.device("cuda")
     q_idx, k_idx, w = x["q_idx"].to(dev), x["k_idx"].to(dev), x["w"].to(dev)
     idx, sc = dsa.dsa_index_score_topk(q_idx, k_idx, w, wl.k_pools, q_pos0=wl.q_pos0,
