@@ -239,6 +239,18 @@ def test_large_row_paths_and_sampling():
     assert np.all(idx0.cpu().numpy() == np.arange(wl.k_pools)[None, :])
 
 
+def test_largest_k_2048_pools():
+    # the largest k the ABI accepts (2048 pools, 8192 attended tokens per
+    # query), on rows longer than the LDS list (sampled threshold) and on rows
+    # shorter than k (every pool, -1 padding)
+    wl = inputs.custom("k2048", s_q=160, s_k=40000, q_pos0=39840, h_idx=32, d_idx=128,
+                       k_pools=2048, h=16, d=128, idx_std=1 / math.sqrt(128), number=470)
+    run_case(wl, rows=np.arange(0, 160, 5), chunk_q=64, check_scores=False)
+    wl = inputs.custom("k2048_short", s_q=96, s_k=8200, q_pos0=8104, h_idx=16, d_idx=64,
+                       k_pools=2048, h=8, d=64, n_tail=3, number=471)
+    run_case(wl, rows=np.arange(0, 96, 7), chunk_q=64, check_scores=False)
+
+
 def _host_topk_ids(scores, n, k):
     """Exact top-k of one row of fp32 scores by (-score, id), ascending ids,
     -1 padded: the selection rule restated on the host."""
