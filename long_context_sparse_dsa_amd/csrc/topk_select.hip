@@ -30,8 +30,9 @@
 // One workgroup (4 waves) per query row:
 //   n <= k       every eligible pool;
 //   n <= CAP     the whole row goes to an LDS list (id, score, delta);
-//   n >  CAP     a 4096-element sample of the row (256 blocks of 16) gives a
-//                threshold tau on the l keys; one coalesced pass keeps
+//   n >  CAP     a sample of the row (blocks of 16 contiguous pools: 128 for
+//                bounded rows up to 64k pools, 384 beyond, half that for final
+//                rows) gives a threshold tau on the l keys; one coalesced pass keeps
 //                {u >= tau} in the LDS list, in id order.  The list then holds
 //                every pool that can matter when at least k of its l keys
 //                are >= tau and it fits; otherwise the row is handled in
@@ -55,8 +56,8 @@ constexpr int SAMPLE_LEN = 16;
 // sample blocks of SAMPLE_LEN: more for long rows, where k is a smaller
 // fraction of the row, and twice as many for bounded rows, whose threshold
 // takes a wider margin (the sample lives in the three list arrays)
-constexpr int SAMPLE_BLOCKS_SHORT = 256;
-constexpr int SAMPLE_BLOCKS_LONG = 768;
+constexpr int SAMPLE_BLOCKS_SHORT = 128;
+constexpr int SAMPLE_BLOCKS_LONG = 384;
 constexpr int64_t LONG_ROW = 65536;
 static_assert(SAMPLE_BLOCKS_LONG * SAMPLE_LEN <= 3 * CAP, "the sample lives in the list");
 
