@@ -42,6 +42,7 @@
 // On a list, L and U come from radix-256 selections, and the kept band
 // members from one more over their full scores.
 #include <math.h>
+#include <stddef.h>
 
 #include "common.h"
 #include "internal.h"
@@ -59,6 +60,13 @@ constexpr int SAMPLE_LEN = 16;
 constexpr int SAMPLE_BLOCKS_SHORT = 128;
 constexpr int SAMPLE_BLOCKS_LONG = 384;
 constexpr int64_t LONG_ROW = 65536;
+// rows up to this many pools go whole to the list, longer ones take the
+// sample; the sample's blocks then lie inside the row and apart
+constexpr int WHOLE_BOUNDED = 4096;
+constexpr int WHOLE_FINAL = 2048;
+static_assert(WHOLE_BOUNDED <= CAP && WHOLE_FINAL <= CAP, "a whole row must fit the list");
+static_assert(SAMPLE_BLOCKS_SHORT * SAMPLE_LEN <= WHOLE_BOUNDED, "sample blocks overlap");
+static_assert(SAMPLE_BLOCKS_SHORT / 2 * SAMPLE_LEN <= WHOLE_FINAL, "sample blocks overlap");
 static_assert(SAMPLE_BLOCKS_LONG * SAMPLE_LEN <= 3 * CAP, "the sample lives in the list");
 
 // list entry tags: id in bits 0-28 (ids < 2^29), class in bits 29-30, and
@@ -68,7 +76,13 @@ constexpr uint32_t C_OUT = 0u, C_IN = 1u, C_BAND = 2u;
 constexpr uint32_t RESCORE = 1u << 31;
 __device__ __forceinline__ uint32_t cls_of(uint32_t t) { return (t >> 29) & 3u; }
 
+// The workgroup's LDS.  d is last: rows of final scores never touch it, and
+// their kernel is launched without it (fewer bytes, more workgroups per CU).
 struct SelShared {
+    uint32_t hist[512];
+    float w[32];  // head weights of the row's query tile (approximate rows)
+    uint32_t tmp[8];
+    uint32_t wtot[8 * (NT / 64)];  // per-slot wave totals of block_excl_scan_slots (<= 8 slots)
     union {
         struct {
             alignas(16) uint32_t idc[CAP];  // tagged pool ids
@@ -77,10 +91,13 @@ struct SelShared {
         };
         alignas(16) uint32_t sample[3 * CAP];  // sample keys, before the list is built
     };
-    uint32_t hist[512];
-    uint32_t tmp[8];
-    uint32_t wtot[8 * (NT / 64)];  // per-slot wave totals of block_excl_scan_slots (<= 8 slots)
 };
+constexpr size_t LDS_BOUNDED = sizeof(SelShared);
+constexpr size_t LDS_FINAL = sizeof(SelShared) - CAP * sizeof(float);
+static_assert(offsetof(SelShared, d) == LDS_FINAL, "d must be the last member");
+static_assert(LDS_BOUNDED <= 64 * 1024, "dynamic LDS beyond 64 KiB needs an opt-in");
+// the sample of a row of final scores lies below d
+static_assert(SAMPLE_BLOCKS_LONG / 2 * SAMPLE_LEN <= 2 * CAP, "final-row sample beyond idc and s");
 
 // Wave-level inclusive scans on DPP: row shifts 1, 2, 4, 8 within each row
 // of 16 lanes, then row broadcasts of lanes 15 and 31 into the later rows.
@@ -481,6 +498,11 @@ struct Rescorer {
         qi = (int)(i % QPT);
     }
 
+    // the 32 head weights of row i's query tile
+    static __device__ const float* weights(const uint8_t* tiles, int64_t i) {
+        return reinterpret_cast<const float*>(tiles + (i / QPT) * G.tb + G.qb);
+    }
+
     // Score of pool p (this lane's column); the value is valid on lane
     // owner() of each column (col or col + 32).  w: the tile's 32 head
     // weights, staged in LDS.
@@ -559,17 +581,15 @@ struct Rescorer {
 // Rescore the entries j < nr whose tag tag_of(j) has the RESCORE bit: the
 // tag's id bits name the pool, and its full score goes to put(j, value).
 // The 4 waves take blocks of 32 entries in turn and skip blocks with nothing
-// to rescore.  Called by the whole workgroup; the head weights of the tile
-// are staged in sh.hist.
+// to rescore.  Called by the whole workgroup after a barrier that follows
+// the staging of the tile's head weights in sh.w at the kernel's start.
 template <int HI, int DI, class TagOf, class Put>
 __device__ void rescore(uint32_t nr, TagOf tag_of, Put put, const SelectArgs& a, int64_t i,
                         SelShared& sh) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31;
     Rescorer<HI, DI> r;
     r.init(a.tiles, i);
-    float* w = reinterpret_cast<float*>(sh.hist);
-    if (threadIdx.x < 32) w[threadIdx.x] = reinterpret_cast<const float*>(r.tile + r.G.qb)[threadIdx.x];
-    __syncthreads();
+    const float* w = sh.w;
     const uint32_t nblk = (nr + 31) / 32;
     if ((uint32_t)wave >= nblk) return;
     const int own = r.owner(col);
@@ -748,8 +768,11 @@ __device__ void select_row_bounded(const SelectArgs& a, int64_t i, float* row, i
 }
 
 template <int HI, int DI, bool BOUNDS>
-__global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
-    __shared__ SelShared sh;
+// 3 workgroups per CU for approximate rows (LDS and registers), 4 for rows
+// of final scores, which need neither the bounds array nor the rescoring.
+__global__ __launch_bounds__(NT, BOUNDS ? 3 : 4) void topk_select_kernel(SelectArgs a) {
+    extern __shared__ __align__(16) uint8_t sel_lds[];
+    SelShared& sh = *reinterpret_cast<SelShared*>(sel_lds);
     const int tid = threadIdx.x;
     const int i = blockIdx.x;
     const int64_t qrow = a.row0 + i;
@@ -761,6 +784,8 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
     float* row = a.buf + (int64_t)i * a.ld;
     const f32x2 A = BOUNDS ? *reinterpret_cast<const f32x2*>(a.qbound + 2 * i) : f32x2{0.0f, 0.0f};
     auto delta = [&](int64_t p) { return BOUNDS ? bound_delta(A, a.mu, p) : 0.0f; };
+    // read by the rescoring, always after at least one barrier
+    if (BOUNDS && tid < 32) sh.w[tid] = Rescorer<HI, DI>::weights(a.tiles, i)[tid];
 
     if (n <= k) {
         for (int j = tid; j < k; j += NT) out[j] = j < n ? j : -1;
@@ -785,7 +810,7 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
     }
 
     int m = 0;  // list length
-    if (n <= CAP) {
+    if (n <= (BOUNDS ? WHOLE_BOUNDED : WHOLE_FINAL)) {
         // the whole row; rows are 16-byte aligned and padded to 4
         for (int e = 4 * tid; e < (int)n; e += 4 * NT) {
             const f32x4 v = load_row4(row, e, n);
@@ -804,7 +829,7 @@ __global__ __launch_bounds__(NT, 3) void topk_select_kernel(SelectArgs a) {
         const int nb = (n > LONG_ROW ? SAMPLE_BLOCKS_LONG : SAMPLE_BLOCKS_SHORT) / (BOUNDS ? 1 : 2);
         const int ns = nb * SAMPLE_LEN;
         // SU 16-byte pieces per thread in flight at once (ns / 4 is a
-        // multiple of NT; the blocks lie inside the row, n > CAP)
+        // multiple of NT; the blocks lie inside the row)
         constexpr int SU = 6;
         for (int s0 = 0; s0 < ns / 4; s0 += SU * NT) {
             f32x4 v[SU], mv[SU][2];
@@ -983,9 +1008,9 @@ template <int HI>
 hipError_t launch_bounded_h(const SelectArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.rows);
     switch (a.d_idx) {
-        case 64: topk_select_kernel<HI, 64, true><<<grid, NT, 0, stream>>>(a); break;
-        case 96: topk_select_kernel<HI, 96, true><<<grid, NT, 0, stream>>>(a); break;
-        case 128: topk_select_kernel<HI, 128, true><<<grid, NT, 0, stream>>>(a); break;
+        case 64: topk_select_kernel<HI, 64, true><<<grid, NT, LDS_BOUNDED, stream>>>(a); break;
+        case 96: topk_select_kernel<HI, 96, true><<<grid, NT, LDS_BOUNDED, stream>>>(a); break;
+        case 128: topk_select_kernel<HI, 128, true><<<grid, NT, LDS_BOUNDED, stream>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -996,7 +1021,7 @@ hipError_t launch_bounded_h(const SelectArgs& a, hipStream_t stream) {
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     if (!a.qbound) {
-        topk_select_kernel<32, 128, false><<<dim3((unsigned)a.rows), NT, 0, stream>>>(a);
+        topk_select_kernel<32, 128, false><<<dim3((unsigned)a.rows), NT, LDS_FINAL, stream>>>(a);
         return hipGetLastError();
     }
     switch (a.h_idx) {
