@@ -312,17 +312,22 @@ def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, keys):
                  check_scores=False)
 
 
-@pytest.mark.parametrize("h_idx,d_idx,scales", [
-    (32, 96, (1.0, 1.0)), (32, 128, (-0.5, 1.0)), (4, 64, (-2.0, 0.5)), (8, 96, (1.0, 3.0)),
+@pytest.mark.parametrize("h_idx,d_idx,scales,s_k", [
+    (32, 96, (1.0, 1.0), 20000), (32, 128, (-0.5, 1.0), 20000), (4, 64, (-2.0, 0.5), 20000),
+    (8, 96, (1.0, 3.0), 20000),
+    # rows of about 3000 pools: sampled, though they would fit the list
+    (32, 96, (1.0, 1.0), 12200),
+    # rows of about 2000 pools: the whole row goes to the list
+    (32, 128, (1.0, 1.0), 8200),
 ])
-def test_fp8_selection_equals_exact_topk_of_dense_scores(h_idx, d_idx, scales):
+def test_fp8_selection_equals_exact_topk_of_dense_scores(h_idx, d_idx, scales, s_k):
     # The fp8 indexer selects on final scores: the chunk path's ids and kept
     # scores must be exactly the top-k of the dense scores (same kernel,
     # masked stores), for both signs of q_scale * k_scale, with rows longer
-    # than the LDS list (sampled threshold).
-    wl = inputs.custom(f"fp8_topk_{h_idx}x{d_idx}", s_q=192, s_k=20000, q_pos0=19808,
+    # than the LDS list (sampled threshold) and shorter ones.
+    wl = inputs.custom(f"fp8_topk_{h_idx}x{d_idx}_{s_k}", s_q=192, s_k=s_k, q_pos0=s_k - 192,
                        h_idx=h_idx, d_idx=d_idx, k_pools=300, h=16, d=128, fp8=True,
-                       number=440 + h_idx + d_idx)
+                       number=440 + h_idx + d_idx + (s_k != 20000) * s_k // 100)
     _say(f"[case] {wl.name} scales={scales}")
     x = inputs.make_inputs(wl, attention=False)
     dev = torch.device("cuda")
