@@ -866,6 +866,20 @@ __global__ __launch_bounds__(NT, BOUNDS ? 3 : 4) void topk_select_kernel(SelectA
         const float mu = (float)k * (float)ns / (float)n;
         uint32_t r = (uint32_t)ceilf(BOUNDS ? mu + 5.0f * sqrtf(mu) + 8.0f : mu + 4.0f * sqrtf(mu) + 4.0f);
         if (r > (uint32_t)ns) r = ns;
+        // the first compaction batch does not depend on tau: its loads are
+        // in flight while the threshold is found
+        constexpr int VB = 8;
+        constexpr int BATCH = 4 * NT * VB;
+        const int64_t last = (n - 1) & ~(int64_t)3;
+        f32x4 v[VB];
+        auto load_batch = [&](int64_t base) {
+#pragma unroll
+            for (int u = 0; u < VB; ++u) {
+                const int64_t e = base + (int64_t)(u * NT + tid) * 4;
+                v[u] = *reinterpret_cast<const f32x4*>(row + (e < n ? e : last));
+            }
+        };
+        load_batch(0);
         const uint32_t tau = sample_threshold(ns, r, sh);  // at least r sample l keys are >= tau
         __syncthreads();
 
@@ -873,18 +887,14 @@ __global__ __launch_bounds__(NT, BOUNDS ? 3 : 4) void topk_select_kernel(SelectA
         // 16-byte pieces per thread, all loads of a batch in flight at once
         // (pieces past the row read its last piece and are masked).  Rows
         // hold no -0, so order_key(x) >= tau is x >= ftau.
-        constexpr int VB = 8;
-        constexpr int BATCH = 4 * NT * VB;
         const float ftau = key_to_float(tau);
-        const int64_t last = (n - 1) & ~(int64_t)3;
         uint32_t count = 0, cnt_l = 0;
         for (int64_t base = 0; base < n; base += BATCH) {
-            f32x4 v[VB];
+            if (base > 0) load_batch(base);
             int lim[VB];  // elements of piece u below lim[u] lie in the row
 #pragma unroll
             for (int u = 0; u < VB; ++u) {
                 const int64_t e = base + (int64_t)(u * NT + tid) * 4;
-                v[u] = *reinterpret_cast<const f32x4*>(row + (e < n ? e : last));
                 lim[u] = e + 4 <= n ? 4 : (e < n ? (int)(n - e) : 0);
             }
             uint32_t c[VB], off[VB];
