@@ -29,18 +29,21 @@
 //
 // One workgroup (4 waves) per query row:
 //   n <= k       every eligible pool;
-//   n <= CAP     the whole row goes to an LDS list (id, score, delta);
-//   n >  CAP     a sample of the row (blocks of 16 contiguous pools: 128 for
+//   n <= WHOLE   the whole row goes to an LDS list (id, score, delta);
+//                WHOLE is 4096 pools for approximate rows, 2048 for final ones
+//   n >  WHOLE   a sample of the row (blocks of 16 contiguous pools: 128 for
 //                bounded rows up to 64k pools, 384 beyond, half that for final
 //                rows) gives a threshold tau on the l keys; one coalesced pass keeps
-//                {u >= tau} in the LDS list, in id order.  The list then holds
-//                every pool that can matter when at least k of its l keys
-//                are >= tau and it fits; otherwise the row is handled in
-//                global memory (slow path, still exact): L and U by radix
-//                over the row, the band rescored in place, and an exact
-//                selection over the row.
-// On a list, L and U come from radix-256 selections, and the kept band
-// members from one more over their full scores.
+//                {u >= tau} in the LDS list (at most CAP = 4096 entries), in
+//                id order.  The list then holds every pool that can matter
+//                when at least k of its l keys are >= tau and it fits;
+//                otherwise the row is handled in
+//                global memory (slow path, still exact): L' and U' from the
+//                same histograms over the row, the band rescored in place,
+//                and an exact radix selection over the row.
+// On a list, safe bounds L' <= L and U' >= U come from 256-bin histograms
+// linear in value, and the kept band members from a radix selection over
+// their full scores.
 #include <math.h>
 #include <stddef.h>
 
