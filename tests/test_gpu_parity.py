@@ -260,13 +260,14 @@ def _host_topk_ids(scores, n, k):
     return np.sort(order[:k]).astype(np.int32)
 
 
-@pytest.mark.parametrize("s_k,q_pos0,keys", [
-    (65536, 65344, "random"), (65536, 65344, "near_constant"),    # bounded rows of 16k pools
-    (131072, 130880, "random"), (131072, 130880, "near_constant"),  # bounded rows of 32k pools
-    (80192, 80000, "random"),                                       # rows of 20k pools, scored in full
-    (65536, 65344, "pool_constant"),  # every pooled key exactly bf16: no correction term at all
+@pytest.mark.parametrize("s_k,q_pos0,keys,k_pools", [
+    (65536, 65344, "random", 512), (65536, 65344, "near_constant", 512),  # bounded, 16k pools
+    (131072, 130880, "random", 512), (131072, 130880, "near_constant", 512),  # 32k pools
+    (80192, 80000, "random", 512),                      # rows of 20k pools, scored in full
+    (65536, 65344, "pool_constant", 512),  # every pooled key exactly bf16: no correction term
+    (16448, 16256, "random", 64),  # bounded rows of 4064-4111 pools: whole list, then sampled
 ])
-def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, keys):
+def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, keys, k_pools):
     # The chunk buffer holds scores taken without the E4M3 correction; the
     # selection rescores only the pools its error bound cannot decide.  The
     # kept ids must be exactly the top-k of the full scores, which
@@ -280,9 +281,9 @@ def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, keys):
     # different summation order, which the bound must cover.
     near_constant = keys == "near_constant"
     wl = inputs.custom("full_topk", s_q=192, s_k=s_k, q_pos0=q_pos0, h_idx=32, d_idx=128,
-                       k_pools=512, h=16, d=128, idx_std=1 / math.sqrt(128),
+                       k_pools=k_pools, h=16, d=128, idx_std=1 / math.sqrt(128),
                        number=380 + {"random": 0, "near_constant": 1, "pool_constant": 2}[keys]
-                       + (s_k - 65536) // 4096)
+                       + (s_k - 65536) // 4096 + (k_pools != 512) * 1000)
     x = inputs.make_inputs(wl, attention=False)
     if near_constant:
         rng = np.random.default_rng(7)
