@@ -114,10 +114,17 @@ def work_counts(wl):
                 b_bwd_dq=b_bwd_dq)
 
 
-def cpu_baseline(wl, x, target_s: float, gate=None, fp8=False):
-    """The oracle as it stands, on a strided sample of query rows."""
+def cpu_baseline(wl, x, target_s: float, gate=None, fp8=False, gpu=None):
+    """The oracle as it stands, on a strided sample of query rows.
+
+    gpu (optional): host copies of the timed run's ids ("idx") and attention
+    output ("out").  The oracle's ids of the sampled rows are then compared
+    with them under the boundary rule of the test suite, and the oracle's
+    attention on the GPU's ids with the GPU's output, so the line carries the
+    parity of the very call it timed (returned as a second value)."""
     from oracle import oracle
     threads = os.cpu_count() or 1
+    last = {}
 
     def run(rows):
         t0 = time.perf_counter()
@@ -129,6 +136,7 @@ def cpu_baseline(wl, x, target_s: float, gate=None, fp8=False):
                                        q_pos0=wl.q_pos0, rows=rows, gate=gate)
         oracle.sparse_attn(x["q"], x["k"], x["v"], idx, wl.k_pools, q_pos0=wl.q_pos0, rows=rows,
                            n_tail=wl.n_tail, scale=float(np.float32(1 / math.sqrt(wl.d))))
+        last["rows"], last["idx"] = rows, idx
         return time.perf_counter() - t0
 
     def strided(r):
@@ -144,9 +152,52 @@ def cpu_baseline(wl, x, target_s: float, gate=None, fp8=False):
     r = int(max(probe, min(wl.s_q, (target_s - fixed) / per_row)))
     rows = strided(r)
     t = run(rows)
-    return {"value": r / t, "unit": "queries/s", "cores": threads, "kind": "oracle",
+    base = {"value": r / t, "unit": "queries/s", "cores": threads, "kind": "oracle",
             "sample": f"{r} query rows evenly spaced over the {wl.s_q} queries of {wl.name} "
                       f"(pooling of all keys included), {t:.1f} s"}
+    if gpu is None:
+        return base, None
+    return base, timed_call_parity(wl, x, gate, fp8, gpu, last["rows"], last["idx"])
+
+
+def timed_call_parity(wl, x, gate, fp8, gpu, rows, ora_idx):
+    """Boundary-rule comparison of the timed call's ids with the oracle's on
+    the baseline's rows, the structural check of every id row, and the
+    attention output on up to 256 of the rows (oracle fed the GPU's ids)."""
+    from oracle import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import parity
+    pos = wl.q_pos0 + np.arange(wl.s_q)
+    out = {"rows": int(len(rows)), "rule": "ids equal the oracle's except pools within "
+           "1e-3 |s_k| + 1e-6 max s of the k-th score; attention within 2e-2 absolute"}
+    try:
+        parity.validate_index_rows(gpu["idx"], pos, wl.n_pools, wl.k_pools)
+        g = gpu["idx"][rows]
+        differ = np.array([set(a.tolist()) != set(b.tolist()) for a, b in zip(g, ora_idx)])
+        st = {"swaps": 0, "rows_with_swaps": 0, "worst_row": 0}
+        if differ.any():
+            # dense oracle scores only for the rows whose sets differ
+            dr = rows[differ]
+            if fp8:
+                s_o = oracle.index_scores_fp8(x["q_idx8"], x["k_idx8"], x["w"], q_pos0=wl.q_pos0,
+                                              rows=dr, gate=gate)
+            else:
+                s_o = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0,
+                                          rows=dr, gate=gate)
+            st = parity.check_index_rows(g[differ], ora_idx[differ], s_o, wl.q_pos0 + dr,
+                                         wl.n_pools, wl.k_pools)
+        out.update(swaps=st["swaps"], rows_with_swaps=st["rows_with_swaps"],
+                   worst_row=st["worst_row"])
+        ar = rows[np.linspace(0, len(rows) - 1, min(256, len(rows))).round().astype(np.int64)]
+        o_o, lse_o = oracle.sparse_attn(x["q"], x["k"], x["v"], gpu["idx"][ar], wl.k_pools,
+                                        q_pos0=wl.q_pos0, rows=ar, n_tail=wl.n_tail,
+                                        scale=float(np.float32(1 / math.sqrt(wl.d))))
+        err = np.abs(gpu["out"][ar].astype(np.float64) - o_o).max()
+        assert err <= parity.ATTN_ABS, f"attention error {err}"
+        out.update(attn_rows=int(len(ar)), attn_max_abs_err=float(err), ok=True)
+    except AssertionError as e:
+        out.update(ok=False, error=str(e)[:300])
+    return out
 
 
 def backward(args, wl, x, g, gate, chunk_q, ws, idx, out, stream):
@@ -378,9 +429,11 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds,
-                                              None if gate is None else gate.cpu().numpy(),
-                                              fp8=args.fp8)
+        gpu_out = {"idx": idx.cpu().numpy(), "out": out.float().cpu().numpy()}
+        result["cpu_baseline"], result["parity"] = cpu_baseline(
+            wl, x, args.cpu_seconds, None if gate is None else gate.cpu().numpy(), fp8=args.fp8,
+            gpu=gpu_out)
+        log(f"parity of the timed call: {result['parity']}")
     print(json.dumps(result), flush=True)
 
 

@@ -25,3 +25,14 @@ def pytest_collection_modifyitems(config, items):
 def gpu_available():
     import torch
     return torch.cuda.is_available()
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # DSA_PARITY_RECORD=<file>: write the boundary-swap counts of every
+    # index comparison this run made (a markdown table)
+    path = os.environ.get("DSA_PARITY_RECORD")
+    if not path:
+        return
+    import parity
+    if parity.SWAP_LOG:
+        parity.write_swap_record(path)

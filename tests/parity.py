@@ -39,13 +39,43 @@ def eligible(t: int, n_pools: int) -> int:
     return min(t // 4, n_pools)
 
 
+def validate_index_rows(idx: np.ndarray, positions, n_pools: int, k: int) -> None:
+    """Host-side structural check of id rows before they feed attention,
+    which trusts them: a row for position t holds m = min(n(t), k) distinct
+    pool ids in strictly ascending order, each with 4p + 3 < t (p < n(t)),
+    followed by k - m entries of -1.  Vectorised, so it runs on every row of
+    a full-size output."""
+    idx = np.asarray(idx)
+    pos = np.asarray(positions, dtype=np.int64)
+    assert idx.ndim == 2 and idx.shape == (len(pos), k), f"id rows of shape {idx.shape}"
+    n = np.minimum(pos // 4, n_pools)
+    m = np.minimum(n, k)
+    valid = np.arange(k)[None, :] < m[:, None]
+    bad_pad = (~valid) & (idx != -1)
+    assert not bad_pad.any(), f"rows {np.nonzero(bad_pad.any(1))[0][:8]}: padding is not -1"
+    bad_rng = valid & ((idx < 0) | (idx >= n[:, None]))
+    assert not bad_rng.any(), \
+        f"rows {np.nonzero(bad_rng.any(1))[0][:8]}: id not strictly before the query's pool"
+    both = valid[:, 1:] & valid[:, :-1]
+    bad_ord = both & (idx[:, 1:] <= idx[:, :-1])
+    assert not bad_ord.any(), f"rows {np.nonzero(bad_ord.any(1))[0][:8]}: ids not ascending"
+
+
+# (case label, stats) of every index comparison made in this process; the
+# test session writes them out when DSA_PARITY_RECORD names a file
+SWAP_LOG: list = []
+
+
 def check_index_rows(gpu_idx: np.ndarray, ora_idx: np.ndarray, ora_scores: np.ndarray,
-                     positions, n_pools: int, k: int) -> dict:
+                     positions, n_pools: int, k: int, label: str | None = None) -> dict:
     """gpu_idx / ora_idx [R, k] int32; ora_scores [R, P] fp32 (dense oracle
-    scores of the same rows); positions [R] sequence positions t."""
+    scores of the same rows); positions [R] sequence positions t.  Returns
+    the boundary-swap counts (and logs them under ``label``)."""
     swaps = 0
     rows_with_swaps = 0
     worst = 0
+    nontrivial = 0
+    validate_index_rows(gpu_idx, positions, n_pools, k)
     for r, t in enumerate(positions):
         n = eligible(int(t), n_pools)
         g = gpu_idx[r]
@@ -55,6 +85,7 @@ def check_index_rows(gpu_idx: np.ndarray, ora_idx: np.ndarray, ora_scores: np.nd
             assert np.array_equal(g, expect), f"row t={t}: trivial row differs"
             assert np.array_equal(o, expect), f"row t={t}: oracle trivial row differs"
             continue
+        nontrivial += 1
         assert np.all(g >= 0) and np.all(g < n), f"row t={t}: id out of range"
         assert np.all(np.diff(g) > 0), f"row t={t}: ids not strictly ascending"
         gs, os_ = set(g.tolist()), set(o.tolist())
@@ -71,8 +102,27 @@ def check_index_rows(gpu_idx: np.ndarray, ora_idx: np.ndarray, ora_scores: np.nd
             swaps += sw
             rows_with_swaps += 1
             worst = max(worst, sw)
-    return {"swaps": swaps, "rows_with_swaps": rows_with_swaps, "worst_row": worst,
-            "rows": len(positions)}
+    stats = {"swaps": swaps, "rows_with_swaps": rows_with_swaps, "worst_row": worst,
+             "rows": len(positions), "rows_beyond_k": nontrivial}
+    if label is not None:
+        SWAP_LOG.append((label, stats))
+    return stats
+
+
+def write_swap_record(path: str) -> None:
+    """Markdown table of the logged index comparisons."""
+    lines = ["| case | rows checked | rows with n(t) > k | swaps | rows with swaps | "
+             "largest swaps in a row |", "|---|---|---|---|---|---|"]
+    tot = {"rows": 0, "rows_beyond_k": 0, "swaps": 0, "rows_with_swaps": 0, "worst_row": 0}
+    for label, st in SWAP_LOG:
+        lines.append(f"| {label} | {st['rows']} | {st['rows_beyond_k']} | {st['swaps']} | "
+                     f"{st['rows_with_swaps']} | {st['worst_row']} |")
+        for key in tot:
+            tot[key] = max(tot[key], st[key]) if key == "worst_row" else tot[key] + st[key]
+    lines.append(f"| **all** | {tot['rows']} | {tot['rows_beyond_k']} | {tot['swaps']} | "
+                 f"{tot['rows_with_swaps']} | {tot['worst_row']} |")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def check_scores(gpu: np.ndarray, ref: np.ndarray) -> float:

@@ -1,9 +1,14 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
-Every case prints what it runs before touching the GPU.  Small cases check
-every row; the full-size workloads check sampled rows (first and last rows,
-4-aligned boundaries, a strided sweep) in the same launch configuration the
-benchmark times.
+Every case prints what it runs before touching the GPU.  Each case runs the
+indexer twice: with the kept scores requested (score_out) and without them,
+the call the benchmark times.  The two id arrays must be identical bit for
+bit, every id row must pass the host-side structural check (causal,
+ascending, -1 padded) before it feeds attention, and the ids are compared
+with the oracle's under the boundary rule.  Small cases check every row; the
+full-size workloads check sampled rows (first and last rows, 4-aligned
+boundaries, a strided sweep, the first and last row of every chunk) with the
+default chunking, as the benchmark runs it.
 """
 import math
 import sys
@@ -32,7 +37,7 @@ def _lib():
 
 
 def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=None,
-             check_scores=True, x=None, fp8=False, scales=(1.0, 1.0), gate=None):
+             check_scores=True, x=None, fp8=False, scales=(1.0, 1.0), gate=None, tag=""):
     _say(f"[case] {wl.name} s_q={wl.s_q} s_k={wl.s_k} q_pos0={wl.q_pos0} "
          f"H_I={wl.h_idx} D_I={wl.d_idx} k={wl.k_pools} H={wl.h} D={wl.d} Dv={wl.dv} "
          f"n_tail={wl.n_tail} chunk_q={chunk_q} fp8={fp8} scales={scales} "
@@ -48,17 +53,26 @@ def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=N
                      k_scale=torch.tensor([scales[1]], dtype=torch.float32, device=dev))
     g_dev = None if gate is None else gate.to(dev)
     g_np = None if gate is None else gate.numpy()
-    if gate is None:
-        idx_g, sc_g = dsa.dsa_index_score_topk(q_idx, k_idx, w, wl.k_pools, q_pos0=wl.q_pos0,
-                                               chunk_q=chunk_q, want_scores=True, **sc_kw)
-    else:
-        idx_g, sc_g = dsa.dsa_index_score_topk_gated(q_idx, k_idx, g_dev, w, wl.k_pools,
-                                                     q_pos0=wl.q_pos0, chunk_q=chunk_q,
-                                                     want_scores=True, **sc_kw)
+
+    def indexer(want_scores):
+        if gate is None:
+            return dsa.dsa_index_score_topk(q_idx, k_idx, w, wl.k_pools, q_pos0=wl.q_pos0,
+                                            chunk_q=chunk_q, want_scores=want_scores, **sc_kw)
+        return dsa.dsa_index_score_topk_gated(q_idx, k_idx, g_dev, w, wl.k_pools,
+                                              q_pos0=wl.q_pos0, chunk_q=chunk_q,
+                                              want_scores=want_scores, **sc_kw)
+
+    idx_g, sc_g = indexer(True)
+    # the benchmark's call: no score_out (other branches in the chunk loop
+    # and the selection), same ids required
+    idx_b, _ = indexer(False)
     torch.cuda.synchronize()
+    assert torch.equal(idx_g, idx_b), "ids without score_out differ from ids with it"
+    idx_all = idx_b.cpu().numpy()
+    parity.validate_index_rows(idx_all, wl.q_pos0 + np.arange(wl.s_q), wl.n_pools, wl.k_pools)
     rows = np.arange(wl.s_q) if rows is None else np.asarray(rows, dtype=np.int64)
     pos = wl.q_pos0 + rows
-    idx_g_rows = idx_g.cpu().numpy()[rows]
+    idx_g_rows = idx_all[rows]
     sc_g_rows = sc_g.cpu().numpy()[rows]
     if fp8:
         idx_o, sc_o = oracle.index_topk_fp8(x[qn], x[kn], x["w"], wl.k_pools, q_scale=scales[0],
@@ -71,7 +85,11 @@ def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=N
                                         q_pos0=wl.q_pos0, rows=rows, gate=g_np)
         s_o = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0, rows=rows,
                                   gate=g_np)
-    stats = parity.check_index_rows(idx_g_rows, idx_o, s_o, pos, wl.n_pools, wl.k_pools)
+    label = (f"{wl.name} (s_q={wl.s_q}, s_k={wl.s_k}, k={wl.k_pools}, chunk_q={chunk_q or 'default'}"
+             f"{', fp8' if fp8 else ''}{', gated' if gate is not None else ''}"
+             f"{', ' + tag if tag else ''})")
+    stats = parity.check_index_rows(idx_g_rows, idx_o, s_o, pos, wl.n_pools, wl.k_pools,
+                                    label=label)
     _say(f"  index: {stats}")
     # the kept pools' scores against the oracle's dense scores
     for r in range(len(rows)):
@@ -106,7 +124,7 @@ def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=N
         _say(f"  scores: worst error / bound = {worst:.3g}")
     if attention:
         q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
-        o_g, lse_g = dsa.dsa_sparse_attn_fwd(q, k, v, idx_g, q_pos0=wl.q_pos0,
+        o_g, lse_g = dsa.dsa_sparse_attn_fwd(q, k, v, idx_b, q_pos0=wl.q_pos0,
                                              n_tail=wl.n_tail, want_lse=True)
         torch.cuda.synchronize()
         scale = float(np.float32(1.0 / math.sqrt(wl.d)))
@@ -116,7 +134,7 @@ def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=N
         eo, el = parity.check_attention(o_g.float().cpu().numpy()[rows],
                                         lse_g.cpu().numpy()[rows], o_o, lse_o)
         _say(f"  attention: max |do| = {eo:.3g}, max |dlse| = {el:.3g}")
-    return x, idx_g
+    return x, idx_b
 
 
 # ---------------------------------------------------------------- gated pooling
@@ -223,7 +241,21 @@ def test_ties_resolve_to_lower_ids():
         k[4 * (10 + r): 4 * (11 + r)] = k[4 * r: 4 * (r + 1)]
     k[200:1100] = (k[200:1100].float() * 0.25).to(torch.bfloat16)
     x1["k_idx"] = k
-    run_case(wl, chunk_q=64, x=x1, attention=False)
+    _, idx1 = run_case(wl, chunk_q=64, x=x1, attention=False)
+    # pools j and j + 10 have bit-identical pooled keys, hence identical
+    # scores: whenever exactly one of them is kept it must be the lower id
+    # (an exact tie lies inside the boundary band, so the oracle comparison
+    # alone would accept the wrong copy as a swap)
+    idx1 = idx1.cpu().numpy()
+    straddles = 0
+    for t in range(wl.s_q):
+        kept = set(idx1[t].tolist())
+        for j in range(10):
+            if (j in kept) != (j + 10 in kept):
+                straddles += 1
+                assert j in kept, f"row {t}: the higher copy {j + 10} of pool {j} was kept"
+    _say(f"  tie pairs split by the boundary: {straddles}")
+    assert straddles > 100  # the case does exercise the rule (the oracle splits 530)
 
 
 def test_large_row_paths_and_sampling():
@@ -297,8 +329,11 @@ def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, keys, k_pools):
     q_idx, k_idx, w = x["q_idx"].to(dev), x["k_idx"].to(dev), x["w"].to(dev)
     idx, sc = dsa.dsa_index_score_topk(q_idx, k_idx, w, wl.k_pools, q_pos0=wl.q_pos0,
                                        chunk_q=64, want_scores=True)
+    idx_b, _ = dsa.dsa_index_score_topk(q_idx, k_idx, w, wl.k_pools, q_pos0=wl.q_pos0,
+                                        chunk_q=64)
     full = dsa.dsa_index_scores(q_idx, k_idx, w, row0=0, n_rows=wl.s_q, q_pos0=wl.q_pos0)
     torch.cuda.synchronize()
+    assert torch.equal(idx, idx_b), "ids without score_out differ from ids with it"
     idx, sc, full = idx.cpu().numpy(), sc.cpu().numpy(), full.cpu().numpy()
     for i in range(wl.s_q):
         n = min((wl.q_pos0 + i) // 4, wl.n_pools)
@@ -337,8 +372,11 @@ def test_fp8_selection_equals_exact_topk_of_dense_scores(h_idx, d_idx, scales, s
               k_scale=torch.tensor([scales[1]], dtype=torch.float32, device=dev))
     idx, sc = dsa.dsa_index_score_topk(q8, k8, w, wl.k_pools, q_pos0=wl.q_pos0, chunk_q=64,
                                        want_scores=True, **kw)
+    idx_b, _ = dsa.dsa_index_score_topk(q8, k8, w, wl.k_pools, q_pos0=wl.q_pos0, chunk_q=64,
+                                        **kw)
     full = dsa.dsa_index_scores(q8, k8, w, row0=0, n_rows=wl.s_q, q_pos0=wl.q_pos0, **kw)
     torch.cuda.synchronize()
+    assert torch.equal(idx, idx_b), "ids without score_out differ from ids with it"
     idx, sc, full = idx.cpu().numpy(), sc.cpu().numpy(), full.cpu().numpy()
     for i in range(wl.s_q):
         n = min((wl.q_pos0 + i) // 4, wl.n_pools)
@@ -388,45 +426,63 @@ def test_fp8_indexer(h_idx, d_idx, scales):
 
 # ---------------------------------------------------------------- the page's workloads
 
+def _full_size_rows(wl, n, fp8=False, chunk_q=0):
+    """A strided sample of n rows plus the first and last row of every
+    selection launch of the default (or given) chunking."""
+    _, cq = dsa.dsa_index_workspace_size(wl.s_q, wl.s_k, wl.h_idx, wl.d_idx, wl.k_pools, 4,
+                                         chunk_q, dsa.DSA_FP8_E4M3 if fp8 else dsa.DSA_BF16)
+    ends = [r for c0 in range(0, wl.s_q, cq) for r in (c0, min(wl.s_q, c0 + cq) - 1)]
+    rows = inputs.sample_rows(wl.s_q, n, extra=ends)
+    _say(f"[rows] {wl.name}: {len(rows)} rows, chunks of {cq} queries "
+         f"({(wl.s_q + cq - 1) // cq} selection launches, each with checked rows)")
+    return rows
+
+
 def test_workload_s32k_sampled():
     wl = inputs.WORKLOADS["s32k"]
-    run_case(wl, rows=inputs.sample_rows(wl.s_q, 384))
+    run_case(wl, rows=_full_size_rows(wl, 384))
+
+
+def test_workload_s32k_chunks_of_256_sampled():
+    # the workload as described: queries scored and selected in chunks of 256
+    wl = inputs.WORKLOADS["s32k"]
+    run_case(wl, rows=_full_size_rows(wl, 256, chunk_q=256), chunk_q=256, tag="chunks of 256")
 
 
 @pytest.mark.slow
 def test_workload_s128k_sampled():
     wl = inputs.WORKLOADS["s128k"]
-    run_case(wl, rows=inputs.sample_rows(wl.s_q, 160), check_scores=False)
+    run_case(wl, rows=_full_size_rows(wl, 1024))
 
 
 @pytest.mark.slow
 def test_workload_s128k_gated_sampled():
     # the headline shape with per-token k-pool gates (bf16 indexer)
     wl = inputs.WORKLOADS["s128k"]
-    run_case(wl, rows=inputs.sample_rows(wl.s_q, 120), check_scores=False, attention=False,
-             gate=inputs.make_gates(wl))
+    run_case(wl, rows=_full_size_rows(wl, 256), attention=False, gate=inputs.make_gates(wl))
 
 
 @pytest.mark.slow
 def test_workload_nope_s64k_fp8_gated_sampled():
     wl = inputs.WORKLOADS["nope_s64k"]
-    run_case(wl, rows=inputs.sample_rows(wl.s_q, 120), check_scores=False, attention=False,
-             fp8=True, gate=inputs.make_gates(wl))
+    run_case(wl, rows=_full_size_rows(wl, 256, fp8=True), attention=False, fp8=True,
+             gate=inputs.make_gates(wl))
 
 
 @pytest.mark.slow
 def test_workload_nope_s64k_sampled():
     wl = inputs.WORKLOADS["nope_s64k"]
-    run_case(wl, rows=inputs.sample_rows(wl.s_q, 160), check_scores=False)
+    run_case(wl, rows=_full_size_rows(wl, 512))
 
 
 @pytest.mark.slow
 def test_workload_nope_s64k_fp8_sampled():
     wl = inputs.WORKLOADS["nope_s64k"]
-    run_case(wl, rows=inputs.sample_rows(wl.s_q, 160), check_scores=False, fp8=True)
+    run_case(wl, rows=_full_size_rows(wl, 512, fp8=True), fp8=True)
 
 
 @pytest.mark.slow
 def test_workload_share_1m_sampled():
+    # at least one checked row in every selection launch (1536-query chunks)
     wl = inputs.WORKLOADS["share_1m"]
-    run_case(wl, rows=inputs.sample_rows(wl.s_q, 40), check_scores=False)
+    run_case(wl, rows=_full_size_rows(wl, 128))

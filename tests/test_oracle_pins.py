@@ -702,3 +702,29 @@ def test_page_figures_keys_per_query_from_the_oracle():
     assert np.allclose(np.exp(lse), fig["keys_per_query"]["-"], rtol=1e-12)
     # the chunk buffer cap the ABI enforces is the page's
     assert fig["chunk_buffer_cap_bytes"]["-"] == 2 ** 31
+
+
+def test_index_row_validator_accepts_oracle_rows_and_catches_planted_mistakes():
+    # the host-side check the GPU tests run on every id row before attention:
+    # the oracle's rows pass, and each kind of malformed row is caught
+    import parity
+    wl = inputs.custom("validator", s_q=90, s_k=90, h_idx=4, d_idx=64, k_pools=6, number=910)
+    x = inputs.make_inputs(wl, attention=False)
+    idx, _ = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], wl.k_pools)
+    pos = np.arange(wl.s_q)
+    parity.validate_index_rows(idx, pos, wl.n_pools, wl.k_pools)
+    t = 80  # n(t) = 20 > k
+    for plant in ("order", "causal", "pad", "duplicate", "short"):
+        bad = idx.copy()
+        if plant == "order":
+            bad[t, [0, 1]] = bad[t, [1, 0]]
+        elif plant == "causal":
+            bad[t, -1] = t // 4          # the pool holding t itself
+        elif plant == "pad":
+            bad[10, -1] = 0              # n(10) = 2: entries 2.. must be -1
+        elif plant == "duplicate":
+            bad[t, 1] = bad[t, 0]
+        else:
+            bad[t, -1] = -1              # fewer than min(n, k) ids
+        with pytest.raises(AssertionError):
+            parity.validate_index_rows(bad, pos, wl.n_pools, wl.k_pools)
