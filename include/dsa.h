@@ -123,6 +123,37 @@ dsa_status dsa_index_score_topk(const void *q_idx, const void *k_idx, const floa
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * dsa_index_score_topk for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and the same results, bit for bit, with
+ * no workspace argument.  The workspace lives in a scratch array of
+ * DSA_NOALLOC_SCRATCH_BYTES that is part of the library's device image: each
+ * GPU the library runs on holds its own copy from the time the library's
+ * code is loaded on it until the process ends.  The call allocates nothing
+ * (no hipMalloc, no events: profiling does not record it).
+ *   chunk_q   0 = the largest multiple of 64 queries (at most the default of
+ *             dsa_index_score_topk) whose workspace fits the scratch array;
+ *             a given chunk_q whose workspace does not fit returns
+ *             DSA_ERR_WORKSPACE
+ * Every other argument is that of dsa_index_score_topk.  Shapes whose pooled
+ * key table plus one 64-query chunk exceed the scratch array (beyond about
+ * 412K pools, 1.65M keys, at d_idx = 128 with the bf16 indexer; 690K pools
+ * with fp8) return DSA_ERR_UNSUPPORTED.  At 128K keys the chunk fits 1728
+ * queries, at 1M keys 128.  All calls on one
+ * GPU share its scratch array: calls that overlap in time on one GPU (other
+ * streams or threads) race and give undefined results; calls ordered on one
+ * stream are safe.  The scratch contents left by a call are never read by
+ * the next one (every part is written before it is read).
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+dsa_status dsa_index_score_topk_noalloc(const void *q_idx, const void *k_idx,
+                                        const float *q_scale, const float *k_scale,
+                                        const float *w, int64_t w_stride_q, int64_t s_q,
+                                        int64_t s_k, int64_t q_pos0, int h_idx, int d_idx,
+                                        int pool_size, int k_pools, int64_t chunk_q, int dtype,
+                                        int32_t *idx_out, float *score_out, void *stream);
+
+/*
  * dsa_index_score_topk with gated pooling (section "DSA: Gather by Token
  * Position": per-token k-pool gate scores weight each key within its pool).
  * The pooled key is the gate-weighted sum

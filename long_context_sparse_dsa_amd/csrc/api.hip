@@ -62,6 +62,10 @@ struct Prof {
     std::vector<hipEvent_t> pool;
 } g_prof;
 
+// Set while the no-allocation entry point runs on this thread: no profiling
+// events are created or recorded (creating one allocates).
+thread_local bool t_no_events = false;
+
 hipEvent_t take_event() {
     if (!g_prof.pool.empty()) {
         hipEvent_t e = g_prof.pool.back();
@@ -79,6 +83,7 @@ struct Timed {
     hipStream_t s;
     hipEvent_t a = nullptr, b = nullptr;
     Timed(int k, hipStream_t st) : kind(k), s(st) {
+        if (t_no_events) return;
         std::lock_guard<std::mutex> lk(g_prof.mu);
         if (!g_prof.on) return;
         a = take_event();
@@ -339,6 +344,76 @@ dsa_status bwd_layout(int64_t s_q, int64_t s_k, int h, int64_t chunk_q, int64_t*
     return DSA_OK;
 }
 
+// ------------------------------------------------------------ scratch
+
+// The workspace of dsa_index_score_topk_noalloc (declared at file scope
+// below): the largest chunk of a multiple of 64 queries whose workspace fits
+// in max_bytes, or the caller's chunk_q if it fits.
+dsa_status chunk_within(const IndexShape& sh, int64_t chunk_q, int64_t max_bytes, int64_t* out) {
+    int64_t cq = 0;
+    dsa_status st = resolve_chunk(sh, chunk_q, &cq);
+    if (st != DSA_OK) return st;
+    if (chunk_q != 0) {
+        const int64_t need = layout(sh, cq, true).total;
+        if (need > max_bytes)
+            return fail(DSA_ERR_WORKSPACE,
+                        "chunk_q %lld needs %lld bytes of scratch; the no-allocation entry "
+                        "point has %lld (pass chunk_q = 0 to fit the chunk to it)",
+                        (long long)chunk_q, (long long)need, (long long)max_bytes);
+    } else {
+        cq = cq / 64 * 64;
+        while (cq > 64 && layout(sh, cq, true).total > max_bytes) cq -= 64;
+        const int64_t need = layout(sh, cq, true).total;
+        if (need > max_bytes)
+            return fail(DSA_ERR_UNSUPPORTED,
+                        "these shapes need %lld bytes of scratch (pooled keys and one chunk of "
+                        "64 queries); the no-allocation entry point has %lld",
+                        (long long)need, (long long)max_bytes);
+    }
+    *out = cq;
+    return DSA_OK;
+}
+
+}  // namespace
+
+// Scratch memory of dsa_index_score_topk_noalloc: one copy per GPU in the
+// library's device image, allocated with the code object on each device the
+// library runs on and held until the process ends.  In host code `scratch`
+// only names the symbol; its device address comes from hipGetSymbolAddress.
+constexpr int64_t kScratchBytes = int64_t(256) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the first call on it) with that device current.
+dsa_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DSA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(DSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned no address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSA_OK;
+}
+
+struct NoEvents {
+    NoEvents() { t_no_events = true; }
+    ~NoEvents() { t_no_events = false; }
+};
+
 }  // namespace
 
 extern "C" {
@@ -526,6 +601,32 @@ dsa_status dsa_index_score_topk(const void* q_idx, const void* k_idx, const floa
     return index_score_topk(q_idx, k_idx, nullptr, q_scale, k_scale, w, w_stride_q, s_q, s_k,
                             q_pos0, h_idx, d_idx, pool_size, k_pools, chunk_q, dtype, idx_out,
                             score_out, workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_index_score_topk_noalloc(const void* q_idx, const void* k_idx,
+                                        const float* q_scale, const float* k_scale,
+                                        const float* w, int64_t w_stride_q, int64_t s_q,
+                                        int64_t s_k, int64_t q_pos0, int h_idx, int d_idx,
+                                        int pool_size, int k_pools, int64_t chunk_q, int dtype,
+                                        int32_t* idx_out, float* score_out, void* stream) {
+    g_err[0] = 0;
+    IndexShape sh{s_q, s_k, q_pos0, h_idx, d_idx, pool_size, k_pools, dtype, s_k / 4};
+    dsa_status st = check_index_shape(sh, true);
+    if (st != DSA_OK) return st;
+    if ((st = check_index_ptrs(q_idx, k_idx, q_scale, k_scale, w, w_stride_q, sh)) != DSA_OK)
+        return st;
+    if (s_q > 0 && !idx_out) return fail(DSA_ERR_INVALID_ARG, "idx_out must be non-null");
+    if (!aligned16(idx_out) || !aligned16(score_out))
+        return fail(DSA_ERR_INVALID_ARG, "idx_out and score_out must be 16-byte aligned");
+    int64_t cq = 0;
+    if ((st = chunk_within(sh, chunk_q, kScratchBytes, &cq)) != DSA_OK) return st;
+    if (s_q == 0) return DSA_OK;
+    void* ws = nullptr;
+    if ((st = scratch_address(&ws)) != DSA_OK) return st;
+    NoEvents quiet;
+    return index_score_topk(q_idx, k_idx, nullptr, q_scale, k_scale, w, w_stride_q, s_q, s_k,
+                            q_pos0, h_idx, d_idx, pool_size, k_pools, cq, dtype, idx_out,
+                            score_out, ws, (size_t)kScratchBytes, stream);
 }
 
 dsa_status dsa_index_score_topk_gated(const void* q_idx, const void* k_idx, const float* k_gate,

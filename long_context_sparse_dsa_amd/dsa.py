@@ -63,6 +63,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dsa_index_score_topk.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _i64, _int,
             _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.dsa_index_score_topk_noalloc.restype = _int
+        lib.dsa_index_score_topk_noalloc.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _i64, _int,
+            _vp, _vp, _vp]
         lib.dsa_index_score_topk_gated.restype = _int
         lib.dsa_index_score_topk_gated.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _i64,
@@ -214,6 +218,32 @@ def dsa_index_score_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tens
     Returns (idx [S_q, k_pools] int32, scores [S_q, k_pools] fp32 or None)."""
     return _score_topk("dsa_index_score_topk", q_idx, k_idx, None, w, k_pools, q_pos0, chunk_q,
                        q_scale, k_scale, idx_out, score_out, want_scores, workspace, stream)
+
+
+def dsa_index_score_topk_noalloc(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
+                                 k_pools: int, *, q_pos0: int = 0, chunk_q: int = 0,
+                                 q_scale: torch.Tensor | None = None,
+                                 k_scale: torch.Tensor | None = None,
+                                 idx_out: torch.Tensor | None = None,
+                                 score_out: torch.Tensor | None = None,
+                                 want_scores: bool = False, stream=None):
+    """dsa_index_score_topk without a workspace: the library uses its own
+    per-GPU scratch array and allocates nothing.  Outputs not passed in are
+    allocated here, by the caller's side of the boundary.
+
+    Returns (idx [S_q, k_pools] int32, scores [S_q, k_pools] fp32 or None)."""
+    lib = load_library()
+    s_q, s_k, h_idx, d_idx, w_stride, dtype = _indexer_shapes(q_idx, k_idx, w)
+    dev = q_idx.device
+    if idx_out is None:
+        idx_out = torch.empty((s_q, k_pools), dtype=torch.int32, device=dev)
+    if score_out is None and want_scores:
+        score_out = torch.empty((s_q, k_pools), dtype=torch.float32, device=dev)
+    _check(lib.dsa_index_score_topk_noalloc(
+        _ptr(q_idx), _ptr(k_idx), _ptr(q_scale), _ptr(k_scale), _ptr(w), w_stride, s_q, s_k,
+        q_pos0, h_idx, d_idx, 4, k_pools, chunk_q, dtype, _ptr(idx_out), _ptr(score_out),
+        _stream(stream)))
+    return idx_out, score_out
 
 
 def dsa_index_score_topk_gated(q_idx: torch.Tensor, k_idx: torch.Tensor, k_gate: torch.Tensor,

@@ -14,9 +14,12 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests at the end, large ones last, so a quick failure shows first.
+    # GPU tests at the end, large ones last, so a quick failure shows first;
+    # the no-allocation entry point's tests after everything else, so that
+    # they run on a GPU whose scratch array earlier tests have already used.
     def key(item):
-        return (1 if item.get_closest_marker("gpu") else 0,
+        return (1 if item.module.__name__.endswith("test_zz_no_alloc") else 0,
+                1 if item.get_closest_marker("gpu") else 0,
                 1 if item.get_closest_marker("slow") else 0)
     items.sort(key=key)
 

@@ -243,3 +243,24 @@ def test_sparse_attn_bwd_workspace_layout(lib):
     with pytest.raises(dsa.DsaError) as e:
         dsa.dsa_sparse_attn_bwd_workspace_size(131072, (1 << 20) + 4, 16, 65536)
     assert e.value.status == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_before_touching_the_device(lib):
+    # argument and size checks come before any HIP call, so these run on a
+    # host without a GPU; the fake pointers are never dereferenced
+    p = ctypes.c_void_p(4096)
+    nul = ctypes.c_void_p(None)
+
+    def call(s_q, s_k, chunk_q, q=p, dtype=dsa.DSA_BF16, k_pools=512):
+        return lib.dsa_index_score_topk_noalloc(q, p, nul, nul, p, 0, s_q, s_k, 0, 32, 128, 4,
+                                                k_pools, chunk_q, dtype, p, nul, nul)
+
+    # pooled keys of 2M tokens do not fit the 256 MiB scratch array
+    assert call(64, 1 << 21, 0) == dsa.DSA_ERR_UNSUPPORTED
+    assert b"scratch" in lib.dsa_last_error()
+    # a chunk whose buffer does not fit it
+    assert call(8192, 131072, 8192) == dsa.DSA_ERR_WORKSPACE
+    assert call(64, 131072, 100) == dsa.DSA_ERR_UNSUPPORTED        # not a multiple of 64
+    assert call(64, 131072, 0, q=nul) == dsa.DSA_ERR_INVALID_ARG  # missing q_idx
+    assert call(64, 131072, 0, k_pools=0) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(0, 131072, 0) == dsa.DSA_OK                        # no query: nothing to do
