@@ -84,6 +84,68 @@ def copy_calibration():
                       "launches": 3}), flush=True)
 
 
+def measure_peaks():
+    """The chip's sustained rates on this machine, from the probes in
+    libdsa_peaks.so (a bf16 and an fp8 matrix-core loop, a 1 GiB device
+    copy), each the best of three launches timed with events on the current
+    stream.  Reported beside the published peaks; the roofline fractions stay
+    against the published ones."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_sparse_dsa_amd", "libdsa_peaks.so"))
+    lib.dsa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    lib.dsa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    sink = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def best(launch):
+        rates = []
+        for rep in range(4):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            work = launch()
+            b.record(stream)
+            b.synchronize()
+            if rep:  # the first launch warms up
+                rates.append(work / (a.elapsed_time(b) * 1e-3))
+        return max(rates)
+
+    def mfma(kind):
+        fl = ctypes.c_double(0)
+        if lib.dsa_probe_mfma(kind, 40000, ctypes.c_void_p(sink.data_ptr()), ctypes.byref(fl), sp):
+            raise RuntimeError("mfma probe launch failed")
+        return fl.value
+
+    def copy():
+        if lib.dsa_probe_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n,
+                              sp):
+            raise RuntimeError("copy probe launch failed")
+        return 2.0 * n
+    out = {"mfma_bf16_tflops": best(lambda: mfma(0)) / 1e12,
+           "mfma_fp8_tflops": best(lambda: mfma(1)) / 1e12,
+           "copy_read_plus_write_gbs": best(copy) / 1e9,
+           "published": {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "mfma_fp8_tflops": PEAK_FP8_TFLOPS,
+                         "hbm_gbs": PEAK_HBM_GBS},
+           "probe": "matrix-core loops (bf16 32x32x16, scaled fp8 32x32x64; 4 independent "
+                    "chains per wave, 4 waves per SIMD) and a 1 GiB device copy, best of 3 "
+                    "launches after a warm-up"}
+    del src, dst, sink
+    return out
+
+
+def step_stats(times_ms):
+    t = sorted(times_ms)
+    return {"ms_per_step_median": t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1]
+                                                                          + t[len(t) // 2]),
+            "ms_per_step_min": t[0]}
+
+
 def work_counts(wl):
     """Algorithmic work of one step (closed forms over the query positions)."""
     t = wl.q_pos0 + np.arange(wl.s_q, dtype=np.int64)
@@ -234,16 +296,20 @@ def backward(args, wl, x, g, gate, chunk_q, ws, idx, out, stream):
         log(f"warmup step {i + 1}/{args.warmup} done")
     dsa.dsa_profile_read()
     dsa.dsa_profile_enable(True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dsa.dsa_profile_enable(False)
     stats = dsa.dsa_profile_read()
     ms = (t1 - t0) * 1e3 / args.steps
-    log(f"timed {args.steps} backward steps: {ms:.3f} ms/step; kernels {stats}")
+    per_step = step_stats([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    log(f"timed {args.steps} backward steps: {ms:.3f} ms/step ({per_step}); kernels {stats}")
     w = work_counts(wl)
     stages = {}
     for name, (launches, total) in stats.items():
@@ -266,8 +332,8 @@ def backward(args, wl, x, g, gate, chunk_q, ws, idx, out, stream):
     result = {
         "metric": "DSA sparse-attention backward queries/sec (dq, dk, dv)",
         "value": wl.s_q / (ms / 1e3), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "warmup": args.warmup, "ms_per_step": ms, **per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "s_q": wl.s_q, "s_k": wl.s_k, "q_pos0": wl.q_pos0,
                    "k_pools": wl.k_pools, "attention": f"{wl.h}x{wl.d}", "kv_heads": 1,
                    "n_tail": wl.n_tail, "bwd_chunk_q": bwd_chunk},
@@ -291,6 +357,8 @@ def main():
     ap.add_argument("--chunk-q", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the in-run matrix-core and copy probes")
     ap.add_argument("--gated", action="store_true",
                     help="gated pooling: per-token k-pool gates weight each key of a pool")
     ap.add_argument("--fp8", action="store_true",
@@ -357,16 +425,20 @@ def main():
         log(f"warmup step {i + 1}/{args.warmup} done")
     dsa.dsa_profile_read()
     dsa.dsa_profile_enable(True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dsa.dsa_profile_enable(False)
     stats = dsa.dsa_profile_read()
     ms = (t1 - t0) * 1e3 / args.steps
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step; kernels {stats}")
+    per_step = step_stats([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step ({per_step}); kernels {stats}")
 
     w = work_counts(wl)
     qps = wl.s_q / (ms / 1e3)
@@ -420,6 +492,7 @@ def main():
                    "attention": f"{wl.h}x{wl.d}", "kv_heads": 1, "n_tail": wl.n_tail,
                    "chunk_q": chunk_q, "pooling": "gated" if args.gated else "mean",
                    "indexer_dtype": "e4m3" if args.fp8 else "bf16"},
+        **per_step,
         "tflops": tflops, "tflops_frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "roofline": dict(rl[dominant], kernel=dominant) if dominant in rl else None,
         "stages": stages,
@@ -427,6 +500,9 @@ def main():
                  "f_attn": w["f_attn"], "b_attn": w["b_attn"], "b_select": w["b_select"]},
         "peak_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
     }
+    if not args.no_peaks:
+        result["peaks_measured"] = measure_peaks()
+        log(f"measured peaks: {result['peaks_measured']}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         gpu_out = {"idx": idx.cpu().numpy(), "out": out.float().cpu().numpy()}

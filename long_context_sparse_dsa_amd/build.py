@@ -18,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsa.so")
+PROBE_SRC = os.path.join(PKG, "probe", "peaks.hip")
+PROBE_LIB = os.path.join(PKG, "libdsa_peaks.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
@@ -47,19 +49,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """libdsa.so (the DSA path) and libdsa_peaks.so (the benchmark's peak
+    probes, a separate library)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        fut_probe = ex.submit(_compile, PROBE_SRC)
+        objs = list(ex.map(_compile, srcs))
+        probe_obj = fut_probe.result()
+    _link(objs, LIB)
+    _link([probe_obj], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
