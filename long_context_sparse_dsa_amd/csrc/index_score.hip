@@ -548,15 +548,22 @@ struct ScoreK {
 // layout with 32 contraction bytes per lane, and takes one E8M0 scale per
 // lane for the row (A) or column (B) block that lane holds.
 //
-// Workgroup = 4 waves; each wave owns NB = 2 blocks of 32 consecutive pools
+// Workgroup = 4 waves; each wave owns NB blocks of 32 consecutive pools
 // (hi and lo of the pooled keys resident as B fragments); the workgroup owns
-// 256 pools and a range of gq chunk rows, walked one packed query tile (32
+// 128 NB pools and a range of gq chunk rows, walked one packed query tile (32
 // (query, head) rows) at a time through double-buffered LDS.  Every thread
 // moves the same 16-byte pieces of every tile, from precomputed offsets, two
 // tiles ahead in registers and one ahead in LDS; the loop issues the same
 // memory operations every tile (prefetches past the last tile read the
 // chunk's spare tiles, stores of a chunk buffer are never masked), so its
 // memory-counter waits cover only the prefetch they need.
+//
+// Every workgroup reads each query tile of its rows from L2, so the pools a
+// workgroup covers set the L2 traffic per flop: at 256 pools per workgroup
+// these re-reads kept the L2 busy about 90% of the scorer's cycles.  The
+// bound path at 8 or more heads therefore runs with NB = 4 (512 pools per
+// workgroup, 244 VGPRs at d_idx = 128); the full-score path also holds the
+// correction's fragments and keeps NB = 2.
 //
 // EXACT = false: the chunk-buffer contract of ScoreArgs (any entry may be
 // written, ineligible pools get -inf).  EXACT = true: only eligible entries of
@@ -570,7 +577,8 @@ struct ScoreK {
 // fma(A1, m1, fma(A2, m2, s~)).
 template <int HI, int DI, int NB, bool EXACT, bool LO>
 __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
-    static_assert(NB == 2, "the epilogue pairs the two pool blocks of a wave");
+    static_assert(NB % 2 == 0 && (NB == 2 || (HI != 4 && !LO)),
+                  "the epilogue pairs the pool blocks of a wave");
     using T = QTile<DI, LO>;
     constexpr int QPT = 32 / HI;      // queries per tile
     constexpr int NSB = DI / 16;      // bf16 MFMA steps (16 dims each)
@@ -639,7 +647,7 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     // instruction fills a contiguous 1 KiB (256 B) slice.
     constexpr int D = NBUF - 1;
     constexpr int NDMA = CPT + 1;                     // direct loads per tile
-    constexpr int S = HI == 4 ? 8 : QPT;              // score stores per tile
+    constexpr int S = HI == 4 ? 8 : QPT * (NB / 2);   // score stores per tile
     // (wave-uniform tile addresses, per-lane offsets)
     const uint8_t* tile0 = a.tiles + (int64_t)(i_begin / QPT) * T::G.tb;
     uint32_t voff[CPT + 1];
@@ -674,11 +682,12 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
     f32x2 mu_st[NB] = {};
     // and the first chunk row for which each of those pools is eligible
     // (4p + 3 < t, t = t_row0 + i; never for p >= n_pools), as a 32-bit
-    // threshold on the row index: the -inf mask of a store is one compare
+    // threshold on the row index: the -inf mask of a store is one compare.
+    // (HI >= 8: entry m serves the stores of pool blocks 2m, 2m + 1.)
     int e_st[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        const int64_t p = HI == 4 ? p_wave + nb * 32 + col : p_wave + lane;
+        const int64_t p = HI == 4 ? p_wave + nb * 32 + col : p_wave + 64 * (nb / 2) + lane;
         if constexpr (!LO)
             if (p < a.n_pools) mu_st[nb] = *reinterpret_cast<const f32x2*>(a.mu + 2 * p);
         const int64_t e = p < a.n_pools ? 4 * p + 4 - t_row0 : (int64_t)INT32_MAX;
@@ -804,25 +813,29 @@ __global__ __launch_bounds__(256, 2) void index_score_bf16_kernel(ScoreK a) {
                         put(tile_i0 + 2 * g4 + half, (int)p_wave + nb * 32 + col, part[nb][g4],
                             mu_st[nb], e_st[nb]);
             } else {
-                // lane l < 32 ends with pool block 0, lane l >= 32 with block 1:
-                // one store of 64 consecutive pools per query
+                // lane l < 32 ends with pool block 2m, lane l >= 32 with block
+                // 2m + 1: one store of 64 consecutive pools per query and pair
+#pragma unroll
+                for (int m = 0; m < NB / 2; ++m)
 #pragma unroll
                 for (int u = 0; u < QPT; ++u) {
+                    const int b0 = 2 * m, b1 = 2 * m + 1;
                     float x0, x1;
                     if constexpr (CHAINS) {
-                        x0 = part[0][0] + part[0][2];
-                        x1 = part[1][0] + part[1][2];
+                        x0 = part[b0][0] + part[b0][2];
+                        x1 = part[b1][0] + part[b1][2];
                     } else if constexpr (HI == 32) {
-                        x0 = (part[0][0] + part[0][1]) + (part[0][2] + part[0][3]);
-                        x1 = (part[1][0] + part[1][1]) + (part[1][2] + part[1][3]);
+                        x0 = (part[b0][0] + part[b0][1]) + (part[b0][2] + part[b0][3]);
+                        x1 = (part[b1][0] + part[b1][1]) + (part[b1][2] + part[b1][3]);
                     } else if constexpr (HI == 16) {
-                        x0 = part[0][2 * u] + part[0][2 * u + 1];
-                        x1 = part[1][2 * u] + part[1][2 * u + 1];
+                        x0 = part[b0][2 * u] + part[b0][2 * u + 1];
+                        x1 = part[b1][2 * u] + part[b1][2 * u + 1];
                     } else {
-                        x0 = part[0][u];
-                        x1 = part[1][u];
+                        x0 = part[b0][u];
+                        x1 = part[b1][u];
                     }
-                    put(tile_i0 + u, (int)p_wave + lane, add_halves2(x0, x1), mu_st[0], e_st[0]);
+                    put(tile_i0 + u, (int)p_wave + 64 * m + lane, add_halves2(x0, x1), mu_st[b0],
+                        e_st[b0]);
                 }
             }
         }
@@ -836,6 +849,9 @@ template <int HI, int DI>
 static hipError_t launch_score_bf16_t(const ScoreArgs& a, hipStream_t stream) {
     constexpr int NB = 2;
     constexpr int PB = 128 * NB;
+    // the bound path at 8+ heads: 4 pool blocks per wave, 512 pools per
+    // workgroup, so that each query tile read from L2 serves twice the pools
+    constexpr int NBB = HI == 4 ? 2 : 4;
     constexpr int QPT = 32 / HI;
     ScoreK k;
     k.tiles = a.tiles;
@@ -858,7 +874,10 @@ static hipError_t launch_score_bf16_t(const ScoreArgs& a, hipStream_t stream) {
     // scores without the correction term
     if (a.exact) index_score_bf16_kernel<HI, DI, NB, true, true><<<grid, 256, 0, stream>>>(k);
     else if (!a.qbound) index_score_bf16_kernel<HI, DI, NB, false, true><<<grid, 256, 0, stream>>>(k);
-    else index_score_bf16_kernel<HI, DI, NB, false, false><<<grid, 256, 0, stream>>>(k);
+    else {
+        const dim3 gb((unsigned)((a.n_chunk + 128 * NBB - 1) / (128 * NBB)), grid.y);
+        index_score_bf16_kernel<HI, DI, NBB, false, false><<<gb, 256, 0, stream>>>(k);
+    }
     return hipGetLastError();
 }
 
