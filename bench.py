@@ -31,6 +31,10 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 MALL_BYTES = 256 << 20        # MI355X last-level (Infinity) cache
+# L2 read bandwidth from the unit counts and clock: 8 XCDs x 16 L2 channels
+# x 128 bytes per clock x 2.4 GHz (no published figure; the in-run probe
+# reads about 85% of it)
+PEAK_L2_GBS = 8 * 16 * 128 * 2.4
 METRIC = "DSA fwd queries/sec at S=128k (indexer+topk+attn); TFLOP/s vs MFMA peak"
 
 
@@ -69,6 +73,89 @@ def measured_traffic(kernel: str, workload: str):
     return t["hbm_bytes_per_launch"]
 
 
+KERNEL_KINDS = [("pool_keys", "pool_keys"), ("pack_queries", "pack_queries"),
+                ("index_score", "index_score"), ("topk_select", "topk_select"),
+                ("sparse_attn_kernel", "sparse_attn"), ("attn_bwd_dq", "attn_bwd_dq"),
+                ("bwd_select_bits", "attn_bwd_select"), ("attn_bwd_dkv", "attn_bwd_dkv")]
+
+
+def kernel_kind(name: str):
+    for key, kind in KERNEL_KINDS:
+        if key in name:
+            return kind
+    return None
+
+
+def _counter_rows(d: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"{d}: expected one counter_collection.csv, found {len(files)}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def traffic_summary(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+    """HBM bytes per launch and kernel kind from two rocprofv3 runs of one
+    bench.py step (--pmc FETCH_SIZE, then --pmc WRITE_SIZE), each scaled by
+    what the same counter reads for the 1 GiB copy of --copy-calibration.
+    Writes profiles/traffic_<kind>_<workload>.json (read by the bench's
+    roofline) and prints the summary table."""
+    def per_kind(d, counter):
+        tot, n = {}, {}
+        for r in _counter_rows(d):
+            if r["Counter_Name"] != counter:
+                continue
+            k = kernel_kind(r["Kernel_Name"])
+            if k is None:
+                continue
+            tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"]) * 1024.0
+            n[k] = n.get(k, 0) + 1
+        return tot, n
+
+    def calibration(d, counter):
+        # the largest single dispatch of the calibration run is the 1 GiB copy
+        v = max(float(r["Counter_Value"]) for r in _counter_rows(d) if r["Counter_Name"] == counter)
+        return (1 << 30) / (v * 1024.0)
+    ff, wf = calibration(cal_fetch_dir, "FETCH_SIZE"), calibration(cal_write_dir, "WRITE_SIZE")
+    fb, fn = per_kind(fetch_dir, "FETCH_SIZE")
+    wb, _ = per_kind(write_dir, "WRITE_SIZE")
+    print(f"FETCH_SIZE factor {ff:.4f}, WRITE_SIZE factor {wf:.4f} (1 GiB copy)\n")
+    print("| kernel | launches | fetched B/launch (calibrated) | written B/launch (calibrated) |")
+    print("|---|---|---|---|")
+    for k in [kind for _, kind in KERNEL_KINDS if kind in fb]:
+        f = fb[k] * ff / fn[k]
+        w = wb.get(k, 0.0) * wf / fn[k]
+        print(f"| {k} | {fn[k]} | {f:.4g} | {w:.4g} |")
+        if k in KERNEL_SOURCES:
+            with open(os.path.join(ROOT, "profiles", f"traffic_{k}_{workload}.json"), "w") as fh:
+                json.dump({"kernel": k, "workload": workload, "launches_per_step": fn[k],
+                           "fetch_bytes_per_launch": f, "write_bytes_per_launch": w,
+                           "hbm_bytes_per_launch": f + w, "fetch_factor": ff, "write_factor": wf,
+                           "source_sha256": kernel_source_hash(k),
+                           "summary": f"profiles/l2_egress_traffic_{workload}.md"}, fh, indent=1)
+
+
+def trace_summary(d):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"{d}: expected one kernel_stats.csv, found {len(files)}")
+    with open(files[0]) as fh:
+        rows = list(csv.DictReader(fh))
+    print("| kernel | calls | total ms | average us | min us | max us | % |")
+    print("|---|---|---|---|---|---|---|")
+    for r in rows:
+        name = r["Name"].replace("dsa::(anonymous namespace)::", "").replace("dsa::", "")
+        name = name[:90]
+        print(f"| `{name}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+              f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+              f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+
+
 def copy_calibration():
     """A plain device copy of known size, for scaling the FETCH_SIZE and
     WRITE_SIZE counters: the counter values of this run divided by the bytes
@@ -97,6 +184,8 @@ def measure_peaks():
                                    ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
     lib.dsa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                    ctypes.c_void_p]
+    lib.dsa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p]
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     sink = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
@@ -127,14 +216,23 @@ def measure_peaks():
                               sp):
             raise RuntimeError("copy probe launch failed")
         return 2.0 * n
+    def read(buf, nbytes, passes):
+        if lib.dsa_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, passes,
+                              ctypes.c_void_p(sink.data_ptr()), sp):
+            raise RuntimeError("read probe launch failed")
+        return float(nbytes) * passes
+    l2_bytes = 16 << 20  # 2 MiB per XCD of the 4 MiB L2s
     out = {"mfma_bf16_tflops": best(lambda: mfma(0)) / 1e12,
            "mfma_fp8_tflops": best(lambda: mfma(1)) / 1e12,
            "copy_read_plus_write_gbs": best(copy) / 1e9,
+           "l2_read_gbs": best(lambda: read(src, l2_bytes, 256)) / 1e9,
+           "hbm_read_gbs": best(lambda: read(src, n, 4)) / 1e9,
            "published": {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "mfma_fp8_tflops": PEAK_FP8_TFLOPS,
                          "hbm_gbs": PEAK_HBM_GBS},
            "probe": "matrix-core loops (bf16 32x32x16, scaled fp8 32x32x64; 4 independent "
-                    "chains per wave, 4 waves per SIMD) and a 1 GiB device copy, best of 3 "
-                    "launches after a warm-up"}
+                    "chains per wave, 4 waves per SIMD), a 1 GiB device copy, 256 passes of "
+                    "reads over 16 MiB (L2-resident) and 4 passes over 1 GiB (memory), best "
+                    "of 3 launches after a warm-up"}
     del src, dst, sink
     return out
 
@@ -316,9 +414,13 @@ def backward(args, wl, x, g, gate, chunk_q, ws, idx, out, stream):
         st = {"ms_per_step": total / args.steps, "launches_per_step": launches / args.steps}
         t_s = total / 1e3
         if name == "attn_bwd_dq":
+            # the forward's gather: served by the L2s when every key and
+            # value row fits the last-level cache, else by memory
             a = w["b_bwd_dq"] * args.steps / t_s / 1e9
-            st.update(bound="hbm", achieved=a, peak=PEAK_HBM_GBS, unit="GB/s",
-                      frac=a / PEAK_HBM_GBS, tflops=w["f_bwd_dq"] * args.steps / t_s / 1e12)
+            l2 = wl.s_k * (wl.d + wl.dv) * 2 <= MALL_BYTES
+            peak = PEAK_L2_GBS if l2 else PEAK_HBM_GBS
+            st.update(bound="l2" if l2 else "hbm", achieved=a, peak=peak, unit="GB/s",
+                      frac=a / peak, tflops=w["f_bwd_dq"] * args.steps / t_s / 1e12)
         elif name == "attn_bwd_dkv":
             a = w["f_bwd_dkv"] * args.steps / t_s / 1e12
             st.update(bound="mfma", achieved=a, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
@@ -368,9 +470,21 @@ def main():
                          "forward path; the forward's ids, output and lse are made first")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
+                                                           "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="(host only) turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs of one step "
+                         "of --workload into profiles/traffic_<kernel>_<workload>.json")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="(host only) table of a rocprofv3 --kernel-trace --stats run")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.traffic_summary:
+        traffic_summary(args.workload, *args.traffic_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -457,13 +571,13 @@ def main():
         elif name == "sparse_attn":
             a = w["b_attn"] * args.steps / t_s / 1e9
             if wl.s_k * (wl.d + wl.dv) * 2 <= MALL_BYTES:
-                # every gathered key/value row is cache-resident (the rows
-                # are re-read from the 256 MiB last-level cache, not HBM):
-                # the gather rate is reported, the roof is the matrix cores
+                # every gathered key/value row is cache-resident: counters
+                # show the gather served by the L2s (one L2 request per
+                # 128-byte line of a gathered row, 89% hits at 128k), so
+                # the roof is the L2 read bandwidth
                 f = w["f_attn"] * args.steps / t_s / 1e12
-                rl[name] = {"bound": "mfma", "achieved": f, "peak": PEAK_BF16_TFLOPS,
-                            "unit": "TFLOP/s", "frac": f / PEAK_BF16_TFLOPS, "traffic": None,
-                            "gather_GBps": a}
+                rl[name] = {"bound": "l2", "achieved": a, "peak": PEAK_L2_GBS, "unit": "GB/s",
+                            "frac": a / PEAK_L2_GBS, "traffic": None, "tflops": f}
             else:
                 rl[name] = {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": a / PEAK_HBM_GBS, "traffic": None}
@@ -501,8 +615,19 @@ def main():
         "peak_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
     }
     if not args.no_peaks:
-        result["peaks_measured"] = measure_peaks()
-        log(f"measured peaks: {result['peaks_measured']}")
+        result["peaks_measured"] = pk = measure_peaks()
+        log(f"measured peaks: {pk}")
+        # each stage's rate against the probe of its own roof, too
+        probe_of = {"mfma": "mfma_fp8_tflops" if args.fp8 else "mfma_bf16_tflops",
+                    "hbm": "hbm_read_gbs", "l2": "l2_read_gbs"}
+        for st in stages.values():
+            if "bound" in st and st["bound"] in probe_of:
+                if st["bound"] == "mfma" and st is not stages.get("index_score"):
+                    continue
+                st["frac_of_measured_peak"] = st["achieved"] / pk[probe_of[st["bound"]]]
+        if result["roofline"] is not None:
+            result["roofline"]["frac_of_measured_peak"] = \
+                stages[result["roofline"]["kernel"]].get("frac_of_measured_peak")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         gpu_out = {"idx": idx.cpu().numpy(), "out": out.float().cpu().numpy()}

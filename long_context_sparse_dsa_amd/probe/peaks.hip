@@ -5,6 +5,10 @@
 //                 per wave so that no instruction waits on another, on every
 //                 SIMD (four waves per SIMD); operands vary by lane.
 //   copy       -- a 16-byte-per-lane device copy, src -> dst.
+//   read       -- 16-byte-per-lane reads of a buffer, `passes` times over;
+//                 a buffer that fits the L2s (each XCD keeps the part its
+//                 workgroups read) measures L2 read bandwidth, a large one
+//                 read once measures memory read bandwidth.
 // The caller times one launch with events on `stream`; the library returns
 // the algorithmic work of that launch.
 #include <hip/hip_runtime.h>
@@ -64,6 +68,18 @@ __global__ __launch_bounds__(256) void copy16(const u32x4* __restrict__ src, u32
         dst[i] = src[i];
 }
 
+__global__ __launch_bounds__(256) void read16(const u32x4* __restrict__ src, int64_t n, int passes,
+                                              uint32_t* sink) {
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int p = 0; p < passes; ++p) {
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+             i += (int64_t)gridDim.x * 256)
+            acc += src[i];
+        asm volatile("" ::: "memory");  // every pass reads again
+    }
+    if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9E3779B9u) sink[threadIdx.x] = acc[0];
+}
+
 }  // namespace
 
 extern "C" {
@@ -87,6 +103,17 @@ int dsa_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
         return 1;
     copy16<<<256 * 16, 256, 0, static_cast<hipStream_t>(stream)>>>(
         static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// bytes: a multiple of 16; src 16-byte aligned; sink: 256 uint32 of device
+// memory (never written in practice).  Reads the buffer `passes` times.
+int dsa_probe_read(const void* src, int64_t bytes, int passes, uint32_t* sink, void* stream) {
+    if (!src || !sink || bytes <= 0 || (bytes & 15) || passes < 1 ||
+        (reinterpret_cast<uintptr_t>(src) & 15))
+        return 1;
+    read16<<<256 * 8, 256, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const u32x4*>(src), bytes / 16, passes, sink);
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
