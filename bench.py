@@ -1,11 +1,11 @@
 """Throughput of the DSA forward path on one MI355X.
 
 A step is one pass of the whole path over one sequence's queries: pool the
-indexer keys, score every query against every earlier pool in query chunks,
-keep the top-k pools per query (int32 ids), and run sparse attention over
-the kept tokens.  Inputs are seeded synthetic tensors resident in HBM before
-the timed region (the page's own throughput runs used random tokens and
-random-initialised weights).
+indexer keys, score each query against each pool before it (a chunk of
+queries at a time), keep the top-k pools per query (int32 ids), and run
+sparse attention over the kept tokens.  Inputs are seeded synthetic tensors
+resident in HBM before the timed region (the page's own throughput figures
+come from synthetic runs with untrained weights).
 
 Prints one JSON line: queries/s for the whole path, TFLOP/s of the
 algorithmic work, the roofline of the dominant kernel (from HIP events around

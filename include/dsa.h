@@ -4,10 +4,10 @@
  *
  * The method (SkyRL blog, "Scaling Training to 1M Token Context on
  * GLM-5.3-Flash"):
- *   section "DeepSeek Sparse Attention (DSA) Optimizations" -- a lightweight
- *     indexer scores every query against every earlier pool of 4 tokens and
- *     keeps the best pools, so that attention reads only 2048 tokens
- *     (512 pools x 4);
+ *   section "DeepSeek Sparse Attention (DSA) Optimizations" -- a small
+ *     indexer rates each query's whole causal past, 4 tokens (one pool) at
+ *     a time, keeps the highest-rated pools, and attention then touches
+ *     only 2048 tokens (512 pools x 4);
  *   section "Making Sparse Attention Actually Sparse" -- NoPE heads are
  *     narrower than the rotary shapes and the pooled selection can return
  *     2,051 keys; unsupported shapes must not silently fall back to dense;

@@ -1,8 +1,8 @@
 // Pooling of the indexer keys and chunked lightning-indexer scoring.
 //
 // SkyRL blog "Scaling Training to 1M Token Context on GLM-5.3-Flash",
-// section "DeepSeek Sparse Attention (DSA) Optimizations": every query is
-// scored against every earlier pool of 4 tokens; section "Over Time:
+// section "DeepSeek Sparse Attention (DSA) Optimizations": each query gets
+// a score for each 4-token pool before it; section "Over Time:
 // Chunking": scores are fp32 and are produced a chunk of queries at a time
 // into a buffer whose size does not grow with the sequence.
 //

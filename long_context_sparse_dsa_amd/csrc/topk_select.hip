@@ -30,11 +30,12 @@
 // One workgroup (4 waves) per query row:
 //   n <= k       every eligible pool;
 //   n <= WHOLE   the whole row goes to an LDS list (id, score, delta);
-//                WHOLE is 4096 pools for approximate rows, 2048 for final ones
+//                WHOLE is the list's capacity for approximate rows (3072
+//                or 4096 pools, see CAP_SHORT), 2048 for final ones
 //   n >  WHOLE   a sample of the row (blocks of 16 contiguous pools: 128 for
 //                bounded rows up to 64k pools, 384 beyond, half that for final
 //                rows) gives a threshold tau on the l keys; one coalesced pass keeps
-//                {u >= tau} in the LDS list (at most CAP = 4096 entries), in
+//                {u >= tau} in the LDS list (at most its capacity), in
 //                id order.  The list then holds every pool that can matter
 //                when at least k of its l keys are >= tau and it fits;
 //                otherwise the row is handled in
@@ -55,7 +56,12 @@ namespace dsa {
 namespace {
 
 constexpr int NT = 256;
+// list capacity: rows of up to LONG_ROW pools use a 3072-entry list, whose
+// 38 KiB of LDS lets 4 workgroups share a CU, where the kernel then fits 128
+// VGPRs (D_I = 64, or 96 with at least 16 heads); longer rows, whose sampled
+// lists are larger, and the other shapes a 4096-entry list (3 per CU)
 constexpr int CAP = 4096;
+constexpr int CAP_SHORT = 3072;
 constexpr int SAMPLE_LEN = 16;
 // sample blocks of SAMPLE_LEN: more for long rows, where k is a smaller
 // fraction of the row, and twice as many for bounded rows, whose threshold
@@ -63,14 +69,15 @@ constexpr int SAMPLE_LEN = 16;
 constexpr int SAMPLE_BLOCKS_SHORT = 128;
 constexpr int SAMPLE_BLOCKS_LONG = 384;
 constexpr int64_t LONG_ROW = 65536;
-// rows up to this many pools go whole to the list, longer ones take the
-// sample; the sample's blocks then lie inside the row and apart
-constexpr int WHOLE_BOUNDED = 4096;
+// rows up to this many pools go whole to the list (bounded rows: the list's
+// capacity), longer ones take the sample; the sample's blocks then lie
+// inside the row and apart
 constexpr int WHOLE_FINAL = 2048;
-static_assert(WHOLE_BOUNDED <= CAP && WHOLE_FINAL <= CAP, "a whole row must fit the list");
-static_assert(SAMPLE_BLOCKS_SHORT * SAMPLE_LEN <= WHOLE_BOUNDED, "sample blocks overlap");
+static_assert(WHOLE_FINAL <= CAP_SHORT, "a whole row must fit the list");
+static_assert(SAMPLE_BLOCKS_SHORT * SAMPLE_LEN <= CAP_SHORT, "sample blocks overlap");
 static_assert(SAMPLE_BLOCKS_SHORT / 2 * SAMPLE_LEN <= WHOLE_FINAL, "sample blocks overlap");
 static_assert(SAMPLE_BLOCKS_LONG * SAMPLE_LEN <= 3 * CAP, "the sample lives in the list");
+static_assert(SAMPLE_BLOCKS_SHORT * SAMPLE_LEN <= 3 * CAP_SHORT, "the sample lives in the list");
 
 // list entry tags: id in bits 0-28 (ids < 2^29), class in bits 29-30, and
 // bit 31 set when the entry's full score must be computed
@@ -79,26 +86,35 @@ constexpr uint32_t C_OUT = 0u, C_IN = 1u, C_BAND = 2u;
 constexpr uint32_t RESCORE = 1u << 31;
 __device__ __forceinline__ uint32_t cls_of(uint32_t t) { return (t >> 29) & 3u; }
 
-// The workgroup's LDS.  d is last: rows of final scores never touch it, and
-// their kernel is launched without it (fewer bytes, more workgroups per CU).
-struct SelShared {
+// The workgroup's LDS, for a list of LCAP entries.  d is last: rows of final
+// scores never touch it, and their kernel is launched without it (fewer
+// bytes, more workgroups per CU).
+template <int LCAP>
+struct SelSharedT {
+    static constexpr int CAP = LCAP;
     uint32_t hist[512];
     float w[32];  // head weights of the row's query tile (approximate rows)
     uint32_t tmp[8];
     uint32_t wtot[8 * (NT / 64)];  // per-slot wave totals of block_excl_scan_slots (<= 8 slots)
     union {
         struct {
-            alignas(16) uint32_t idc[CAP];  // tagged pool ids
-            alignas(16) float s[CAP];       // scores: approximate, then full where rescored
-            alignas(16) float d[CAP];       // bounds delta; then the entries to rescore
+            alignas(16) uint32_t idc[LCAP];  // tagged pool ids
+            alignas(16) float s[LCAP];       // scores: approximate, then full where rescored
+            alignas(16) float d[LCAP];       // bounds delta; then the entries to rescore
         };
-        alignas(16) uint32_t sample[3 * CAP];  // sample keys, before the list is built
+        alignas(16) uint32_t sample[3 * LCAP];  // sample keys, before the list is built
     };
 };
-constexpr size_t LDS_BOUNDED = sizeof(SelShared);
-constexpr size_t LDS_FINAL = sizeof(SelShared) - CAP * sizeof(float);
-static_assert(offsetof(SelShared, d) == LDS_FINAL, "d must be the last member");
-static_assert(LDS_BOUNDED <= 64 * 1024, "dynamic LDS beyond 64 KiB needs an opt-in");
+using SelShared = SelSharedT<CAP>;
+using SelSharedShort = SelSharedT<CAP_SHORT>;
+template <int LCAP>
+constexpr size_t lds_bounded() { return sizeof(SelSharedT<LCAP>); }
+template <int LCAP>
+constexpr size_t lds_final() { return sizeof(SelSharedT<LCAP>) - LCAP * sizeof(float); }
+static_assert(offsetof(SelShared, d) == lds_final<CAP>(), "d must be the last member");
+static_assert(offsetof(SelSharedShort, d) == lds_final<CAP_SHORT>(), "d must be the last member");
+static_assert(lds_bounded<CAP>() <= 64 * 1024, "dynamic LDS beyond 64 KiB needs an opt-in");
+static_assert(4 * lds_bounded<CAP_SHORT>() <= 160 * 1024, "4 short-list workgroups per CU");
 // the sample of a row of final scores lies below d
 static_assert(SAMPLE_BLOCKS_LONG / 2 * SAMPLE_LEN <= 2 * CAP, "final-row sample beyond idc and s");
 
@@ -131,7 +147,8 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int /*lane*/) {
 }
 
 // Exclusive prefix over the workgroup; *total receives the sum.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SelShared& sh, uint32_t* total) {
+template <class SH>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SH& sh, uint32_t* total) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t inc = wave_incl_scan(v, lane);
     if (lane == 63) sh.tmp[wave] = inc;
@@ -152,9 +169,9 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SelShared& sh, u
 // slot-major: all threads' slot 0, then all threads' slot 1, ...  (the order
 // of elements base + (u*NT + tid)*4 + j).  Returns the offsets in `off` and
 // the grand total.
-template <int VB, int NW>
+template <int VB, int NW, class SH>
 __device__ __forceinline__ uint32_t block_excl_scan_slots(const uint32_t (&c)[VB],
-                                                          uint32_t (&off)[VB], SelShared& sh,
+                                                          uint32_t (&off)[VB], SH& sh,
                                                           uint32_t (&wtot)[NW]) {
     static_assert(VB * (NT / 64) <= NW, "one wave total per slot and wave");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -182,7 +199,8 @@ __device__ __forceinline__ uint32_t block_excl_scan_slots(const uint32_t (&c)[VB
     return base;
 }
 
-__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, SelShared& sh) {
+template <class SH>
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, SH& sh) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     mn = wave_incl_scan_op(mn, 0xFFFFFFFFu, MinOp{});
     mx = wave_incl_scan_op(mx, 0u, MaxOp{});
@@ -198,7 +216,8 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, SelShar
 
 
 // Sum over the workgroup.
-__device__ __forceinline__ uint32_t block_sum(uint32_t v, SelShared& sh) {
+template <class SH>
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, SH& sh) {
     uint32_t tot;
     (void)block_excl_scan(v, sh, &tot);
     return tot;
@@ -271,9 +290,9 @@ __device__ __forceinline__ void narrow(uint32_t& lo, uint32_t& hi, int shift, ui
 // as soon as every in-range key is kept.  Digits are counted with LDS
 // atomics (integer, so the counts do not depend on their order) and found by
 // one wave's suffix scan.
-template <class KeyAt>
+template <class KeyAt, class SH>
 __device__ void radix_narrow(int64_t n, KeyAt key_at, uint32_t& lo, uint32_t& hi,
-                             uint32_t& remaining, bool to_end, SelShared& sh) {
+                             uint32_t& remaining, bool to_end, SH& sh) {
     const int tid = threadIdx.x, wave = tid >> 6;
     uint32_t* hist = sh.hist;
     for (int shift = first_shift(lo, hi); shift >= 0 && lo != hi; shift = next_shift(shift)) {
@@ -339,9 +358,9 @@ __device__ __forceinline__ int value_bin(float x, float vmin, float scale) {
 // linear in value, and one for the smallest l in the bins that hold the k
 // largest l and the largest u in the bins up to the one holding the k-th
 // largest u.  The bins widen the band by at most one bin each way.
-template <class Key2At>
+template <class Key2At, class SH>
 __device__ void band_bounds(int m, Key2At key2_at, uint32_t k, uint32_t& Lk, uint32_t& Uk,
-                            SelShared& sh) {
+                            SH& sh) {
     const int tid = threadIdx.x, wave = tid >> 6;
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
     for (int e = tid; e < m; e += NT) {
@@ -382,8 +401,8 @@ __device__ void band_bounds(int m, Key2At key2_at, uint32_t k, uint32_t& Lk, uin
 }
 
 // Smallest and largest member key (min = 0xFFFFFFFF, max = 0 when none).
-template <class KeyAt>
-__device__ void member_minmax(int64_t n, KeyAt key_at, uint32_t& mn, uint32_t& mx, SelShared& sh) {
+template <class KeyAt, class SH>
+__device__ void member_minmax(int64_t n, KeyAt key_at, uint32_t& mn, uint32_t& mx, SH& sh) {
     mn = 0xFFFFFFFFu;
     mx = 0u;
     for (int64_t e = threadIdx.x; e < n; e += NT) {
@@ -401,7 +420,8 @@ __device__ void member_minmax(int64_t n, KeyAt key_at, uint32_t& mn, uint32_t& m
 // in their bit patterns, which would lump the upper tail into one bin) gives
 // the highest bin b whose suffix holds r keys; tau is the smallest sample key
 // in bins >= b.
-__device__ uint32_t sample_threshold(int ns, uint32_t r, SelShared& sh) {
+template <class SH>
+__device__ uint32_t sample_threshold(int ns, uint32_t r, SH& sh) {
     constexpr int NBIN = 256;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
@@ -459,8 +479,8 @@ __device__ uint32_t sample_threshold(int ns, uint32_t r, SelShared& sh) {
 // slots [0, count) through put(slot, e); returns count.  Thread tid takes a
 // contiguous segment of odd length, so that a wave's LDS reads at that
 // stride touch every bank once.
-template <class Flag, class Put>
-__device__ uint32_t compact(int n, Flag flag, Put put, SelShared& sh) {
+template <class Flag, class Put, class SH>
+__device__ uint32_t compact(int n, Flag flag, Put put, SH& sh) {
     const int tid = threadIdx.x;
     const int seg = ((n + NT - 1) / NT) | 1;
     const int e0 = min(n, tid * seg), e1 = min(n, e0 + seg);
@@ -487,7 +507,7 @@ __device__ uint32_t compact(int n, Flag flag, Put put, SelShared& sh) {
 // nothing is live across blocks and every load of a block is in flight
 // before its first MFMA: a gather costs one memory latency, not one per
 // MFMA.
-template <int HI, int DI>
+template <int HI, int DI, bool SPLIT = false>
 struct Rescorer {
     static constexpr QueryTileGeom G = query_tile_geom(DI);
     static constexpr int QPT = 32 / HI;
@@ -512,10 +532,13 @@ struct Rescorer {
     __device__ float score(const uint16_t* khi, const uint8_t* klo, const uint8_t* klo_scale,
                            int64_t p, const float* w) const {
         const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+        // SPLIT: half the bf16 steps' operands (and the fp8 ones) load first,
+        // the other half while their MFMAs run (fewer registers live)
+        constexpr int H1 = SPLIT ? NSB / 2 : NSB;
         bf16x8 af[NSB], bhi[NSB];
         i32x8 af8[NSF], blo[NSF];
 #pragma unroll
-        for (int s = 0; s < NSB; ++s) {
+        for (int s = 0; s < H1; ++s) {
             af[s] = as_bf16x8(ldg16(tile + tile_bf16_piece(G, col, 2 * s + half)));
             bhi[s] = as_bf16x8(ldg16(khi + p * DI + 16 * s + 8 * half));
         }
@@ -540,16 +563,30 @@ struct Rescorer {
         f32x16 acc;
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+        if constexpr (SPLIT) {
 #pragma unroll
-        for (int s = 0; s < NSB; ++s)
+            for (int s = 0; s < H1; ++s)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], bhi[s], acc, 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 2 * H1 + 4 * NSF + 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, H1, 0);
+#pragma unroll
+            for (int s = H1; s < NSB; ++s) {
+                af[s] = as_bf16x8(ldg16(tile + tile_bf16_piece(G, col, 2 * s + half)));
+                bhi[s] = as_bf16x8(ldg16(khi + p * DI + 16 * s + 8 * half));
+            }
+        }
+        // (the same MFMA sequence either way: the score is bit for bit the
+        // scoring kernel's)
+#pragma unroll
+        for (int s = SPLIT ? H1 : 0; s < NSB; ++s)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], bhi[s], acc, 0, 0, 0);
 #pragma unroll
         for (int s = 0; s < NSF; ++s)
             acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af8[s], blo[s], acc, 0, 0, 0, qsc,
                                                                   0, bsc);
         // every load first, then the MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x020, 2 * NSB + 4 * NSF + 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, NSB + NSF, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 * (NSB - (SPLIT ? H1 : 0)) + (SPLIT ? 0 : 4 * NSF + 2), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NSB - (SPLIT ? H1 : 0) + NSF, 0);
         float part[4];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
@@ -586,11 +623,12 @@ struct Rescorer {
 // The 4 waves take blocks of 32 entries in turn and skip blocks with nothing
 // to rescore.  Called by the whole workgroup after a barrier that follows
 // the staging of the tile's head weights in sh.w at the kernel's start.
-template <int HI, int DI, class TagOf, class Put>
+template <int HI, int DI, class TagOf, class Put, class SH>
 __device__ void rescore(uint32_t nr, TagOf tag_of, Put put, const SelectArgs& a, int64_t i,
-                        SelShared& sh) {
+                        SH& sh) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31;
-    Rescorer<HI, DI> r;
+    // the short-list kernel runs 4 workgroups per CU: operands in two rounds
+    Rescorer<HI, DI, SH::CAP == CAP_SHORT> r;
     r.init(a.tiles, i);
     const float* w = sh.w;
     const uint32_t nblk = (nr + 31) / 32;
@@ -612,8 +650,8 @@ __device__ void rescore(uint32_t nr, TagOf tag_of, Put put, const SelectArgs& a,
 // Emit the kept ids of the list (in id order) to out[0..k): every C_IN
 // entry, and the C_BAND entries with key > hi plus the first `remaining`
 // with key in [lo, hi].  ALL_BAND: every entry is a band entry (untagged).
-template <bool ALL_BAND>
-__device__ void emit_list(int m, uint32_t lo, uint32_t hi, uint32_t remaining, SelShared& sh,
+template <bool ALL_BAND, class SH>
+__device__ void emit_list(int m, uint32_t lo, uint32_t hi, uint32_t remaining, SH& sh,
                           int32_t* out, float* score_out, int k_out) {
     const int tid = threadIdx.x;
     const int seg = ((m + NT - 1) / NT) | 1;
@@ -662,7 +700,8 @@ __device__ __forceinline__ f32x4 load_row4(const float* row, int64_t e, int64_t 
 }
 
 // Exact selection directly over a row of final scores in global memory.
-__device__ void select_row(const float* row, int64_t n, int k, SelShared& sh, int32_t* out,
+template <class SH>
+__device__ void select_row(const float* row, int64_t n, int k, SH& sh, int32_t* out,
                            float* score_out) {
     const int tid = threadIdx.x;
     auto key_at = [&](int64_t e, uint32_t& key) {
@@ -736,9 +775,9 @@ __device__ __forceinline__ float bound_delta(f32x2 A, const float* mu, int64_t p
 // over the row.  Pools outside the band keep their approximate scores, which
 // lie strictly above U (kept) or below L (dropped) and so cannot change the
 // set.
-template <int HI, int DI>
+template <int HI, int DI, class SH>
 __device__ void select_row_bounded(const SelectArgs& a, int64_t i, float* row, int64_t n, f32x2 A,
-                                   SelShared& sh, int32_t* out, float* score_out) {
+                                   SH& sh, int32_t* out, float* score_out) {
     const int tid = threadIdx.x;
     uint32_t Lk, Uk;
     band_bounds((int)n, [&](int64_t e, uint32_t& lk, uint32_t& uk) {
@@ -747,8 +786,8 @@ __device__ void select_row_bounded(const SelectArgs& a, int64_t i, float* row, i
         uk = order_key(x);
     }, (uint32_t)a.k_pools, Lk, Uk, sh);
     uint32_t* ids = reinterpret_cast<uint32_t*>(sh.d);
-    for (int64_t base = 0; base < n; base += CAP) {
-        const int w = (int)min((int64_t)CAP, n - base);
+    for (int64_t base = 0; base < n; base += SH::CAP) {
+        const int w = (int)min((int64_t)SH::CAP, n - base);
         // this window's pools in LDS first: the rescoring below writes the row
         for (int e = tid; e < w; e += NT) {
             const float x = row[base + e], dl = bound_delta(A, a.mu, base + e);
@@ -770,12 +809,14 @@ __device__ void select_row_bounded(const SelectArgs& a, int64_t i, float* row, i
     select_row(row, n, a.k_pools, sh, out, score_out);
 }
 
-template <int HI, int DI, bool BOUNDS>
-// 3 workgroups per CU for approximate rows (LDS and registers), 4 for rows
-// of final scores, which need neither the bounds array nor the rescoring.
-__global__ __launch_bounds__(NT, BOUNDS ? 3 : 4) void topk_select_kernel(SelectArgs a) {
+template <int HI, int DI, bool BOUNDS, int LCAP>
+// Approximate rows: 4 workgroups per CU with the short list (38 KiB of LDS,
+// 128 VGPRs), 3 with the long one (LDS and registers).  Rows of final scores
+// need neither the bounds array nor the rescoring: 4 workgroups per CU.
+__global__ __launch_bounds__(NT, BOUNDS && LCAP == CAP ? 3 : 4) void topk_select_kernel(SelectArgs a) {
+    using SH = SelSharedT<LCAP>;
     extern __shared__ __align__(16) uint8_t sel_lds[];
-    SelShared& sh = *reinterpret_cast<SelShared*>(sel_lds);
+    SH& sh = *reinterpret_cast<SH*>(sel_lds);
     const int tid = threadIdx.x;
     const int i = blockIdx.x;
     const int64_t qrow = a.row0 + i;
@@ -813,7 +854,7 @@ __global__ __launch_bounds__(NT, BOUNDS ? 3 : 4) void topk_select_kernel(SelectA
     }
 
     int m = 0;  // list length
-    if (n <= (BOUNDS ? WHOLE_BOUNDED : WHOLE_FINAL)) {
+    if (n <= (BOUNDS ? LCAP : WHOLE_FINAL)) {
         // the whole row; rows are 16-byte aligned and padded to 4
         for (int e = 4 * tid; e < (int)n; e += 4 * NT) {
             const f32x4 v = load_row4(row, e, n);
@@ -829,11 +870,13 @@ __global__ __launch_bounds__(NT, BOUNDS ? 3 : 4) void topk_select_kernel(SelectA
         __syncthreads();
     } else {
         // threshold on the l keys from nb blocks of SAMPLE_LEN
-        const int nb = (n > LONG_ROW ? SAMPLE_BLOCKS_LONG : SAMPLE_BLOCKS_SHORT) / (BOUNDS ? 1 : 2);
+        // (the short list's launcher keeps its rows within LONG_ROW pools)
+        const int nb = (LCAP == CAP && n > LONG_ROW ? SAMPLE_BLOCKS_LONG : SAMPLE_BLOCKS_SHORT) /
+                       (BOUNDS ? 1 : 2);
         const int ns = nb * SAMPLE_LEN;
         // SU 16-byte pieces per thread in flight at once (ns / 4 is a
         // multiple of NT; the blocks lie inside the row)
-        constexpr int SU = 6;
+        constexpr int SU = LCAP == CAP ? 6 : 4;
         for (int s0 = 0; s0 < ns / 4; s0 += SU * NT) {
             f32x4 v[SU], mv[SU][2];
 #pragma unroll
@@ -917,7 +960,7 @@ __global__ __launch_bounds__(NT, BOUNDS ? 3 : 4) void topk_select_kernel(SelectA
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if ((j < lim[u]) & (v[u][j] >= ftau)) {
-                        if (pos < (uint32_t)CAP) {
+                        if (pos < (uint32_t)LCAP) {
                             sh.s[pos] = v[u][j];
                             sh.idc[pos] = (uint32_t)(e + j);
                         }
@@ -930,9 +973,9 @@ __global__ __launch_bounds__(NT, BOUNDS ? 3 : 4) void topk_select_kernel(SelectA
         __syncthreads();
         // the bounds of the kept entries, and how many have l key >= tau
         if constexpr (BOUNDS) {
-            // every gather of the thread in flight at once (mm <= CAP)
-            const int mm = (int)min(count, (uint32_t)CAP);
-            constexpr int GU = CAP / NT;
+            // every gather of the thread in flight at once (mm <= LCAP)
+            const int mm = (int)min(count, (uint32_t)LCAP);
+            constexpr int GU = LCAP / NT;
             float dl[GU];
 #pragma unroll
             for (int u = 0; u < GU; ++u) {
@@ -952,7 +995,7 @@ __global__ __launch_bounds__(NT, BOUNDS ? 3 : 4) void topk_select_kernel(SelectA
             cnt_l = count;
         }
         __syncthreads();
-        if (count > (uint32_t)CAP || cnt_l < (uint32_t)k) {
+        if (count > (uint32_t)LCAP || cnt_l < (uint32_t)k) {
             if constexpr (BOUNDS) {
                 if (A[1] > 0.0f) {
                     select_row_bounded<HI, DI>(a, i, row, n, A, sh, out, sout);
@@ -1017,16 +1060,38 @@ __global__ __launch_bounds__(NT, BOUNDS ? 3 : 4) void topk_select_kernel(SelectA
     emit_list<false>(m, lo, hi, remaining, sh, out, sout, k);
 }
 
+// Shapes whose short-list kernel fits 128 VGPRs without spilling (the
+// rescoring's operands grow with D_I and, below 16 heads, take more lanes).
+template <int HI, int DI>
+constexpr bool short_list_fits() { return DI == 64 || (DI == 96 && HI >= 16); }
+
+template <int HI, int DI>
+hipError_t launch_bounded_di(const SelectArgs& a, bool long_rows, hipStream_t stream) {
+    const dim3 grid((unsigned)a.rows);
+    if constexpr (short_list_fits<HI, DI>()) {
+        if (!long_rows) {
+            topk_select_kernel<HI, DI, true, CAP_SHORT>
+                <<<grid, NT, lds_bounded<CAP_SHORT>(), stream>>>(a);
+            return hipGetLastError();
+        }
+    }
+    topk_select_kernel<HI, DI, true, CAP><<<grid, NT, lds_bounded<CAP>(), stream>>>(a);
+    return hipGetLastError();
+}
+
+// The short list when it fits and no row of the chunk has more than
+// LONG_ROW pools.
 template <int HI>
 hipError_t launch_bounded_h(const SelectArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)a.rows);
+    const int64_t t_last = a.q_pos0 + a.row0 + a.rows - 1;
+    const int64_t n_max = (t_last >> 2) < a.n_pools ? (t_last >> 2) : a.n_pools;
+    const bool long_rows = n_max > LONG_ROW;
     switch (a.d_idx) {
-        case 64: topk_select_kernel<HI, 64, true><<<grid, NT, LDS_BOUNDED, stream>>>(a); break;
-        case 96: topk_select_kernel<HI, 96, true><<<grid, NT, LDS_BOUNDED, stream>>>(a); break;
-        case 128: topk_select_kernel<HI, 128, true><<<grid, NT, LDS_BOUNDED, stream>>>(a); break;
+        case 64: return launch_bounded_di<HI, 64>(a, long_rows, stream);
+        case 96: return launch_bounded_di<HI, 96>(a, long_rows, stream);
+        case 128: return launch_bounded_di<HI, 128>(a, long_rows, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -1034,7 +1099,7 @@ hipError_t launch_bounded_h(const SelectArgs& a, hipStream_t stream) {
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     if (!a.qbound) {
-        topk_select_kernel<32, 128, false><<<dim3((unsigned)a.rows), NT, LDS_FINAL, stream>>>(a);
+        topk_select_kernel<32, 128, false, CAP><<<dim3((unsigned)a.rows), NT, lds_final<CAP>(), stream>>>(a);
         return hipGetLastError();
     }
     switch (a.h_idx) {

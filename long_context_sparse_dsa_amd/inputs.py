@@ -9,9 +9,9 @@ Context on GLM-5.3-Flash" describes for GLM-5.3-Flash's DSA layers (section
 "DeepSeek Sparse Attention (DSA) Optimizations": pools of 4 tokens, 2048
 selected tokens; "Making Sparse Attention Actually Sparse": NoPE heads and
 2,051 keys; "Over Time: Chunking": a few hundred queries per chunk; "Across
-GPUs: Sharding": one GPU's share of the queries).  The page measured on
-random tokens with random-initialised weights (section "Intro"), so seeded
-random inputs are the page's own kind of workload.
+GPUs: Sharding": one GPU's share of the queries).  The page's throughput
+and memory figures come from synthetic runs (untrained weights, random token
+ids; section "Intro"), so seeded random inputs match its own workload.
 
 Recipe: numpy PCG64 seeded with ``seed`` (by default 1000 + the workload
 number), seven independent sub-streams from ``SeedSequence(seed).spawn(7)``

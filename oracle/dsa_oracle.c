@@ -12,8 +12,8 @@
  * What is computed, and where it comes from (SkyRL blog, "Scaling Training
  * to 1M Token Context on GLM-5.3-Flash"):
  *   - section "DeepSeek Sparse Attention (DSA) Optimizations": an indexer
- *     scores every query against every earlier pool of 4 tokens, then the
- *     attention reads only the selected tokens (2048 = 512 pools x 4);
+ *     rates, for each query, each pool of 4 tokens lying wholly before it;
+ *     attention then reads the chosen tokens alone (2048 = 512 pools x 4);
  *   - section "Making Sparse Attention Actually Sparse": NoPE heads (no
  *     rotary channels, so narrower heads) and 2,051 selected keys;
  *   - section "Splitting the DSA Indexer / Over Time: Chunking": scores are
@@ -47,9 +47,9 @@
  *     max_d |mean code value| <= 448 * 2^e, so that the quantisation is a
  *     round-to-nearest-even of an exactly scaled value and no precision
  *     choice can change a code;
- *   - gated pooling (section "DSA: Gather by Token Position" names k-pool
- *     gate scores that weight each key within a pool; no normalisation is
- *     printed): with a per-token gate array g the pooled key is the plain
+ *   - gated pooling (section "DSA: Gather by Token Position" mentions
+ *     per-token gate scores applied to the keys inside each pool; it prints
+ *     no normalisation): with a per-token gate array g the pooled key is the plain
  *     gate-weighted sum kbar_p = sum_r g[4p+r] * k[4p+r], the caller
  *     supplying normalised gates.  Without gates the mean is used, which is
  *     the gated sum with every gate equal to 1/4.

@@ -297,7 +297,10 @@ def _host_topk_ids(scores, n, k):
     (131072, 130880, "random", 512), (131072, 130880, "near_constant", 512),  # 32k pools
     (80192, 80000, "random", 512),                      # rows of 20k pools, scored in full
     (65536, 65344, "pool_constant", 512),  # every pooled key exactly bf16: no correction term
-    (16448, 16256, "random", 64),  # bounded rows of 4064-4111 pools: whole list, then sampled
+    (16448, 16256, "random", 64),  # bounded rows of 4064-4111 pools, sampled
+    (12480, 12288, "random", 64),  # 96-wide heads, rows of 3072-3119 pools: whole short list,
+                                   # then sampled
+    (12480, 12288, "near_constant", 64),  # the short list overflows into the slow path
 ])
 def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, keys, k_pools):
     # The chunk buffer holds scores taken without the E4M3 correction; the
@@ -312,14 +315,15 @@ def test_selection_equals_exact_topk_of_full_scores(s_k, q_pos0, keys, k_pools):
     # chunk's scores still differ from the full ones by the rounding of a
     # different summation order, which the bound must cover.
     near_constant = keys == "near_constant"
-    wl = inputs.custom("full_topk", s_q=192, s_k=s_k, q_pos0=q_pos0, h_idx=32, d_idx=128,
-                       k_pools=k_pools, h=16, d=128, idx_std=1 / math.sqrt(128),
+    d_idx = 96 if s_k == 12480 else 128
+    wl = inputs.custom("full_topk", s_q=192, s_k=s_k, q_pos0=q_pos0, h_idx=32, d_idx=d_idx,
+                       k_pools=k_pools, h=16, d=128, idx_std=1 / math.sqrt(d_idx),
                        number=380 + {"random": 0, "near_constant": 1, "pool_constant": 2}[keys]
-                       + (s_k - 65536) // 4096 + (k_pools != 512) * 1000)
+                       + (s_k - 65536) // 4096 + (k_pools != 512) * 1000 + (d_idx != 128) * 2000)
     x = inputs.make_inputs(wl, attention=False)
     if near_constant:
         rng = np.random.default_rng(7)
-        base = rng.standard_normal(wl.d_idx).astype(np.float32) / np.float32(math.sqrt(128))
+        base = rng.standard_normal(wl.d_idx).astype(np.float32) / np.float32(math.sqrt(wl.d_idx))
         noise = rng.standard_normal((wl.s_k, wl.d_idx)).astype(np.float32)
         x["k_idx"] = torch.from_numpy(base[None, :] * (1 + np.float32(0.01) * noise)).to(
             torch.bfloat16)

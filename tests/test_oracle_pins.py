@@ -2,7 +2,7 @@
 
 Method source: SkyRL blog "Scaling Training to 1M Token Context on
 GLM-5.3-Flash" -- section "DeepSeek Sparse Attention (DSA) Optimizations"
-(score every earlier pool of 4 tokens, attend only to the selected tokens),
+(rate each 4-token pool before the query, attend to the chosen tokens alone),
 "Making Sparse Attention Actually Sparse" (2,051 keys), "Over Time: Chunking"
 (fp32 scores) and "Across GPUs: Sharding" (int32 pool ids).  The page prints
 no worked example, so the pins are: hand-derived closed forms on tiny inputs,
