@@ -380,13 +380,14 @@ def backward(args, wl, x, g, gate, chunk_q, ws, idx, out, stream):
     dq = torch.empty((wl.s_q, wl.h, wl.d), dtype=torch.float32, device=dev)
     dk = torch.empty((wl.s_k, wl.d), dtype=torch.float32, device=dev)
     dv = torch.empty((wl.s_k, wl.dv), dtype=torch.float32, device=dev)
-    nbytes, bwd_chunk = dsa.dsa_sparse_attn_bwd_workspace_size(wl.s_q, wl.s_k, wl.h)
+    nbytes, bwd_chunk = dsa.dsa_sparse_attn_bwd_workspace_size(wl.s_q, wl.s_k, wl.h,
+                                                               args.bwd_chunk_q)
     bws = dsa.new_workspace(nbytes, dev)
 
     def step():
         dsa.dsa_sparse_attn_bwd(g["q"], g["k"], g["v"], idx, o, dout, lse, q_pos0=wl.q_pos0,
-                                n_tail=wl.n_tail, dq=dq, dk=dk, dv=dv, workspace=bws,
-                                stream=stream)
+                                n_tail=wl.n_tail, chunk_q=bwd_chunk, dq=dq, dk=dk, dv=dv,
+                                workspace=bws, stream=stream)
 
     for i in range(args.warmup):
         step()
@@ -457,6 +458,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="s128k")
     ap.add_argument("--chunk-q", type=int, default=0)
+    ap.add_argument("--bwd-chunk-q", type=int, default=0,
+                    help="queries per transposition chunk of the backward (0 = the library's "
+                         "default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
