@@ -105,9 +105,9 @@ SMALL = [
     (129, 131, 2, 16, 128, 64, 64, 3, 0),      # k covers every pool: dense causal
     (2500, 2500, 0, 2, 64, 64, 4, 1, 0),       # 80 bitmap words per chunk: two scan windows
     (3000, 3001, 0, 16, 96, 96, 6, 3, 2048),   # two chunks, several windows each
-    # 282 bitmap words in the chunk: two expansion windows of 256 words; the
-    # first pools are kept by nearly every query: over 1024 entries per pool
-    # group, so the entry list is filled several times
+    # 282 bitmap words in one chunk (five scan windows of 64 words); the first
+    # pools are kept by nearly every query, so the first pool groups walk
+    # thousands of entries
     (9000, 9000, 0, 2, 64, 64, 512, 1, 0),
     (2600, 2600, 0, 4, 128, 128, 200, 3, 0),   # about 1700 entries in the first groups
 ]
