@@ -234,10 +234,11 @@ dsa_status dsa_sparse_attn_fwd(const void *q, const void *k, const void *v, cons
  * Bytes of device workspace dsa_sparse_attn_bwd needs: delta = dout . out
  * per query and head (fp32 [s_q, h], rounded up to 256 bytes), then the
  * bitmap that transposes one chunk of queries' selections,
- * ceil(s_k / 4) x chunk_q / 32 32-bit words.  chunk_q = 0 picks the default
- * (min(16384, s_q rounded up to 64)), returned through *chunk_q_used when
- * that pointer is non-NULL; otherwise a multiple of 64 up to 65536 whose
- * bitmap stays within 2 GiB.  Pure host computation.
+ * ceil(s_k / 4) x chunk_q / 32 32-bit words.  chunk_q = 0 picks the default,
+ * max(2048, ceil(s_k / 4) / 32) rounded up to a multiple of 64, at most 16384
+ * and at most s_q rounded up to 64, returned through *chunk_q_used when that
+ * pointer is non-NULL; otherwise a multiple of 64 up to 65536 whose bitmap
+ * stays within 2 GiB.  Pure host computation.
  */
 dsa_status dsa_sparse_attn_bwd_workspace_size(int64_t s_q, int64_t s_k, int h, int64_t chunk_q,
                                               size_t *bytes, int64_t *chunk_q_used);

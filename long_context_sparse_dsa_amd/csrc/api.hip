@@ -319,21 +319,28 @@ dsa_status check_attn_shape(int64_t s_q, int64_t s_k, int64_t q_pos0, int h, int
 
 // Backward: queries per transposition chunk (a multiple of 64), and the
 // workspace: delta [s_q, h] fp32, then the chunk bitmap
-// [ceil(s_k / 4)][chunk / 32] words.
-constexpr int64_t kBwdChunkDefault = 16384;
+// [ceil(s_k / 4)][chunk / 32] words.  Default chunk: max(2048, pool slots /
+// 32), at most 16384.  Every chunk pays a pass of the key-major kernel over
+// all pool slots, so the chunk grows with them; smaller chunks keep more of
+// a chunk's query rows in the L2s.  (Measured best of 512 .. 32768: 2048 at
+// 8K, 16K and 32K slots, 8192 at 262144 slots.)
+constexpr int64_t kBwdChunkMin = 2048;
+constexpr int64_t kBwdChunkMax = 16384;
 constexpr int64_t kBwdBitmapCap = int64_t(2) << 30;
 
 dsa_status bwd_layout(int64_t s_q, int64_t s_k, int h, int64_t chunk_q, int64_t* chunk_used,
                       int64_t* delta_bytes, int64_t* bits_bytes) {
     if (chunk_q < 0) return fail(DSA_ERR_INVALID_ARG, "chunk_q %lld < 0", (long long)chunk_q);
+    const int64_t slots = (s_k + 3) / 4;
     if (chunk_q == 0) {
-        chunk_q = round_up(s_q > 0 ? s_q : 1, 64);
-        if (chunk_q > kBwdChunkDefault) chunk_q = kBwdChunkDefault;
+        int64_t c = round_up(slots / 32 > kBwdChunkMin ? slots / 32 : kBwdChunkMin, 64);
+        if (c > kBwdChunkMax) c = kBwdChunkMax;
+        const int64_t all = round_up(s_q > 0 ? s_q : 1, 64);
+        chunk_q = c < all ? c : all;
     }
     if (chunk_q % 64 != 0 || chunk_q > kMaxChunk)
         return fail(DSA_ERR_UNSUPPORTED, "chunk_q %lld: must be a multiple of 64 up to %lld",
                     (long long)chunk_q, (long long)kMaxChunk);
-    const int64_t slots = (s_k + 3) / 4;
     const int64_t bits = slots * (chunk_q / 32) * 4;
     if (bits > kBwdBitmapCap)
         return fail(DSA_ERR_UNSUPPORTED, "chunk_q %lld: the chunk bitmap (%lld bytes) exceeds 2 GiB",
