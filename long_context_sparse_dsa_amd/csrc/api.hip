@@ -341,7 +341,7 @@ dsa_status bwd_layout(int64_t s_q, int64_t s_k, int h, int64_t chunk_q, int64_t*
     if (chunk_q % 64 != 0 || chunk_q > kMaxChunk)
         return fail(DSA_ERR_UNSUPPORTED, "chunk_q %lld: must be a multiple of 64 up to %lld",
                     (long long)chunk_q, (long long)kMaxChunk);
-    const int64_t bits = slots * (chunk_q / 32) * 4;
+    const int64_t bits = round_up(slots, 4) * (chunk_q / 32) * 4;
     if (bits > kBwdBitmapCap)
         return fail(DSA_ERR_UNSUPPORTED, "chunk_q %lld: the chunk bitmap (%lld bytes) exceeds 2 GiB",
                     (long long)chunk_q, (long long)bits);
@@ -787,7 +787,7 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     a.delta = reinterpret_cast<float*>(ws);
     a.bits = reinterpret_cast<uint32_t*>(ws + db);
-    a.words = cq / 32;
+    a.stride = round_up((s_k + 3) / 4, 4);
     {
         Timed tm(K_BWD_DQ, s);
         hipError_t e = dsa::launch_attn_bwd_dq(a, s);
@@ -798,8 +798,7 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
         const int rows = (int)(s_q - r0 < cq ? s_q - r0 : cq);
         {
             Timed tm(K_BWD_BITS, s);
-            hipError_t e = dsa::launch_fill_f32(reinterpret_cast<float*>(a.bits), bb / 4, 0.0f, s);
-            if (e == hipSuccess) e = dsa::launch_attn_bwd_bits(a, r0, rows, s);
+            hipError_t e = dsa::launch_attn_bwd_bits(a, r0, rows, s);
             if (e != hipSuccess) return hip_fail(e, "attn_bwd_select launch");
         }
         Timed tm(K_BWD_DKV, s);

@@ -158,8 +158,8 @@ struct AttnBwdArgs {
     float* dk;                // [s_k, d]
     float* dv_grad;           // [s_k, dv]
     float* delta;             // workspace: dout . out per query and head [s_q, h]
-    uint32_t* bits;           // workspace: chunk bitmap [ceil(s_k / 4)][words]
-    int64_t words;            // words per bitmap row (chunk queries / 32)
+    uint32_t* bits;           // workspace: chunk bitmap [chunk / 32][stride] words
+    int64_t stride;           // pool slots per bitmap word row: ceil(s_k / 4) rounded up to 4
 };
 // dq and delta (query-major pass).
 hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t stream);

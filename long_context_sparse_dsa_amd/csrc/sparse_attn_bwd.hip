@@ -16,8 +16,8 @@
 //      tokens in tiles of 32 slots and forms D and dq.
 //   2. Pool-major: the gradient of a key row sums over the queries that
 //      attend it.  One chunk of queries at a time, the selections are
-//      transposed into a bitmap [pool slot][chunk query] by integer atomic
-//      OR (the same bits in any order).  One workgroup per 4 pool slots
+//      transposed into a bitmap [chunk query / 32][pool slot] of 32-bit words
+//      by integer atomic OR in LDS (the same bits in any order).  One workgroup per 4 pool slots
 //      (16 tokens) walks the set bits of its 4 rows in increasing query
 //      order, recomputes P and dS for its tokens against each query, and
 //      accumulates dk and dv in registers; each chunk's sum is added to dk
@@ -296,28 +296,48 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(DqK a) {
 
 // ---------------------------------------------------------------- transposed selection
 
-// Chunk bitmap: bit (r % 32) of word [slot][r / 32] is set when chunk query
-// row r attends a token of pool slot `slot` -- a kept pool id in [0, P), or
-// its own pool when it has tail tokens there.  One wave per query row; all
-// ids of a row are distinct, so lanes of a wave never hit one word, and the
-// OR of the rows is the same in any order.
+// Chunk bitmap, word-major: bit (r % 32) of word [r / 32][slot] (row stride
+// `stride` slots, a multiple of 4) is set when chunk query row r attends a
+// token of pool slot `slot` -- a kept pool id in [0, P), or its own pool when
+// it has tail tokens there.  One workgroup per (word column c, range of
+// BITS_RANGE slots): its 32 query rows OR their bits into an LDS copy of the
+// range with LDS atomics (the same bits in any order), then it writes every
+// word of the range, zeros included, so the bitmap needs no clearing.
+constexpr int BITS_RANGE = 16384;  // 64 KiB of LDS
+
 __global__ __launch_bounds__(256) void bwd_select_bits_kernel(
     const int32_t* __restrict__ idx, int k_pools, int64_t row0, int rows, int64_t q_pos0,
-    int64_t n_pools, int64_t s_k, int n_tail, uint32_t* bits, int64_t words) {
-    const int lane = threadIdx.x & 63;
-    const int r = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    if (r >= rows) return;
-    const int64_t i = row0 + r;
-    const uint32_t bit = 1u << (r & 31);
-    uint32_t* colw = bits + (r >> 5);
-    const int32_t* irow = idx + i * k_pools;
-    for (int j = lane; j < k_pools; j += 64) {
-        const int32_t p = irow[j];
-        if (p >= 0 && (int64_t)p < n_pools) atomicOr(colw + (int64_t)p * words, bit);
+    int64_t n_pools, int64_t s_k, int n_tail, uint32_t* bits, int64_t stride) {
+    __shared__ __attribute__((aligned(16))) uint32_t lw[BITS_RANGE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = (int)blockIdx.x;
+    const int64_t s0 = (int64_t)blockIdx.y * BITS_RANGE;
+    const int64_t s1 = s0 + BITS_RANGE < stride ? s0 + BITS_RANGE : stride;
+    const int width = (int)(s1 - s0);  // a multiple of 4
+    for (int e = 4 * tid; e < BITS_RANGE; e += 4 * 256)
+        *reinterpret_cast<u32x4*>(lw + e) = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    // rows 32 c + 8 wave .. +7 of the chunk
+    for (int rr = 0; rr < 8; ++rr) {
+        const int r = 8 * wave + rr;
+        const int row = 32 * c + r;
+        if (row >= rows) break;
+        const int64_t i = row0 + row;
+        const uint32_t bit = 1u << r;
+        const int32_t* irow = idx + i * k_pools;
+        for (int j = lane; j < k_pools; j += 64) {
+            const int32_t p = irow[j];
+            if (p >= 0 && (int64_t)p < n_pools && p >= s0 && p < s1) atomicOr(&lw[p - s0], bit);
+        }
+        const int64_t t = q_pos0 + i;
+        const int64_t own = t >> 2;
+        if (lane == 0 && n_tail > 0 && (t & 3) != 0 && 4 * own < s_k && own >= s0 && own < s1)
+            atomicOr(&lw[own - s0], bit);
     }
-    const int64_t t = q_pos0 + i;
-    if (lane == 0 && n_tail > 0 && (t & 3) != 0 && 4 * (t >> 2) < s_k)
-        atomicOr(colw + (t >> 2) * words, bit);
+    __syncthreads();
+    uint32_t* dst = bits + (int64_t)c * stride + s0;
+    for (int e = 4 * tid; e < width; e += 4 * 256)
+        *reinterpret_cast<u32x4*>(dst + e) = *reinterpret_cast<const u32x4*>(lw + e);
 }
 
 // ---------------------------------------------------------------- pass 2: dk, dv
@@ -329,8 +349,8 @@ struct DkvK {
     const uint16_t* dout;
     const float* lse;
     const float* delta;
-    const uint32_t* bits;   // [slots][words]
-    int64_t words;
+    const uint32_t* bits;   // [chunk / 32][stride]
+    int64_t stride;
     int64_t s_k, q_pos0, row0;
     int rows;
     int64_t slots;          // pool slots: ceil(s_k / 4)
@@ -414,14 +434,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
         // wave.  The words of the next window are loaded while this one is
         // consumed.
         const int nw = (a.rows + 31) / 32;
-        const uint32_t* brow[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            brow[j] = (4 * g + j < a.slots) ? a.bits + (4 * g + j) * a.words : nullptr;
+        // the 4 slots' words of one word column are one 16-byte piece (slots
+        // past the last pool read as zero: the stride is padded to 4)
+        const uint32_t* bcol = a.bits + 4 * g;
         auto load_words = [&](int wb, uint32_t (&dst)[4]) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (wb + lane < nw) x = ldg16(bcol + (int64_t)(wb + lane) * a.stride);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                dst[j] = (brow[j] && wb + lane < nw) ? brow[j][wb + lane] : 0u;
+            for (int j = 0; j < 4; ++j) dst[j] = x[j];
         };
         uint32_t ww[4], pw[4];
         load_words(0, pw);
@@ -691,8 +711,9 @@ hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_attn_bwd_bits(const AttnBwdArgs& a, int64_t row0, int rows, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
-    bwd_select_bits_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(
-        a.idx, a.k_pools, row0, rows, a.q_pos0, a.s_k / 4, a.s_k, a.n_tail, a.bits, a.words);
+    const dim3 grid((unsigned)((rows + 31) / 32), (unsigned)((a.stride + BITS_RANGE - 1) / BITS_RANGE));
+    bwd_select_bits_kernel<<<grid, 256, 0, stream>>>(a.idx, a.k_pools, row0, rows, a.q_pos0,
+                                                     a.s_k / 4, a.s_k, a.n_tail, a.bits, a.stride);
     return hipGetLastError();
 }
 
@@ -708,7 +729,7 @@ hipError_t launch_attn_bwd_dkv(const AttnBwdArgs& a, int64_t row0, int rows, int
     k.lse = a.lse;
     k.delta = a.delta;
     k.bits = a.bits;
-    k.words = a.words;
+    k.stride = a.stride;
     k.s_k = a.s_k;
     k.q_pos0 = a.q_pos0;
     k.row0 = row0;

@@ -228,8 +228,8 @@ def test_sparse_attn_bwd_rejects_before_launch(lib, over, status):
 
 
 def test_sparse_attn_bwd_workspace_layout(lib):
-    # delta [s_q, h] fp32 rounded to 256 B, then the chunk bitmap
-    # ceil(s_k / 4) rows x chunk / 32 words
+    # delta [s_q, h] fp32 rounded to 256 B, then the chunk bitmap:
+    # chunk / 32 rows of ceil(s_k / 4) words, rounded up to 4
     # default chunk: max(2048, pool slots / 32), at most 16384 and s_q
     nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(131072, 131072, 16)
     assert cq == 2048
@@ -241,7 +241,7 @@ def test_sparse_attn_bwd_workspace_layout(lib):
     _, cq = dsa.dsa_sparse_attn_bwd_workspace_size(1000, 1 << 20, 16)
     assert cq == 1024
     nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(100, 203, 5, 64)
-    assert cq == 64 and nbytes == 2048 + 51 * 2 * 4
+    assert cq == 64 and nbytes == 2048 + 52 * 2 * 4
     nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(100, 203, 5)
     assert cq == 128
     # one GPU's share of 1M keys: 262144 pool rows; 65536 queries per chunk
