@@ -35,8 +35,9 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 constexpr int64_t kMaxKPools = 2048;
 constexpr int64_t kDefaultChunkMax = 8192;
 constexpr int64_t kDefaultBufferBudget = int64_t(3) << 29;  // 1.5 GiB
-// Top-k workgroups resident at once on MI355X: 256 CUs x 3.  Default chunks
-// are a multiple of it, so that no selection launch ends on a partial wave.
+// Top-k workgroups resident at once on MI355X for rows of long-list shapes:
+// 256 CUs x 3.  Default chunks that the buffer budget limits (long rows) are
+// a multiple of it, so that no selection launch ends on a partial wave.
 constexpr int64_t kSelectWave = 768;
 constexpr int64_t kMaxChunk = 1 << 16;
 constexpr int64_t kScoreBufferCap = int64_t(2) << 30;  // per chunk, as the page keeps it
