@@ -40,6 +40,7 @@ METRIC = "DSA fwd queries/sec at S=128k (indexer+topk+attn); TFLOP/s vs MFMA pea
 
 KERNEL_SOURCES = {
     "index_score": ["index_score.hip", "common.h"],
+    "index_score_full": ["index_score.hip", "common.h"],
     "topk_select": ["topk_select.hip", "common.h"],
     "sparse_attn": ["sparse_attn.hip", "common.h"],
     "pool_keys": ["index_score.hip", "common.h"],
@@ -80,6 +81,10 @@ KERNEL_KINDS = [("pool_keys", "pool_keys"), ("pack_queries", "pack_queries"),
 
 
 def kernel_kind(name: str):
+    # the bf16 scorer with the correction term (its last template argument,
+    # LO, is true) is the library's "index_score_full" kind
+    if "index_score_bf16_kernel" in name and name.split("(")[0].rstrip().endswith("true>"):
+        return "index_score_full"
     for key, kind in KERNEL_KINDS:
         if key in name:
             return kind
@@ -124,7 +129,9 @@ def traffic_summary(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir
     print(f"FETCH_SIZE factor {ff:.4f}, WRITE_SIZE factor {wf:.4f} (1 GiB copy)\n")
     print("| kernel | launches | fetched B/launch (calibrated) | written B/launch (calibrated) |")
     print("|---|---|---|---|")
-    for k in [kind for _, kind in KERNEL_KINDS if kind in fb]:
+    order = [kind for _, kind in KERNEL_KINDS]
+    order.insert(order.index("index_score") + 1, "index_score_full")
+    for k in [kind for kind in order if kind in fb]:
         f = fb[k] * ff / fn[k]
         w = wb.get(k, 0.0) * wf / fn[k]
         print(f"| {k} | {fn[k]} | {f:.4g} | {w:.4g} |")
@@ -242,6 +249,30 @@ def step_stats(times_ms):
     return {"ms_per_step_median": t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1]
                                                                           + t[len(t) // 2]),
             "ms_per_step_min": t[0]}
+
+
+def score_paths(wl, chunk_q, fp8):
+    """Per query chunk of the indexer call without score_out: which scorer
+    kernel the library runs.  Mirrors the library's rule (bf16 chunks whose
+    first and last rows together see more than 32 k pools are scored without
+    the correction term and bounded; chunks whose rows all see at most k
+    pools are not scored).  Returns (bounded chunks, full chunks, pairs of
+    each); the bench checks the launch counts against the library's."""
+    nb = nf = 0
+    pb = pf = 0
+    for c0 in range(0, wl.s_q, chunk_q):
+        rows = min(chunk_q, wl.s_q - c0)
+        t = wl.q_pos0 + c0 + np.arange(rows, dtype=np.int64)
+        n = np.minimum(t // 4, wl.n_pools)
+        if n[-1] == 0 or n[-1] <= wl.k_pools:
+            continue
+        if not fp8 and n[0] + n[-1] > 2 * 16 * wl.k_pools:
+            nb, pb = nb + 1, pb + int(n.sum())
+        elif fp8:
+            nb, pb = nb + 1, pb + int(n.sum())
+        else:
+            nf, pf = nf + 1, pf + int(n.sum())
+    return nb, nf, pb, pf
 
 
 def work_counts(wl):
@@ -561,14 +592,23 @@ def main():
     w = work_counts(wl)
     qps = wl.s_q / (ms / 1e3)
     tflops = (w["f_score"] + w["f_attn"]) / (ms / 1e3) / 1e12
+    # the two scorer kernels and their algorithmic flops
+    nb, nf, pb, pf = score_paths(wl, chunk_q, args.fp8)
+    f_path = {"index_score": 2.0 * wl.h_idx * wl.d_idx * pb,
+              "index_score_full": 2.0 * wl.h_idx * wl.d_idx * pf}
+    for name, n_exp in (("index_score", nb), ("index_score_full", nf)):
+        got = stats.get(name, (0, 0.0))[0]
+        if got != n_exp * args.steps:
+            raise SystemExit(f"{name}: {got} launches in {args.steps} steps, expected "
+                             f"{n_exp * args.steps} (the scorer path rule changed?)")
     stages = {}
     for name, (launches, total) in stats.items():
         stages[name] = {"ms_per_step": total / args.steps, "launches_per_step": launches / args.steps}
     rl = {}
     for name, (launches, total) in stats.items():
         t_s = total / 1e3
-        if name == "index_score":
-            a = w["f_score"] * args.steps / t_s / 1e12
+        if name in f_path:
+            a = f_path[name] * args.steps / t_s / 1e12
             peak = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
             rl[name] = {"bound": "mfma", "achieved": a, "peak": peak,
                         "unit": "TFLOP/s", "frac": a / peak, "traffic": None}
@@ -615,6 +655,8 @@ def main():
         "roofline": dict(rl[dominant], kernel=dominant) if dominant in rl else None,
         "stages": stages,
         "work": {"pairs": w["pairs"], "tokens": w["tokens"], "f_score": w["f_score"],
+                 "f_score_bounded": f_path["index_score"],
+                 "f_score_full": f_path["index_score_full"],
                  "f_attn": w["f_attn"], "b_attn": w["b_attn"], "b_select": w["b_select"]},
         "peak_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
     }
@@ -626,7 +668,8 @@ def main():
                     "hbm": "hbm_read_gbs", "l2": "l2_read_gbs"}
         for st in stages.values():
             if "bound" in st and st["bound"] in probe_of:
-                if st["bound"] == "mfma" and st is not stages.get("index_score"):
+                if st["bound"] == "mfma" and st is not stages.get("index_score") \
+                        and st is not stages.get("index_score_full"):
                     continue
                 st["frac_of_measured_peak"] = st["achieved"] / pk[probe_of[st["bound"]]]
         if result["roofline"] is not None:

@@ -283,8 +283,11 @@ dsa_status dsa_sparse_attn_bwd(const void *q, const void *k, const void *v, cons
  * by HIP events on its own stream; dsa_profile_read synchronises on those
  * events and reports, per kernel kind, the number of launches and the summed
  * duration in milliseconds, then clears the record.  Kinds: "pool_keys",
- * "pack_queries", "index_score", "topk_select", "sparse_attn",
- * "attn_bwd_dq", "attn_bwd_select", "attn_bwd_dkv".
+ * "pack_queries", "index_score" (the bf16 scorer of bounded chunks, without
+ * the correction term, and the fp8 scorer), "index_score_full" (the bf16
+ * scorer with the correction term: chunks of short rows and
+ * dsa_index_scores), "topk_select", "sparse_attn", "attn_bwd_dq",
+ * "attn_bwd_select", "attn_bwd_dkv".
  */
 typedef struct {
     char name[32];

@@ -45,11 +45,15 @@ constexpr int64_t kScoreBufferCap = int64_t(2) << 30;  // per chunk, as the page
 // ------------------------------------------------------------ profiling
 
 enum Kind {
-    K_POOL = 0, K_PACK, K_SCORE, K_SELECT, K_ATTN, K_BWD_DQ, K_BWD_BITS, K_BWD_DKV, K_COUNT
+    K_POOL = 0, K_PACK, K_SCORE, K_SELECT, K_ATTN, K_BWD_DQ, K_BWD_BITS, K_BWD_DKV,
+    K_SCORE_FULL, K_COUNT
 };
+// index_score: the bf16 scorer without the correction term (bounded chunks)
+// and the fp8 scorer; index_score_full: the bf16 scorer with it (chunks of
+// short rows, and the dense-score entry point), a separate kernel
 const char* kKindName[K_COUNT] = {"pool_keys", "pack_queries", "index_score", "topk_select",
                                   "sparse_attn", "attn_bwd_dq", "attn_bwd_select",
-                                  "attn_bwd_dkv"};
+                                  "attn_bwd_dkv", "index_score_full"};
 
 struct Rec {
     int kind;
@@ -513,7 +517,7 @@ static dsa_status index_score_topk(const void* q_idx, const void* k_idx, const f
                 a.qbound = reinterpret_cast<const float*>(ws + L.qbound);
                 a.mu = reinterpret_cast<const float*>(ws + L.mu);
             }
-            Timed tm(K_SCORE, s);
+            Timed tm(bounded || dtype != DSA_BF16 ? K_SCORE : K_SCORE_FULL, s);
             e = dsa::launch_index_score(a, s);
             if (e != hipSuccess) return hip_fail(e, "index_score launch");
         }
@@ -593,7 +597,7 @@ static dsa_status index_scores(const void* q_idx, const void* k_idx, const float
         a.exact = 1;
         a.buf = scores_out + (r0 - row0) * sh.n_pools;
         a.ld = sh.n_pools;
-        Timed tm(K_SCORE, s);
+        Timed tm(dtype == DSA_BF16 ? K_SCORE_FULL : K_SCORE, s);
         e = dsa::launch_index_score(a, s);
         if (e != hipSuccess) return hip_fail(e, "index_score launch");
     }
