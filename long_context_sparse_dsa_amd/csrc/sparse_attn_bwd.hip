@@ -65,6 +65,12 @@ __device__ __forceinline__ u32x2 tr_read(const uint16_t* tile, int base_row, int
     return __builtin_bit_cast(u32x2, t4);
 }
 
+// Buffer resource over `bytes` bytes at p (raw, 32-bit offsets; reads at or
+// beyond `bytes` return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
 // ---------------------------------------------------------------- pass 1: dq
 
 struct DqK {
@@ -514,12 +520,34 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
             float ld;         // lane l: (l < 32 ? A : B), (l & 16 ? delta : lse), head l & 15
             uint32_t mask[2];
         };
+        // D = DV = 128: a query's q (and dout) rows are h x 256 contiguous
+        // bytes, and lane L's piece r is byte 16 (L + 64 r) of them (head
+        // L / 16 + 4 r): one buffer load with a scalar base per query, whose
+        // range ends with the h rows (pieces of heads >= h read as zero), and
+        // one store at toff(L / 16 + 4 r, 8 (L % 16)) = base_b + 4 r (W + 16),
+        // b = (r ^ r / 2) & 1 selecting one of two lane bases.
+        constexpr bool ROWS128 = D == 128 && DV == 128;
+        const uint32_t goff = 16u * (uint32_t)lane;
+        const uint32_t qbytes = (uint32_t)(a.h * D * 2), obytes = (uint32_t)(a.h * DV * 2);
+        const int tbase = (lane >> 4) * (D + 16);
+        const int sbase0 = tbase + ((lane & 15) << 3), sbase1 = tbase + (((lane & 15) ^ 1) << 3);
         auto load_pair = [&](int rowA, uint32_t mA, int rowB, uint32_t mB, Pair& P) {
             P.mask[0] = mA;
             P.mask[1] = mB;
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int64_t qi = a.row0 + (x ? rowB : rowA);
+                if constexpr (ROWS128) {
+                    const __amdgpu_buffer_rsrc_t rq = rsrc_of(a.q + qi * a.h * D, qbytes);
+                    const __amdgpu_buffer_rsrc_t ro = rsrc_of(a.dout + qi * a.h * DV, obytes);
+#pragma unroll
+                    for (int r = 0; r < QPL; ++r)
+                        P.q[x][r] = __builtin_amdgcn_raw_buffer_load_b128(rq, goff + 1024u * r, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < OPL; ++r)
+                        P.o[x][r] = __builtin_amdgcn_raw_buffer_load_b128(ro, goff + 1024u * r, 0, 0);
+                    continue;
+                }
 #pragma unroll
                 for (int r = 0; r < QPL; ++r) {
                     const int gi = lane + 64 * r, hh = gi / QCH;
@@ -543,6 +571,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
         auto stash_pair = [&](const Pair& P) {
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
+                if constexpr (ROWS128) {
+#pragma unroll
+                    for (int r = 0; r < QPL; ++r)
+                        *reinterpret_cast<u32x4*>(sq[x] + (((r ^ (r >> 1)) & 1) ? sbase1 : sbase0) +
+                                                  4 * r * (D + 16)) = P.q[x][r];
+#pragma unroll
+                    for (int r = 0; r < OPL; ++r)
+                        *reinterpret_cast<u32x4*>(so[x] + (((r ^ (r >> 1)) & 1) ? sbase1 : sbase0) +
+                                                  4 * r * (DV + 16)) = P.o[x][r];
+                    continue;
+                }
 #pragma unroll
                 for (int r = 0; r < QPL; ++r) {
                     const int gi = lane + 64 * r, hh = gi / QCH;
