@@ -520,48 +520,45 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
             float ld;         // lane l: (l < 32 ? A : B), (l & 16 ? delta : lse), head l & 15
             uint32_t mask[2];
         };
-        // D = DV = 128: a query's q (and dout) rows are h x 256 contiguous
-        // bytes, and lane L's piece r is byte 16 (L + 64 r) of them (head
-        // L / 16 + 4 r): one buffer load with a scalar base per query, whose
-        // range ends with the h rows (pieces of heads >= h read as zero), and
-        // one store at toff(L / 16 + 4 r, 8 (L % 16)) = base_b + 4 r (W + 16),
-        // b = (r ^ r / 2) & 1 selecting one of two lane bases.
+        // A query's q (and dout) rows are h x 2W contiguous bytes, and lane
+        // L's piece r is byte 16 (L + 64 r) of them: one buffer load with a
+        // scalar base per query, whose range ends with the h rows (pieces of
+        // heads >= h read as zero).  Its LDS place toff(g / CH, 8 (g % CH)),
+        // g = L + 64 r, is fixed per lane: at W = 128 it is base_b + 4 r
+        // (W + 16) with b = (r ^ r / 2) & 1 choosing one of two lane bases;
+        // at other widths one precomputed offset per piece.
         constexpr bool ROWS128 = D == 128 && DV == 128;
         const uint32_t goff = 16u * (uint32_t)lane;
         const uint32_t qbytes = (uint32_t)(a.h * D * 2), obytes = (uint32_t)(a.h * DV * 2);
         const int tbase = (lane >> 4) * (D + 16);
         const int sbase0 = tbase + ((lane & 15) << 3), sbase1 = tbase + (((lane & 15) ^ 1) << 3);
+        int qst[ROWS128 ? 1 : QPL], ost[ROWS128 ? 1 : OPL];
+        if constexpr (!ROWS128) {
+#pragma unroll
+            for (int r = 0; r < QPL; ++r) {
+                const int g = lane + 64 * r;
+                qst[r] = toff<D>(g / QCH, 8 * (g % QCH));
+            }
+#pragma unroll
+            for (int r = 0; r < OPL; ++r) {
+                const int g = lane + 64 * r;
+                ost[r] = toff<DV>(g / OCH, 8 * (g % OCH));
+            }
+        }
         auto load_pair = [&](int rowA, uint32_t mA, int rowB, uint32_t mB, Pair& P) {
             P.mask[0] = mA;
             P.mask[1] = mB;
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int64_t qi = a.row0 + (x ? rowB : rowA);
-                if constexpr (ROWS128) {
-                    const __amdgpu_buffer_rsrc_t rq = rsrc_of(a.q + qi * a.h * D, qbytes);
-                    const __amdgpu_buffer_rsrc_t ro = rsrc_of(a.dout + qi * a.h * DV, obytes);
+                const __amdgpu_buffer_rsrc_t rq = rsrc_of(a.q + qi * a.h * D, qbytes);
+                const __amdgpu_buffer_rsrc_t ro = rsrc_of(a.dout + qi * a.h * DV, obytes);
 #pragma unroll
-                    for (int r = 0; r < QPL; ++r)
-                        P.q[x][r] = __builtin_amdgcn_raw_buffer_load_b128(rq, goff + 1024u * r, 0, 0);
+                for (int r = 0; r < QPL; ++r)
+                    P.q[x][r] = __builtin_amdgcn_raw_buffer_load_b128(rq, goff + 1024u * r, 0, 0);
 #pragma unroll
-                    for (int r = 0; r < OPL; ++r)
-                        P.o[x][r] = __builtin_amdgcn_raw_buffer_load_b128(ro, goff + 1024u * r, 0, 0);
-                    continue;
-                }
-#pragma unroll
-                for (int r = 0; r < QPL; ++r) {
-                    const int gi = lane + 64 * r, hh = gi / QCH;
-                    u32x4 val = {0u, 0u, 0u, 0u};
-                    if (hh < a.h) val = ldg16(a.q + (qi * a.h + hh) * D + 8 * (gi % QCH));
-                    P.q[x][r] = val;
-                }
-#pragma unroll
-                for (int r = 0; r < OPL; ++r) {
-                    const int gi = lane + 64 * r, hh = gi / OCH;
-                    u32x4 val = {0u, 0u, 0u, 0u};
-                    if (hh < a.h) val = ldg16(a.dout + (qi * a.h + hh) * DV + 8 * (gi % OCH));
-                    P.o[x][r] = val;
-                }
+                for (int r = 0; r < OPL; ++r)
+                    P.o[x][r] = __builtin_amdgcn_raw_buffer_load_b128(ro, goff + 1024u * r, 0, 0);
             }
             const int64_t ql = a.row0 + ((lane >> 5) ? rowB : rowA);
             const int hl = lane & 15;
@@ -580,17 +577,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
                     for (int r = 0; r < OPL; ++r)
                         *reinterpret_cast<u32x4*>(so[x] + (((r ^ (r >> 1)) & 1) ? sbase1 : sbase0) +
                                                   4 * r * (DV + 16)) = P.o[x][r];
-                    continue;
-                }
+                } else {
+                    // (pieces of heads >= h hold zeros: their rows stay zero)
 #pragma unroll
-                for (int r = 0; r < QPL; ++r) {
-                    const int gi = lane + 64 * r, hh = gi / QCH;
-                    if (hh < a.h) *reinterpret_cast<u32x4*>(sq[x] + toff<D>(hh, 8 * (gi % QCH))) = P.q[x][r];
-                }
+                    for (int r = 0; r < QPL; ++r)
+                        *reinterpret_cast<u32x4*>(sq[x] + qst[r]) = P.q[x][r];
 #pragma unroll
-                for (int r = 0; r < OPL; ++r) {
-                    const int gi = lane + 64 * r, hh = gi / OCH;
-                    if (hh < a.h) *reinterpret_cast<u32x4*>(so[x] + toff<DV>(hh, 8 * (gi % OCH))) = P.o[x][r];
+                    for (int r = 0; r < OPL; ++r)
+                        *reinterpret_cast<u32x4*>(so[x] + ost[r]) = P.o[x][r];
                 }
             }
             sl[lane] = P.ld;
