@@ -439,6 +439,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
         // lane L keeps in `mine` the bits of its word that are entries of this
         // wave.  The words of the next window are loaded while this one is
         // consumed.
+        // token masks of the 4 slots (slots past s_k hold fewer or no tokens)
+        uint32_t slot_tokens = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t left = a.s_k - 4 * (4 * g + j);
+            const uint32_t m = left >= 4 ? 0xFu : (left > 0 ? (1u << left) - 1u : 0u);
+            slot_tokens |= m << (4 * j);
+        }
         const int nw = (a.rows + 31) / 32;
         // the 4 slots' words of one word column are one 16-byte piece (slots
         // past the last pool read as zero: the stride is padded to 4)
@@ -495,20 +503,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
             const int b = __builtin_ctz(cbits);
             cbits &= cbits - 1;
             row = 32 * (wbase + cl) + b;
+            // the entry's 4 slot bits, spread to nibbles, times the slots'
+            // token masks
+            const uint32_t b4 = ((cw[0] >> b) & 1u) | (((cw[1] >> b) & 1u) << 1) |
+                                (((cw[2] >> b) & 1u) << 2) | (((cw[3] >> b) & 1u) << 3);
+            const uint32_t spread = (b4 & 1u) | ((b4 & 2u) << 3) | ((b4 & 4u) << 6) | ((b4 & 8u) << 9);
+            mask = (spread * 0xFu) & slot_tokens;
             const int64_t t = a.q_pos0 + a.row0 + row;
-            mask = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (!((cw[j] >> b) & 1u)) continue;
-                const int64_t p = 4 * g + j;
-                const int64_t left = a.s_k - 4 * p;       // tokens of the slot
-                uint32_t m = left >= 4 ? 0xFu : (1u << left) - 1u;
-                if (p == (t >> 2)) {                      // own pool: the tail
-                    const int r = (int)(t & 3);
-                    const int u0 = max(0, r - a.n_tail);
-                    m &= ((1u << r) - 1u) & ~((1u << u0) - 1u);
-                }
-                mask |= m << (4 * j);
+            if ((t >> 4) == g) {
+                // the query's own pool is in this group (its bit comes from
+                // the tail only): the tail tokens before t
+                const int j = (int)((t >> 2) & 3);
+                const int r = (int)(t & 3);
+                const int u0 = max(0, r - a.n_tail);
+                const uint32_t tail = ((1u << r) - 1u) & ~((1u << u0) - 1u);
+                mask &= ~((~tail & 0xFu) << (4 * j));
             }
             return true;
         };
