@@ -71,6 +71,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
 
+// The same transposed read at a precomputed element offset.
+__device__ __forceinline__ u32x2 tr_at(const uint16_t* p) {
+    const v4i16 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+    return __builtin_bit_cast(u32x2, t4);
+}
+
 // ---------------------------------------------------------------- pass 1: dq
 
 struct DqK {
@@ -542,6 +548,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
         const int tbase = (lane >> 4) * (D + 16);
         const int sbase0 = tbase + ((lane & 15) << 3), sbase1 = tbase + (((lane & 15) ^ 1) << 3);
         int qst[ROWS128 ? 1 : QPL], ost[ROWS128 ? 1 : OPL];
+        // Lane offsets of the reads, fixed per lane: the A-operand piece of
+        // step s is toff(col, 32 s + 8 grp) = col (W + 16) + 32 s + 8 (grp ^
+        // b(col)); the transposed read of rows 4 grp .. +3 at element 16 m is
+        // toff(4 grp + col / 4, 16 m + 4 (col % 4)) = tr + 16 m.
+        const int bsw = ((col >> 2) ^ (col >> 3)) & 1;
+        const int qrd = col * (D + 16) + 8 * (grp ^ bsw);
+        const int ord = col * (DV + 16) + 8 * (grp ^ bsw);
+        const int trow = 4 * grp + (col >> 2), c3 = col & 3;
+        const int btr = ((trow >> 2) ^ (trow >> 3)) & 1;
+        const int qtr = trow * (D + 16) + 8 * ((c3 >> 1) ^ btr) + 4 * (c3 & 1);
+        const int otr = trow * (DV + 16) + 8 * ((c3 >> 1) ^ btr) + 4 * (c3 & 1);
         if constexpr (!ROWS128) {
 #pragma unroll
             for (int r = 0; r < QPL; ++r) {
@@ -625,12 +642,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
                 f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f}, pacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
-                    const u32x4 qa = *reinterpret_cast<const u32x4*>(sq[x] + toff<D>(col, 32 * s + 8 * grp));
+                    const u32x4 qa = *reinterpret_cast<const u32x4*>(sq[x] + qrd + 32 * s);
                     sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa), kf[s], sacc, 0, 0, 0);
                 }
 #pragma unroll
                 for (int s = 0; s < VS; ++s) {
-                    const u32x4 oa = *reinterpret_cast<const u32x4*>(so[x] + toff<DV>(col, 32 * s + 8 * grp));
+                    const u32x4 oa = *reinterpret_cast<const u32x4*>(so[x] + ord + 32 * s);
                     pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(oa), vf[s], pacc, 0, 0, 0);
                 }
                 // accumulator i: head 4 grp + i, token col
@@ -653,15 +670,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
             const bf16x8 pf = as_bf16x8(pw), df = as_bf16x8(dw);
 #pragma unroll
             for (int m = 0; m < MV; ++m) {
-                const u32x2 x0 = tr_read<DV>(so[0], 4 * grp, 16 * m, col);
-                const u32x2 x1 = tr_read<DV>(so[1], 4 * grp, 16 * m, col);
+                const u32x2 x0 = tr_at(so[0] + otr + 16 * m);
+                const u32x2 x1 = tr_at(so[1] + otr + 16 * m);
                 const u32x4 ow = {x0[0], x0[1], x1[0], x1[1]};
                 dva[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, as_bf16x8(ow), dva[m], 0, 0, 0);
             }
 #pragma unroll
             for (int m = 0; m < MK; ++m) {
-                const u32x2 x0 = tr_read<D>(sq[0], 4 * grp, 16 * m, col);
-                const u32x2 x1 = tr_read<D>(sq[1], 4 * grp, 16 * m, col);
+                const u32x2 x0 = tr_at(sq[0] + qtr + 16 * m);
+                const u32x2 x1 = tr_at(sq[1] + qtr + 16 * m);
                 const u32x4 qw = {x0[0], x0[1], x1[0], x1[1]};
                 dka[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(df, as_bf16x8(qw), dka[m], 0, 0, 0);
             }
