@@ -874,6 +874,16 @@ __global__ __launch_bounds__(NT, BOUNDS && LCAP == CAP ? 3 : 4) void topk_select
         const int nb = (LCAP == CAP && n > LONG_ROW ? SAMPLE_BLOCKS_LONG : SAMPLE_BLOCKS_SHORT) /
                        (BOUNDS ? 1 : 2);
         const int ns = nb * SAMPLE_LEN;
+        // b n / nb for the four block counts (a uniform branch; constant
+        // divisors become shifts and multiplications)
+        auto blk_start = [&](int64_t bn) -> int64_t {
+            switch (nb) {
+                case SAMPLE_BLOCKS_LONG: return bn / SAMPLE_BLOCKS_LONG;
+                case SAMPLE_BLOCKS_LONG / 2: return bn / (SAMPLE_BLOCKS_LONG / 2);
+                case SAMPLE_BLOCKS_SHORT: return bn / SAMPLE_BLOCKS_SHORT;
+                default: return bn / (SAMPLE_BLOCKS_SHORT / 2);
+            }
+        };
         // SU 16-byte pieces per thread in flight at once (ns / 4 is a
         // multiple of NT; the blocks lie inside the row)
         constexpr int SU = LCAP == CAP ? 6 : 4;
@@ -884,7 +894,7 @@ __global__ __launch_bounds__(NT, BOUNDS && LCAP == CAP ? 3 : 4) void topk_select
                 const int s4 = s0 + u * NT + tid;
                 if (s4 >= ns / 4) continue;
                 const int b = (4 * s4) / SAMPLE_LEN, o = (4 * s4) % SAMPLE_LEN;
-                const int64_t e = (((int64_t)b * n / nb) & ~(int64_t)(SAMPLE_LEN - 1)) + o;
+                const int64_t e = (blk_start((int64_t)b * n) & ~(int64_t)(SAMPLE_LEN - 1)) + o;
                 v[u] = *reinterpret_cast<const f32x4*>(row + e);
                 if constexpr (BOUNDS) {
                     mv[u][0] = *reinterpret_cast<const f32x4*>(a.mu + 2 * e);
