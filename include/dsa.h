@@ -11,8 +11,9 @@
  *   section "Making Sparse Attention Actually Sparse" -- NoPE heads are
  *     narrower than the rotary shapes and the pooled selection can return
  *     2,051 keys; unsupported shapes must not silently fall back to dense;
- *   section "Splitting the DSA Indexer / Over Time: Chunking" -- score and
- *     select a few hundred queries at a time so indexer memory is constant;
+ *   section "Splitting the DSA Indexer / Over Time: Chunking" -- queries are
+ *     scored and selected in chunks of hundreds, which bounds the indexer's
+ *     memory whatever the context length;
  *   section "Across GPUs: Sharding" -- the selected pool ids are small and
  *     are handed on as int32.
  * The page prints no score formula; the library computes the standard

@@ -5,7 +5,7 @@ it holds none of the method's arithmetic, so both the GPU path and the CPU
 oracle can consume its arrays.
 
 The workloads follow the shapes the SkyRL blog "Scaling Training to 1M Token
-Context on GLM-5.3-Flash" describes for GLM-5.3-Flash's DSA layers (section
+Context on GLM-5.3-Flash" describes for the DSA layers of GLM-5.3-Flash (section
 "DeepSeek Sparse Attention (DSA) Optimizations": pools of 4 tokens, 2048
 selected tokens; "Making Sparse Attention Actually Sparse": NoPE heads and
 2,051 keys; "Over Time: Chunking": a few hundred queries per chunk; "Across

@@ -17,7 +17,7 @@
  *   - section "Making Sparse Attention Actually Sparse": NoPE heads (no
  *     rotary channels, so narrower heads) and 2,051 selected keys;
  *   - section "Splitting the DSA Indexer / Over Time: Chunking": scores are
- *     fp32 and are scored and selected a few hundred queries at a time;
+ *     fp32, formed and selected for chunks of hundreds of queries;
  *   - section "Across GPUs: Sharding": selected pool indices are int32.
  * The page prints no formula for the indexer score.  The reading used here
  * is the standard lightning-indexer form: a head-weighted sum of ReLU'd dot

@@ -373,8 +373,8 @@ def test_fp8_scores_close_to_exact_scores():
 
 
 # ---------------------------------------------------------------- gated pooling
-# section "DSA: Gather by Token Position": k-pool gate scores weight each key
-# within a pool.  Reading: kbar_p = sum_r g[4p+r] k[4p+r] with caller-normalised
+# section "DSA: Gather by Token Position": each key of a pool is scaled by its
+# own k-pool gate score before the pool is formed.  Reading: kbar_p = sum_r g[4p+r] k[4p+r] with caller-normalised
 # gates; no gates means the mean.
 
 def test_gated_pooling_with_quarter_gates_is_the_mean():
