@@ -11,6 +11,7 @@ boundaries, a strided sweep, the first and last row of every chunk) with the
 default chunking, as the benchmark runs it.
 """
 import math
+import os
 import sys
 
 import numpy as np
@@ -74,17 +75,31 @@ def run_case(wl, rows=None, chunk_q=0, w_per_query=False, attention=True, seed=N
     pos = wl.q_pos0 + rows
     idx_g_rows = idx_all[rows]
     sc_g_rows = sc_g.cpu().numpy()[rows]
-    if fp8:
-        idx_o, sc_o = oracle.index_topk_fp8(x[qn], x[kn], x["w"], wl.k_pools, q_scale=scales[0],
-                                            k_scale=scales[1], q_pos0=wl.q_pos0, rows=rows,
-                                            gate=g_np)
-        s_o = oracle.index_scores_fp8(x[qn], x[kn], x["w"], q_scale=scales[0],
-                                      k_scale=scales[1], q_pos0=wl.q_pos0, rows=rows, gate=g_np)
+    def oracle_rows(rs):
+        if fp8:
+            i_o, c_o = oracle.index_topk_fp8(x[qn], x[kn], x["w"], wl.k_pools, q_scale=scales[0],
+                                             k_scale=scales[1], q_pos0=wl.q_pos0, rows=rs,
+                                             gate=g_np)
+            d_o = oracle.index_scores_fp8(x[qn], x[kn], x["w"], q_scale=scales[0],
+                                          k_scale=scales[1], q_pos0=wl.q_pos0, rows=rs, gate=g_np)
+        else:
+            i_o, c_o = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], wl.k_pools,
+                                         q_pos0=wl.q_pos0, rows=rs, gate=g_np)
+            d_o = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0, rows=rs,
+                                      gate=g_np)
+        return i_o, c_o, d_o
+
+    # long row lists go to the oracle in batches, each reported when done
+    batch = 256 if len(rows) > 512 else len(rows)
+    parts = []
+    for b0 in range(0, len(rows), max(1, batch)):
+        parts.append(oracle_rows(rows[b0:b0 + batch]))
+        if batch < len(rows):
+            _say(f"  oracle rows {min(len(rows), b0 + batch)}/{len(rows)}")
+    if parts:
+        idx_o, sc_o, s_o = (np.concatenate([p[j] for p in parts]) for j in range(3))
     else:
-        idx_o, sc_o = oracle.index_topk(x["q_idx"], x["k_idx"], x["w"], wl.k_pools,
-                                        q_pos0=wl.q_pos0, rows=rows, gate=g_np)
-        s_o = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], q_pos0=wl.q_pos0, rows=rows,
-                                  gate=g_np)
+        idx_o, sc_o, s_o = oracle_rows(rows)
     label = (f"{wl.name} (s_q={wl.s_q}, s_k={wl.s_k}, k={wl.k_pools}, chunk_q={chunk_q or 'default'}"
              f"{', fp8' if fp8 else ''}{', gated' if gate is not None else ''}"
              f"{', ' + tag if tag else ''})")
@@ -456,7 +471,7 @@ def test_workload_s32k_chunks_of_256_sampled():
 @pytest.mark.slow
 def test_workload_s128k_sampled():
     wl = inputs.WORKLOADS["s128k"]
-    run_case(wl, rows=_full_size_rows(wl, 1024))
+    run_case(wl, rows=_full_size_rows(wl, 2048))
 
 
 @pytest.mark.slow
@@ -487,6 +502,10 @@ def test_workload_nope_s64k_fp8_sampled():
 
 @pytest.mark.slow
 def test_workload_share_1m_sampled():
-    # at least one checked row in every selection launch (1536-query chunks)
+    # at least one checked row in every selection launch (1536-query chunks).
+    # The oracle needs about 2 s of one core per row at this size, so the
+    # default run checks a strided 128 plus the chunk ends; DSA_PARITY_WIDE=1
+    # checks 2048 strided rows plus the ends (several minutes of CPU).
     wl = inputs.WORKLOADS["share_1m"]
-    run_case(wl, rows=_full_size_rows(wl, 128))
+    n = 2048 if os.environ.get("DSA_PARITY_WIDE") == "1" else 128
+    run_case(wl, rows=_full_size_rows(wl, n), tag="wide" if n > 128 else "")
