@@ -168,19 +168,19 @@ def _sampled(name, n):
 
 @pytest.mark.slow
 def test_workload_s32k_sampled():
-    _sampled("s32k", 48)
+    _sampled("s32k", 256)
 
 
 @pytest.mark.slow
 def test_workload_s128k_sampled():
-    _sampled("s128k", 48)
+    _sampled("s128k", 512)
 
 
 @pytest.mark.slow
 def test_workload_nope_s64k_sampled():
-    _sampled("nope_s64k", 48)
+    _sampled("nope_s64k", 256)
 
 
 @pytest.mark.slow
 def test_workload_share_1m_sampled():
-    _sampled("share_1m", 32)
+    _sampled("share_1m", 256)
