@@ -184,3 +184,19 @@ def test_workload_nope_s64k_sampled():
 @pytest.mark.slow
 def test_workload_share_1m_sampled():
     _sampled("share_1m", 256)
+
+
+@pytest.mark.slow
+def test_workload_s128k_indexer_ids_sampled():
+    # the backward as the benchmark runs it: ids from the indexer on the
+    # workload's own keys (pools with large key norms are kept by many
+    # queries, so some pool groups walk far more entries than the rest)
+    wl = inputs.WORKLOADS["s128k"]
+    _say(f"[bwd] {wl.name}: ids from dsa_index_score_topk (k={wl.k_pools})")
+    x = inputs.make_inputs(wl, attention=False)
+    dev = torch.device("cuda")
+    idx, _ = dsa.dsa_index_score_topk(x["q_idx"].to(dev), x["k_idx"].to(dev), x["w"].to(dev),
+                                      wl.k_pools, q_pos0=wl.q_pos0)
+    idx = idx.cpu().numpy()
+    del x
+    run_bwd(wl, rows=inputs.sample_rows(wl.s_q, 256), idx=idx)
