@@ -408,12 +408,25 @@ __global__ __launch_bounds__(256) void pack_queries_kernel(const uint16_t* __res
     if (act) {
         *reinterpret_cast<u32x4*>(dst + T::bf16_piece(r, 2 * c)) = raw[0];
         *reinterpret_cast<u32x4*>(dst + T::bf16_piece(r, 2 * c + 1)) = raw[1];
+        // v_cvt_pk_fp8_f32 rounds to the nearest E4M3 value, ties to even,
+        // exactly as e4m3_code does for |x| <= 448 (the scaled row's range),
+        // and v_cvt_f32_fp8 decodes exactly; two codes per conversion
 #pragma unroll
-        for (int b = 0; b < 16; ++b) {
-            const uint32_t code = e4m3_code(ldexpf(x[b], -e));
-            const float v = e4m3_value(code);
-            n8 = fmaf(v, v, n8);
-            o[b >> 2] |= code << ((b & 3) * 8);
+        for (int j = 0; j < 4; ++j) {
+            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * j], -e), ldexpf(x[4 * j + 1], -e),
+                                                     0, false);
+            wd = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * j + 2], -e), ldexpf(x[4 * j + 3], -e),
+                                                 wd, true);
+            o[j] = (uint32_t)wd;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float v[4] = {__builtin_amdgcn_cvt_f32_fp8((int)o[j], 0),
+                                __builtin_amdgcn_cvt_f32_fp8((int)o[j], 1),
+                                __builtin_amdgcn_cvt_f32_fp8((int)o[j], 2),
+                                __builtin_amdgcn_cvt_f32_fp8((int)o[j], 3)};
+#pragma unroll
+            for (int b = 0; b < 4; ++b) n8 = fmaf(v[b], v[b], n8);
         }
         *reinterpret_cast<u32x4*>(dst + T::fp8_piece(r, c)) = o;
     }

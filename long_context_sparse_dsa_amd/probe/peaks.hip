@@ -11,6 +11,10 @@
 //                 read once measures memory read bandwidth.
 // The caller times one launch with events on `stream`; the library returns
 // the algorithmic work of that launch.
+//   e4m3       -- not a rate: the matrix-core E4M3 conversions the query
+//                 packing uses (v_cvt_pk_fp8_f32, v_cvt_f32_fp8) applied to
+//                 a caller's list of floats, for a test against the
+//                 definition of the format.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -80,6 +84,18 @@ __global__ __launch_bounds__(256) void read16(const u32x4* __restrict__ src, int
     if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9E3779B9u) sink[threadIdx.x] = acc[0];
 }
 
+// code[i] = the E4M3 code v_cvt_pk_fp8_f32 gives x[i]; value[i] = that
+// code decoded by v_cvt_f32_fp8.
+__global__ __launch_bounds__(256) void e4m3_round_trip(const float* x, uint8_t* code,
+                                                       float* value, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int c = __builtin_amdgcn_cvt_pk_fp8_f32(x[i], 0.0f, 0, false) & 0xFF;
+        code[i] = (uint8_t)c;
+        value[i] = __builtin_amdgcn_cvt_f32_fp8(c, 0);
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,6 +130,15 @@ int dsa_probe_read(const void* src, int64_t bytes, int passes, uint32_t* sink, v
         return 1;
     read16<<<256 * 8, 256, 0, static_cast<hipStream_t>(stream)>>>(
         static_cast<const u32x4*>(src), bytes / 16, passes, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// x: n floats; code: n bytes; value: n floats (device memory).
+int dsa_probe_e4m3(const float* x, uint8_t* code, float* value, int64_t n, void* stream) {
+    if (!x || !code || !value || n < 0) return 1;
+    if (n == 0) return 0;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    e4m3_round_trip<<<(unsigned)blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(x, code, value, n);
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

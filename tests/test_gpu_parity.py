@@ -431,6 +431,41 @@ def test_k_and_v_may_alias():
     run_case(wl, chunk_q=64, x=x)
 
 
+def test_hardware_e4m3_conversion_matches_the_format_definition():
+    # The query packing encodes its scaled rows (bf16 values times a power of
+    # two, |x| <= 448) with v_cvt_pk_fp8_f32 and decodes them with
+    # v_cvt_f32_fp8.  Both against the oracle's E4M3 definition (nearest
+    # value, ties to the even mantissa, sign kept): every bf16 value up to
+    # 448, float32 subnormals, and random float32 values up to 448.
+    import ctypes
+    import os
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(dsa.__file__), "libdsa_peaks.so"))
+    lib.dsa_probe_e4m3.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_void_p]
+    bf = (np.arange(1 << 16, dtype=np.uint32) << 16).view(np.float32)
+    rng = np.random.default_rng(977)
+    sub = (rng.integers(1, 1 << 23, 2000, dtype=np.uint32) |
+           (rng.integers(0, 2, 2000, dtype=np.uint32) << 31)).view(np.float32)
+    rnd = rng.uniform(-448.0, 448.0, 100000).astype(np.float32)
+    x = np.concatenate([bf, sub, rnd])
+    x = x[np.isfinite(x) & (np.abs(x) <= 448.0)]
+    _say(f"[case] hardware E4M3 round trip of {len(x)} floats")
+    dev = torch.device("cuda")
+    xd = torch.from_numpy(x).to(dev)
+    code = torch.empty(len(x), dtype=torch.uint8, device=dev)
+    val = torch.empty(len(x), dtype=torch.float32, device=dev)
+    rc = lib.dsa_probe_e4m3(xd.data_ptr(), code.data_ptr(), val.data_ptr(), len(x),
+                            torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    code, val = code.cpu().numpy(), val.cpu().numpy()
+    want = np.array([oracle.e4m3_encode(float(v)) for v in x], dtype=np.uint8)
+    bad = np.flatnonzero(code != want)
+    assert bad.size == 0, (f"{bad.size} codes differ, first x={x[bad[0]]!r}: "
+                           f"hardware 0x{code[bad[0]]:02x}, definition 0x{want[bad[0]]:02x}")
+    dec = np.array([oracle.e4m3_value(int(c)) for c in range(256)], dtype=np.float64)
+    assert np.array_equal(val.astype(np.float64), dec[code])
+
+
 @pytest.mark.parametrize("h_idx,d_idx,scales", [
     (32, 96, (1.0, 1.0)), (32, 128, (0.5, 2.0)), (4, 64, (1.0, 1.0)), (16, 96, (-1.5, 0.25)),
     (8, 128, (3.0, 1.0)),
