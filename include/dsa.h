@@ -107,7 +107,8 @@ dsa_status dsa_index_workspace_size(int64_t s_q, int64_t s_k, int h_idx, int d_i
  *   score_out [s_q, k_pools] fp32  optional (NULL): the kept pools' scores,
  *                                  -inf for padding
  *   workspace                      >= dsa_index_workspace_size(...) bytes
- * Supported: h_idx in {4, 8, 16, 32}; d_idx in {64, 96, 128}; s_k < 2^31.
+ * Supported: h_idx in {4, 8, 16, 32}; d_idx in {64, 96, 128}; s_q, s_k < 2^31;
+ * q_pos0 < 2^40.
  * The fp32 score of a pool is a +0.0 when zero (never -0.0).
  * bf16 indexer: the score of a pool is q . hi on bf16 matrix cores plus the
  * correction q . lo on scaled E4M3 matrix cores, exactly as

@@ -121,7 +121,9 @@ dsa_status check_index_shape(const IndexShape& sh, bool need_k) {
                     (long long)sh.s_q, (long long)sh.s_k, (long long)sh.q_pos0);
     if (sh.s_k >= (int64_t(1) << 31) || sh.s_q >= (int64_t(1) << 31) ||
         sh.q_pos0 >= (int64_t(1) << 40))
-        return fail(DSA_ERR_UNSUPPORTED, "s_q and s_k must be below 2^31");
+        return fail(DSA_ERR_UNSUPPORTED,
+                    "s_q and s_k must be below 2^31 and q_pos0 below 2^40 (s_q=%lld s_k=%lld "
+                    "q_pos0=%lld)", (long long)sh.s_q, (long long)sh.s_k, (long long)sh.q_pos0);
     if (sh.pool_size != 4)
         return fail(DSA_ERR_UNSUPPORTED, "pool_size %d: only pools of 4 tokens are supported",
                     sh.pool_size);
