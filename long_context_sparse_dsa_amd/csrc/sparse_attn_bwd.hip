@@ -312,24 +312,30 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(DqK a) {
 // `stride` slots, a multiple of 4) is set when chunk query row r attends a
 // token of pool slot `slot` -- a kept pool id in [0, P), or its own pool when
 // it has tail tokens there.  One workgroup per (word column c, range of
-// BITS_RANGE slots): its 32 query rows OR their bits into an LDS copy of the
+// `range` slots): its 32 query rows OR their bits into an LDS copy of the
 // range with LDS atomics (the same bits in any order), then it writes every
-// word of the range, zeros included, so the bitmap needs no clearing.
-constexpr int BITS_RANGE = 16384;  // 64 KiB of LDS
+// word of the range, zeros included, so the bitmap needs no clearing.  The
+// launcher narrows the range (16384 slots, 64 KiB of LDS, down to 2048) until
+// the launch has about a thousand workgroups; every workgroup reads all ids
+// of its 32 rows and keeps those in its range.
+constexpr int BITS_RANGE_MAX = 16384;
+constexpr int BITS_RANGE_MIN = 2048;
 
 __global__ __launch_bounds__(256) void bwd_select_bits_kernel(
     const int32_t* __restrict__ idx, int k_pools, int64_t row0, int rows, int64_t q_pos0,
-    int64_t n_pools, int64_t s_k, int n_tail, uint32_t* bits, int64_t stride) {
-    __shared__ __attribute__((aligned(16))) uint32_t lw[BITS_RANGE];
+    int64_t n_pools, int64_t s_k, int n_tail, uint32_t* bits, int64_t stride, int range) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t lw[];  // range words
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = (int)blockIdx.x;
-    const int64_t s0 = (int64_t)blockIdx.y * BITS_RANGE;
-    const int64_t s1 = s0 + BITS_RANGE < stride ? s0 + BITS_RANGE : stride;
+    const int64_t s0 = (int64_t)blockIdx.y * range;
+    const int64_t s1 = s0 + range < stride ? s0 + range : stride;
     const int width = (int)(s1 - s0);  // a multiple of 4
-    for (int e = 4 * tid; e < BITS_RANGE; e += 4 * 256)
+    const int64_t p_end = s1 < n_pools ? s1 : n_pools;  // kept ids in [s0, p_end) count
+    for (int e = 4 * tid; e < width; e += 4 * 256)
         *reinterpret_cast<u32x4*>(lw + e) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
-    // rows 32 c + 8 wave .. +7 of the chunk
+    // rows 32 c + 8 wave .. +7 of the chunk; each row's ids are loaded 8 per
+    // lane at a time, all in flight before the first atomic
     for (int rr = 0; rr < 8; ++rr) {
         const int r = 8 * wave + rr;
         const int row = 32 * c + r;
@@ -337,9 +343,16 @@ __global__ __launch_bounds__(256) void bwd_select_bits_kernel(
         const int64_t i = row0 + row;
         const uint32_t bit = 1u << r;
         const int32_t* irow = idx + i * k_pools;
-        for (int j = lane; j < k_pools; j += 64) {
-            const int32_t p = irow[j];
-            if (p >= 0 && (int64_t)p < n_pools && p >= s0 && p < s1) atomicOr(&lw[p - s0], bit);
+        for (int j0 = 0; j0 < k_pools; j0 += 512) {
+            int32_t pv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + lane + 64 * u;
+                pv[u] = j < k_pools ? irow[j] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (pv[u] >= s0 && pv[u] < p_end) atomicOr(&lw[pv[u] - s0], bit);
         }
         const int64_t t = q_pos0 + i;
         const int64_t own = t >> 2;
@@ -770,9 +783,13 @@ hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_attn_bwd_bits(const AttnBwdArgs& a, int64_t row0, int rows, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((rows + 31) / 32), (unsigned)((a.stride + BITS_RANGE - 1) / BITS_RANGE));
-    bwd_select_bits_kernel<<<grid, 256, 0, stream>>>(a.idx, a.k_pools, row0, rows, a.q_pos0,
-                                                     a.s_k / 4, a.s_k, a.n_tail, a.bits, a.stride);
+    const int64_t cols = (rows + 31) / 32;
+    int range = BITS_RANGE_MAX;
+    while (range > BITS_RANGE_MIN && cols * ((a.stride + range - 1) / range) < 1024) range /= 2;
+    const dim3 grid((unsigned)cols, (unsigned)((a.stride + range - 1) / range));
+    bwd_select_bits_kernel<<<grid, 256, (size_t)range * 4u, stream>>>(
+        a.idx, a.k_pools, row0, rows, a.q_pos0, a.s_k / 4, a.s_k, a.n_tail, a.bits, a.stride,
+        range);
     return hipGetLastError();
 }
 
