@@ -236,9 +236,13 @@ dsa_status dsa_sparse_attn_fwd(const void *q, const void *k, const void *v, cons
  * Bytes of device workspace dsa_sparse_attn_bwd needs: delta = dout . out
  * per query and head (fp32 [s_q, h], rounded up to 256 bytes), then the
  * bitmap that transposes one chunk of queries' selections, chunk_q / 32 rows
- * of ceil(s_k / 4) 32-bit words (rounded up to a multiple of 4).  chunk_q = 0
+ * of ceil(s_k / 4) 32-bit words (rounded up to a multiple of 4; the bitmap
+ * rounded up to 256 bytes), then two arrays of one 32-bit word per group of 4
+ * pools (ceil(ceil(s_k / 4) / 4) words each, rounded up to 256 bytes): the
+ * groups' entry counts and the order the key-major pass takes them in.
+ * chunk_q = 0
  * picks the default,
- * max(2048, ceil(s_k / 4) / 32) rounded up to a multiple of 64, at most 16384
+ * max(1024, ceil(s_k / 4) / 32) rounded up to a multiple of 64, at most 16384
  * and at most s_q rounded up to 64, returned through *chunk_q_used when that
  * pointer is non-NULL; otherwise a multiple of 64 up to 65536 whose bitmap
  * stays within 2 GiB.  Pure host computation.

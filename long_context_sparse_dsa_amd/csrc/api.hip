@@ -326,12 +326,13 @@ dsa_status check_attn_shape(int64_t s_q, int64_t s_k, int64_t q_pos0, int h, int
 
 // Backward: queries per transposition chunk (a multiple of 64), and the
 // workspace: delta [s_q, h] fp32, then the chunk bitmap
-// [ceil(s_k / 4)][chunk / 32] words.  Default chunk: max(2048, pool slots /
-// 32), at most 16384.  Every chunk pays a pass of the key-major kernel over
-// all pool slots, so the chunk grows with them; smaller chunks keep more of
-// a chunk's query rows in the L2s.  (Measured best of 512 .. 32768: 2048 at
-// 8K, 16K and 32K slots, 8192 at 262144 slots.)
-constexpr int64_t kBwdChunkMin = 2048;
+// [chunk / 32][ceil(s_k / 4)] words, then the pool groups' entry counts and
+// order.  Default chunk: max(1024, pool slots / 32), at most 16384.  Every
+// chunk pays a pass of the key-major kernel over all pool slots, so the chunk
+// grows with them; smaller chunks keep more of a chunk's query rows in the
+// L2s.  (Measured best of 256 .. 16384 with the pool groups taken most
+// entries first: 1024 at 8K, 16K and 32K slots, 8192 to 16384 at 262144.)
+constexpr int64_t kBwdChunkMin = 1024;
 constexpr int64_t kBwdChunkMax = 16384;
 constexpr int64_t kBwdBitmapCap = int64_t(2) << 30;
 
@@ -354,7 +355,8 @@ dsa_status bwd_layout(int64_t s_q, int64_t s_k, int h, int64_t chunk_q, int64_t*
                     (long long)chunk_q, (long long)bits);
     *chunk_used = chunk_q;
     *delta_bytes = round_up(s_q * h * 4, 256);
-    *bits_bytes = bits;
+    // the bitmap, then the pool groups' entry counts and their order
+    *bits_bytes = round_up(bits, 256) + 2 * round_up(round_up(slots, 4) / 4 * 4, 256);
     return DSA_OK;
 }
 
@@ -795,12 +797,25 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
     a.delta = reinterpret_cast<float*>(ws);
     a.bits = reinterpret_cast<uint32_t*>(ws + db);
     a.stride = round_up((s_k + 3) / 4, 4);
+    const int64_t bitmap_bytes = round_up(a.stride * (cq / 32) * 4, 256);
+    const int64_t group_bytes = round_up(a.stride / 4 * 4, 256);
+    a.group_counts = reinterpret_cast<uint32_t*>(ws + db + bitmap_bytes);
+    a.group_order = reinterpret_cast<int32_t*>(ws + db + bitmap_bytes + group_bytes);
     {
         Timed tm(K_BWD_DQ, s);
         hipError_t e = dsa::launch_attn_bwd_dq(a, s);
         if (e != hipSuccess) return hip_fail(e, "attn_bwd_dq launch");
     }
     if (s_k == 0) return DSA_OK;
+    {
+        // the order of the pool groups, from the bitmap of the last chunk
+        // (its queries see every pool the others see)
+        Timed tm(K_BWD_BITS, s);
+        const int64_t last0 = (s_q - 1) / cq * cq;
+        hipError_t e = dsa::launch_attn_bwd_bits(a, last0, (int)(s_q - last0), s);
+        if (e == hipSuccess) e = dsa::launch_attn_bwd_order(a, (int)(s_q - last0), s);
+        if (e != hipSuccess) return hip_fail(e, "attn_bwd_select launch");
+    }
     for (int64_t r0 = 0, c = 0; r0 < s_q; r0 += cq, ++c) {
         const int rows = (int)(s_q - r0 < cq ? s_q - r0 : cq);
         {

@@ -331,28 +331,45 @@ __global__ __launch_bounds__(256) void bwd_select_bits_kernel(
     const int64_t s1 = s0 + range < stride ? s0 + range : stride;
     const int width = (int)(s1 - s0);  // a multiple of 4
     const int64_t p_end = s1 < n_pools ? s1 : n_pools;  // kept ids in [s0, p_end) count
+    // rows 32 c + 8 wave .. +7 of the chunk: the first 512 ids of all 8 rows
+    // (8 per lane and row) are loaded at once, while the range is cleared and
+    // before the first atomic; ids past 512 follow row by row, 8 per lane at
+    // a time
+    int32_t pv[8][8];
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+        const int row = 32 * c + 8 * wave + rr;
+        const int32_t* irow = idx + (row0 + row) * k_pools;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = lane + 64 * u;
+            pv[rr][u] = row < rows && j < k_pools ? irow[j] : -1;
+        }
+    }
     for (int e = 4 * tid; e < width; e += 4 * 256)
         *reinterpret_cast<u32x4*>(lw + e) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
-    // rows 32 c + 8 wave .. +7 of the chunk; each row's ids are loaded 8 per
-    // lane at a time, all in flight before the first atomic
+#pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
         const int r = 8 * wave + rr;
         const int row = 32 * c + r;
         if (row >= rows) break;
         const int64_t i = row0 + row;
         const uint32_t bit = 1u << r;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (pv[rr][u] >= s0 && pv[rr][u] < p_end) atomicOr(&lw[pv[rr][u] - s0], bit);
         const int32_t* irow = idx + i * k_pools;
-        for (int j0 = 0; j0 < k_pools; j0 += 512) {
-            int32_t pv[8];
+        for (int j0 = 512; j0 < k_pools; j0 += 512) {
+            int32_t pw[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int j = j0 + lane + 64 * u;
-                pv[u] = j < k_pools ? irow[j] : -1;
+                pw[u] = j < k_pools ? irow[j] : -1;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (pv[u] >= s0 && pv[u] < p_end) atomicOr(&lw[pv[u] - s0], bit);
+                if (pw[u] >= s0 && pw[u] < p_end) atomicOr(&lw[pw[u] - s0], bit);
         }
         const int64_t t = q_pos0 + i;
         const int64_t own = t >> 2;
@@ -365,6 +382,46 @@ __global__ __launch_bounds__(256) void bwd_select_bits_kernel(
         *reinterpret_cast<u32x4*>(dst + e) = *reinterpret_cast<const u32x4*>(lw + e);
 }
 
+// Entries per pool group in the bitmap of one chunk (nw word rows): the set
+// bits of the OR of the group's 4 slot rows.
+__global__ __launch_bounds__(256) void bwd_group_counts_kernel(const uint32_t* __restrict__ bits,
+                                                               int64_t stride, int nw,
+                                                               int64_t groups, uint32_t* counts) {
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= groups) return;
+    uint32_t c = 0;
+#pragma unroll 8
+    for (int w = 0; w < nw; ++w) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(bits + (int64_t)w * stride + 4 * g);
+        c += __popc(x[0] | x[1] | x[2] | x[3]);
+    }
+    counts[g] = c;
+}
+
+// The pool groups in decreasing order of their entry counts, bucketed by the
+// highest set bit of the count (the order inside a bucket is arbitrary: each
+// group's gradients are formed by one workgroup whatever its position).
+__global__ __launch_bounds__(1024) void bwd_group_order_kernel(const uint32_t* __restrict__ counts,
+                                                               int64_t groups, int32_t* order) {
+    __shared__ uint32_t hist[33], off[33];
+    const int tid = threadIdx.x;
+    if (tid < 33) hist[tid] = 0u;
+    __syncthreads();
+    auto bucket = [](uint32_t c) { return c ? 32 - __builtin_clz(c) : 0; };
+    for (int64_t g = tid; g < groups; g += 1024) atomicAdd(&hist[bucket(counts[g])], 1u);
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t sum = 0u;
+        for (int b = 32; b >= 0; --b) {
+            off[b] = sum;
+            sum += hist[b];
+        }
+    }
+    __syncthreads();
+    for (int64_t g = tid; g < groups; g += 1024)
+        order[atomicAdd(&off[bucket(counts[g])], 1u)] = (int32_t)g;
+}
+
 // ---------------------------------------------------------------- pass 2: dk, dv
 
 struct DkvK {
@@ -374,6 +431,7 @@ struct DkvK {
     const uint16_t* dout;
     const float* lse;
     const float* delta;
+    const int32_t* order;   // pool groups in the order workgroups take them
     const uint32_t* bits;   // [chunk / 32][stride]
     int64_t stride;
     int64_t s_k, q_pos0, row0;
@@ -414,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int col = lane & 15, grp = lane >> 4;
-    const int64_t g = blockIdx.x;
+    const int64_t g = a.order[blockIdx.x];
     const int64_t tok0 = 16 * g;
     const int64_t t_last = a.q_pos0 + a.row0 + a.rows - 1;
     uint16_t* st = stage_all + wave * STAGE;
@@ -793,6 +851,15 @@ hipError_t launch_attn_bwd_bits(const AttnBwdArgs& a, int64_t row0, int rows, hi
     return hipGetLastError();
 }
 
+hipError_t launch_attn_bwd_order(const AttnBwdArgs& a, int rows, hipStream_t stream) {
+    const int64_t groups = a.stride / 4;
+    if (groups <= 0 || rows <= 0) return hipSuccess;
+    bwd_group_counts_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, stream>>>(
+        a.bits, a.stride, (rows + 31) / 32, groups, a.group_counts);
+    bwd_group_order_kernel<<<1, 1024, 0, stream>>>(a.group_counts, groups, a.group_order);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn_bwd_dkv(const AttnBwdArgs& a, int64_t row0, int rows, int accumulate,
                                hipStream_t stream) {
     const int64_t slots = (a.s_k + 3) / 4;
@@ -804,6 +871,7 @@ hipError_t launch_attn_bwd_dkv(const AttnBwdArgs& a, int64_t row0, int rows, int
     k.dout = a.dout;
     k.lse = a.lse;
     k.delta = a.delta;
+    k.order = a.group_order;
     k.bits = a.bits;
     k.stride = a.stride;
     k.s_k = a.s_k;

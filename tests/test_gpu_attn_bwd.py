@@ -103,12 +103,12 @@ SMALL = [
     (200, 203, 0, 1, 64, 128, 5, 2, 64),       # one head, s_k with a partial pool
     (333, 1000, 667, 5, 128, 96, 40, 1, 64),   # queries late in the sequence
     (129, 131, 2, 16, 128, 64, 64, 3, 0),      # k covers every pool: dense causal
-    (2500, 2500, 0, 2, 64, 64, 4, 1, 0),       # 80 bitmap words per chunk: two scan windows
-    (3000, 3001, 0, 16, 96, 96, 6, 3, 2048),   # two chunks, several windows each
+    (2500, 2500, 0, 2, 64, 64, 4, 1, 2560),    # 80 bitmap words per chunk: two scan windows
+    (3000, 3001, 0, 16, 96, 96, 6, 3, 2048),   # two chunks (2048 and 952 queries)
     # 282 bitmap words in one chunk (five scan windows of 64 words); the first
     # pools are kept by nearly every query, so the first pool groups walk
     # thousands of entries
-    (9000, 9000, 0, 2, 64, 64, 512, 1, 0),
+    (9000, 9000, 0, 2, 64, 64, 512, 1, 9024),
     (2600, 2600, 0, 4, 128, 128, 200, 3, 0),   # about 1700 entries in the first groups
 ]
 
