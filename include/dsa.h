@@ -235,9 +235,10 @@ dsa_status dsa_sparse_attn_fwd(const void *q, const void *k, const void *v, cons
 /*
  * Bytes of device workspace dsa_sparse_attn_bwd needs: delta = dout . out
  * per query and head (fp32 [s_q, h], rounded up to 256 bytes), then the
- * bitmap that transposes one chunk of queries' selections, chunk_q / 32 rows
- * of ceil(s_k / 4) 32-bit words (rounded up to a multiple of 4; the bitmap
- * rounded up to 256 bytes), then two arrays of one 32-bit word per group of 4
+ * bitmap that transposes the queries' selections, chunk_q / 32 rows of
+ * ceil(s_k / 4) 32-bit words (rounded up to a multiple of 4) per chunk, for
+ * every chunk when that takes at most 1 GiB, else for one chunk (rounded up
+ * to 256 bytes), then two arrays of one 32-bit word per group of 4
  * pools (ceil(ceil(s_k / 4) / 4) words each, rounded up to 256 bytes): the
  * groups' entry counts and the order the key-major pass takes them in.
  * chunk_q = 0

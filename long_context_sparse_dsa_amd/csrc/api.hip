@@ -333,6 +333,9 @@ dsa_status check_attn_shape(int64_t s_q, int64_t s_k, int64_t q_pos0, int h, int
 // L2s.  (Measured best of 256 .. 16384 with the pool groups taken most
 // entries first: 1024 at 8K, 16K and 32K slots, 8192 to 16384 at 262144.)
 constexpr int64_t kBwdChunkMin = 1024;
+// The bitmaps of all chunks are built by one launch when together they take
+// at most this many bytes (else one chunk's bitmap at a time).
+constexpr int64_t kBwdBitmapAll = int64_t(1) << 30;
 constexpr int64_t kBwdChunkMax = 16384;
 constexpr int64_t kBwdBitmapCap = int64_t(2) << 30;
 
@@ -353,10 +356,14 @@ dsa_status bwd_layout(int64_t s_q, int64_t s_k, int h, int64_t chunk_q, int64_t*
     if (bits > kBwdBitmapCap)
         return fail(DSA_ERR_UNSUPPORTED, "chunk_q %lld: the chunk bitmap (%lld bytes) exceeds 2 GiB",
                     (long long)chunk_q, (long long)bits);
+    const int64_t nchunks = s_q > 0 ? (s_q + chunk_q - 1) / chunk_q : 1;
+    const int64_t all = bits * nchunks;
     *chunk_used = chunk_q;
     *delta_bytes = round_up(s_q * h * 4, 256);
-    // the bitmap, then the pool groups' entry counts and their order
-    *bits_bytes = round_up(bits, 256) + 2 * round_up(round_up(slots, 4) / 4 * 4, 256);
+    // the bitmap (of every chunk when that fits kBwdBitmapAll), then the pool
+    // groups' entry counts and their order
+    *bits_bytes = round_up(all <= kBwdBitmapAll ? all : bits, 256) +
+                  2 * round_up(round_up(slots, 4) / 4 * 4, 256);
     return DSA_OK;
 }
 
@@ -797,7 +804,10 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
     a.delta = reinterpret_cast<float*>(ws);
     a.bits = reinterpret_cast<uint32_t*>(ws + db);
     a.stride = round_up((s_k + 3) / 4, 4);
-    const int64_t bitmap_bytes = round_up(a.stride * (cq / 32) * 4, 256);
+    const int64_t chunk_bits = a.stride * (cq / 32) * 4;
+    const int64_t nchunks = (s_q + cq - 1) / cq;
+    const bool all_bits = chunk_bits * nchunks <= kBwdBitmapAll;
+    const int64_t bitmap_bytes = round_up(all_bits ? chunk_bits * nchunks : chunk_bits, 256);
     const int64_t group_bytes = round_up(a.stride / 4 * 4, 256);
     a.group_counts = reinterpret_cast<uint32_t*>(ws + db + bitmap_bytes);
     a.group_order = reinterpret_cast<int32_t*>(ws + db + bitmap_bytes + group_bytes);
@@ -807,18 +817,33 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
         if (e != hipSuccess) return hip_fail(e, "attn_bwd_dq launch");
     }
     if (s_k == 0) return DSA_OK;
+    // the bitmap word rows of chunk query rows from r0 on (every chunk's
+    // rows in one array when they fit, else the one chunk's)
+    uint32_t* const bits0 = a.bits;
+    auto chunk_bits_at = [&](int64_t r0) {
+        return all_bits ? bits0 + (r0 / 32) * a.stride : bits0;
+    };
     {
-        // the order of the pool groups, from the bitmap of the last chunk
+        // every chunk's bitmap when they fit (one launch), else the last
+        // chunk's; the order of the pool groups comes from the last chunk's
         // (its queries see every pool the others see)
         Timed tm(K_BWD_BITS, s);
         const int64_t last0 = (s_q - 1) / cq * cq;
-        hipError_t e = dsa::launch_attn_bwd_bits(a, last0, (int)(s_q - last0), s);
+        hipError_t e;
+        if (all_bits) {
+            a.bits = bits0;
+            e = dsa::launch_attn_bwd_bits(a, 0, (int)s_q, s);
+        } else {
+            e = dsa::launch_attn_bwd_bits(a, last0, (int)(s_q - last0), s);
+        }
+        a.bits = chunk_bits_at(last0);
         if (e == hipSuccess) e = dsa::launch_attn_bwd_order(a, (int)(s_q - last0), s);
         if (e != hipSuccess) return hip_fail(e, "attn_bwd_select launch");
     }
     for (int64_t r0 = 0, c = 0; r0 < s_q; r0 += cq, ++c) {
         const int rows = (int)(s_q - r0 < cq ? s_q - r0 : cq);
-        {
+        a.bits = chunk_bits_at(r0);
+        if (!all_bits) {
             Timed tm(K_BWD_BITS, s);
             hipError_t e = dsa::launch_attn_bwd_bits(a, r0, rows, s);
             if (e != hipSuccess) return hip_fail(e, "attn_bwd_select launch");
