@@ -824,20 +824,23 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
         return all_bits ? bits0 + (r0 / 32) * a.stride : bits0;
     };
     {
-        // every chunk's bitmap when they fit (one launch), else the last
-        // chunk's; the order of the pool groups comes from the last chunk's
-        // (its queries see every pool the others see)
+        // every chunk's bitmap when they fit (one launch); the order of the
+        // pool groups comes from the selections of the last chunk_q queries
+        // (from a word boundary: they see every pool the others see, and a
+        // short last chunk does not make the order arbitrary), built on their
+        // own when the bitmaps do not fit
         Timed tm(K_BWD_BITS, s);
-        const int64_t last0 = (s_q - 1) / cq * cq;
+        const int64_t w0 = s_q > cq ? round_up(s_q - cq, 32) : 0;
         hipError_t e;
         if (all_bits) {
             a.bits = bits0;
             e = dsa::launch_attn_bwd_bits(a, 0, (int)s_q, s);
+            a.bits = bits0 + (w0 / 32) * a.stride;
         } else {
-            e = dsa::launch_attn_bwd_bits(a, last0, (int)(s_q - last0), s);
+            a.bits = bits0;
+            e = dsa::launch_attn_bwd_bits(a, w0, (int)(s_q - w0), s);
         }
-        a.bits = chunk_bits_at(last0);
-        if (e == hipSuccess) e = dsa::launch_attn_bwd_order(a, (int)(s_q - last0), s);
+        if (e == hipSuccess) e = dsa::launch_attn_bwd_order(a, (int)(s_q - w0), s);
         if (e != hipSuccess) return hip_fail(e, "attn_bwd_select launch");
     }
     for (int64_t r0 = 0, c = 0; r0 < s_q; r0 += cq, ++c) {
