@@ -1,8 +1,8 @@
 """Parity rules between the GPU path and the CPU oracle.
 
 Index sets (pages: SkyRL blog, section "DeepSeek Sparse Attention (DSA)
-Optimizations" -- keep the best pools; the tolerance below is this build's
-reading of "exact up to the selection boundary"):
+Optimizations" -- keep the best pools; the sets must be exact except where
+pools tie at the k-th score to within rounding, read as the band below):
   * rows with n(t) <= k must equal [0 .. n(t)-1] padded with -1, exactly;
   * other rows must hold k distinct, ascending, eligible ids, and the
     symmetric difference with the oracle's set may only contain pools whose
