@@ -382,8 +382,8 @@ __global__ __launch_bounds__(256) void bwd_select_bits_kernel(
         *reinterpret_cast<u32x4*>(dst + e) = *reinterpret_cast<const u32x4*>(lw + e);
 }
 
-// Entries per pool group in the bitmap of one chunk (nw word rows): the set
-// bits of the OR of the group's 4 slot rows.
+// Entries per pool group in nw word rows of the bitmap (32 queries each):
+// the set bits of the OR of the group's 4 slot rows.
 __global__ __launch_bounds__(256) void bwd_group_counts_kernel(const uint32_t* __restrict__ bits,
                                                                int64_t stride, int nw,
                                                                int64_t groups, uint32_t* counts) {
