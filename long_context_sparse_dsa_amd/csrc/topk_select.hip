@@ -62,12 +62,12 @@ constexpr int NT = 256;
 // lists are larger, and the other shapes a 4096-entry list (3 per CU)
 constexpr int CAP = 4096;
 constexpr int CAP_SHORT = 3072;
-constexpr int SAMPLE_LEN = 16;
+constexpr int SAMPLE_LEN = 32;  // one 128-byte line of fp32 scores per block
 // sample blocks of SAMPLE_LEN: more for long rows, where k is a smaller
 // fraction of the row, and twice as many for bounded rows, whose threshold
 // takes a wider margin (the sample lives in the three list arrays)
-constexpr int SAMPLE_BLOCKS_SHORT = 128;
-constexpr int SAMPLE_BLOCKS_LONG = 384;
+constexpr int SAMPLE_BLOCKS_SHORT = 64;
+constexpr int SAMPLE_BLOCKS_LONG = 192;
 constexpr int64_t LONG_ROW = 65536;
 // rows up to this many pools go whole to the list (bounded rows: the list's
 // capacity), longer ones take the sample; the sample's blocks then lie
