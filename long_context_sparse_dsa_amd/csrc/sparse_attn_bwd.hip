@@ -15,13 +15,16 @@
 //   1. Query-major, the forward's gather: one wave per query walks its
 //      tokens in tiles of 32 slots and forms D and dq.
 //   2. Pool-major: the gradient of a key row sums over the queries that
-//      attend it.  One chunk of queries at a time, the selections are
-//      transposed into a bitmap [chunk query / 32][pool slot] of 32-bit words
-//      by integer atomic OR in LDS (the same bits in any order).  One workgroup per 4 pool slots
-//      (16 tokens) walks the set bits of its 4 rows in increasing query
-//      order, recomputes P and dS for its tokens against each query, and
-//      accumulates dk and dv in registers; each chunk's sum is added to dk
-//      and dv in chunk order.
+//      attend it.  The selections are transposed into bitmaps [chunk query
+//      / 32][pool slot] of 32-bit words by integer atomic OR in LDS (the same
+//      bits in any order), those of all chunks at once when they fit the
+//      workspace.  One workgroup per 4 pool slots (16 tokens) walks, one
+//      chunk of queries at a time, the set bits of its 4 rows in increasing
+//      query order, recomputes P and dS for its tokens against each query,
+//      and accumulates dk and dv in registers; each chunk's sum is added to
+//      dk and dv in chunk order.  The workgroups take the groups of 4 slots
+//      most entries first, so that those resident together walk the chunk's
+//      queries together and find each query's rows in the L2.
 #include <math.h>
 
 #include "common.h"
