@@ -187,6 +187,20 @@ def test_workload_share_1m_sampled():
 
 
 @pytest.mark.slow
+def test_per_chunk_bitmaps_with_a_short_last_chunk():
+    # 1M keys and 33000 queries: the bitmaps of all chunks would exceed 1 GiB,
+    # so each chunk's is built in turn (8192-query chunks, the last of 232),
+    # and the pool groups are ordered from the last 8192 queries, which span
+    # two chunks
+    wl = inputs.custom("bwd_per_chunk", s_q=33000, s_k=1 << 20, q_pos0=(1 << 20) - 33000,
+                       h=16, d=128, dv=128, k_pools=512, n_tail=0)
+    nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(wl.s_q, wl.s_k, wl.h)
+    assert cq == 8192 and nbytes < (1 << 30)
+    ends = [r for c0 in range(0, wl.s_q, cq) for r in (c0, min(wl.s_q, c0 + cq) - 1)]
+    run_bwd(wl, rows=inputs.sample_rows(wl.s_q, 64, extra=ends))
+
+
+@pytest.mark.slow
 def test_workload_s128k_indexer_ids_sampled():
     # the backward as the benchmark runs it: ids from the indexer on the
     # workload's own keys (pools with large key norms are kept by many
