@@ -325,9 +325,9 @@ dsa_status check_attn_shape(int64_t s_q, int64_t s_k, int64_t q_pos0, int h, int
 }
 
 // Backward: queries per transposition chunk (a multiple of 64), and the
-// workspace: delta [s_q, h] fp32, then the chunk bitmap
-// [chunk / 32][ceil(s_k / 4)] words, then the pool groups' entry counts and
-// order.  Default chunk: max(1024, pool slots / 32), at most 16384.  Every
+// workspace: delta [s_q, h] fp32, then the bitmaps [chunk / 32][ceil(s_k / 4)]
+// words of every chunk when they fit kBwdBitmapAll (else of one chunk), then
+// the pool groups' entry counts and order.  Default chunk: max(1024, pool slots / 32), at most 16384.  Every
 // chunk pays a pass of the key-major kernel over all pool slots, so the chunk
 // grows with them; smaller chunks keep more of a chunk's query rows in the
 // L2s.  (Measured best of 256 .. 16384 with the pool groups taken most
