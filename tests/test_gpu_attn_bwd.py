@@ -110,6 +110,7 @@ SMALL = [
     # thousands of entries
     (9000, 9000, 0, 2, 64, 64, 512, 1, 9024),
     (2600, 2600, 0, 4, 128, 128, 200, 3, 0),   # about 1700 entries in the first groups
+    (3000, 3000, 0, 4, 64, 64, 700, 1, 0),     # rows of more than 512 ids (a second id pass)
 ]
 
 
