@@ -238,9 +238,10 @@ dsa_status dsa_sparse_attn_fwd(const void *q, const void *k, const void *v, cons
  * bitmap that transposes the queries' selections, chunk_q / 32 rows of
  * ceil(s_k / 4) 32-bit words (rounded up to a multiple of 4) per chunk, for
  * every chunk when that takes at most 1 GiB, else for one chunk (rounded up
- * to 256 bytes), then two arrays of one 32-bit word per group of 4
- * pools (ceil(ceil(s_k / 4) / 4) words each, rounded up to 256 bytes): the
- * groups' entry counts and the order the key-major pass takes them in.
+ * to 256 bytes), then two arrays of one 32-bit word per pool slot
+ * (ceil(s_k / 4) rounded up to a multiple of 4 words each, rounded up to 256
+ * bytes): the slots' entry counts and their order, which groups them in fours
+ * for the key-major pass.
  * chunk_q = 0
  * picks the default,
  * max(1024, ceil(s_k / 4) / 32) rounded up to a multiple of 64, at most 16384

@@ -327,7 +327,7 @@ dsa_status check_attn_shape(int64_t s_q, int64_t s_k, int64_t q_pos0, int h, int
 // Backward: queries per transposition chunk (a multiple of 64), and the
 // workspace: delta [s_q, h] fp32, then the bitmaps [chunk / 32][ceil(s_k / 4)]
 // words of every chunk when they fit kBwdBitmapAll (else of one chunk), then
-// the pool groups' entry counts and order.  Default chunk: max(1024, pool slots / 32), at most 16384.  Every
+// the pool slots' entry counts and order.  Default chunk: max(1024, pool slots / 32), at most 16384.  Every
 // chunk pays a pass of the key-major kernel over all pool slots, so the chunk
 // grows with them; smaller chunks keep more of a chunk's query rows in the
 // L2s.  (Measured best of 256 .. 16384 with the pool groups taken most
@@ -361,9 +361,9 @@ dsa_status bwd_layout(int64_t s_q, int64_t s_k, int h, int64_t chunk_q, int64_t*
     *chunk_used = chunk_q;
     *delta_bytes = round_up(s_q * h * 4, 256);
     // the bitmap (of every chunk when that fits kBwdBitmapAll), then the pool
-    // groups' entry counts and their order
+    // slots' entry counts and their order
     *bits_bytes = round_up(all <= kBwdBitmapAll ? all : bits, 256) +
-                  2 * round_up(round_up(slots, 4) / 4 * 4, 256);
+                  2 * round_up(round_up(slots, 4) * 4, 256);
     return DSA_OK;
 }
 
@@ -808,9 +808,9 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
     const int64_t nchunks = (s_q + cq - 1) / cq;
     const bool all_bits = chunk_bits * nchunks <= kBwdBitmapAll;
     const int64_t bitmap_bytes = round_up(all_bits ? chunk_bits * nchunks : chunk_bits, 256);
-    const int64_t group_bytes = round_up(a.stride / 4 * 4, 256);
-    a.group_counts = reinterpret_cast<uint32_t*>(ws + db + bitmap_bytes);
-    a.group_order = reinterpret_cast<int32_t*>(ws + db + bitmap_bytes + group_bytes);
+    const int64_t slot_bytes = round_up(a.stride * 4, 256);
+    a.slot_counts = reinterpret_cast<uint32_t*>(ws + db + bitmap_bytes);
+    a.slot_perm = reinterpret_cast<int32_t*>(ws + db + bitmap_bytes + slot_bytes);
     {
         Timed tm(K_BWD_DQ, s);
         hipError_t e = dsa::launch_attn_bwd_dq(a, s);
@@ -824,8 +824,9 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
         return all_bits ? bits0 + (r0 / 32) * a.stride : bits0;
     };
     {
-        // every chunk's bitmap when they fit (one launch); the order of the
-        // pool groups comes from the selections of the last chunk_q queries
+        // every chunk's bitmap when they fit (one launch); the pool groups
+        // (slots in fours, those kept by the most queries first) come from
+        // the selections of the last chunk_q queries
         // (from a word boundary: they see every pool the others see, and a
         // short last chunk does not make the order arbitrary), built on their
         // own when the bitmaps do not fit

@@ -160,15 +160,15 @@ struct AttnBwdArgs {
     float* delta;             // workspace: dout . out per query and head [s_q, h]
     uint32_t* bits;           // workspace: chunk bitmap [chunk / 32][stride] words
     int64_t stride;           // pool slots per bitmap word row: ceil(s_k / 4) rounded up to 4
-    uint32_t* group_counts;   // workspace: entries per pool group [stride / 4]
-    int32_t* group_order;     // workspace: pool groups, most entries first [stride / 4]
+    uint32_t* slot_counts;    // workspace: entries per pool slot [stride]
+    int32_t* slot_perm;       // workspace: pool slots, most entries first [stride]
 };
 // dq and delta (query-major pass).
 hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t stream);
 // ORs the selections of query rows [row0, row0 + rows) into a cleared bitmap.
 hipError_t launch_attn_bwd_bits(const AttnBwdArgs& a, int64_t row0, int rows, hipStream_t stream);
-// The order in which the key-major pass takes the pool groups: most entries
-// of the current bitmap (rows query rows) first.
+// The pool groups of the key-major pass: the pool slots ordered by their
+// entries in the current bitmap (rows query rows), most first, in fours.
 hipError_t launch_attn_bwd_order(const AttnBwdArgs& a, int rows, hipStream_t stream);
 // dk, dv of the chunk's queries: stored (accumulate = 0) or added.
 hipError_t launch_attn_bwd_dkv(const AttnBwdArgs& a, int64_t row0, int rows, int accumulate,

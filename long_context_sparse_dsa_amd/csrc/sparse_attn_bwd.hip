@@ -385,44 +385,83 @@ __global__ __launch_bounds__(256) void bwd_select_bits_kernel(
         *reinterpret_cast<u32x4*>(dst + e) = *reinterpret_cast<const u32x4*>(lw + e);
 }
 
-// Entries per pool group in nw word rows of the bitmap (32 queries each):
-// the set bits of the OR of the group's 4 slot rows.
-__global__ __launch_bounds__(256) void bwd_group_counts_kernel(const uint32_t* __restrict__ bits,
-                                                               int64_t stride, int nw,
-                                                               int64_t groups, uint32_t* counts) {
-    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (g >= groups) return;
+// Entries per pool slot in nw word rows of the bitmap (32 queries each).
+__global__ __launch_bounds__(256) void bwd_slot_counts_kernel(const uint32_t* __restrict__ bits,
+                                                              int64_t stride, int nw,
+                                                              uint32_t* counts) {
+    const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (s >= stride) return;
     uint32_t c = 0;
 #pragma unroll 8
-    for (int w = 0; w < nw; ++w) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(bits + (int64_t)w * stride + 4 * g);
-        c += __popc(x[0] | x[1] | x[2] | x[3]);
-    }
-    counts[g] = c;
+    for (int w = 0; w < nw; ++w) c += __popc(bits[(int64_t)w * stride + s]);
+    counts[s] = c;
 }
 
-// The pool groups in decreasing order of their entry counts, bucketed by the
-// highest set bit of the count (the order inside a bucket is arbitrary: each
-// group's gradients are formed by one workgroup whatever its position).
-__global__ __launch_bounds__(1024) void bwd_group_order_kernel(const uint32_t* __restrict__ counts,
-                                                               int64_t groups, int32_t* order) {
-    __shared__ uint32_t hist[33], off[33];
-    const int tid = threadIdx.x;
-    if (tid < 33) hist[tid] = 0u;
+// The pool slots in decreasing order of their entry counts (of `rows`
+// queries), in ORDER_BUCKETS equal bands of the count, and in increasing slot
+// order inside a band: a stable split, so the order is a function of the
+// counts alone.  One workgroup of 16 waves takes 1024 slots at a time; a
+// slot's place is its band's start, plus the band's slots of earlier tiles
+// and earlier waves of this tile, plus its rank among the lanes of its wave
+// in the same band (found by ballots, one per band present in the wave).
+constexpr int ORDER_BUCKETS = 64;
+
+__global__ __launch_bounds__(1024) void bwd_slot_order_kernel(const uint32_t* __restrict__ counts,
+                                                              int64_t stride, int rows,
+                                                              int32_t* perm) {
+    constexpr int NB = ORDER_BUCKETS;
+    static_assert(NB == 64, "one band per lane when a wave clears its counts");
+    __shared__ uint32_t base[NB];       // next place of each band
+    __shared__ uint32_t wcnt[16][NB];   // this tile: slots per wave and band, then their offsets
+    __shared__ uint32_t tile_n[NB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // band 0 holds the most entries
+    auto band = [&](uint32_t c) {
+        const uint64_t b = (uint64_t)c * NB / ((uint64_t)rows + 1);
+        return NB - 1 - (int)(b < NB ? b : NB - 1);
+    };
+    if (tid < NB) base[tid] = 0u;
     __syncthreads();
-    auto bucket = [](uint32_t c) { return c ? 32 - __builtin_clz(c) : 0; };
-    for (int64_t g = tid; g < groups; g += 1024) atomicAdd(&hist[bucket(counts[g])], 1u);
+    for (int64_t s = tid; s < stride; s += 1024) atomicAdd(&base[band(counts[s])], 1u);
     __syncthreads();
     if (tid == 0) {
         uint32_t sum = 0u;
-        for (int b = 32; b >= 0; --b) {
-            off[b] = sum;
-            sum += hist[b];
+        for (int b = 0; b < NB; ++b) {
+            const uint32_t n = base[b];
+            base[b] = sum;
+            sum += n;
         }
     }
-    __syncthreads();
-    for (int64_t g = tid; g < groups; g += 1024)
-        order[atomicAdd(&off[bucket(counts[g])], 1u)] = (int32_t)g;
+    for (int64_t t0 = 0; t0 < stride; t0 += 1024) {
+        wcnt[wave][lane] = 0u;
+        __syncthreads();
+        const int64_t s = t0 + tid;
+        const bool valid = s < stride;
+        const int b = valid ? band(counts[s]) : -1;
+        int rank = 0;
+        for (uint64_t todo = __ballot(valid); todo;) {
+            const int lead = __builtin_ctzll(todo);
+            const int lb = __builtin_amdgcn_readlane(b, lead);
+            const uint64_t m = __ballot(b == lb);
+            if (b == lb) rank = __popcll(m & ((1ull << lane) - 1ull));
+            if (lane == lead) wcnt[wave][lb] = (uint32_t)__popcll(m);
+            todo &= ~m;
+        }
+        __syncthreads();
+        if (tid < NB) {
+            uint32_t run = 0u;
+            for (int w = 0; w < 16; ++w) {
+                const uint32_t n = wcnt[w][tid];
+                wcnt[w][tid] = run;
+                run += n;
+            }
+            tile_n[tid] = run;
+        }
+        __syncthreads();
+        if (valid) perm[base[b] + wcnt[wave][b] + rank] = (int32_t)s;
+        __syncthreads();
+        if (tid < NB) base[tid] += tile_n[tid];
+    }
 }
 
 // ---------------------------------------------------------------- pass 2: dk, dv
@@ -434,7 +473,7 @@ struct DkvK {
     const uint16_t* dout;
     const float* lse;
     const float* delta;
-    const int32_t* order;   // pool groups in the order workgroups take them
+    const int32_t* perm;    // [stride] pool slots; group g holds perm[4 g .. 4 g + 3]
     const uint32_t* bits;   // [chunk / 32][stride]
     int64_t stride;
     int64_t s_k, q_pos0, row0;
@@ -475,9 +514,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int col = lane & 15, grp = lane >> 4;
-    const int64_t g = a.order[blockIdx.x];
-    const int64_t tok0 = 16 * g;
+    // the group's 4 pool slots (slots >= a.slots pad the order and hold no
+    // tokens); its token 4 j + r is token r of slot j
+    int64_t slot[4];
+    int64_t tmin = INT64_MAX;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        slot[j] = a.perm[4 * (int64_t)blockIdx.x + j];
+        if (slot[j] < a.slots && 4 * slot[j] < tmin) tmin = 4 * slot[j];
+    }
     const int64_t t_last = a.q_pos0 + a.row0 + a.rows - 1;
+    // row of token 4 j + r (r < 4) in k, v, dk and dv; -1 past s_k
+    auto token_row = [&](int tok) -> int64_t {
+        const int j = tok >> 2;
+        const int64_t sj = j == 0 ? slot[0] : j == 1 ? slot[1] : j == 2 ? slot[2] : slot[3];
+        const int64_t t = 4 * sj + (tok & 3);
+        return sj < a.slots && t < a.s_k ? t : -1;
+    };
+    bool found = false;     // this wave had an entry
     uint16_t* st = stage_all + wave * STAGE;
     uint16_t* sq[2] = {st, st + QT};
     uint16_t* so[2] = {st + 2 * QT, st + 2 * QT + OT};
@@ -489,30 +543,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
 #pragma unroll
     for (int m = 0; m < MV; ++m) dva[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // tokens tok0 .. tok0 + 15 are attended only by queries after them
-    if (tok0 < t_last) {
+    // a token is attended only by queries after it
+    if (tmin < t_last) {
         // rows of heads >= h stay zero in LDS (never written below)
         if (a.h < 16) {
             for (int e = lane * 8; e < STAGE; e += 64 * 8)
                 *reinterpret_cast<u32x4*>(st + e) = u32x4{0u, 0u, 0u, 0u};
         }
-        // B operands of S and dP: lane (col = token, grp) holds key / value
-        // row tok0 + col, elements 32 s + 8 grp .. +8 (zero past s_k)
-        bf16x8 kf[KS], vf[VS];
-        const bool tok_ok = tok0 + col < a.s_k;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (tok_ok) x = ldg16(a.k + (tok0 + col) * D + 32 * s + 8 * grp);
-            kf[s] = as_bf16x8(x);
-        }
-#pragma unroll
-        for (int s = 0; s < VS; ++s) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (tok_ok) x = ldg16(a.v + (tok0 + col) * DV + 32 * s + 8 * grp);
-            vf[s] = as_bf16x8(x);
-        }
-
         // ---- entry scan.  Windows of 64 bitmap words (2048 chunk queries):
         // lane L holds word wbase + L of the 4 rows; a wave-wide prefix sum of
         // the per-word entry counts gives every entry its global index, and
@@ -523,19 +560,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
         uint32_t slot_tokens = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t left = a.s_k - 4 * (4 * g + j);
+            const int64_t left = slot[j] < a.slots ? a.s_k - 4 * slot[j] : 0;
             const uint32_t m = left >= 4 ? 0xFu : (left > 0 ? (1u << left) - 1u : 0u);
             slot_tokens |= m << (4 * j);
         }
         const int nw = (a.rows + 31) / 32;
-        // the 4 slots' words of one word column are one 16-byte piece (slots
-        // past the last pool read as zero: the stride is padded to 4)
-        const uint32_t* bcol = a.bits + 4 * g;
+        // the 4 slots' words of word row wb + lane (the padding slots'
+        // columns hold zeros)
         auto load_words = [&](int wb, uint32_t (&dst)[4]) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (wb + lane < nw) x = ldg16(bcol + (int64_t)(wb + lane) * a.stride);
+            const uint32_t* brow = a.bits + (int64_t)(wb + lane) * a.stride;
+            const bool ok = wb + lane < nw;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dst[j] = x[j];
+            for (int j = 0; j < 4; ++j) dst[j] = ok ? brow[slot[j]] : 0u;
         };
         uint32_t ww[4], pw[4];
         load_words(0, pw);
@@ -590,14 +626,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
             const uint32_t spread = (b4 & 1u) | ((b4 & 2u) << 3) | ((b4 & 4u) << 6) | ((b4 & 8u) << 9);
             mask = (spread * 0xFu) & slot_tokens;
             const int64_t t = a.q_pos0 + a.row0 + row;
-            if ((t >> 4) == g) {
-                // the query's own pool is in this group (its bit comes from
-                // the tail only): the tail tokens before t
-                const int j = (int)((t >> 2) & 3);
-                const int r = (int)(t & 3);
-                const int u0 = max(0, r - a.n_tail);
-                const uint32_t tail = ((1u << r) - 1u) & ~((1u << u0) - 1u);
-                mask &= ~((~tail & 0xFu) << (4 * j));
+            const int64_t own = t >> 2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (slot[j] == own) {
+                    // the query's own pool is in this group (its bit comes
+                    // from the tail only): the tail tokens before t
+                    const int r = (int)(t & 3);
+                    const int u0 = max(0, r - a.n_tail);
+                    const uint32_t tail = ((1u << r) - 1u) & ~((1u << u0) - 1u);
+                    mask &= ~((~tail & 0xFu) << (4 * j));
+                }
             }
             return true;
         };
@@ -705,6 +744,25 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
 
         Pair nxt;
         bool have = fetch(nxt);
+        found = have;
+        // B operands of S and dP: lane (col = token, grp) holds key / value
+        // row of token col, elements 32 s + 8 grp .. +8 (zero past s_k)
+        bf16x8 kf[KS], vf[VS];
+        if (have) {
+            const int64_t tr = token_row(col);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                u32x4 x = {0u, 0u, 0u, 0u};
+                if (tr >= 0) x = ldg16(a.k + tr * D + 32 * s + 8 * grp);
+                kf[s] = as_bf16x8(x);
+            }
+#pragma unroll
+            for (int s = 0; s < VS; ++s) {
+                u32x4 x = {0u, 0u, 0u, 0u};
+                if (tr >= 0) x = ldg16(a.v + tr * DV + 32 * s + 8 * grp);
+                vf[s] = as_bf16x8(x);
+            }
+        }
         while (have) {
             stash_pair(nxt);
             uint32_t mask[2] = {nxt.mask[0], nxt.mask[1]};
@@ -757,12 +815,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
                 dka[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(df, as_bf16x8(qw), dka[m], 0, 0, 0);
             }
         }
-    } else if (a.accumulate) {
-        return;  // nothing to add (uniform over the workgroup)
     }
+    // a group without entries in this chunk has nothing to add
+    if (!__syncthreads_or(found ? 1 : 0) && a.accumulate) return;
 
     // ---- sum of the 4 waves in wave order, then store or add
-    __syncthreads();
     float* red = reinterpret_cast<float*>(stage_all);
     // accumulator i of lane (col, grp): token 4 grp + i, column 16 m + col
 #pragma unroll
@@ -777,11 +834,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(DkvK a) {
     constexpr int C4 = (D + DV) / 4;
     for (int e = threadIdx.x; e < 16 * C4; e += 256) {
         const int tok = e / C4, c = 4 * (e % C4);
-        if (tok0 + tok >= a.s_k) continue;
+        const int64_t tr = token_row(tok);
+        if (tr < 0) continue;
         f32x4 s = *reinterpret_cast<const f32x4*>(red + tok * RED + c);
 #pragma unroll
         for (int wv = 1; wv < 4; ++wv) s += *reinterpret_cast<const f32x4*>(red + (wv * 16 + tok) * RED + c);
-        float* dst = c < D ? a.dk + (tok0 + tok) * D + c : a.dv + (tok0 + tok) * DV + (c - D);
+        float* dst = c < D ? a.dk + tr * D + c : a.dv + tr * DV + (c - D);
         if (c < D) s *= a.scale;
         if (a.accumulate) s += *reinterpret_cast<const f32x4*>(dst);
         *reinterpret_cast<f32x4*>(dst) = s;
@@ -855,11 +913,10 @@ hipError_t launch_attn_bwd_bits(const AttnBwdArgs& a, int64_t row0, int rows, hi
 }
 
 hipError_t launch_attn_bwd_order(const AttnBwdArgs& a, int rows, hipStream_t stream) {
-    const int64_t groups = a.stride / 4;
-    if (groups <= 0 || rows <= 0) return hipSuccess;
-    bwd_group_counts_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, stream>>>(
-        a.bits, a.stride, (rows + 31) / 32, groups, a.group_counts);
-    bwd_group_order_kernel<<<1, 1024, 0, stream>>>(a.group_counts, groups, a.group_order);
+    if (a.stride <= 0 || rows <= 0) return hipSuccess;
+    bwd_slot_counts_kernel<<<(unsigned)((a.stride + 255) / 256), 256, 0, stream>>>(
+        a.bits, a.stride, (rows + 31) / 32, a.slot_counts);
+    bwd_slot_order_kernel<<<1, 1024, 0, stream>>>(a.slot_counts, a.stride, rows, a.slot_perm);
     return hipGetLastError();
 }
 
@@ -874,7 +931,7 @@ hipError_t launch_attn_bwd_dkv(const AttnBwdArgs& a, int64_t row0, int rows, int
     k.dout = a.dout;
     k.lse = a.lse;
     k.delta = a.delta;
-    k.order = a.group_order;
+    k.perm = a.slot_perm;
     k.bits = a.bits;
     k.stride = a.stride;
     k.s_k = a.s_k;

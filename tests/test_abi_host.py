@@ -231,23 +231,23 @@ def test_sparse_attn_bwd_workspace_layout(lib):
     # delta [s_q, h] fp32 rounded to 256 B, then the bitmap: chunk / 32 rows
     # of ceil(s_k / 4) words, rounded up to 4, per chunk, for every chunk
     # when that fits 1 GiB, else for one (rounded to 256 B), then the pool
-    # groups' counts and order, one word per group of 4 slots each, rounded
+    # slots' counts and order, one word per slot (the stride) each, rounded
     # to 256 B
     # default chunk: max(1024, pool slots / 32), at most 16384 and s_q
     nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(131072, 131072, 16)
     assert cq == 1024
-    assert nbytes == 131072 * 16 * 4 + 128 * (32768 * 32 * 4) + 2 * 8192 * 4
+    assert nbytes == 131072 * 16 * 4 + 128 * (32768 * 32 * 4) + 2 * 32768 * 4
     # one GPU's share of 1M keys: every chunk's bitmap would take 4 GiB, so
     # one chunk's (8192 queries)
     nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(131072, 1 << 20, 16)
     assert cq == 8192
-    assert nbytes == 131072 * 16 * 4 + 262144 * 256 * 4 + 2 * 65536 * 4
+    assert nbytes == 131072 * 16 * 4 + 262144 * 256 * 4 + 2 * 262144 * 4
     _, cq = dsa.dsa_sparse_attn_bwd_workspace_size(131072, 1 << 22, 16)
     assert cq == 16384
     _, cq = dsa.dsa_sparse_attn_bwd_workspace_size(1000, 1 << 20, 16)
     assert cq == 1024
     nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(100, 203, 5, 64)
-    # 51 slots -> stride 52, 13 groups; two chunks' bitmaps of 2 word rows
+    # 51 slots -> stride 52; two chunks' bitmaps of 2 word rows
     assert cq == 64 and nbytes == 2048 + 1024 + 2 * 256
     nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(100, 203, 5)
     assert cq == 128
