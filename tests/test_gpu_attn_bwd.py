@@ -55,6 +55,24 @@ def stratified_idx(s_q, q_pos0, n_pools, k, seed, block=16384):
     return out
 
 
+def skewed_idx(s_q, q_pos0, n_pools, k, seed, sigma=2.0):
+    """Kept-pool rows [s_q, k] int32 where a few pools are kept by most
+    queries: each query draws k distinct eligible pools with probability
+    proportional to a per-pool log-normal weight (sigma), sorted ascending;
+    every eligible pool (then -1) when a query has at most k."""
+    rng = np.random.default_rng(seed)
+    weight = np.exp(sigma * rng.standard_normal(n_pools))
+    out = np.full((s_q, k), -1, dtype=np.int32)
+    for r in range(s_q):
+        n = min((q_pos0 + r) // 4, n_pools)
+        if n <= k:
+            out[r, :n] = np.arange(n)
+            continue
+        p = weight[:n] / weight[:n].sum()
+        out[r] = np.sort(rng.choice(n, size=k, replace=False, p=p))
+    return out
+
+
 def run_bwd(wl, rows=None, chunk_q=0, seed=None, idx=None, check=True):
     seed = wl.seed if seed is None else seed
     _say(f"[bwd] {wl.name} s_q={wl.s_q} s_k={wl.s_k} q_pos0={wl.q_pos0} H={wl.h} D={wl.d} "
@@ -119,6 +137,21 @@ def test_small_all_rows(s_q, s_k, q_pos0, h, d, dv, k_pools, n_tail, chunk_q):
     wl = inputs.custom("bwd_small", s_q=s_q, s_k=s_k, q_pos0=q_pos0, h=h, d=d, dv=dv,
                        k_pools=k_pools, n_tail=n_tail)
     run_bwd(wl, chunk_q=chunk_q, seed=s_q + h)
+
+
+@pytest.mark.parametrize("chunk_q", [0, 256])
+def test_popular_pools_all_rows(chunk_q):
+    # the key-major pass groups the pool slots by how many queries of the
+    # last chunk keep them: with skewed selections its groups hold slots from
+    # all over the sequence (also the query's own pool, whose tail tokens are
+    # attended, and the padding slots of 2003 keys = 500 pools and 3 tokens,
+    # 501 slots)
+    wl = inputs.custom("bwd_popular", s_q=2000, s_k=2003, h=16, d=128, dv=128, k_pools=48,
+                       n_tail=3)
+    idx = skewed_idx(wl.s_q, wl.q_pos0, wl.n_pools, wl.k_pools, seed=77)
+    kept = np.bincount(idx[idx >= 0], minlength=wl.n_pools)
+    assert kept.max() > wl.s_q // 2, "the draw should make some pools popular"
+    run_bwd(wl, chunk_q=chunk_q, seed=78, idx=idx)
 
 
 def test_deterministic_bitwise():
