@@ -18,12 +18,16 @@
 //      attend it.  The selections are transposed into bitmaps [chunk query
 //      / 32][pool slot] of 32-bit words by integer atomic OR in LDS (the same
 //      bits in any order), those of all chunks at once when they fit the
-//      workspace.  One workgroup per 4 pool slots (16 tokens) walks, one
-//      chunk of queries at a time, the set bits of its 4 rows in increasing
-//      query order, recomputes P and dS for its tokens against each query,
-//      and accumulates dk and dv in registers; each chunk's sum is added to
-//      dk and dv in chunk order.  The workgroups take the groups of 4 slots
-//      most entries first, so that those resident together walk the chunk's
+//      workspace.  The pool slots are ordered by the number of queries of
+//      the last chunk that keep them, most first, and taken 4 at a time: a
+//      query that keeps one often-kept pool tends to keep others, so a
+//      group's visits serve more pools than 4 neighbouring slots would.  One
+//      workgroup per group (16 tokens) walks, one chunk of queries at a
+//      time, the set bits of its 4 rows in increasing query order,
+//      recomputes P and dS for its tokens against each query, and
+//      accumulates dk and dv in registers; each chunk's sum is added to dk
+//      and dv in chunk order.  The workgroups take the groups in that order,
+//      so that those resident together have similar work, walk the chunk's
 //      queries together and find each query's rows in the L2.
 #include <math.h>
 
