@@ -244,7 +244,8 @@ dsa_status dsa_sparse_attn_fwd(const void *q, const void *k, const void *v, cons
  * for the key-major pass.
  * chunk_q = 0
  * picks the default,
- * max(1024, ceil(s_k / 4) / 32) rounded up to a multiple of 64, at most 16384
+ * max(1024, min(1536, 3 P / 32), P / 32) with P = ceil(s_k / 4), rounded up to a
+ * multiple of 64, at most 16384
  * and at most s_q rounded up to 64, returned through *chunk_q_used when that
  * pointer is non-NULL; otherwise a multiple of 64 up to 65536 whose bitmap
  * stays within 2 GiB.  Pure host computation.

@@ -327,12 +327,15 @@ dsa_status check_attn_shape(int64_t s_q, int64_t s_k, int64_t q_pos0, int h, int
 // Backward: queries per transposition chunk (a multiple of 64), and the
 // workspace: delta [s_q, h] fp32, then the bitmaps [chunk / 32][ceil(s_k / 4)]
 // words of every chunk when they fit kBwdBitmapAll (else of one chunk), then
-// the pool slots' entry counts and order.  Default chunk: max(1024, pool slots / 32), at most 16384.  Every
-// chunk pays a pass of the key-major kernel over all pool slots, so the chunk
-// grows with them; smaller chunks keep more of a chunk's query rows in the
-// L2s.  (Measured best of 256 .. 16384 with the pool groups taken most
-// entries first: 1024 at 8K, 16K and 32K slots, 8192 to 16384 at 262144.)
+// the pool slots' entry counts and order.  Default chunk: max(1024,
+// min(1536, 3 slots / 32), slots / 32), at most 16384.  Every chunk pays a
+// pass of the key-major kernel over all pool slots, so the chunk grows with
+// them; smaller chunks keep more of a chunk's query rows in the L2s.
+// (Measured best of 768 .. 2048 with the slots grouped by count: 1024 at 8K
+// slots, 1536 at 16K and 32K; of 2048 .. 16384 before: 8192 to 16384 at
+// 262144.)
 constexpr int64_t kBwdChunkMin = 1024;
+constexpr int64_t kBwdChunkMid = 1536;
 // The bitmaps of all chunks are built by one launch when together they take
 // at most this many bytes (else one chunk's bitmap at a time).
 constexpr int64_t kBwdBitmapAll = int64_t(1) << 30;
@@ -344,7 +347,10 @@ dsa_status bwd_layout(int64_t s_q, int64_t s_k, int h, int64_t chunk_q, int64_t*
     if (chunk_q < 0) return fail(DSA_ERR_INVALID_ARG, "chunk_q %lld < 0", (long long)chunk_q);
     const int64_t slots = (s_k + 3) / 4;
     if (chunk_q == 0) {
-        int64_t c = round_up(slots / 32 > kBwdChunkMin ? slots / 32 : kBwdChunkMin, 64);
+        int64_t c = 3 * slots / 32 < kBwdChunkMid ? 3 * slots / 32 : kBwdChunkMid;
+        if (c < kBwdChunkMin) c = kBwdChunkMin;
+        if (slots / 32 > c) c = slots / 32;
+        c = round_up(c, 64);
         if (c > kBwdChunkMax) c = kBwdChunkMax;
         const int64_t all = round_up(s_q > 0 ? s_q : 1, 64);
         chunk_q = c < all ? c : all;

@@ -233,10 +233,15 @@ def test_sparse_attn_bwd_workspace_layout(lib):
     # when that fits 1 GiB, else for one (rounded to 256 B), then the pool
     # slots' counts and order, one word per slot (the stride) each, rounded
     # to 256 B
-    # default chunk: max(1024, pool slots / 32), at most 16384 and s_q
+    # default chunk: max(1024, min(1536, 3 slots / 32), slots / 32), at most
+    # 16384 and s_q (86 chunks of 1536 queries at 128k)
     nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(131072, 131072, 16)
+    assert cq == 1536
+    assert nbytes == 131072 * 16 * 4 + 86 * (32768 * 48 * 4) + 2 * 32768 * 4
+    _, cq = dsa.dsa_sparse_attn_bwd_workspace_size(65536, 65536, 16)
+    assert cq == 1536
+    _, cq = dsa.dsa_sparse_attn_bwd_workspace_size(32768, 32768, 16)
     assert cq == 1024
-    assert nbytes == 131072 * 16 * 4 + 128 * (32768 * 32 * 4) + 2 * 32768 * 4
     # one GPU's share of 1M keys: every chunk's bitmap would take 4 GiB, so
     # one chunk's (8192 queries)
     nbytes, cq = dsa.dsa_sparse_attn_bwd_workspace_size(131072, 1 << 20, 16)
